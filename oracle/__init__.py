@@ -1,0 +1,141 @@
+"""fp64 CPU oracle for channels-last GroupNorm(+SiLU) -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports it and never falls back to it.
+
+The arithmetic lives in ``gn_oracle.c`` (plain C, fp64, two-pass); this module
+only marshals numpy arrays through ctypes.  The definition it follows is the
+channels-last GroupNorm with optional SiLU of "FLUX.2 VAE decoder fast path
+behind quality=high", Modifications section 1 "Kernel": per-(batch, group)
+statistics over (N, L, C) rows with C innermost, affine transform, optional
+SiLU.
+
+Parity status of each function (what pins it, see ``tests/test_oracle_pins.py``):
+  * ``group_stats`` -- pinned: exact rational brute force, library
+    GroupNorm/LayerNorm/InstanceNorm, invariants.
+  * ``gn_silu`` -- pinned: exact-arithmetic brute force (Fraction/Decimal),
+    torch's fp64 CPU ``group_norm`` + ``silu``, LayerNorm (G=1) and
+    InstanceNorm (G=C) identities, closed-form cases, invariants.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgnoracle.so")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _as_bits(x_bits):
+    x = np.ascontiguousarray(x_bits)
+    if x.dtype != np.uint16:
+        raise TypeError("oracle input must be bf16 bit patterns (uint16)")
+    return x
+
+
+class Oracle:
+    """ctypes front end of one build of ``gn_oracle.c``."""
+
+    def __init__(self, lib_path):
+        lib = ctypes.CDLL(lib_path)
+        i64 = ctypes.c_int64
+        vp = ctypes.c_void_p
+        lib.gno_group_stats.argtypes = [vp, i64, i64, i64, i64, vp, vp]
+        lib.gno_group_stats.restype = ctypes.c_int
+        lib.gno_gn_silu.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_double,
+                                    ctypes.c_int, vp, vp, vp, vp]
+        lib.gno_gn_silu.restype = ctypes.c_int
+        lib.gno_max_threads.argtypes = []
+        lib.gno_max_threads.restype = ctypes.c_int
+        lib.gno_set_threads.argtypes = [ctypes.c_int]
+        lib.gno_set_threads.restype = None
+        self.lib = lib
+        self.path = lib_path
+
+    def max_threads(self) -> int:
+        return int(self.lib.gno_max_threads())
+
+    def set_threads(self, n: int) -> None:
+        self.lib.gno_set_threads(int(n))
+
+    def group_stats(self, x_bits, N, L, C, G):
+        """fp64 mean and biased variance per (n, g); arrays of shape (N, G)."""
+        x = _as_bits(x_bits)
+        if x.size != N * L * C:
+            raise ValueError("x has %d elements, expected N*L*C = %d" % (x.size, N * L * C))
+        mean = np.empty(max(N * G, 1), np.float64)
+        var = np.empty(max(N * G, 1), np.float64)
+        rc = self.lib.gno_group_stats(_ptr(x), N, L, C, G, _ptr(mean), _ptr(var))
+        if rc != 0:
+            raise ValueError("oracle rejected shape N=%d L=%d C=%d G=%d" % (N, L, C, G))
+        return mean[: N * G].reshape(N, G), var[: N * G].reshape(N, G)
+
+    def gn_silu(self, x_bits, gamma, beta, N, L, C, G, eps, apply_silu,
+                out_dtype=np.float64, return_stats=False):
+        """GroupNorm(+SiLU) of dense [N, L, C] bf16 bits, computed in fp64.
+
+        ``out_dtype`` float64 returns the fp64 result; float32 returns it
+        rounded once to fp32 (for the largest shapes, to halve host memory).
+        gamma/beta are float32 arrays of length C, or None (ones / zeros).
+        """
+        x = _as_bits(x_bits)
+        if x.size != N * L * C:
+            raise ValueError("x has %d elements, expected N*L*C = %d" % (x.size, N * L * C))
+        g = None if gamma is None else np.ascontiguousarray(gamma, np.float32)
+        b = None if beta is None else np.ascontiguousarray(beta, np.float32)
+        for name, a in (("gamma", g), ("beta", b)):
+            if a is not None and a.size != C:
+                raise ValueError("%s must have C=%d entries" % (name, C))
+        out = np.empty(max(N * L * C, 1), np.dtype(out_dtype))
+        mean = np.empty(max(N * G, 1), np.float64)
+        var = np.empty(max(N * G, 1), np.float64)
+        o64 = out if out.dtype == np.float64 else None
+        o32 = out if out.dtype == np.float32 else None
+        if o64 is None and o32 is None:
+            raise TypeError("out_dtype must be float64 or float32")
+        rc = self.lib.gno_gn_silu(_ptr(x), _ptr(g), _ptr(b), N, L, C, G, float(eps),
+                                  1 if apply_silu else 0, _ptr(o64), _ptr(o32),
+                                  _ptr(mean), _ptr(var))
+        if rc != 0:
+            raise ValueError("oracle rejected arguments N=%d L=%d C=%d G=%d eps=%r"
+                             % (N, L, C, G, eps))
+        y = out[: N * L * C].reshape(N, L, C)
+        if return_stats:
+            return y, mean[: N * G].reshape(N, G), var[: N * G].reshape(N, G)
+        return y
+
+
+_default = None
+
+
+def _get():
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        _default = Oracle(_LIB_PATH)
+    return _default
+
+
+def max_threads() -> int:
+    return _get().max_threads()
+
+
+def set_threads(n: int) -> None:
+    _get().set_threads(n)
+
+
+def group_stats(x_bits, N, L, C, G):
+    return _get().group_stats(x_bits, N, L, C, G)
+
+
+def gn_silu(x_bits, gamma, beta, N, L, C, G, eps, apply_silu, out_dtype=np.float64,
+            return_stats=False):
+    return _get().gn_silu(x_bits, gamma, beta, N, L, C, G, eps, apply_silu,
+                          out_dtype=out_dtype, return_stats=return_stats)

@@ -1,0 +1,150 @@
+/*
+ * gn_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, fp64 CPU implementation of GroupNorm with optional SiLU over
+ * dense channels-last activations.  Only the test suite, the smoke check and
+ * the benchmark's CPU-baseline leg may load it; the product path never does.
+ * It shares no code with the HIP library.
+ *
+ * What it computes (source: "FLUX.2 VAE decoder fast path behind
+ * quality=high", Modifications section 1 "Kernel": channels-last GroupNorm
+ * over (N, L, C) rows with C innermost, per-(batch, group) mean/rstd, the
+ * affine transform, then an optional SiLU; the Motivation section names the
+ * op pair as the GroupNorm -> SiLU chains of the diffusers VAE decoder).
+ * The plain definition, written out:
+ *
+ *   x  has N samples of L rows of C channels, element (n, l, c) at offset
+ *      (n*L + l)*C + c; C is split into G contiguous groups of Cg = C/G
+ *      channels, channel c belongs to group c / Cg.
+ *   For each (n, g), over the M = L*Cg elements of the group:
+ *      mu    = (1/M) * sum x                      (first pass)
+ *      var   = (1/M) * sum (x - mu)^2             (second pass, biased)
+ *      rstd  = 1 / sqrt(var + eps)
+ *   For each element:
+ *      t = gamma[c] * (x - mu) * rstd + beta[c]
+ *      y = apply_silu ? t / (1 + exp(-t)) : t      (SiLU(t) = t * sigmoid(t))
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ * the variance is the biased (divide by M) one; eps sits inside the square
+ * root; groups are contiguous channel blocks; SiLU comes after the affine;
+ * a NULL gamma means all ones and a NULL beta all zeros.
+ *
+ * All arithmetic is IEEE fp64 in the order written above: no blocking, no
+ * fused passes, no reassociation.  OpenMP only splits independent groups
+ * (statistics) and independent rows (elementwise output) across threads; the
+ * order of every sum is the plain sequential one.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* bf16 is the upper half of an IEEE binary32; widening is exact. */
+static double bf16_bits_to_double(uint16_t bits) {
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static int check_shape(int64_t N, int64_t L, int64_t C, int64_t G) {
+    if (N < 0 || L < 0 || C <= 0 || G <= 0 || C % G != 0) return -1;
+    return 0;
+}
+
+int gno_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void gno_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* Per-(n, g) mean and biased variance, two passes in fp64.
+ * mean_out, var_out: N*G doubles, index n*G + g.  Returns 0, or -1 on a bad
+ * shape. */
+int gno_group_stats(const uint16_t *x, int64_t N, int64_t L, int64_t C, int64_t G,
+                    double *mean_out, double *var_out) {
+    if (check_shape(N, L, C, G)) return -1;
+    const int64_t Cg = C / G;
+    const int64_t M = L * Cg;
+    int64_t ng;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (ng = 0; ng < N * G; ++ng) {
+        const int64_t n = ng / G, g = ng % G;
+        const uint16_t *xs = x + n * L * C + g * Cg;
+        double sum = 0.0;
+        for (int64_t l = 0; l < L; ++l)
+            for (int64_t j = 0; j < Cg; ++j) sum += bf16_bits_to_double(xs[l * C + j]);
+        const double mu = (M > 0) ? sum / (double)M : 0.0;
+        double ss = 0.0;
+        for (int64_t l = 0; l < L; ++l)
+            for (int64_t j = 0; j < Cg; ++j) {
+                const double d = bf16_bits_to_double(xs[l * C + j]) - mu;
+                ss += d * d;
+            }
+        mean_out[ng] = mu;
+        var_out[ng] = (M > 0) ? ss / (double)M : 0.0;
+    }
+    return 0;
+}
+
+/* y = SiLU(t) = t * sigmoid(t), written as t / (1 + exp(-t)).  For t far
+ * below zero exp(-t) overflows to +inf and the quotient is -0, the limit. */
+static double silu(double t) { return t / (1.0 + exp(-t)); }
+
+/* Full GroupNorm(+SiLU).  Exactly one of out64 / out32 is non-NULL; out32
+ * receives the fp64 result rounded once to fp32 (storage for the large
+ * shapes only).  mean_out/var_out (may be NULL) receive the statistics.
+ * Returns 0, or -1 on a bad argument. */
+int gno_gn_silu(const uint16_t *x, const float *gamma, const float *beta, int64_t N,
+                int64_t L, int64_t C, int64_t G, double eps, int apply_silu,
+                double *out64, float *out32, double *mean_out, double *var_out) {
+    if (check_shape(N, L, C, G)) return -1;
+    if ((out64 == NULL) == (out32 == NULL)) return -1;
+    if (!(eps >= 0.0)) return -1;
+    const int64_t Cg = C / G;
+    double *mean = mean_out, *var = var_out;
+    /* statistics storage: caller-provided or a small heap block */
+    double *heap = NULL;
+    if (mean == NULL || var == NULL) {
+        const size_t ng = (size_t)(N * G > 0 ? N * G : 1);
+        heap = (double *)malloc(sizeof(double) * 2 * ng);
+        if (heap == NULL) return -1;
+        mean = heap;
+        var = heap + ng;
+    }
+    gno_group_stats(x, N, L, C, G, mean, var);
+    int64_t row;
+#pragma omp parallel for schedule(static)
+    for (row = 0; row < N * L; ++row) {
+        const int64_t n = row / L;
+        for (int64_t c = 0; c < C; ++c) {
+            const int64_t g = c / Cg;
+            const double mu = mean[n * G + g];
+            const double rstd = 1.0 / sqrt(var[n * G + g] + eps);
+            const double ga = gamma ? (double)gamma[c] : 1.0;
+            const double be = beta ? (double)beta[c] : 0.0;
+            const double xv = bf16_bits_to_double(x[row * C + c]);
+            const double t = ga * ((xv - mu) * rstd) + be;
+            const double yv = apply_silu ? silu(t) : t;
+            if (out64)
+                out64[row * C + c] = yv;
+            else
+                out32[row * C + c] = (float)yv;
+        }
+    }
+    free(heap);
+    return 0;
+}

@@ -1,0 +1,82 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a copy of the oracle's C source (on the CPU,
+in a temporary directory), compiles it with the same flags, and runs a
+battery of the pins from ``test_oracle_pins`` against it.  At least one pin
+must fail for every mutant, and none may fail for the unmodified source.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle as oracle_pkg
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle_pkg.__file__), "gn_oracle.c")
+
+MUTANTS = {
+    "unbiased variance": ("var_out[ng] = (M > 0) ? ss / (double)M : 0.0;",
+                          "var_out[ng] = (M > 1) ? ss / (double)(M - 1) : 0.0;"),
+    "eps outside the square root": ("1.0 / sqrt(var[n * G + g] + eps)",
+                                    "1.0 / (sqrt(var[n * G + g]) + eps)"),
+    "beta dropped": ("((xv - mu) * rstd) + be;", "((xv - mu) * rstd);"),
+    "gamma dropped": ("const double t = ga * ((xv - mu) * rstd) + be;",
+                      "const double t = ((xv - mu) * rstd) + be;"),
+    "mean added instead of subtracted": ("(xv - mu)", "(xv + mu)"),
+    "channel->group map by modulo": ("const int64_t g = c / Cg;", "const int64_t g = c % G;"),
+    "SiLU with the wrong sign": ("t / (1.0 + exp(-t))", "t / (1.0 + exp(t))"),
+    "group offset dropped in stats": ("x + n * L * C + g * Cg;", "x + n * L * C + g;"),
+    "row stride Cg instead of C in the mean": (
+        "sum += bf16_bits_to_double(xs[l * C + j]);",
+        "sum += bf16_bits_to_double(xs[l * Cg + j]);"),
+    "second moment not centred": (
+        "const double d = bf16_bits_to_double(xs[l * C + j]) - mu;",
+        "const double d = bf16_bits_to_double(xs[l * C + j]);"),
+    "sample index ignored": ("const int64_t n = row / L;", "const int64_t n = 0;"),
+}
+
+
+def battery():
+    return [
+        ("bruteforce", lambda o: pins.test_exact_bruteforce_stats_and_output(o, 2, 2, 4)),
+        ("torch_gn", lambda o: pins.test_torch_group_norm_fp64(o, 2, 37, 64, 8, True)),
+        ("torch_gn_nosilu", lambda o: pins.test_torch_group_norm_fp64(o, 1, 64, 128, 32, False)),
+        ("closed_var_eps", pins.test_closed_form_biased_variance_and_eps_inside_sqrt),
+        ("closed_affine_silu", pins.test_closed_form_affine_and_silu),
+        ("moments", lambda o: pins.test_normalised_moments(o, 8.0)),
+        ("constant_group", pins.test_constant_group_gives_beta),
+    ]
+
+
+def build_variant(tmp_path, name, source):
+    c = tmp_path / (name + ".c")
+    so = tmp_path / (name + ".so")
+    c.write_text(source)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+                    "-ffp-contract=off", "-o", str(so), str(c), "-lm"], check=True)
+    return oracle_pkg.Oracle(str(so))
+
+
+def failing_pins(o):
+    failed = []
+    for name, fn in battery():
+        try:
+            fn(o)
+        except Exception:  # an assertion, or a shape the mutant gets wrong
+            failed.append(name)
+    return failed
+
+
+def test_unmodified_source_passes_battery(tmp_path):
+    o = build_variant(tmp_path, "original", open(SRC).read())
+    assert failing_pins(o) == []
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, mutant):
+    old, new = MUTANTS[mutant]
+    src = open(SRC).read()
+    assert old in src, "mutation target no longer in the oracle source: %r" % old
+    o = build_variant(tmp_path, "mutant", src.replace(old, new))
+    assert failing_pins(o), "no pin caught the planted mistake: " + mutant
