@@ -1,0 +1,244 @@
+"""ctypes binding of libgnsilu.so (argument marshalling only).
+
+Every step of the GroupNorm(+SiLU) path runs in the library's HIP kernels;
+this module turns torch tensors into device pointers, sizes and the current
+HIP stream, and maps status codes to Python results.  torch provides device
+memory and streams, nothing else.  There is no CPU fallback: if the library
+is missing, importing this module raises.
+
+Tensor-level API (the pair of "FLUX.2 VAE decoder fast path behind
+quality=high", Modifications section 1 "Kernel"):
+
+    group_norm_silu_4d(x, num_groups, weight, bias, eps, apply_silu, out)
+    group_norm_silu_rows(x, num_groups, weight, bias, eps, apply_silu, out)
+
+Each returns the output tensor, or None when the input is outside the
+supported set so the caller falls back: not a GPU tensor, autograd enabled,
+not bf16, C not a power of two, C > 2048, not channels-last (4-D) / not
+contiguous rows, fp32 weight/bias missing.  Arguments no GroupNorm accepts
+raise ValueError; a failed HIP call raises RuntimeError.
+
+The raw C entry points are re-exported under their C names (gn_silu_nhwc,
+gn_silu_rows, gn_silu_nhwc_strided, gn_stats_rows, gn_apply_rows,
+gn_profile_rows, gn_plan_rows, gn_kernel_name, gn_status_string, gn_version).
+"""
+import ctypes
+import enum
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgnsilu.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        "libgnsilu.so is not built (expected at %s); build it with "
+        "`python groupnorm_silu_normalization_amd/_build.py`" % LIB_PATH)
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_f32 = ctypes.c_float
+_int = ctypes.c_int
+_i64x4 = ctypes.c_int64 * 4
+
+lib.gn_silu_nhwc.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _int, _vp]
+lib.gn_silu_rows.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _vp]
+_i64p = ctypes.POINTER(ctypes.c_int64)
+lib.gn_silu_nhwc_strided.argtypes = [_vp, _i64p, _vp, _vp, _vp, _i64p, _i64, _i64, _i64, _i64,
+                                     _i64, _f32, _int, _vp]
+lib.gn_stats_rows.argtypes = [_vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp]
+lib.gn_apply_rows.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]
+lib.gn_profile_rows.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _vp,
+                                _int, ctypes.POINTER(_f32), ctypes.POINTER(_int)]
+for _name in ("gn_silu_nhwc", "gn_silu_rows", "gn_silu_nhwc_strided", "gn_stats_rows",
+              "gn_apply_rows", "gn_profile_rows"):
+    getattr(lib, _name).restype = _int
+lib.gn_plan_rows.argtypes = [_i64, _i64, _i64, _i64, _i64p]
+lib.gn_plan_rows.restype = _int
+lib.gn_kernel_name.argtypes = [_int]
+lib.gn_kernel_name.restype = ctypes.c_char_p
+lib.gn_status_string.argtypes = [_int]
+lib.gn_status_string.restype = ctypes.c_char_p
+lib.gn_version.argtypes = []
+lib.gn_version.restype = _int
+
+# C entry points under their own names.
+gn_silu_nhwc = lib.gn_silu_nhwc
+gn_silu_rows = lib.gn_silu_rows
+gn_silu_nhwc_strided = lib.gn_silu_nhwc_strided
+gn_stats_rows = lib.gn_stats_rows
+gn_apply_rows = lib.gn_apply_rows
+gn_profile_rows = lib.gn_profile_rows
+gn_kernel_name = lib.gn_kernel_name
+gn_plan_rows = lib.gn_plan_rows
+gn_status_string = lib.gn_status_string
+gn_version = lib.gn_version
+
+MAX_CHANNELS = 2048
+
+
+class GnStatus(enum.IntEnum):
+    OK = 0
+    UNSUPPORTED = 1
+    INVALID_ARGUMENT = 2
+    DEVICE_ERROR = 3
+
+
+def status_text(code: int) -> str:
+    return lib.gn_status_string(int(code)).decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _affine_ok(p, C, device, name):
+    """None -> fine (absent); returns False when unsupported; raises if invalid."""
+    torch = _torch()
+    if p is None:
+        return True
+    if not isinstance(p, torch.Tensor):
+        raise TypeError("%s must be a tensor or None" % name)
+    if p.numel() != C:
+        raise ValueError("%s must have C=%d elements, got %d" % (name, C, p.numel()))
+    if p.dtype != torch.float32 or p.device != device or not p.is_contiguous():
+        return False
+    return True
+
+
+def _common_checks(x, weight, bias, C):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("x must be a torch.Tensor")
+    if x.device.type != "cuda" or torch.version.hip is None:
+        return False
+    if torch.is_grad_enabled():
+        return False
+    if x.dtype != torch.bfloat16:
+        return False
+    if C <= 0 or (C & (C - 1)) != 0 or C > MAX_CHANNELS:
+        return False
+    if not _affine_ok(weight, C, x.device, "weight") or not _affine_ok(bias, C, x.device, "bias"):
+        return False
+    return True
+
+
+def _result(code, out):
+    if code == GnStatus.OK:
+        return out
+    if code == GnStatus.UNSUPPORTED:
+        return None
+    if code == GnStatus.INVALID_ARGUMENT:
+        raise ValueError(status_text(code))
+    raise RuntimeError(status_text(code))
+
+
+def _check_groups(C, num_groups):
+    if not isinstance(num_groups, int) or num_groups <= 0 or C % num_groups != 0:
+        raise ValueError("num_groups=%r must be a positive divisor of C=%d" % (num_groups, C))
+
+
+def group_norm_silu_4d(x, num_groups, weight=None, bias=None, eps=1e-6, apply_silu=True,
+                       out=None):
+    """GroupNorm(+SiLU) of a channels-last bf16 tensor of logical shape (N, C, H, W)."""
+    torch = _torch()
+    if isinstance(x, torch.Tensor) and x.dim() != 4:
+        raise ValueError("group_norm_silu_4d expects a 4-D tensor, got %d-D" % x.dim())
+    N, C, H, W = x.shape if isinstance(x, torch.Tensor) else (0, 0, 0, 0)
+    if not _common_checks(x, weight, bias, C):
+        return None
+    _check_groups(C, num_groups)
+    if not x.is_contiguous(memory_format=torch.channels_last):
+        return None
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.channels_last)
+    elif out.shape != x.shape or out.dtype != x.dtype or out.device != x.device:
+        raise ValueError("out must match x in shape, dtype and device")
+    code = lib.gn_silu_nhwc_strided(
+        _ptr(x), _i64x4(*x.stride()), _ptr(weight), _ptr(bias), _ptr(out), _i64x4(*out.stride()),
+        N, H, W, C, num_groups, float(eps), 1 if apply_silu else 0, _stream_handle(x))
+    return _result(code, out)
+
+
+def group_norm_silu_rows(x, num_groups, weight=None, bias=None, eps=1e-6, apply_silu=True,
+                         out=None):
+    """GroupNorm(+SiLU) of contiguous bf16 rows of shape (N, L, C), C innermost."""
+    torch = _torch()
+    if isinstance(x, torch.Tensor) and x.dim() != 3:
+        raise ValueError("group_norm_silu_rows expects a 3-D (N, L, C) tensor, got %d-D" % x.dim())
+    N, L, C = x.shape if isinstance(x, torch.Tensor) else (0, 0, 0)
+    if not _common_checks(x, weight, bias, C):
+        return None
+    _check_groups(C, num_groups)
+    if not x.is_contiguous():
+        return None
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    elif (out.shape != x.shape or out.dtype != x.dtype or out.device != x.device
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous tensor matching x")
+    code = lib.gn_silu_rows(_ptr(x), _ptr(weight), _ptr(bias), _ptr(out), N, L, C, num_groups,
+                            float(eps), 1 if apply_silu else 0, _stream_handle(x))
+    return _result(code, out)
+
+
+def group_stats_rows(x, num_groups, eps=1e-6):
+    """Per-(n, g) fp32 mean and rstd of contiguous (N, L, C) bf16 rows (steps one and two)."""
+    torch = _torch()
+    N, L, C = x.shape
+    mean = torch.empty((N, num_groups), dtype=torch.float32, device=x.device)
+    rstd = torch.empty_like(mean)
+    code = lib.gn_stats_rows(_ptr(x), N, L, C, num_groups, float(eps), _ptr(mean), _ptr(rstd),
+                             _stream_handle(x))
+    r = _result(code, (mean, rstd))
+    return r
+
+
+def apply_rows(x, mean, rstd, weight=None, bias=None, apply_silu=True, out=None):
+    """Step three alone on contiguous (N, L, C) bf16 rows, given per-(n, g) mean/rstd."""
+    torch = _torch()
+    N, L, C = x.shape
+    G = mean.shape[-1]
+    if out is None:
+        out = torch.empty_like(x)
+    code = lib.gn_apply_rows(_ptr(x), _ptr(mean), _ptr(rstd), _ptr(weight), _ptr(bias),
+                             _ptr(out), N, L, C, G, 1 if apply_silu else 0, _stream_handle(x))
+    return _result(code, out)
+
+
+PLAN_FIELDS = ("vec", "tiles", "full", "tpc1", "K1", "tpc2", "K2", "scratch_bytes")
+
+
+def plan_rows(N, L, C, G):
+    """The library's launch plan for a rows shape (dict), or None if declined."""
+    buf = (_i64 * 8)()
+    code = lib.gn_plan_rows(N, L, C, G, buf)
+    r = _result(code, True)
+    if r is None:
+        return None
+    return dict(zip(PLAN_FIELDS, list(buf)))
+
+
+def profile_rows(x, num_groups, weight, bias, eps, apply_silu, out, iters):
+    """Mean per-kernel milliseconds over `iters` full calls (events around each launch)."""
+    N, L, C = x.shape
+    ms = (_f32 * 4)()
+    nk = _int(0)
+    code = lib.gn_profile_rows(_ptr(x), _ptr(weight), _ptr(bias), _ptr(out), N, L, C, num_groups,
+                               float(eps), 1 if apply_silu else 0, _stream_handle(x), int(iters),
+                               ms, ctypes.byref(nk))
+    if code != GnStatus.OK:
+        _result(code, None)
+        raise RuntimeError("profiling declined: " + status_text(code))
+    return {lib.gn_kernel_name(i).decode(): float(ms[i]) for i in range(nk.value)}

@@ -1,0 +1,447 @@
+// gn_api.hip -- host side of libgnsilu.so: argument checks, the launch plan,
+// the per-(device, stream) scratch buffer and the C-ABI entry points declared
+// in include/gnsilu.h.
+//
+// The contract follows "FLUX.2 VAE decoder fast path behind quality=high",
+// Modifications section 1 "Kernel": group_norm_silu_4d / group_norm_silu_rows
+// return a result, or decline inputs outside the supported set (C not a power
+// of two, C > 2048, not channels-last) so that the caller falls back.  Here
+// "decline" is the status GN_UNSUPPORTED.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "gn_kernels.hpp"
+#include "gnsilu.h"
+
+namespace gnsilu {
+namespace {
+
+constexpr int kUnroll1 = 4;           // loads in flight per lane, statistics pass
+constexpr int kUnroll2 = 4;           // loads in flight per lane, apply pass
+constexpr int64_t kStatsBlocks = 2048;  // target workgroups of the statistics pass
+constexpr int64_t kApplyBlocks = 4096;  // target workgroups of the apply pass
+constexpr int kApplyReverse = 1;        // apply walks chunks last-to-first
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+inline int ilog2(int64_t v) {
+    int r = 0;
+    while ((int64_t{1} << r) < v) ++r;
+    return r;
+}
+
+struct Plan {
+    int vec;        // 8: 16-byte lanes; 1: 2-byte lanes (C < 8 with L*C not a multiple of 8)
+    Geometry stats;  // chunking of steps 1 and 2
+    Geometry apply;  // chunking of step 3
+    int64_t N;
+    double inv_m;   // 1 / (L*Cg)
+};
+
+// The plan depends on the shape only, never on the device, so the order of
+// every floating-point reduction is fixed by (N, L, C, G).
+Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G) {
+    Plan p;
+    p.N = N;
+    const int64_t E = L * C;
+    p.vec = (E % 8 == 0) ? 8 : 1;
+    const int64_t tile = int64_t{kThreads} * p.vec;
+    Geometry g;
+    g.E = E;
+    g.tiles = ceil_div(E, tile);
+    g.full = E / tile;
+    g.C = static_cast<int>(C);
+    g.cg_shift = ilog2(C / G);
+    g.G = static_cast<int>(G);
+    const int64_t total = N * g.tiles;
+    p.stats = g;
+    p.stats.tpc = std::max<int64_t>(1, ceil_div(total, kStatsBlocks));
+    p.stats.K = ceil_div(g.tiles, p.stats.tpc);
+    p.apply = g;
+    p.apply.tpc = std::max<int64_t>(1, ceil_div(total, kApplyBlocks));
+    p.apply.K = ceil_div(g.tiles, p.apply.tpc);
+    p.inv_m = 1.0 / (static_cast<double>(L) * static_cast<double>(C / G));
+    return p;
+}
+
+size_t partial_floats(const Plan &p) {
+    return static_cast<size_t>(p.N) * p.stats.G * p.stats.K;
+}
+
+// Checks with no HIP call.  INVALID before UNSUPPORTED.
+gn_status check_shape(const void *x, const void *y, int64_t N, int64_t L, int64_t C, int64_t G,
+                      float eps, int apply_silu, bool need_y) {
+    if (x == nullptr || (need_y && y == nullptr)) return GN_INVALID_ARGUMENT;
+    if (N < 0 || L < 0 || C <= 0 || G <= 0 || C % G != 0) return GN_INVALID_ARGUMENT;
+    if (!(eps >= 0.0f) || std::isinf(eps)) return GN_INVALID_ARGUMENT;
+    if (apply_silu != 0 && apply_silu != 1) return GN_INVALID_ARGUMENT;
+    if (L > 0 && N > INT64_MAX / L) return GN_INVALID_ARGUMENT;
+    if (N * L > 0 && C > INT64_MAX / (N * L)) return GN_INVALID_ARGUMENT;
+    if (!is_pow2(C) || C > GN_MAX_CHANNELS) return GN_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(x) & 15u) != 0) return GN_UNSUPPORTED;
+    if (need_y && (reinterpret_cast<uintptr_t>(y) & 15u) != 0) return GN_UNSUPPORTED;
+    // Grid extents: a dispatch holds at most 2^32 work-items, i.e. 2^24
+    // workgroups of 256.  The plan launches N*K <= kApplyBlocks + N
+    // workgroups for the streaming passes and N*G for the finalize.
+    if (N > (int64_t{1} << 24) - 2 * kApplyBlocks || N * G >= (int64_t{1} << 24))
+        return GN_UNSUPPORTED;
+    return GN_OK;
+}
+
+// Restores the caller's current device on scope exit.
+struct DeviceGuard {
+    int prev = -1;
+    bool changed = false;
+    gn_status enter(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) return GN_DEVICE_ERROR;
+        if (prev != dev) {
+            if (hipSetDevice(dev) != hipSuccess) return GN_DEVICE_ERROR;
+            changed = true;
+        }
+        return GN_OK;
+    }
+    ~DeviceGuard() {
+        if (changed) (void)hipSetDevice(prev);
+    }
+};
+
+gn_status stream_device(hipStream_t s, int *dev) {
+    if (s == nullptr) return hipGetDevice(dev) == hipSuccess ? GN_OK : GN_DEVICE_ERROR;
+    hipDevice_t d;
+    if (hipStreamGetDevice(s, &d) != hipSuccess) {
+        (void)hipGetLastError();
+        return GN_INVALID_ARGUMENT;
+    }
+    *dev = static_cast<int>(d);
+    return GN_OK;
+}
+
+// A pointer the kernels may dereference: device (or managed) memory on `dev`.
+bool on_device(const void *ptr, int dev) {
+    if (ptr == nullptr) return true;  // optional argument absent
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, ptr) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    if (a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged) return false;
+    return a.device == dev;
+}
+
+// ---- scratch buffer per (device, stream) ----------------------------------
+struct Scratch {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex &scratch_mutex() {
+    static std::mutex *m = new std::mutex;  // never destroyed: outlives atexit teardown
+    return *m;
+}
+std::map<std::pair<int, uintptr_t>, Scratch> &scratch_map() {
+    static auto *m = new std::map<std::pair<int, uintptr_t>, Scratch>;
+    return *m;
+}
+
+// Caller holds scratch_mutex().  Grows the buffer when needed; the old one is
+// released only after the stream has drained the work that used it.
+gn_status scratch_for(int dev, hipStream_t s, size_t bytes, void **out) {
+    Scratch &sc = scratch_map()[{dev, reinterpret_cast<uintptr_t>(s)}];
+    if (sc.bytes < bytes) {
+        if (sc.ptr != nullptr) {
+            if (hipStreamSynchronize(s) != hipSuccess) return GN_DEVICE_ERROR;
+            (void)hipFree(sc.ptr);
+            sc.ptr = nullptr;
+            sc.bytes = 0;
+        }
+        size_t sz = size_t{1} << 16;
+        while (sz < bytes) sz <<= 1;
+        if (hipMalloc(&sc.ptr, sz) != hipSuccess) {
+            (void)hipGetLastError();
+            sc.ptr = nullptr;
+            return GN_DEVICE_ERROR;
+        }
+        sc.bytes = sz;
+    }
+    *out = sc.ptr;
+    return GN_OK;
+}
+
+// ---- launches ---------------------------------------------------------------
+struct Events {
+    hipEvent_t ev[6];  // start/stop of each of the three kernels
+};
+
+void launch_stats(const Plan &p, const uint16_t *x, float *part_s, float *part_q, float eps,
+                  float *mean, float *rstd, hipStream_t s, const Events *ev) {
+    const dim3 block(kThreads);
+    const dim3 grid1(static_cast<unsigned>(p.N * p.stats.K));
+    if (ev) (void)hipEventRecord(ev->ev[0], s);
+    if (p.vec == 8)
+        gn_partial_stats<8, kUnroll1><<<grid1, block, 0, s>>>(x, p.stats, part_s, part_q);
+    else
+        gn_partial_stats<1, kUnroll1><<<grid1, block, 0, s>>>(x, p.stats, part_s, part_q);
+    if (ev) (void)hipEventRecord(ev->ev[1], s);
+    const dim3 grid2(static_cast<unsigned>(p.N * p.stats.G));
+    if (ev) (void)hipEventRecord(ev->ev[2], s);
+    gn_finalize_stats<<<grid2, block, 0, s>>>(x, p.stats, p.inv_m, eps, part_s, part_q, mean,
+                                              rstd);
+    if (ev) (void)hipEventRecord(ev->ev[3], s);
+}
+
+void launch_apply(const Plan &p, const uint16_t *x, uint16_t *y, const float *mean,
+                  const float *rstd, const float *gamma, const float *beta, int silu,
+                  hipStream_t s, const Events *ev) {
+    const dim3 block(kThreads);
+    const dim3 grid(static_cast<unsigned>(p.N * p.apply.K));
+    if (ev) (void)hipEventRecord(ev->ev[4], s);
+    if (p.vec == 8) {
+        if (silu)
+            gn_apply<8, kUnroll2, true><<<grid, block, 0, s>>>(x, y, p.apply, kApplyReverse, mean,
+                                                               rstd, gamma, beta);
+        else
+            gn_apply<8, kUnroll2, false><<<grid, block, 0, s>>>(x, y, p.apply, kApplyReverse, mean,
+                                                                rstd, gamma, beta);
+    } else {
+        if (silu)
+            gn_apply<1, kUnroll2, true><<<grid, block, 0, s>>>(x, y, p.apply, kApplyReverse, mean,
+                                                               rstd, gamma, beta);
+        else
+            gn_apply<1, kUnroll2, false><<<grid, block, 0, s>>>(x, y, p.apply, kApplyReverse, mean,
+                                                                rstd, gamma, beta);
+    }
+    if (ev) (void)hipEventRecord(ev->ev[5], s);
+}
+
+// Everything a compute entry point needs after its argument checks.
+struct Call {
+    hipStream_t stream;
+    int dev;
+    DeviceGuard guard;
+};
+
+gn_status begin_call(void *stream, const std::vector<const void *> &ptrs, Call *c) {
+    c->stream = static_cast<hipStream_t>(stream);
+    gn_status st = stream_device(c->stream, &c->dev);
+    if (st != GN_OK) return st;
+    st = c->guard.enter(c->dev);
+    if (st != GN_OK) return st;
+    for (const void *q : ptrs)
+        if (!on_device(q, c->dev)) return GN_UNSUPPORTED;
+    return GN_OK;
+}
+
+gn_status finish_launch() {
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? GN_OK : GN_DEVICE_ERROR;
+}
+
+// The full path, optionally with events around each kernel.
+gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y, int64_t N,
+                   int64_t L, int64_t C, int64_t G, float eps, int apply_silu, void *stream,
+                   int iters, float *kernel_ms) {
+    gn_status st = check_shape(x, y, N, L, C, G, eps, apply_silu, true);
+    if (st != GN_OK) return st;
+    if (N * L == 0) {
+        if (kernel_ms)
+            for (int i = 0; i < 3; ++i) kernel_ms[i] = 0.0f;
+        return GN_OK;
+    }
+    Call c;
+    st = begin_call(stream, {x, y, gamma, beta}, &c);
+    if (st != GN_OK) return st;
+
+    const Plan p = make_plan(N, L, C, G);
+    const size_t nparts = partial_floats(p);
+    const size_t nstats = static_cast<size_t>(N) * G;
+    const size_t bytes = sizeof(float) * (2 * nparts + 2 * nstats);
+
+    std::lock_guard<std::mutex> lock(scratch_mutex());
+    void *ws = nullptr;
+    st = scratch_for(c.dev, c.stream, bytes, &ws);
+    if (st != GN_OK) return st;
+    float *part_s = static_cast<float *>(ws);
+    float *part_q = part_s + nparts;
+    float *mean = part_q + nparts;
+    float *rstd = mean + nstats;
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    uint16_t *yb = static_cast<uint16_t *>(y);
+
+    if (iters <= 0) {
+        launch_stats(p, xb, part_s, part_q, eps, mean, rstd, c.stream, nullptr);
+        launch_apply(p, xb, yb, mean, rstd, gamma, beta, apply_silu, c.stream, nullptr);
+        return finish_launch();
+    }
+
+    // Measured form: events around every launch, in batches.
+    constexpr int kBatch = 64;
+    std::vector<Events> evs(kBatch);
+    for (auto &e : evs)
+        for (auto &h : e.ev)
+            if (hipEventCreate(&h) != hipSuccess) return GN_DEVICE_ERROR;
+    double sum_ms[3] = {0.0, 0.0, 0.0};
+    st = GN_OK;
+    for (int done = 0; done < iters && st == GN_OK;) {
+        const int nb = std::min(kBatch, iters - done);
+        for (int i = 0; i < nb; ++i) {
+            launch_stats(p, xb, part_s, part_q, eps, mean, rstd, c.stream, &evs[i]);
+            launch_apply(p, xb, yb, mean, rstd, gamma, beta, apply_silu, c.stream, &evs[i]);
+        }
+        st = finish_launch();
+        if (st == GN_OK && hipStreamSynchronize(c.stream) != hipSuccess) st = GN_DEVICE_ERROR;
+        for (int i = 0; i < nb && st == GN_OK; ++i)
+            for (int kk = 0; kk < 3; ++kk) {
+                float ms = 0.0f;
+                if (hipEventElapsedTime(&ms, evs[i].ev[2 * kk], evs[i].ev[2 * kk + 1]) !=
+                    hipSuccess)
+                    st = GN_DEVICE_ERROR;
+                sum_ms[kk] += ms;
+            }
+        done += nb;
+    }
+    for (auto &e : evs)
+        for (auto &h : e.ev) (void)hipEventDestroy(h);
+    if (st != GN_OK) return st;
+    for (int kk = 0; kk < 3; ++kk) kernel_ms[kk] = static_cast<float>(sum_ms[kk] / iters);
+    return GN_OK;
+}
+
+// Dense channels-last check for logical (N, C, H, W) strides.  A dimension
+// of extent 1 may carry any stride, as in torch's channels_last test.
+bool dense_nhwc(const int64_t st[4], int64_t N, int64_t H, int64_t W, int64_t C) {
+    const int64_t ext[4] = {N, C, H, W};
+    const int64_t want[4] = {H * W * C, 1, W * C, C};
+    for (int d = 0; d < 4; ++d)
+        if (ext[d] > 1 && st[d] != want[d]) return false;
+    return true;
+}
+
+const char *kKernelNames[] = {"gn_partial_stats", "gn_finalize_stats", "gn_apply"};
+
+}  // namespace
+}  // namespace gnsilu
+
+using namespace gnsilu;
+
+extern "C" {
+
+gn_status gn_silu_rows(const void *x, const float *gamma, const float *beta, void *y, int64_t N,
+                       int64_t L, int64_t C, int64_t G, float eps, int apply_silu,
+                       void *stream) {
+    return run_rows(x, gamma, beta, y, N, L, C, G, eps, apply_silu, stream, 0, nullptr);
+}
+
+gn_status gn_silu_nhwc(const void *x, const float *gamma, const float *beta, void *y, int64_t N,
+                       int64_t H, int64_t W, int64_t C, int64_t G, float eps, int apply_silu,
+                       void *stream) {
+    if (H < 0 || W < 0) return GN_INVALID_ARGUMENT;
+    if (W > 0 && H > INT64_MAX / W) return GN_INVALID_ARGUMENT;
+    return gn_silu_rows(x, gamma, beta, y, N, H * W, C, G, eps, apply_silu, stream);
+}
+
+gn_status gn_silu_nhwc_strided(const void *x, const int64_t x_strides[4], const float *gamma,
+                               const float *beta, void *y, const int64_t y_strides[4],
+                               int64_t N, int64_t H, int64_t W, int64_t C, int64_t G,
+                               float eps, int apply_silu, void *stream) {
+    if (x_strides == nullptr || y_strides == nullptr) return GN_INVALID_ARGUMENT;
+    if (H < 0 || W < 0) return GN_INVALID_ARGUMENT;
+    if (W > 0 && H > INT64_MAX / W) return GN_INVALID_ARGUMENT;
+    // Argument errors take precedence over layout refusals.
+    gn_status st = check_shape(x, y, N, H * W, C, G, eps, apply_silu, true);
+    if (st == GN_INVALID_ARGUMENT) return st;
+    if (!dense_nhwc(x_strides, N, H, W, C) || !dense_nhwc(y_strides, N, H, W, C))
+        return GN_UNSUPPORTED;
+    return gn_silu_rows(x, gamma, beta, y, N, H * W, C, G, eps, apply_silu, stream);
+}
+
+gn_status gn_stats_rows(const void *x, int64_t N, int64_t L, int64_t C, int64_t G, float eps,
+                        float *mean_out, float *rstd_out, void *stream) {
+    if (mean_out == nullptr || rstd_out == nullptr) return GN_INVALID_ARGUMENT;
+    gn_status st = check_shape(x, nullptr, N, L, C, G, eps, 0, false);
+    if (st != GN_OK) return st;
+    if (N * L == 0) return GN_OK;
+    Call c;
+    st = begin_call(stream, {x, mean_out, rstd_out}, &c);
+    if (st != GN_OK) return st;
+    const Plan p = make_plan(N, L, C, G);
+    const size_t nparts = partial_floats(p);
+    std::lock_guard<std::mutex> lock(scratch_mutex());
+    void *ws = nullptr;
+    st = scratch_for(c.dev, c.stream, sizeof(float) * 2 * nparts, &ws);
+    if (st != GN_OK) return st;
+    float *part_s = static_cast<float *>(ws);
+    launch_stats(p, static_cast<const uint16_t *>(x), part_s, part_s + nparts, eps, mean_out,
+                 rstd_out, c.stream, nullptr);
+    return finish_launch();
+}
+
+gn_status gn_apply_rows(const void *x, const float *mean, const float *rstd, const float *gamma,
+                        const float *beta, void *y, int64_t N, int64_t L, int64_t C, int64_t G,
+                        int apply_silu, void *stream) {
+    if (mean == nullptr || rstd == nullptr) return GN_INVALID_ARGUMENT;
+    gn_status st = check_shape(x, y, N, L, C, G, 0.0f, apply_silu, true);
+    if (st != GN_OK) return st;
+    if (N * L == 0) return GN_OK;
+    Call c;
+    st = begin_call(stream, {x, y, mean, rstd, gamma, beta}, &c);
+    if (st != GN_OK) return st;
+    const Plan p = make_plan(N, L, C, G);
+    launch_apply(p, static_cast<const uint16_t *>(x), static_cast<uint16_t *>(y), mean, rstd,
+                 gamma, beta, apply_silu, c.stream, nullptr);
+    return finish_launch();
+}
+
+gn_status gn_profile_rows(const void *x, const float *gamma, const float *beta, void *y,
+                          int64_t N, int64_t L, int64_t C, int64_t G, float eps, int apply_silu,
+                          void *stream, int iters, float *kernel_ms, int *n_kernels) {
+    if (kernel_ms == nullptr || n_kernels == nullptr || iters < 1 || iters > 100000)
+        return GN_INVALID_ARGUMENT;
+    *n_kernels = 3;
+    return run_rows(x, gamma, beta, y, N, L, C, G, eps, apply_silu, stream, iters, kernel_ms);
+}
+
+gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_out[8]) {
+    if (plan_out == nullptr) return GN_INVALID_ARGUMENT;
+    static const uint16_t aligned_probe[8] __attribute__((aligned(16))) = {};
+    const gn_status st = check_shape(aligned_probe, aligned_probe, N, L, C, G, 0.0f, 0, true);
+    if (st != GN_OK) return st;
+    if (N * L == 0) {
+        for (int i = 0; i < 8; ++i) plan_out[i] = 0;
+        return GN_OK;
+    }
+    const Plan p = make_plan(N, L, C, G);
+    plan_out[0] = p.vec;
+    plan_out[1] = p.stats.tiles;
+    plan_out[2] = p.stats.full;
+    plan_out[3] = p.stats.tpc;
+    plan_out[4] = p.stats.K;
+    plan_out[5] = p.apply.tpc;
+    plan_out[6] = p.apply.K;
+    plan_out[7] = static_cast<int64_t>(
+        sizeof(float) * (2 * partial_floats(p) + 2 * static_cast<size_t>(N) * G));
+    return GN_OK;
+}
+
+const char *gn_kernel_name(int i) {
+    return (i >= 0 && i < 3) ? kKernelNames[i] : nullptr;
+}
+
+const char *gn_status_string(gn_status s) {
+    switch (s) {
+        case GN_OK: return "GN_OK";
+        case GN_UNSUPPORTED: return "GN_UNSUPPORTED: input outside the supported set; fall back";
+        case GN_INVALID_ARGUMENT: return "GN_INVALID_ARGUMENT: not a valid GroupNorm call";
+        case GN_DEVICE_ERROR: return "GN_DEVICE_ERROR: a HIP call failed";
+    }
+    return "unknown gn_status";
+}
+
+int gn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,361 @@
+// gn_kernels.hpp -- gfx950 (CDNA4) kernels of the channels-last GroupNorm(+SiLU)
+// path: partial statistics, finalize, fused apply (+SiLU).
+//
+// The three steps are the ones of "FLUX.2 VAE decoder fast path behind
+// quality=high", Modifications section 1 "Kernel"; the kernels below are a
+// fresh design for wave64 CDNA4, not a translation of the Triton kernel the
+// pages describe.
+//
+// Data layout: one sample is E = L*C bf16 values, channel fastest.  A "tile"
+// is kThreads*VEC consecutive elements of a sample (2048 for VEC = 8).  C is
+// a power of two <= 2048, so every tile starts on a row boundary and thread
+// `tid` always sees the same VEC channels, (tid*VEC + j) mod C: its channel
+// parameters and partial sums stay in registers for the whole chunk.  A
+// 16-byte load per lane gives 1 KiB per wave instruction, fully coalesced.
+//
+// Numerics: each thread accumulates x - p_g, where the pivot p_g is the first
+// element of its group in row 0 of the sample (x[n, 0, g*Cg]).  Shifting by a
+// value of the group keeps the fp32 sum of squares from cancelling when a
+// group's mean is large against its spread; in exact arithmetic the result is
+// unchanged (mean = p + S/M, var = Q/M - (S/M)^2).  Every reduction runs in an
+// order fixed by (N, L, C, G) alone, so results are bitwise reproducible.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gnsilu {
+
+constexpr int kThreads = 256;  // 4 waves of 64
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Two fp32 -> two bf16, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    return static_cast<uint16_t>(pack_bf16x2(f, 0.0f) & 0xffffu);
+}
+
+// SiLU(t) = t * sigmoid(t) = t / (1 + e^-t), with e^-t = 2^(-t*log2 e):
+// one v_exp_f32 and one v_rcp_f32.  t << 0 gives 2^(+big) = inf, 1/inf = 0,
+// t*0 = -0, the limit; t >> 0 gives t.
+__device__ __forceinline__ float silu_f32(float t) {
+    const float e = __builtin_amdgcn_exp2f(t * -1.4426950408889634f);
+    return t * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// VEC consecutive bf16 values of one lane.
+template <int VEC> struct Pack;
+
+template <> struct Pack<8> {
+    u32x4 w;
+    __device__ __forceinline__ static Pack load(const uint16_t *p) {
+        Pack v;
+        v.w = *reinterpret_cast<const u32x4 *>(p);
+        return v;
+    }
+    __device__ __forceinline__ float get(int j) const {
+        const uint32_t word = w[j >> 1];
+        return (j & 1) ? bf16_hi(word) : bf16_lo(word);
+    }
+    __device__ __forceinline__ static void store(uint16_t *p, const float (&o)[8]) {
+        u32x4 v;
+        v[0] = pack_bf16x2(o[0], o[1]);
+        v[1] = pack_bf16x2(o[2], o[3]);
+        v[2] = pack_bf16x2(o[4], o[5]);
+        v[3] = pack_bf16x2(o[6], o[7]);
+        *reinterpret_cast<u32x4 *>(p) = v;
+    }
+};
+
+template <> struct Pack<1> {
+    uint16_t b;
+    __device__ __forceinline__ static Pack load(const uint16_t *p) {
+        Pack v;
+        v.b = *p;
+        return v;
+    }
+    __device__ __forceinline__ float get(int) const { return bf16_bits_to_f32(b); }
+    __device__ __forceinline__ static void store(uint16_t *p, const float (&o)[1]) {
+        *p = f32_to_bf16_bits(o[0]);
+    }
+};
+
+// Arguments shared by the kernels; the host fills it from the plan.
+struct Geometry {
+    int64_t E;         // elements per sample, L*C
+    int64_t tiles;     // tiles per sample, ceil(E / tile)
+    int64_t full;      // tiles per sample lying entirely inside the sample
+    int64_t tpc;       // tiles per chunk (one workgroup's share)
+    int64_t K;         // chunks per sample
+    int C;             // channels (power of two)
+    int cg_shift;      // log2(C / G)
+    int G;             // groups
+};
+
+// ---------------------------------------------------------------------------
+// Step 1: partial statistics.  One workgroup per (sample n, chunk k); writes
+// the pivot-shifted sum and sum of squares of each group over its chunk to
+// part_s / part_q at [(n*G + g)*K + k].
+// ---------------------------------------------------------------------------
+template <int VEC, int UNROLL>
+__global__ __launch_bounds__(kThreads) void gn_partial_stats(
+    const uint16_t *__restrict__ x, Geometry geo, float *__restrict__ part_s,
+    float *__restrict__ part_q) {
+    constexpr int TILE = kThreads * VEC;
+    __shared__ float red_s[TILE];
+    __shared__ float red_q[TILE];
+
+    const int tid = threadIdx.x;
+    const int64_t wg = blockIdx.x;
+    const int64_t n = wg / geo.K;
+    const int64_t k = wg - n * geo.K;
+    const uint16_t *xs = x + n * geo.E;
+    const int cmask = geo.C - 1;
+
+    float piv[VEC], s[VEC], q[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+        const int c = (tid * VEC + j) & cmask;
+        piv[j] = bf16_bits_to_f32(xs[(c >> geo.cg_shift) << geo.cg_shift]);
+        s[j] = 0.0f;
+        q[j] = 0.0f;
+    }
+
+    const int64_t t_begin = k * geo.tpc;
+    const int64_t t_end = t_begin + geo.tpc < geo.tiles ? t_begin + geo.tpc : geo.tiles;
+    const int64_t t_full_end = t_end < geo.full ? t_end : geo.full;
+    const uint16_t *p = xs + t_begin * TILE + tid * VEC;
+
+    int64_t tt = t_begin;
+    for (; tt + UNROLL <= t_full_end; tt += UNROLL) {
+        Pack<VEC> v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) v[u] = Pack<VEC>::load(p + u * TILE);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                const float d = v[u].get(j) - piv[j];
+                s[j] += d;
+                q[j] = fmaf(d, d, q[j]);
+            }
+        }
+        p += UNROLL * TILE;
+    }
+    for (; tt < t_full_end; ++tt) {
+        const Pack<VEC> v = Pack<VEC>::load(p);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            const float d = v.get(j) - piv[j];
+            s[j] += d;
+            q[j] = fmaf(d, d, q[j]);
+        }
+        p += TILE;
+    }
+    if (tt < t_end) {
+        // The sample's last tile is partial; E is a multiple of VEC, so each
+        // lane's vector lies wholly inside or wholly outside the sample.
+        const int64_t off = tt * TILE + tid * VEC;
+        if (off < geo.E) {
+            const Pack<VEC> v = Pack<VEC>::load(xs + off);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                const float d = v.get(j) - piv[j];
+                s[j] += d;
+                q[j] = fmaf(d, d, q[j]);
+            }
+        }
+    }
+
+    // Workgroup reduction.  Slot i = tid*VEC + j of red_* holds channel
+    // i mod C; the P = TILE/G slots of group g are i = r*C + g*Cg + u.
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+        red_s[tid * VEC + j] = s[j];
+        red_q[tid * VEC + j] = q[j];
+    }
+    __syncthreads();
+
+    const int G = geo.G;
+    const int cgm = (1 << geo.cg_shift) - 1;
+    if (G <= kThreads) {
+        const int tg = kThreads / G;  // threads per group
+        const int g = tid / tg;
+        const int part = tid - g * tg;
+        float as = 0.0f, aq = 0.0f;
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            const int e = part * VEC + j;
+            const int i = (e >> geo.cg_shift) * geo.C + (g << geo.cg_shift) + (e & cgm);
+            as += red_s[i];
+            aq += red_q[i];
+        }
+        __syncthreads();
+        red_s[tid] = as;
+        red_q[tid] = aq;
+        __syncthreads();
+        for (int stride = tg >> 1; stride > 0; stride >>= 1) {
+            if (part < stride) {
+                red_s[tid] += red_s[tid + stride];
+                red_q[tid] += red_q[tid + stride];
+            }
+            __syncthreads();
+        }
+        if (part == 0) {
+            const int64_t o = (n * G + g) * geo.K + k;
+            part_s[o] = red_s[tid];
+            part_q[o] = red_q[tid];
+        }
+    } else {
+        const int P = TILE / G;  // < VEC slots per group
+        for (int g = tid; g < G; g += kThreads) {
+            float as = 0.0f, aq = 0.0f;
+            for (int e = 0; e < P; ++e) {
+                const int i = (e >> geo.cg_shift) * geo.C + (g << geo.cg_shift) + (e & cgm);
+                as += red_s[i];
+                aq += red_q[i];
+            }
+            const int64_t o = (n * G + g) * geo.K + k;
+            part_s[o] = as;
+            part_q[o] = aq;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Step 2: finalize.  One workgroup per (n, g): a fixed-order tree over the K
+// chunk partials, then mean and rstd (the scalar arithmetic in fp64, stored
+// as fp32).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void gn_finalize_stats(
+    const uint16_t *__restrict__ x, Geometry geo, double inv_m, float eps,
+    const float *__restrict__ part_s, const float *__restrict__ part_q,
+    float *__restrict__ mean_out, float *__restrict__ rstd_out) {
+    __shared__ float rs[kThreads];
+    __shared__ float rq[kThreads];
+    const int tid = threadIdx.x;
+    const int64_t ng = blockIdx.x;
+    const int64_t n = ng / geo.G;
+    const int g = static_cast<int>(ng - n * geo.G);
+    const float *ps = part_s + ng * geo.K;
+    const float *pq = part_q + ng * geo.K;
+    float s = 0.0f, q = 0.0f;
+    for (int64_t k = tid; k < geo.K; k += kThreads) {
+        s += ps[k];
+        q += pq[k];
+    }
+    rs[tid] = s;
+    rq[tid] = q;
+    __syncthreads();
+    for (int stride = kThreads / 2; stride > 0; stride >>= 1) {
+        if (tid < stride) {
+            rs[tid] += rs[tid + stride];
+            rq[tid] += rq[tid + stride];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const double ms = static_cast<double>(rs[0]) * inv_m;
+        double var = static_cast<double>(rq[0]) * inv_m - ms * ms;
+        if (var < 0.0) var = 0.0;
+        const float pivot =
+            bf16_bits_to_f32(x[n * geo.E + (static_cast<int64_t>(g) << geo.cg_shift)]);
+        mean_out[ng] = static_cast<float>(static_cast<double>(pivot) + ms);
+        rstd_out[ng] = static_cast<float>(1.0 / sqrt(var + static_cast<double>(eps)));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Step 3: fused apply.  One workgroup per (n, chunk); each lane folds
+// gamma/beta and the group statistics of its VEC channels into scale/shift
+// registers once (scale = gamma*rstd, shift = beta - mean*scale), then
+// streams its chunk: y = SiLU(x*scale + shift), rounded once to bf16.
+// x and y may be the same buffer (each element is read, then written, by one
+// lane), so they carry no __restrict__.
+// ---------------------------------------------------------------------------
+template <int VEC, int UNROLL, bool SILU>
+__global__ __launch_bounds__(kThreads) void gn_apply(
+    const uint16_t *x, uint16_t *y, Geometry geo, int reverse,
+    const float *__restrict__ mean, const float *__restrict__ rstd,
+    const float *__restrict__ gamma, const float *__restrict__ beta) {
+    constexpr int TILE = kThreads * VEC;
+    const int tid = threadIdx.x;
+    const int64_t wg = reverse ? static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x
+                               : static_cast<int64_t>(blockIdx.x);
+    const int64_t n = wg / geo.K;
+    const int64_t k = wg - n * geo.K;
+    const int cmask = geo.C - 1;
+
+    float sc[VEC], sh[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+        const int c = (tid * VEC + j) & cmask;
+        const int64_t gi = n * geo.G + (c >> geo.cg_shift);
+        const float ga = gamma ? gamma[c] : 1.0f;
+        const float be = beta ? beta[c] : 0.0f;
+        sc[j] = ga * rstd[gi];
+        sh[j] = fmaf(-mean[gi], sc[j], be);
+    }
+
+    const int64_t base = n * geo.E;
+    const int64_t t_begin = k * geo.tpc;
+    const int64_t t_end = t_begin + geo.tpc < geo.tiles ? t_begin + geo.tpc : geo.tiles;
+    const int64_t t_full_end = t_end < geo.full ? t_end : geo.full;
+    int64_t off = base + t_begin * TILE + tid * VEC;
+
+    auto transform = [&](const Pack<VEC> &v, float (&o)[VEC]) {
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            const float t = fmaf(v.get(j), sc[j], sh[j]);
+            if constexpr (SILU) {
+                o[j] = silu_f32(t);
+            } else {
+                o[j] = t;
+            }
+        }
+    };
+
+    int64_t tt = t_begin;
+    for (; tt + UNROLL <= t_full_end; tt += UNROLL) {
+        Pack<VEC> v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) v[u] = Pack<VEC>::load(x + off + u * TILE);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            float o[VEC];
+            transform(v[u], o);
+            Pack<VEC>::store(y + off + u * TILE, o);
+        }
+        off += UNROLL * TILE;
+    }
+    for (; tt < t_full_end; ++tt) {
+        const Pack<VEC> v = Pack<VEC>::load(x + off);
+        float o[VEC];
+        transform(v, o);
+        Pack<VEC>::store(y + off, o);
+        off += TILE;
+    }
+    if (tt < t_end) {
+        const int64_t rel = tt * TILE + tid * VEC;
+        if (rel < geo.E) {
+            const Pack<VEC> v = Pack<VEC>::load(x + base + rel);
+            float o[VEC];
+            transform(v, o);
+            Pack<VEC>::store(y + base + rel, o);
+        }
+    }
+}
+
+}  // namespace gnsilu

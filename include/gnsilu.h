@@ -1,0 +1,156 @@
+/*
+ * gnsilu.h -- C ABI of the MI355X (gfx950) channels-last GroupNorm(+SiLU)
+ * library, libgnsilu.so.
+ *
+ * The operation is the one defined in "FLUX.2 VAE decoder fast path behind
+ * quality=high", Modifications section 1 "Kernel": GroupNorm over
+ * channels-last activations viewed as (N, L = H*W, C) rows with C innermost,
+ * computed in three steps -- per-(batch, channel) partial sum / sum of
+ * squares over the rows, a finalize to per-(batch, group) fp32 mean/rstd
+ * with gamma/beta folded into per-(batch, channel) scale/shift, and a fused
+ * elementwise apply with an optional SiLU.  The same section gives the
+ * public pair group_norm_silu_4d / group_norm_silu_rows and the inputs for
+ * which they decline ("callers must fall back"): C not a power of two,
+ * C > 2048, a layout that is not channels-last.
+ *
+ * For each sample n and group g (channels g*Cg .. g*Cg+Cg-1, Cg = C/G),
+ * over the M = L*Cg elements of the group:
+ *     mean = sum(x)/M,  var = sum((x-mean)^2)/M  (biased),
+ *     rstd = 1/sqrt(var + eps)
+ *     t    = gamma[c]*(x - mean)*rstd + beta[c]
+ *     y    = apply_silu ? t*sigmoid(t) : t
+ * Statistics are accumulated in fp32 (shifted by one sample of the group,
+ * which leaves the result unchanged in exact arithmetic); y is rounded once
+ * to bf16, round-to-nearest-even.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors: x and y hold bf16 values as raw 16-bit patterns (uint16 storage),
+ *   dense, element (n, l, c) at offset (n*L + l)*C + c.  gamma and beta are
+ *   fp32[C]; either may be NULL (all ones / all zeros, i.e. GroupNorm
+ *   without affine).  All tensor pointers are DEVICE pointers on the device
+ *   that owns `stream`.  x and y must be 16-byte aligned.
+ * stream: a hipStream_t passed as an opaque pointer; NULL is the null
+ *   stream of the current device.
+ * Ownership: the caller owns x, y, gamma, beta and the statistics buffers;
+ *   they must stay valid until the stream has executed the call.  The
+ *   library owns a scratch buffer per (device, stream) for the partial sums
+ *   (a few hundred KiB for the decoder shapes, grown on demand, held until
+ *   the process ends).  Calls enqueued on one stream from several host
+ *   threads are serialised by the library; calls on different streams use
+ *   different scratch buffers.
+ * Synchrony: every compute call is asynchronous on `stream` and returns once
+ *   the kernels are enqueued; a fault inside a kernel surfaces at the
+ *   caller's next synchronisation (gn_profile_rows excepted, which
+ *   synchronises).
+ * Aliasing: y == x (in place) is allowed.  Any other overlap is undefined.
+ * Determinism: the reduction order is a pure function of (N, L, C, G), so
+ *   the same input gives bitwise-identical output on every call.
+ * Errors (checked in this order; nothing is enqueued unless GN_OK):
+ *   GN_INVALID_ARGUMENT -- input no GroupNorm accepts: x or y NULL; N, L, H
+ *     or W negative; C <= 0; G <= 0; C % G != 0; eps negative, infinite or
+ *     NaN; apply_silu not 0 or 1; N*L*C overflowing int64.
+ *   GN_UNSUPPORTED -- a valid GroupNorm this library declines, so the caller
+ *     falls back: C not a power of two; C > 2048; (strided form) a layout
+ *     that is not dense channels-last; x or y not 16-byte aligned; a tensor
+ *     pointer that is not device memory of the stream's device.
+ *   GN_OK is returned without touching the GPU when N*L == 0.
+ *   GN_DEVICE_ERROR -- a HIP call failed (scratch allocation, launch).
+ */
+#ifndef GNSILU_H
+#define GNSILU_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gn_status {
+    GN_OK = 0,
+    GN_UNSUPPORTED = 1,
+    GN_INVALID_ARGUMENT = 2,
+    GN_DEVICE_ERROR = 3
+} gn_status;
+
+/* Largest channel count the library accepts (Modifications section 1). */
+#define GN_MAX_CHANNELS 2048
+
+/* group_norm_silu_4d: NHWC 4-D activation of logical shape (N, C, H, W)
+ * stored channels-last, i.e. the rows form with L = H*W (the "free permute
+ * view" of Modifications section 1). */
+gn_status gn_silu_nhwc(const void *x, const float *gamma, const float *beta, void *y,
+                       int64_t N, int64_t H, int64_t W, int64_t C, int64_t G,
+                       float eps, int apply_silu, void *stream);
+
+/* group_norm_silu_rows: (N, L, C) rows with C innermost, the form the pages'
+ * tests exercise "as used by attention" (Accuracy section, unit tests). */
+gn_status gn_silu_rows(const void *x, const float *gamma, const float *beta, void *y,
+                       int64_t N, int64_t L, int64_t C, int64_t G,
+                       float eps, int apply_silu, void *stream);
+
+/* Strided form of gn_silu_nhwc.  x_strides / y_strides give the element
+ * strides of the logical (N, C, H, W) dimensions.  Only dense channels-last
+ * storage is accepted -- strides (H*W*C, 1, W*C, C), where a dimension of
+ * extent 1 may carry any stride -- anything else is GN_UNSUPPORTED
+ * (Modifications section 1: no NCHW variant). */
+gn_status gn_silu_nhwc_strided(const void *x, const int64_t x_strides[4],
+                               const float *gamma, const float *beta,
+                               void *y, const int64_t y_strides[4],
+                               int64_t N, int64_t H, int64_t W, int64_t C, int64_t G,
+                               float eps, int apply_silu, void *stream);
+
+/* Steps one and two alone: writes the fp32 per-(n, g) mean and rstd, index
+ * n*G + g, to the device buffers mean_out / rstd_out (N*G floats each) --
+ * the finalize output of Modifications section 1.  Same checks as
+ * gn_silu_rows (y is not used). */
+gn_status gn_stats_rows(const void *x, int64_t N, int64_t L, int64_t C, int64_t G,
+                        float eps, float *mean_out, float *rstd_out, void *stream);
+
+/* Step three alone: the fused elementwise apply (+ optional SiLU) given
+ * per-(n, g) mean / rstd in device memory (N*G floats each, as written by
+ * gn_stats_rows); scale = gamma*rstd and shift = beta - mean*scale are
+ * formed per (n, c) inside the kernel. */
+gn_status gn_apply_rows(const void *x, const float *mean, const float *rstd,
+                        const float *gamma, const float *beta, void *y,
+                        int64_t N, int64_t L, int64_t C, int64_t G,
+                        int apply_silu, void *stream);
+
+/* Measurement helper: runs gn_silu_rows `iters` times on `stream` with a
+ * pair of HIP events around every kernel launch, synchronises, and writes
+ * the mean duration in milliseconds of each kernel of the path to
+ * kernel_ms[0 .. *n_kernels-1] (capacity 4).  gn_kernel_name(i) names them.
+ * iters must be in [1, 100000]. */
+gn_status gn_profile_rows(const void *x, const float *gamma, const float *beta, void *y,
+                          int64_t N, int64_t L, int64_t C, int64_t G,
+                          float eps, int apply_silu, void *stream,
+                          int iters, float *kernel_ms, int *n_kernels);
+
+/* Launch plan of the rows path for a shape, for inspection and tests; no
+ * HIP call.  Writes 8 values to plan_out:
+ *   [0] VEC     bf16 values per lane access (8, or 1 when L*C % 8 != 0)
+ *   [1] tiles   tiles of 256*VEC elements per sample (last one may be partial)
+ *   [2] full    tiles per sample lying wholly inside the sample
+ *   [3] tpc1    tiles per workgroup, statistics pass
+ *   [4] K1      workgroups per sample, statistics pass (N*K1 launched)
+ *   [5] tpc2    tiles per workgroup, apply pass
+ *   [6] K2      workgroups per sample, apply pass (N*K2 launched)
+ *   [7] scratch bytes of library-owned scratch the call needs
+ * Returns the status gn_silu_rows would return from its argument checks
+ * for 16-byte-aligned pointers. */
+gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_out[8]);
+
+/* Name of kernel slot i of gn_profile_rows, or NULL. */
+const char *gn_kernel_name(int i);
+
+/* Static description of a status code. */
+const char *gn_status_string(gn_status s);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int gn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GNSILU_H */

@@ -1,0 +1,142 @@
+"""C-ABI checks that need no GPU.
+
+* libgnsilu.so loads and exports every function include/gnsilu.h declares.
+* The status matrix of the argument checks, which run before any HIP call:
+  GN_INVALID_ARGUMENT for input no GroupNorm accepts, GN_UNSUPPORTED for the
+  inputs the pages' kernel declines (C not a power of two, C > 2048, not
+  channels-last -- "FLUX.2 VAE decoder fast path behind quality=high",
+  Modifications section 1), GN_OK for empty input.  The pointers passed here
+  are never dereferenced: every case returns before the library touches HIP.
+* The Python binding's None contract for inputs it declines on the host.
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gnsilu.h")
+
+gn = pytest.importorskip("groupnorm_silu_normalization_amd")
+from groupnorm_silu_normalization_amd import GnStatus  # noqa: E402
+
+# Fake, 16-byte aligned, never dereferenced device addresses.
+X = ctypes.c_void_p(0x10000)
+Y = ctypes.c_void_p(0x20000)
+I64x4 = ctypes.c_int64 * 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ("gn_silu_nhwc", "gn_silu_rows", "gn_silu_nhwc_strided", "gn_stats_rows",
+                 "gn_apply_rows", "gn_profile_rows", "gn_status_string"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    for n in names:
+        assert hasattr(gn.lib, n), "symbol %s declared but not exported" % n
+    out = subprocess.run(["nm", "-D", "--defined-only", gn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(names) <= exported
+
+
+def test_status_strings_and_version():
+    for s in GnStatus:
+        assert gn.status_text(s).startswith("GN_" + s.name)
+    assert gn.gn_version() >= 100
+    assert [gn.gn_kernel_name(i).decode() for i in range(3)] == [
+        "gn_partial_stats", "gn_finalize_stats", "gn_apply"]
+    assert gn.gn_kernel_name(3) is None and gn.gn_kernel_name(-1) is None
+
+
+def rows(x=X, y=Y, N=1, L=16, C=64, G=32, eps=1e-6, silu=1):
+    return gn.gn_silu_rows(x, None, None, y, N, L, C, G, eps, silu, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x=None), dict(y=None), dict(N=-1), dict(L=-1), dict(C=0), dict(C=-8),
+    dict(G=0), dict(G=-2), dict(C=64, G=3), dict(C=96, G=5), dict(eps=-1e-3),
+    dict(eps=float("nan")), dict(eps=float("inf")), dict(silu=2), dict(silu=-1),
+    dict(N=2 ** 40, L=2 ** 20, C=1024),
+])
+def test_invalid_arguments(kw):
+    assert rows(**kw) == GnStatus.INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("kw", [
+    dict(C=96, G=32), dict(C=4096, G=32), dict(C=24, G=8), dict(C=3000, G=1),
+    dict(x=ctypes.c_void_p(0x10002)), dict(y=ctypes.c_void_p(0x20008)),
+])
+def test_unsupported_inputs(kw):
+    assert rows(**kw) == GnStatus.UNSUPPORTED
+
+
+@pytest.mark.parametrize("N,L", [(0, 16), (1, 0), (0, 0)])
+def test_empty_input_is_ok_without_gpu(N, L):
+    assert rows(N=N, L=L) == GnStatus.OK
+    assert gn.gn_silu_nhwc(X, None, None, Y, N, L, 1, 64, 32, 1e-6, 1, None) == GnStatus.OK
+
+
+def test_nhwc_checks():
+    f = gn.gn_silu_nhwc
+    assert f(X, None, None, Y, 1, -1, 4, 64, 32, 1e-6, 1, None) == GnStatus.INVALID_ARGUMENT
+    assert f(X, None, None, Y, 1, 4, -1, 64, 32, 1e-6, 1, None) == GnStatus.INVALID_ARGUMENT
+    assert f(X, None, None, Y, 1, 4, 4, 96, 32, 1e-6, 1, None) == GnStatus.UNSUPPORTED
+    assert f(X, None, None, Y, 1, 2 ** 40, 2 ** 40, 8, 1, 1e-6, 1, None) == GnStatus.INVALID_ARGUMENT
+
+
+def test_strided_rejects_nchw_and_other_layouts():
+    N, C, H, W = 2, 64, 5, 7
+    cl = I64x4(H * W * C, 1, W * C, C)
+    nchw = I64x4(C * H * W, H * W, W, 1)
+    padded = I64x4(H * W * C + 8, 1, W * C, C)
+    f = gn.gn_silu_nhwc_strided
+    assert f(X, nchw, None, None, Y, cl, N, H, W, C, 32, 1e-6, 1, None) == GnStatus.UNSUPPORTED
+    assert f(X, cl, None, None, Y, nchw, N, H, W, C, 32, 1e-6, 1, None) == GnStatus.UNSUPPORTED
+    assert f(X, padded, None, None, Y, cl, N, H, W, C, 32, 1e-6, 1, None) == GnStatus.UNSUPPORTED
+    # argument errors take precedence over the layout
+    assert f(X, nchw, None, None, Y, cl, N, H, W, C, 7, 1e-6, 1, None) == GnStatus.INVALID_ARGUMENT
+    assert f(X, None, None, None, Y, cl, N, H, W, C, 32, 1e-6, 1, None) == GnStatus.INVALID_ARGUMENT
+    # empty dense input: nothing to do
+    assert f(X, cl, None, None, Y, cl, 0, H, W, C, 32, 1e-6, 1, None) == GnStatus.OK
+
+
+def test_stats_apply_profile_argument_checks():
+    assert gn.gn_stats_rows(X, 1, 16, 64, 32, 1e-6, None, Y, None) == GnStatus.INVALID_ARGUMENT
+    assert gn.gn_stats_rows(X, 1, 16, 64, 32, 1e-6, Y, None, None) == GnStatus.INVALID_ARGUMENT
+    assert gn.gn_stats_rows(X, 1, 16, 96, 32, 1e-6, Y, Y, None) == GnStatus.UNSUPPORTED
+    assert gn.gn_apply_rows(X, None, Y, None, None, Y, 1, 16, 64, 32, 1, None) == GnStatus.INVALID_ARGUMENT
+    ms = (ctypes.c_float * 4)()
+    nk = ctypes.c_int(0)
+    assert gn.gn_profile_rows(X, None, None, Y, 1, 16, 64, 32, 1e-6, 1, None, 0, ms,
+                              ctypes.byref(nk)) == GnStatus.INVALID_ARGUMENT
+
+
+def test_binding_declines_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 64, 4, 4, dtype=torch.bfloat16).to(memory_format=torch.channels_last)
+    with torch.no_grad():
+        assert gn.group_norm_silu_4d(x, 32) is None
+        assert gn.group_norm_silu_rows(torch.zeros(1, 16, 64, dtype=torch.bfloat16), 32) is None
+    with pytest.raises(ValueError):
+        gn.group_norm_silu_4d(torch.zeros(2, 3, dtype=torch.bfloat16), 1)
+    with pytest.raises(TypeError):
+        gn.group_norm_silu_4d([1, 2, 3], 1)
+
+
+def test_header_limits_match_binding():
+    text = open(HEADER).read()
+    assert "#define GN_MAX_CHANNELS 2048" in text
+    assert gn.MAX_CHANNELS == 2048 and math.log2(gn.MAX_CHANNELS).is_integer()

@@ -1,0 +1,368 @@
+"""GPU parity: the HIP path against the fp64 oracle, element by element.
+
+Tolerance (per element, NaN never passes):  |y - ref| <= 1e-2 + 1.6e-2*|ref|.
+The GPU output is bf16 (relative rounding <= 2^-9 = 1.95e-3) computed from
+fp32 statistics; the bound leaves room for the rounding of t = x*scale+shift
+and of SiLU but fails any dropped term, wrong group or wrong pivot.
+
+The five decoder shapes run at full size through gn_silu_nhwc, in the launch
+configuration the benchmark times (the plan depends on the shape only).
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 1e-2, 1.6e-2
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import groupnorm_silu_normalization_amd as gn
+    return gn
+
+
+@pytest.fixture(scope="module")
+def gn():
+    return _gpu()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev_bits(bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def from_dev_bits(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1)
+
+
+def vp(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def compare(y_bits, ref, what):
+    """Element-wise tolerance check; returns (max abs err, violations)."""
+    from gn_inputs import bf16_bits_to_f32
+    ref = ref.reshape(-1)
+    worst, bad, first = 0.0, 0, None
+    step = 1 << 24
+    for s in range(0, ref.size, step):
+        got = bf16_bits_to_f32(y_bits[s:s + step]).astype(np.float64)
+        r = ref[s:s + step].astype(np.float64)
+        err = np.abs(got - r)
+        ok = err <= ATOL + RTOL * np.abs(r)
+        nb = int(np.count_nonzero(~ok))
+        if nb and first is None:
+            i = int(np.flatnonzero(~ok)[0])
+            first = (s + i, float(got[i]), float(r[i]))
+        bad += nb
+        finite = err[np.isfinite(err)]
+        if finite.size:
+            worst = max(worst, float(finite.max()))
+    print("%s: max|y-ref|=%.3e violations=%d/%d first=%s" % (what, worst, bad, ref.size, first),
+          flush=True)
+    assert bad == 0, "%s: %d elements outside tolerance, first %s" % (what, bad, first)
+    return worst
+
+
+def run_rows(gn, dev, x_bits, gamma, beta, N, L, C, G, eps, silu, inplace=False):
+    x = to_dev_bits(x_bits, dev)
+    y = x if inplace else torch.empty_like(x)
+    g = None if gamma is None else torch.from_numpy(gamma).to(dev)
+    b = None if beta is None else torch.from_numpy(beta).to(dev)
+    code = gn.gn_silu_rows(vp(x), vp(g), vp(b), vp(y), N, L, C, G, float(eps), int(silu),
+                           stream(dev))
+    assert code == gn.GnStatus.OK, gn.status_text(code)
+    torch.cuda.synchronize()
+    return from_dev_bits(y)
+
+
+# ---------------------------------------------------------------- workloads
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_decoder_workload_full_size(gn, dev, oracle, idx):
+    from gn_inputs import WORKLOADS, make_inputs
+    w = WORKLOADS[idx]
+    print("case %s %s" % (w.name, w.label()), flush=True)
+    x_bits, gamma, beta = make_inputs(w)
+    x = to_dev_bits(x_bits, dev).reshape(w.N, w.H, w.W, w.C).permute(0, 3, 1, 2)
+    assert x.is_contiguous(memory_format=torch.channels_last)
+    g = torch.from_numpy(gamma).to(dev)
+    b = torch.from_numpy(beta).to(dev)
+    with torch.no_grad():
+        y = gn.group_norm_silu_4d(x, w.G, g, b, w.eps, apply_silu=w.apply_silu)
+    assert y is not None and y.is_contiguous(memory_format=torch.channels_last)
+    torch.cuda.synchronize()
+    y_bits = from_dev_bits(y.permute(0, 2, 3, 1))
+    del x, y
+    ref = oracle.gn_silu(x_bits, gamma, beta, w.N, w.L, w.C, w.G, w.eps, w.apply_silu,
+                         out_dtype=np.float32)
+    compare(y_bits, ref, w.name)
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_decoder_workload_statistics(gn, dev, oracle, idx):
+    """fp32 mean/rstd against the oracle's fp64 ones.
+
+    Bounds: the sums are of pivot-shifted values in runs of at most a few
+    hundred per lane plus fixed trees, so S/M and Q/M carry relative error of
+    order 1e-6; hence |dmean| <= 1e-4*std + 2^-22*|mean| and |drstd|/rstd <= 1e-4.
+    """
+    from gn_inputs import WORKLOADS, make_inputs
+    w = WORKLOADS[idx]
+    x_bits, _, _ = make_inputs(w)
+    x = to_dev_bits(x_bits, dev).reshape(w.N, w.L, w.C)
+    with torch.no_grad():
+        mean, rstd = gn.group_stats_rows(x, w.G, w.eps)
+    torch.cuda.synchronize()
+    m_ref, v_ref = oracle.group_stats(x_bits, w.N, w.L, w.C, w.G)
+    r_ref = 1.0 / np.sqrt(v_ref + np.float64(np.float32(w.eps)))
+    m = mean.cpu().numpy().astype(np.float64)
+    r = rstd.cpu().numpy().astype(np.float64)
+    dm = np.abs(m - m_ref)
+    assert np.all(dm <= 1e-4 * np.sqrt(v_ref) + 2.0 ** -22 * np.abs(m_ref)), dm.max()
+    dr = np.abs(r - r_ref) / r_ref
+    print("%s stats: max|dmean|=%.2e max rel drstd=%.2e" % (w.name, dm.max(), dr.max()))
+    assert np.all(dr <= 1e-4), dr.max()
+
+
+# --------------------------------------------------------------- edge cases
+SWEEP = []
+for _C in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048):
+    for _G in sorted({1, min(32, _C), _C}):
+        for _N, _L in ((1, 1), (2, 3), (1, 257), (2, 1000)):
+            SWEEP.append((_N, _L, _C, _G))
+
+
+@pytest.mark.parametrize("N,L,C,G", SWEEP)
+def test_shape_sweep(gn, dev, oracle, N, L, C, G):
+    from gn_inputs import make_custom
+    x_bits, gamma, beta = make_custom(N, L, C, seed=N * 7919 + L * 31 + C * 3 + G,
+                                      mean_range=(-3, 3), std_range=(0.3, 2))
+    for silu in (0, 1):
+        y = run_rows(gn, dev, x_bits, gamma, beta, N, L, C, G, 1e-6, silu)
+        ref = oracle.gn_silu(x_bits, gamma, beta, N, L, C, G, 1e-6, silu)
+        compare(y, ref, "sweep N=%d L=%d C=%d G=%d silu=%d" % (N, L, C, G, silu))
+
+
+@pytest.mark.parametrize("N,L,C,G", [
+    (3, 70001, 128, 32),    # several tiles per workgroup, unrolled + remainder + ragged tail
+    (2, 5000, 64, 8),       # partial last tile
+    (2, 131072, 64, 8),     # many chunks per sample
+    (1, 4099, 2048, 2048),  # widest rows, one channel per group
+    (1, 4099, 2048, 1),     # widest rows, one group
+    (5, 999, 4, 2),         # 2-byte lanes (L*C not a multiple of 8), several samples
+])
+def test_multi_tile_ragged(gn, dev, oracle, N, L, C, G):
+    from gn_inputs import make_custom
+    x_bits, gamma, beta = make_custom(N, L, C, seed=L + C + G, mean_range=(-6, 6),
+                                      std_range=(0.2, 1.5))
+    y = run_rows(gn, dev, x_bits, gamma, beta, N, L, C, G, 1e-6, 1)
+    ref = oracle.gn_silu(x_bits, gamma, beta, N, L, C, G, 1e-6, 1)
+    compare(y, ref, "ragged N=%d L=%d C=%d G=%d" % (N, L, C, G))
+
+
+def test_rows_variant_as_attention(gn, dev, oracle):
+    """(N, L, C) = (1, 16384, 512), G=32, no SiLU, through group_norm_silu_rows."""
+    from gn_inputs import make_custom
+    N, L, C, G = 1, 16384, 512, 32
+    x_bits, gamma, beta = make_custom(N, L, C, seed=4242, mean_range=(-1, 1), std_range=(0.5, 2))
+    x = to_dev_bits(x_bits, dev).reshape(N, L, C)
+    with torch.no_grad():
+        y = gn.group_norm_silu_rows(x, G, torch.from_numpy(gamma).to(dev),
+                                    torch.from_numpy(beta).to(dev), 1e-6, apply_silu=False)
+    torch.cuda.synchronize()
+    ref = oracle.gn_silu(x_bits, gamma, beta, N, L, C, G, 1e-6, False)
+    compare(from_dev_bits(y), ref, "rows attention")
+
+
+def test_in_place(gn, dev, oracle):
+    from gn_inputs import make_custom
+    N, L, C, G = 2, 3000, 256, 32
+    x_bits, gamma, beta = make_custom(N, L, C, seed=11, mean_range=(-2, 2))
+    y = run_rows(gn, dev, x_bits, gamma, beta, N, L, C, G, 1e-6, 1, inplace=True)
+    compare(y, oracle.gn_silu(x_bits, gamma, beta, N, L, C, G, 1e-6, 1), "in place")
+
+
+def test_no_affine(gn, dev, oracle):
+    from gn_inputs import make_custom
+    N, L, C, G = 2, 777, 64, 16
+    x_bits, _, _ = make_custom(N, L, C, seed=12, mean_range=(-2, 2))
+    for silu in (0, 1):
+        y = run_rows(gn, dev, x_bits, None, None, N, L, C, G, 1e-6, silu)
+        compare(y, oracle.gn_silu(x_bits, None, None, N, L, C, G, 1e-6, silu), "no affine")
+
+
+def test_large_eps_and_constant_groups(gn, dev, oracle):
+    from gn_inputs import f32_to_bf16_bits
+    N, L, C, G = 1, 4096, 64, 8
+    xf = np.random.default_rng(5).normal(0, 1, (N, L, C)).astype(np.float32)
+    xf[:, :, :8] = 2.5  # group 0 constant: output = beta (then SiLU)
+    x_bits = f32_to_bf16_bits(xf).reshape(-1)
+    gamma = np.linspace(0.5, 1.5, C).astype(np.float32)
+    beta = np.linspace(-1, 1, C).astype(np.float32)
+    for eps in (1e-6, 0.5):
+        y = run_rows(gn, dev, x_bits, gamma, beta, N, L, C, G, eps, 1)
+        compare(y, oracle.gn_silu(x_bits, gamma, beta, N, L, C, G, eps, 1), "eps=%g" % eps)
+
+
+def test_exact_statistics_integer_inputs(gn, dev):
+    """Integer x in [-2, 2] with M = L*Cg a power of two and sum of squares
+    below 2^24: every fp32 sum is exact in any order, so the mean must be the
+    exact mean and rstd the correctly rounded 1/sqrt(var + eps).  Catches a
+    dropped or doubled tile, chunk or workgroup.
+    """
+    from gn_inputs import f32_to_bf16_bits
+    N, L, C, G = 2, 131072, 64, 8           # M = 2^20 per group, 1024 chunks per sample
+    xi = np.random.default_rng(21).integers(-2, 3, N * L * C).astype(np.float32)
+    x_bits = f32_to_bf16_bits(xi)
+    x = to_dev_bits(x_bits, dev).reshape(N, L, C)
+    eps = 1e-6
+    with torch.no_grad():
+        mean, rstd = gn.group_stats_rows(x, G, eps)
+    torch.cuda.synchronize()
+    xs = xi.reshape(N, L, G, C // G).astype(np.int64)
+    M = L * (C // G)
+    S = xs.sum(axis=(1, 3))
+    Q = (xs * xs).sum(axis=(1, 3))
+    exact_mean = S / M                       # exact in fp64 (M is a power of two)
+    exact_var = Q / M - exact_mean ** 2      # exact dyadic rationals
+    want_r = (1.0 / np.sqrt(exact_var + np.float64(np.float32(eps)))).astype(np.float32)
+    assert np.array_equal(mean.cpu().numpy(), exact_mean.astype(np.float32))
+    got_r = rstd.cpu().numpy()
+    ulp = np.abs(got_r.view(np.int32) - want_r.view(np.int32))
+    assert ulp.max() <= 1, ulp.max()
+
+
+def test_stats_then_apply_equals_full_path(gn, dev):
+    from gn_inputs import make_custom
+    N, L, C, G = 2, 20000, 128, 32
+    x_bits, gamma, beta = make_custom(N, L, C, seed=31, mean_range=(-2, 2))
+    x = to_dev_bits(x_bits, dev).reshape(N, L, C)
+    g = torch.from_numpy(gamma).to(dev)
+    b = torch.from_numpy(beta).to(dev)
+    with torch.no_grad():
+        full = gn.group_norm_silu_rows(x, G, g, b, 1e-6)
+        mean, rstd = gn.group_stats_rows(x, G, 1e-6)
+        split = gn.apply_rows(x, mean, rstd, g, b, apply_silu=True)
+    torch.cuda.synchronize()
+    assert torch.equal(full.view(torch.int16), split.view(torch.int16))
+
+
+def test_deterministic_repeats(gn, dev):
+    from gn_inputs import WORKLOADS, make_inputs
+    w = WORKLOADS[1]
+    x_bits, gamma, beta = make_inputs(w)
+    x = to_dev_bits(x_bits, dev).reshape(w.N, w.L, w.C)
+    g = torch.from_numpy(gamma).to(dev)
+    b = torch.from_numpy(beta).to(dev)
+    outs = []
+    with torch.no_grad():
+        for _ in range(5):
+            outs.append(gn.group_norm_silu_rows(x, w.G, g, b, w.eps).view(torch.int16).clone())
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_canaries_around_output(gn, dev, oracle):
+    """Writes stay inside y: guard regions on both sides keep their bytes."""
+    from gn_inputs import make_custom
+    N, L, C, G = 1, 5000, 128, 32
+    x_bits, gamma, beta = make_custom(N, L, C, seed=77)
+    n = N * L * C
+    pad = 4096
+    buf = torch.full((n + 2 * pad,), 0x5A5A, dtype=torch.int16, device=dev)
+    y = buf[pad:pad + n]
+    x = to_dev_bits(x_bits, dev)
+    g = torch.from_numpy(gamma).to(dev)
+    b = torch.from_numpy(beta).to(dev)
+    code = gn.gn_silu_rows(vp(x), vp(g), vp(b), vp(y), N, L, C, G, 1e-6, 1, stream(dev))
+    assert code == 0
+    torch.cuda.synchronize()
+    assert bool((buf[:pad] == 0x5A5A).all()) and bool((buf[pad + n:] == 0x5A5A).all())
+    compare(from_dev_bits(y), oracle.gn_silu(x_bits, gamma, beta, N, L, C, G, 1e-6, 1), "canary")
+
+
+def test_side_stream(gn, dev, oracle):
+    from gn_inputs import make_custom
+    N, L, C, G = 1, 9000, 256, 32
+    x_bits, gamma, beta = make_custom(N, L, C, seed=91)
+    s = torch.cuda.Stream(dev)
+    x = to_dev_bits(x_bits, dev).reshape(N, L, C)
+    g = torch.from_numpy(gamma).to(dev)
+    b = torch.from_numpy(beta).to(dev)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s), torch.no_grad():
+        y = gn.group_norm_silu_rows(x, G, g, b, 1e-6)
+    s.synchronize()
+    compare(from_dev_bits(y), oracle.gn_silu(x_bits, gamma, beta, N, L, C, G, 1e-6, 1), "stream")
+
+
+def test_profile_helper(gn, dev):
+    from gn_inputs import WORKLOADS, make_inputs
+    w = WORKLOADS[1]
+    x_bits, gamma, beta = make_inputs(w)
+    x = to_dev_bits(x_bits, dev).reshape(w.N, w.L, w.C)
+    y = torch.empty_like(x)
+    ms = gn.profile_rows(x, w.G, torch.from_numpy(gamma).to(dev), torch.from_numpy(beta).to(dev),
+                         w.eps, True, y, 3)
+    assert set(ms) == {"gn_partial_stats", "gn_finalize_stats", "gn_apply"}
+    assert all(v > 0 for v in ms.values())
+
+
+# ------------------------------------------------------ unsupported contract
+def test_unsupported_inputs_return_none(gn, dev):
+    x = torch.randn(1, 64, 8, 8, device=dev).to(torch.bfloat16)  # NCHW-contiguous
+    g = torch.ones(64, device=dev)
+    with torch.no_grad():
+        assert gn.group_norm_silu_4d(x, 32, g, g) is None                          # not channels_last
+        xc = x.to(memory_format=torch.channels_last)
+        assert gn.group_norm_silu_4d(xc, 32, g, g) is not None
+        assert gn.group_norm_silu_4d(xc.half(), 32, g.half(), g.half()) is None    # fp16
+        x96 = torch.randn(1, 96, 4, 4, device=dev).to(torch.bfloat16).to(memory_format=torch.channels_last)
+        assert gn.group_norm_silu_4d(x96, 32) is None                              # C not pow2
+        x4k = torch.randn(1, 4096, 2, 2, device=dev).to(torch.bfloat16).to(memory_format=torch.channels_last)
+        assert gn.group_norm_silu_4d(x4k, 32) is None                              # C > 2048
+        assert gn.group_norm_silu_4d(xc, 32, g.cpu(), g.cpu()) is None             # host affine
+        with pytest.raises(ValueError):
+            gn.group_norm_silu_4d(xc, 7)                                           # C % G != 0
+    assert gn.group_norm_silu_4d(xc, 32, g, g) is None                             # grad enabled
+
+
+def test_host_pointer_is_unsupported(gn, dev):
+    host = np.zeros(1024, np.uint16)
+    y = torch.empty(1024, dtype=torch.int16, device=dev)
+    code = gn.gn_silu_rows(ctypes.c_void_p(host.ctypes.data), None, None, vp(y), 1, 16, 64, 32,
+                           1e-6, 1, stream(dev))
+    assert code == gn.GnStatus.UNSUPPORTED
+
+
+def test_extent_one_dims_accept_any_stride(gn, dev, oracle):
+    from gn_inputs import make_custom
+    N, C, H, W, G = 1, 64, 1, 50, 8
+    x_bits, gamma, beta = make_custom(N, H * W, C, seed=8)
+    x = to_dev_bits(x_bits, dev)
+    y = torch.empty_like(x)
+    st_x = (ctypes.c_int64 * 4)(12345, 1, 999, C)  # N and H have extent 1
+    st_y = (ctypes.c_int64 * 4)(7, 1, 3, C)
+    g = torch.from_numpy(gamma).to(dev)
+    b = torch.from_numpy(beta).to(dev)
+    code = gn.gn_silu_nhwc_strided(vp(x), st_x, vp(g), vp(b), vp(y), st_y, N, H, W, C, G, 1e-6, 1,
+                                   stream(dev))
+    assert code == 0
+    torch.cuda.synchronize()
+    compare(from_dev_bits(y), oracle.gn_silu(x_bits, gamma, beta, N, H * W, C, G, 1e-6, 1),
+            "extent-1 strides")
