@@ -26,6 +26,14 @@ import ctypes
 import enum
 import os
 
+# torch first: its wheel bundles a HIP runtime (torch/lib/libamdhip64.so,
+# soname libamdhip64.so.7).  Loaded first, it satisfies this library's
+# dependency on libamdhip64.so.7 and the process holds ONE HIP runtime.  Loaded
+# the other way round, the system runtime comes in first and torch then maps
+# its own copy beside it, so tensors allocated by torch are unknown to the
+# runtime that launches these kernels.
+import torch  # noqa: F401
+
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgnsilu.so")
 
@@ -35,6 +43,20 @@ if not os.path.exists(LIB_PATH):
         "`python groupnorm_silu_normalization_amd/_build.py`" % LIB_PATH)
 
 lib = ctypes.CDLL(LIB_PATH)
+
+
+def _hip_runtimes_mapped():
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    except OSError:
+        return []
+
+
+if len(_hip_runtimes_mapped()) > 1:
+    raise ImportError(
+        "two HIP runtimes are loaded in this process (%s); import torch before any other "
+        "library that links libamdhip64" % ", ".join(_hip_runtimes_mapped()))
 
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -90,7 +112,6 @@ def status_text(code: int) -> str:
 
 
 def _torch():
-    import torch
     return torch
 
 

@@ -140,3 +140,13 @@ def test_header_limits_match_binding():
     text = open(HEADER).read()
     assert "#define GN_MAX_CHANNELS 2048" in text
     assert gn.MAX_CHANNELS == 2048 and math.log2(gn.MAX_CHANNELS).is_integer()
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Importing the package before torch must not map a second HIP runtime."""
+    code = ("import groupnorm_silu_normalization_amd, torch\n"
+            "maps = open('/proc/self/maps').read()\n"
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))\n")
+    out = subprocess.run(["python", "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         check=True).stdout.strip().splitlines()[-1]
+    assert out == "1"
