@@ -262,4 +262,6 @@ def profile_rows(x, num_groups, weight, bias, eps, apply_silu, out, iters):
     if code != GnStatus.OK:
         _result(code, None)
         raise RuntimeError("profiling declined: " + status_text(code))
-    return {lib.gn_kernel_name(i).decode(): float(ms[i]) for i in range(nk.value)}
+    # a negative slot is a kernel not launched for this shape (finalize fused
+    # into the statistics kernel)
+    return {lib.gn_kernel_name(i).decode(): float(ms[i]) for i in range(nk.value) if ms[i] >= 0}

@@ -9,6 +9,7 @@
 // "decline" is the status GN_UNSUPPORTED.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <map>
@@ -22,11 +23,20 @@
 namespace gnsilu {
 namespace {
 
-constexpr int kUnroll1 = 4;           // loads in flight per lane, statistics pass
-constexpr int kUnroll2 = 4;           // loads in flight per lane, apply pass
-constexpr int64_t kStatsBlocks = 2048;  // target workgroups of the statistics pass
-constexpr int64_t kApplyBlocks = 4096;  // target workgroups of the apply pass
-constexpr int kApplyReverse = 1;        // apply walks chunks last-to-first
+// Launch plan constants, measured on MI355X (256 CUs, 256 MB Infinity Cache)
+// over the full three-step sequence at the decoder shapes.
+constexpr int kUnrollStats = 8;             // 16-byte loads in flight per lane, step 1
+constexpr int kUnrollApply = 4;             // 16-byte loads in flight per lane, step 3
+constexpr int64_t kStatsBlocks = 256;       // step-1 workgroups in total: one per CU
+constexpr int64_t kStatsMaxTiles = 1024;    // caps each lane's sequential fp32 run
+constexpr int64_t kApplyTilesPerBlock = 16; // step-3 workgroups: total tiles / 16 ...
+constexpr int64_t kApplyMinBlocks = 256;    // ... clamped to [256, 2048]
+constexpr int64_t kApplyMaxBlocks = 2048;
+// Step 1 reads x with ordinary loads, so the tail of x it read last is still
+// in the Infinity Cache when step 3 reads it again; step 3 writes y with
+// nontemporal stores so y does not evict it.  A tensor larger than the cache
+// cannot be served from it, and step 3 then streams x with nontemporal loads.
+constexpr int64_t kCacheResidentBytes = int64_t{256} << 20;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
@@ -35,13 +45,16 @@ inline int ilog2(int64_t v) {
     while ((int64_t{1} << r) < v) ++r;
     return r;
 }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Plan {
-    int vec;        // 8: 16-byte lanes; 1: 2-byte lanes (C < 8 with L*C not a multiple of 8)
-    Geometry stats;  // chunking of steps 1 and 2
-    Geometry apply;  // chunking of step 3
+    int vec;          // 8: 16-byte lanes; 1: 2-byte lanes (C < 8 with L*C not a multiple of 8)
+    bool fused;       // step 2 runs in the tail of step 1 (G <= kThreads)
+    bool apply_ntl;   // step 3 reads x with nontemporal loads
+    Geometry stats;   // chunking of steps 1 and 2
+    Geometry apply;   // chunking of step 3
     int64_t N;
-    double inv_m;   // 1 / (L*Cg)
+    double inv_m;     // 1 / (L*Cg)
 };
 
 // The plan depends on the shape only, never on the device, so the order of
@@ -51,6 +64,8 @@ Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G) {
     p.N = N;
     const int64_t E = L * C;
     p.vec = (E % 8 == 0) ? 8 : 1;
+    p.fused = G <= kThreads;
+    p.apply_ntl = N * E * 2 > kCacheResidentBytes;
     const int64_t tile = int64_t{kThreads} * p.vec;
     Geometry g;
     g.E = E;
@@ -61,17 +76,27 @@ Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G) {
     g.G = static_cast<int>(G);
     const int64_t total = N * g.tiles;
     p.stats = g;
-    p.stats.tpc = std::max<int64_t>(1, ceil_div(total, kStatsBlocks));
+    p.stats.tpc = std::min(kStatsMaxTiles, std::max<int64_t>(1, ceil_div(total, kStatsBlocks)));
     p.stats.K = ceil_div(g.tiles, p.stats.tpc);
     p.apply = g;
-    p.apply.tpc = std::max<int64_t>(1, ceil_div(total, kApplyBlocks));
+    const int64_t apply_blocks =
+        std::min(kApplyMaxBlocks, std::max(kApplyMinBlocks, total / kApplyTilesPerBlock));
+    p.apply.tpc = std::max<int64_t>(1, ceil_div(total, apply_blocks));
     p.apply.K = ceil_div(g.tiles, p.apply.tpc);
     p.inv_m = 1.0 / (static_cast<double>(L) * static_cast<double>(C / G));
     return p;
 }
 
 size_t partial_floats(const Plan &p) {
-    return static_cast<size_t>(p.N) * p.stats.G * p.stats.K;
+    return static_cast<size_t>(p.N) * p.stats.K * p.stats.G;
+}
+
+// Scratch bytes of a call: the arrival counters (one per sample, at the front,
+// 256-byte aligned), the partials, and -- for the full path -- mean and rstd.
+size_t arrivals_bytes(int64_t n) { return align_up(static_cast<size_t>(n) * 4, 256); }
+size_t payload_bytes(const Plan &p, bool with_stats) {
+    return sizeof(float) * (2 * partial_floats(p) +
+                            (with_stats ? 2 * static_cast<size_t>(p.N) * p.stats.G : 0));
 }
 
 // Checks with no HIP call.  INVALID before UNSUPPORTED.
@@ -87,9 +112,12 @@ gn_status check_shape(const void *x, const void *y, int64_t N, int64_t L, int64_
     if ((reinterpret_cast<uintptr_t>(x) & 15u) != 0) return GN_UNSUPPORTED;
     if (need_y && (reinterpret_cast<uintptr_t>(y) & 15u) != 0) return GN_UNSUPPORTED;
     // Grid extents: a dispatch holds at most 2^32 work-items, i.e. 2^24
-    // workgroups of 256.  The plan launches N*K <= kApplyBlocks + N
-    // workgroups for the streaming passes and N*G for the finalize.
-    if (N > (int64_t{1} << 24) - 2 * kApplyBlocks || N * G >= (int64_t{1} << 24))
+    // workgroups of 256.  Step 3 launches at most kApplyMaxBlocks + N
+    // workgroups, step 1 at most total tiles / kStatsMaxTiles + N (+256), the
+    // separate finalize N*G.
+    if (N > (int64_t{1} << 24) - 2 * kApplyMaxBlocks || N * G >= (int64_t{1} << 24))
+        return GN_UNSUPPORTED;
+    if (L > 0 && N * ceil_div(L * C, kThreads) / kStatsMaxTiles > (int64_t{1} << 23))
         return GN_UNSUPPORTED;
     return GN_OK;
 }
@@ -135,9 +163,12 @@ bool on_device(const void *ptr, int dev) {
 }
 
 // ---- scratch buffer per (device, stream) ----------------------------------
+// Layout: [arrival counters: `arrivals` uint32, zero between calls][payload].
+// The counter region only grows, so a payload never overlaps a counter.
 struct Scratch {
-    void *ptr = nullptr;
+    char *ptr = nullptr;
     size_t bytes = 0;
+    int64_t arrivals = 0;
 };
 
 std::mutex &scratch_mutex() {
@@ -149,74 +180,117 @@ std::map<std::pair<int, uintptr_t>, Scratch> &scratch_map() {
     return *m;
 }
 
-// Caller holds scratch_mutex().  Grows the buffer when needed; the old one is
-// released only after the stream has drained the work that used it.
-gn_status scratch_for(int dev, hipStream_t s, size_t bytes, void **out) {
+gn_status zero_counters(unsigned *p, int64_t n, hipStream_t s) {
+    if (n <= 0) return GN_OK;
+    gn_zero_u32<<<static_cast<unsigned>(ceil_div(n, kThreads)), kThreads, 0, s>>>(p, n);
+    return hipGetLastError() == hipSuccess ? GN_OK : GN_DEVICE_ERROR;
+}
+
+// Caller holds scratch_mutex().  Returns the counters (>= n of them, all zero
+// in stream order) and the payload (>= payload bytes).  Grows the buffer when
+// needed; the old one is released only after the stream has drained the work
+// that used it.
+gn_status scratch_for(int dev, hipStream_t s, int64_t n, size_t payload, unsigned **counters,
+                      char **payload_ptr) {
     Scratch &sc = scratch_map()[{dev, reinterpret_cast<uintptr_t>(s)}];
-    if (sc.bytes < bytes) {
+    const int64_t want_arrivals = std::max(sc.arrivals, n);
+    const size_t head = arrivals_bytes(want_arrivals);
+    const size_t need = head + payload;
+    int64_t zero_from = sc.arrivals;
+    if (sc.bytes < need) {
         if (sc.ptr != nullptr) {
             if (hipStreamSynchronize(s) != hipSuccess) return GN_DEVICE_ERROR;
             (void)hipFree(sc.ptr);
             sc.ptr = nullptr;
             sc.bytes = 0;
+            sc.arrivals = 0;
         }
         size_t sz = size_t{1} << 16;
-        while (sz < bytes) sz <<= 1;
-        if (hipMalloc(&sc.ptr, sz) != hipSuccess) {
+        while (sz < need) sz <<= 1;
+        void *p = nullptr;
+        if (hipMalloc(&p, sz) != hipSuccess) {
             (void)hipGetLastError();
-            sc.ptr = nullptr;
             return GN_DEVICE_ERROR;
         }
+        sc.ptr = static_cast<char *>(p);
         sc.bytes = sz;
+        zero_from = 0;
     }
-    *out = sc.ptr;
+    if (want_arrivals > zero_from) {
+        // Counters beyond the old region may hold stale payload bytes.
+        const gn_status st = zero_counters(reinterpret_cast<unsigned *>(sc.ptr) + zero_from,
+                                           want_arrivals - zero_from, s);
+        if (st != GN_OK) return st;
+    }
+    sc.arrivals = want_arrivals;
+    *counters = reinterpret_cast<unsigned *>(sc.ptr);
+    *payload_ptr = sc.ptr + head;
     return GN_OK;
 }
 
 // ---- launches ---------------------------------------------------------------
+// Kernel slots, as reported by gn_profile_rows / gn_kernel_name.
+enum { kSlotStats = 0, kSlotFinalize = 1, kSlotApply = 2, kSlots = 3 };
+const char *kKernelNames[kSlots] = {"gn_partial_stats", "gn_finalize_stats", "gn_apply"};
+
 struct Events {
-    hipEvent_t ev[6];  // start/stop of each of the three kernels
+    hipEvent_t ev[2 * kSlots];  // start/stop per slot
 };
 
-void launch_stats(const Plan &p, const uint16_t *x, float *part_s, float *part_q, float eps,
-                  float *mean, float *rstd, hipStream_t s, const Events *ev) {
+void launch_stats(const Plan &p, const uint16_t *x, const StatsOut &o, hipStream_t s,
+                  const Events *ev) {
     const dim3 block(kThreads);
     const dim3 grid1(static_cast<unsigned>(p.N * p.stats.K));
-    if (ev) (void)hipEventRecord(ev->ev[0], s);
-    if (p.vec == 8)
-        gn_partial_stats<8, kUnroll1><<<grid1, block, 0, s>>>(x, p.stats, part_s, part_q);
+    if (ev) (void)hipEventRecord(ev->ev[2 * kSlotStats], s);
+    if (p.vec == 8) {
+        if (p.fused)
+            gn_partial_stats<8, kUnrollStats, false, true><<<grid1, block, 0, s>>>(x, p.stats, o);
+        else
+            gn_partial_stats<8, kUnrollStats, false, false><<<grid1, block, 0, s>>>(x, p.stats, o);
+    } else {
+        if (p.fused)
+            gn_partial_stats<1, kUnrollStats, false, true><<<grid1, block, 0, s>>>(x, p.stats, o);
+        else
+            gn_partial_stats<1, kUnrollStats, false, false><<<grid1, block, 0, s>>>(x, p.stats, o);
+    }
+    if (ev) (void)hipEventRecord(ev->ev[2 * kSlotStats + 1], s);
+    if (!p.fused) {
+        const dim3 grid2(static_cast<unsigned>(p.N * p.stats.G));
+        if (ev) (void)hipEventRecord(ev->ev[2 * kSlotFinalize], s);
+        gn_finalize_stats<<<grid2, block, 0, s>>>(x, p.stats, o);
+        if (ev) (void)hipEventRecord(ev->ev[2 * kSlotFinalize + 1], s);
+    }
+}
+
+template <int VEC, bool SILU>
+void launch_apply_t(const Plan &p, const uint16_t *x, uint16_t *y, const float *mean,
+                    const float *rstd, const float *gamma, const float *beta, hipStream_t s) {
+    const dim3 block(kThreads);
+    const dim3 grid(static_cast<unsigned>(p.N * p.apply.K));
+    if (p.apply_ntl)
+        gn_apply<VEC, kUnrollApply, SILU, true, true><<<grid, block, 0, s>>>(
+            x, y, p.apply, 0, mean, rstd, gamma, beta);
     else
-        gn_partial_stats<1, kUnroll1><<<grid1, block, 0, s>>>(x, p.stats, part_s, part_q);
-    if (ev) (void)hipEventRecord(ev->ev[1], s);
-    const dim3 grid2(static_cast<unsigned>(p.N * p.stats.G));
-    if (ev) (void)hipEventRecord(ev->ev[2], s);
-    gn_finalize_stats<<<grid2, block, 0, s>>>(x, p.stats, p.inv_m, eps, part_s, part_q, mean,
-                                              rstd);
-    if (ev) (void)hipEventRecord(ev->ev[3], s);
+        gn_apply<VEC, kUnrollApply, SILU, false, true><<<grid, block, 0, s>>>(
+            x, y, p.apply, 0, mean, rstd, gamma, beta);
 }
 
 void launch_apply(const Plan &p, const uint16_t *x, uint16_t *y, const float *mean,
                   const float *rstd, const float *gamma, const float *beta, int silu,
                   hipStream_t s, const Events *ev) {
-    const dim3 block(kThreads);
-    const dim3 grid(static_cast<unsigned>(p.N * p.apply.K));
-    if (ev) (void)hipEventRecord(ev->ev[4], s);
+    if (ev) (void)hipEventRecord(ev->ev[2 * kSlotApply], s);
     if (p.vec == 8) {
         if (silu)
-            gn_apply<8, kUnroll2, true><<<grid, block, 0, s>>>(x, y, p.apply, kApplyReverse, mean,
-                                                               rstd, gamma, beta);
+            launch_apply_t<8, true>(p, x, y, mean, rstd, gamma, beta, s);
         else
-            gn_apply<8, kUnroll2, false><<<grid, block, 0, s>>>(x, y, p.apply, kApplyReverse, mean,
-                                                                rstd, gamma, beta);
+            launch_apply_t<8, false>(p, x, y, mean, rstd, gamma, beta, s);
     } else {
         if (silu)
-            gn_apply<1, kUnroll2, true><<<grid, block, 0, s>>>(x, y, p.apply, kApplyReverse, mean,
-                                                               rstd, gamma, beta);
+            launch_apply_t<1, true>(p, x, y, mean, rstd, gamma, beta, s);
         else
-            gn_apply<1, kUnroll2, false><<<grid, block, 0, s>>>(x, y, p.apply, kApplyReverse, mean,
-                                                                rstd, gamma, beta);
+            launch_apply_t<1, false>(p, x, y, mean, rstd, gamma, beta, s);
     }
-    if (ev) (void)hipEventRecord(ev->ev[5], s);
+    if (ev) (void)hipEventRecord(ev->ev[2 * kSlotApply + 1], s);
 }
 
 // Everything a compute entry point needs after its argument checks.
@@ -242,7 +316,7 @@ gn_status finish_launch() {
     return e == hipSuccess ? GN_OK : GN_DEVICE_ERROR;
 }
 
-// The full path, optionally with events around each kernel.
+// The full path, optionally with events around each kernel (iters > 0).
 gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y, int64_t N,
                    int64_t L, int64_t C, int64_t G, float eps, int apply_silu, void *stream,
                    int iters, float *kernel_ms) {
@@ -250,7 +324,7 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
     if (st != GN_OK) return st;
     if (N * L == 0) {
         if (kernel_ms)
-            for (int i = 0; i < 3; ++i) kernel_ms[i] = 0.0f;
+            for (int i = 0; i < kSlots; ++i) kernel_ms[i] = -1.0f;
         return GN_OK;
     }
     Call c;
@@ -260,22 +334,26 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
     const Plan p = make_plan(N, L, C, G);
     const size_t nparts = partial_floats(p);
     const size_t nstats = static_cast<size_t>(N) * G;
-    const size_t bytes = sizeof(float) * (2 * nparts + 2 * nstats);
 
     std::lock_guard<std::mutex> lock(scratch_mutex());
-    void *ws = nullptr;
-    st = scratch_for(c.dev, c.stream, bytes, &ws);
+    unsigned *counters = nullptr;
+    char *payload = nullptr;
+    st = scratch_for(c.dev, c.stream, N, payload_bytes(p, true), &counters, &payload);
     if (st != GN_OK) return st;
-    float *part_s = static_cast<float *>(ws);
-    float *part_q = part_s + nparts;
-    float *mean = part_q + nparts;
-    float *rstd = mean + nstats;
+    StatsOut o;
+    o.part_s = reinterpret_cast<float *>(payload);
+    o.part_q = o.part_s + nparts;
+    o.mean = o.part_q + nparts;
+    o.rstd = o.mean + nstats;
+    o.arrivals = counters;
+    o.inv_m = p.inv_m;
+    o.eps = eps;
     const uint16_t *xb = static_cast<const uint16_t *>(x);
     uint16_t *yb = static_cast<uint16_t *>(y);
 
     if (iters <= 0) {
-        launch_stats(p, xb, part_s, part_q, eps, mean, rstd, c.stream, nullptr);
-        launch_apply(p, xb, yb, mean, rstd, gamma, beta, apply_silu, c.stream, nullptr);
+        launch_stats(p, xb, o, c.stream, nullptr);
+        launch_apply(p, xb, yb, o.mean, o.rstd, gamma, beta, apply_silu, c.stream, nullptr);
         return finish_launch();
     }
 
@@ -285,30 +363,32 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
     for (auto &e : evs)
         for (auto &h : e.ev)
             if (hipEventCreate(&h) != hipSuccess) return GN_DEVICE_ERROR;
-    double sum_ms[3] = {0.0, 0.0, 0.0};
+    double sum_ms[kSlots] = {0.0, 0.0, 0.0};
     st = GN_OK;
     for (int done = 0; done < iters && st == GN_OK;) {
         const int nb = std::min(kBatch, iters - done);
         for (int i = 0; i < nb; ++i) {
-            launch_stats(p, xb, part_s, part_q, eps, mean, rstd, c.stream, &evs[i]);
-            launch_apply(p, xb, yb, mean, rstd, gamma, beta, apply_silu, c.stream, &evs[i]);
+            launch_stats(p, xb, o, c.stream, &evs[i]);
+            launch_apply(p, xb, yb, o.mean, o.rstd, gamma, beta, apply_silu, c.stream, &evs[i]);
         }
         st = finish_launch();
         if (st == GN_OK && hipStreamSynchronize(c.stream) != hipSuccess) st = GN_DEVICE_ERROR;
         for (int i = 0; i < nb && st == GN_OK; ++i)
-            for (int kk = 0; kk < 3; ++kk) {
+            for (int k = 0; k < kSlots; ++k) {
+                if (k == kSlotFinalize && p.fused) continue;
                 float ms = 0.0f;
-                if (hipEventElapsedTime(&ms, evs[i].ev[2 * kk], evs[i].ev[2 * kk + 1]) !=
-                    hipSuccess)
+                if (hipEventElapsedTime(&ms, evs[i].ev[2 * k], evs[i].ev[2 * k + 1]) != hipSuccess)
                     st = GN_DEVICE_ERROR;
-                sum_ms[kk] += ms;
+                sum_ms[k] += ms;
             }
         done += nb;
     }
     for (auto &e : evs)
         for (auto &h : e.ev) (void)hipEventDestroy(h);
     if (st != GN_OK) return st;
-    for (int kk = 0; kk < 3; ++kk) kernel_ms[kk] = static_cast<float>(sum_ms[kk] / iters);
+    for (int k = 0; k < kSlots; ++k)
+        kernel_ms[k] = (k == kSlotFinalize && p.fused) ? -1.0f
+                                                       : static_cast<float>(sum_ms[k] / iters);
     return GN_OK;
 }
 
@@ -321,8 +401,6 @@ bool dense_nhwc(const int64_t st[4], int64_t N, int64_t H, int64_t W, int64_t C)
         if (ext[d] > 1 && st[d] != want[d]) return false;
     return true;
 }
-
-const char *kKernelNames[] = {"gn_partial_stats", "gn_finalize_stats", "gn_apply"};
 
 }  // namespace
 }  // namespace gnsilu
@@ -372,12 +450,19 @@ gn_status gn_stats_rows(const void *x, int64_t N, int64_t L, int64_t C, int64_t 
     const Plan p = make_plan(N, L, C, G);
     const size_t nparts = partial_floats(p);
     std::lock_guard<std::mutex> lock(scratch_mutex());
-    void *ws = nullptr;
-    st = scratch_for(c.dev, c.stream, sizeof(float) * 2 * nparts, &ws);
+    unsigned *counters = nullptr;
+    char *payload = nullptr;
+    st = scratch_for(c.dev, c.stream, N, payload_bytes(p, false), &counters, &payload);
     if (st != GN_OK) return st;
-    float *part_s = static_cast<float *>(ws);
-    launch_stats(p, static_cast<const uint16_t *>(x), part_s, part_s + nparts, eps, mean_out,
-                 rstd_out, c.stream, nullptr);
+    StatsOut o;
+    o.part_s = reinterpret_cast<float *>(payload);
+    o.part_q = o.part_s + nparts;
+    o.arrivals = counters;
+    o.mean = mean_out;
+    o.rstd = rstd_out;
+    o.inv_m = p.inv_m;
+    o.eps = eps;
+    launch_stats(p, static_cast<const uint16_t *>(x), o, c.stream, nullptr);
     return finish_launch();
 }
 
@@ -402,7 +487,7 @@ gn_status gn_profile_rows(const void *x, const float *gamma, const float *beta, 
                           void *stream, int iters, float *kernel_ms, int *n_kernels) {
     if (kernel_ms == nullptr || n_kernels == nullptr || iters < 1 || iters > 100000)
         return GN_INVALID_ARGUMENT;
-    *n_kernels = 3;
+    *n_kernels = kSlots;
     return run_rows(x, gamma, beta, y, N, L, C, G, eps, apply_silu, stream, iters, kernel_ms);
 }
 
@@ -423,14 +508,11 @@ gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_
     plan_out[4] = p.stats.K;
     plan_out[5] = p.apply.tpc;
     plan_out[6] = p.apply.K;
-    plan_out[7] = static_cast<int64_t>(
-        sizeof(float) * (2 * partial_floats(p) + 2 * static_cast<size_t>(N) * G));
+    plan_out[7] = static_cast<int64_t>(arrivals_bytes(N) + payload_bytes(p, true));
     return GN_OK;
 }
 
-const char *gn_kernel_name(int i) {
-    return (i >= 0 && i < 3) ? kKernelNames[i] : nullptr;
-}
+const char *gn_kernel_name(int i) { return (i >= 0 && i < kSlots) ? kKernelNames[i] : nullptr; }
 
 const char *gn_status_string(gn_status s) {
     switch (s) {
@@ -442,6 +524,6 @@ const char *gn_status_string(gn_status s) {
     return "unknown gn_status";
 }
 
-int gn_version(void) { return 100; }
+int gn_version(void) { return 200; }
 
 }  // extern "C"

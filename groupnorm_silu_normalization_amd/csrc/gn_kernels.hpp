@@ -58,37 +58,57 @@ __device__ __forceinline__ float silu_f32(float t) {
 // VEC consecutive bf16 values of one lane.
 template <int VEC> struct Pack;
 
+// NT: the access carries the nontemporal hint (streaming cache policy), for
+// data this pass touches once.
 template <> struct Pack<8> {
     u32x4 w;
+    template <bool NT = false>
     __device__ __forceinline__ static Pack load(const uint16_t *p) {
         Pack v;
-        v.w = *reinterpret_cast<const u32x4 *>(p);
+        const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+        if constexpr (NT)
+            v.w = __builtin_nontemporal_load(q);
+        else
+            v.w = *q;
         return v;
     }
     __device__ __forceinline__ float get(int j) const {
         const uint32_t word = w[j >> 1];
         return (j & 1) ? bf16_hi(word) : bf16_lo(word);
     }
+    template <bool NT = false>
     __device__ __forceinline__ static void store(uint16_t *p, const float (&o)[8]) {
         u32x4 v;
         v[0] = pack_bf16x2(o[0], o[1]);
         v[1] = pack_bf16x2(o[2], o[3]);
         v[2] = pack_bf16x2(o[4], o[5]);
         v[3] = pack_bf16x2(o[6], o[7]);
-        *reinterpret_cast<u32x4 *>(p) = v;
+        u32x4 *q = reinterpret_cast<u32x4 *>(p);
+        if constexpr (NT)
+            __builtin_nontemporal_store(v, q);
+        else
+            *q = v;
     }
 };
 
 template <> struct Pack<1> {
     uint16_t b;
+    template <bool NT = false>
     __device__ __forceinline__ static Pack load(const uint16_t *p) {
         Pack v;
-        v.b = *p;
+        if constexpr (NT)
+            v.b = __builtin_nontemporal_load(p);
+        else
+            v.b = *p;
         return v;
     }
     __device__ __forceinline__ float get(int) const { return bf16_bits_to_f32(b); }
+    template <bool NT = false>
     __device__ __forceinline__ static void store(uint16_t *p, const float (&o)[1]) {
-        *p = f32_to_bf16_bits(o[0]);
+        if constexpr (NT)
+            __builtin_nontemporal_store(f32_to_bf16_bits(o[0]), p);
+        else
+            *p = f32_to_bf16_bits(o[0]);
     }
 };
 
@@ -104,15 +124,57 @@ struct Geometry {
     int G;             // groups
 };
 
+// Where the statistics go.
+struct StatsOut {
+    float *part_s;        // [N][K][G] pivot-shifted sum of each group over chunk k
+    float *part_q;        // [N][K][G] pivot-shifted sum of squares
+    unsigned *arrivals;   // [N] statistics workgroups of sample n finished (fused
+                          // finalize only); zero between calls
+    float *mean;          // [N][G]
+    float *rstd;          // [N][G]
+    double inv_m;         // 1 / (L*Cg)
+    float eps;
+};
+
+// mean = p + S/M, var = max(Q/M - (S/M)^2, 0), rstd = 1/sqrt(var + eps); the
+// few scalar operations in fp64, results stored as fp32.
+__device__ __forceinline__ void group_moments(float S, float Q, float pivot, double inv_m,
+                                              float eps, float *mean, float *rstd) {
+    const double ms = static_cast<double>(S) * inv_m;
+    double var = static_cast<double>(Q) * inv_m - ms * ms;
+    if (var < 0.0) var = 0.0;
+    *mean = static_cast<float>(static_cast<double>(pivot) + ms);
+    *rstd = static_cast<float>(1.0 / sqrt(var + static_cast<double>(eps)));
+}
+
+// A partial written by step 1.  When the finalize is fused, the partials are
+// agent-scope atomic stores: write-through (sc1), so they are visible to a
+// workgroup on any XCD once the store has completed, without writing back the
+// whole L2 as an agent-scope release fence would.
+template <bool COHERENT>
+__device__ __forceinline__ void store_partial(float *p, float v) {
+    if constexpr (COHERENT)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+
 // ---------------------------------------------------------------------------
 // Step 1: partial statistics.  One workgroup per (sample n, chunk k); writes
 // the pivot-shifted sum and sum of squares of each group over its chunk to
-// part_s / part_q at [(n*G + g)*K + k].
+// part_s / part_q at [(n*K + k)*G + g].
+// FUSED (requires G <= kThreads): the last workgroup of sample n to finish,
+// found with an agent-scope atomic counter, also performs step 2 for that
+// sample -- a fixed-order reduction over the K chunk partials of each group,
+// whichever workgroup happens to be last -- and resets the counter to zero.
+// Ordering: every lane waits for its write-through partial stores to
+// complete (s_waitcnt vmcnt(0)), the workgroup barrier follows, and only then
+// is the arrival counted; the last workgroup reads the partials with
+// agent-scope (coherent) loads.
 // ---------------------------------------------------------------------------
-template <int VEC, int UNROLL>
+template <int VEC, int UNROLL, bool NTL, bool FUSED>
 __global__ __launch_bounds__(kThreads) void gn_partial_stats(
-    const uint16_t *__restrict__ x, Geometry geo, float *__restrict__ part_s,
-    float *__restrict__ part_q) {
+    const uint16_t *__restrict__ x, Geometry geo, StatsOut out) {
     constexpr int TILE = kThreads * VEC;
     __shared__ float red_s[TILE];
     __shared__ float red_q[TILE];
@@ -142,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void gn_partial_stats(
     for (; tt + UNROLL <= t_full_end; tt += UNROLL) {
         Pack<VEC> v[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) v[u] = Pack<VEC>::load(p + u * TILE);
+        for (int u = 0; u < UNROLL; ++u) v[u] = Pack<VEC>::template load<NTL>(p + u * TILE);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
 #pragma unroll
@@ -155,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void gn_partial_stats(
         p += UNROLL * TILE;
     }
     for (; tt < t_full_end; ++tt) {
-        const Pack<VEC> v = Pack<VEC>::load(p);
+        const Pack<VEC> v = Pack<VEC>::template load<NTL>(p);
 #pragma unroll
         for (int j = 0; j < VEC; ++j) {
             const float d = v.get(j) - piv[j];
@@ -169,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void gn_partial_stats(
         // lane's vector lies wholly inside or wholly outside the sample.
         const int64_t off = tt * TILE + tid * VEC;
         if (off < geo.E) {
-            const Pack<VEC> v = Pack<VEC>::load(xs + off);
+            const Pack<VEC> v = Pack<VEC>::template load<NTL>(xs + off);
 #pragma unroll
             for (int j = 0; j < VEC; ++j) {
                 const float d = v.get(j) - piv[j];
@@ -214,9 +276,9 @@ __global__ __launch_bounds__(kThreads) void gn_partial_stats(
             __syncthreads();
         }
         if (part == 0) {
-            const int64_t o = (n * G + g) * geo.K + k;
-            part_s[o] = red_s[tid];
-            part_q[o] = red_q[tid];
+            const int64_t o = (n * geo.K + k) * G + g;
+            store_partial<FUSED>(out.part_s + o, red_s[tid]);
+            store_partial<FUSED>(out.part_q + o, red_q[tid]);
         }
     } else {
         const int P = TILE / G;  // < VEC slots per group
@@ -227,34 +289,91 @@ __global__ __launch_bounds__(kThreads) void gn_partial_stats(
                 as += red_s[i];
                 aq += red_q[i];
             }
-            const int64_t o = (n * G + g) * geo.K + k;
-            part_s[o] = as;
-            part_q[o] = aq;
+            const int64_t o = (n * geo.K + k) * G + g;
+            store_partial<FUSED>(out.part_s + o, as);
+            store_partial<FUSED>(out.part_q + o, aq);
         }
+    }
+
+    if constexpr (FUSED) {
+        __shared__ int last;
+        __builtin_amdgcn_s_waitcnt(0);  // this lane's partial stores have completed ...
+        __syncthreads();                // ... in every lane, before the arrival is counted
+        if (tid == 0) {
+            const unsigned before = __hip_atomic_fetch_add(
+                out.arrivals + n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = (before == static_cast<unsigned>(geo.K - 1));
+        }
+        __syncthreads();
+        if (!last) return;
+        // G <= kThreads: tpg threads per group, thread tid = g + G*j sums the
+        // chunks k = j, j + tpg, ... (coalesced along g), then a tree over j.
+        const int tpg = kThreads / G;
+        const int g = tid & (G - 1);
+        const int j = tid / G;
+        // Loads are issued kBatch at a time so their round trips overlap;
+        // the sums still run over k in increasing order.
+        constexpr int kBatch = 8;
+        const float *ps = out.part_s + n * geo.K * G + g;
+        const float *pq = out.part_q + n * geo.K * G + g;
+        float as = 0.0f, aq = 0.0f;
+        int64_t kk = j;
+        for (; kk + (kBatch - 1) * tpg < geo.K; kk += kBatch * tpg) {
+            float vs[kBatch], vq[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int64_t o = (kk + b * tpg) * G;
+                vs[b] = __hip_atomic_load(ps + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                vq[b] = __hip_atomic_load(pq + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                as += vs[b];
+                aq += vq[b];
+            }
+        }
+        for (; kk < geo.K; kk += tpg) {
+            as += __hip_atomic_load(ps + kk * G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            aq += __hip_atomic_load(pq + kk * G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        red_s[tid] = as;
+        red_q[tid] = aq;
+        __syncthreads();
+        for (int stride = tpg >> 1; stride > 0; stride >>= 1) {
+            if (j < stride) {
+                red_s[tid] += red_s[tid + stride * G];
+                red_q[tid] += red_q[tid + stride * G];
+            }
+            __syncthreads();
+        }
+        if (j == 0) {
+            const float pivot = bf16_bits_to_f32(xs[static_cast<int64_t>(g) << geo.cg_shift]);
+            group_moments(red_s[tid], red_q[tid], pivot, out.inv_m, out.eps,
+                          out.mean + n * G + g, out.rstd + n * G + g);
+        }
+        if (tid == 0)
+            __hip_atomic_store(out.arrivals + n, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Step 2: finalize.  One workgroup per (n, g): a fixed-order tree over the K
-// chunk partials, then mean and rstd (the scalar arithmetic in fp64, stored
-// as fp32).
+// Step 2 as its own kernel, used when G > kThreads (too many groups for one
+// workgroup to finish quickly): one workgroup per (n, g), a fixed-order tree
+// over the K chunk partials.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void gn_finalize_stats(
-    const uint16_t *__restrict__ x, Geometry geo, double inv_m, float eps,
-    const float *__restrict__ part_s, const float *__restrict__ part_q,
-    float *__restrict__ mean_out, float *__restrict__ rstd_out) {
+    const uint16_t *__restrict__ x, Geometry geo, StatsOut out) {
     __shared__ float rs[kThreads];
     __shared__ float rq[kThreads];
     const int tid = threadIdx.x;
     const int64_t ng = blockIdx.x;
     const int64_t n = ng / geo.G;
     const int g = static_cast<int>(ng - n * geo.G);
-    const float *ps = part_s + ng * geo.K;
-    const float *pq = part_q + ng * geo.K;
     float s = 0.0f, q = 0.0f;
     for (int64_t k = tid; k < geo.K; k += kThreads) {
-        s += ps[k];
-        q += pq[k];
+        const int64_t o = (n * geo.K + k) * geo.G + g;
+        s += out.part_s[o];
+        q += out.part_q[o];
     }
     rs[tid] = s;
     rq[tid] = q;
@@ -267,14 +386,17 @@ __global__ __launch_bounds__(kThreads) void gn_finalize_stats(
         __syncthreads();
     }
     if (tid == 0) {
-        const double ms = static_cast<double>(rs[0]) * inv_m;
-        double var = static_cast<double>(rq[0]) * inv_m - ms * ms;
-        if (var < 0.0) var = 0.0;
         const float pivot =
             bf16_bits_to_f32(x[n * geo.E + (static_cast<int64_t>(g) << geo.cg_shift)]);
-        mean_out[ng] = static_cast<float>(static_cast<double>(pivot) + ms);
-        rstd_out[ng] = static_cast<float>(1.0 / sqrt(var + static_cast<double>(eps)));
+        group_moments(rs[0], rq[0], pivot, out.inv_m, out.eps, out.mean + ng, out.rstd + ng);
     }
+}
+
+// Zero-fill for the arrival counters of a fresh scratch buffer (a kernel, so
+// the clearing is ordinary stream work).
+__global__ __launch_bounds__(kThreads) void gn_zero_u32(unsigned *p, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (i < n) p[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -285,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void gn_finalize_stats(
 // x and y may be the same buffer (each element is read, then written, by one
 // lane), so they carry no __restrict__.
 // ---------------------------------------------------------------------------
-template <int VEC, int UNROLL, bool SILU>
+template <int VEC, int UNROLL, bool SILU, bool NTL, bool NTS>
 __global__ __launch_bounds__(kThreads) void gn_apply(
     const uint16_t *x, uint16_t *y, Geometry geo, int reverse,
     const float *__restrict__ mean, const float *__restrict__ rstd,
@@ -331,29 +453,29 @@ __global__ __launch_bounds__(kThreads) void gn_apply(
     for (; tt + UNROLL <= t_full_end; tt += UNROLL) {
         Pack<VEC> v[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) v[u] = Pack<VEC>::load(x + off + u * TILE);
+        for (int u = 0; u < UNROLL; ++u) v[u] = Pack<VEC>::template load<NTL>(x + off + u * TILE);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             float o[VEC];
             transform(v[u], o);
-            Pack<VEC>::store(y + off + u * TILE, o);
+            Pack<VEC>::template store<NTS>(y + off + u * TILE, o);
         }
         off += UNROLL * TILE;
     }
     for (; tt < t_full_end; ++tt) {
-        const Pack<VEC> v = Pack<VEC>::load(x + off);
+        const Pack<VEC> v = Pack<VEC>::template load<NTL>(x + off);
         float o[VEC];
         transform(v, o);
-        Pack<VEC>::store(y + off, o);
+        Pack<VEC>::template store<NTS>(y + off, o);
         off += TILE;
     }
     if (tt < t_end) {
         const int64_t rel = tt * TILE + tid * VEC;
         if (rel < geo.E) {
-            const Pack<VEC> v = Pack<VEC>::load(x + base + rel);
+            const Pack<VEC> v = Pack<VEC>::template load<NTL>(x + base + rel);
             float o[VEC];
             transform(v, o);
-            Pack<VEC>::store(y + base + rel, o);
+            Pack<VEC>::template store<NTS>(y + base + rel, o);
         }
     }
 }

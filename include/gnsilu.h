@@ -35,10 +35,10 @@
  * Ownership: the caller owns x, y, gamma, beta and the statistics buffers;
  *   they must stay valid until the stream has executed the call.  The
  *   library owns a scratch buffer per (device, stream) for the partial sums
- *   (a few hundred KiB for the decoder shapes, grown on demand, held until
- *   the process ends).  Calls enqueued on one stream from several host
- *   threads are serialised by the library; calls on different streams use
- *   different scratch buffers.
+ *   and per-sample arrival counters (tens of KiB for the decoder shapes,
+ *   grown on demand, held until the process ends).  Calls enqueued on one
+ *   stream from several host threads are serialised by the library; calls on
+ *   different streams use different scratch buffers.
  * Synchrony: every compute call is asynchronous on `stream` and returns once
  *   the kernels are enqueued; a fault inside a kernel surfaces at the
  *   caller's next synchronisation (gn_profile_rows excepted, which
@@ -118,8 +118,10 @@ gn_status gn_apply_rows(const void *x, const float *mean, const float *rstd,
 
 /* Measurement helper: runs gn_silu_rows `iters` times on `stream` with a
  * pair of HIP events around every kernel launch, synchronises, and writes
- * the mean duration in milliseconds of each kernel of the path to
- * kernel_ms[0 .. *n_kernels-1] (capacity 4).  gn_kernel_name(i) names them.
+ * the mean duration in milliseconds of each kernel slot of the path to
+ * kernel_ms[0 .. *n_kernels-1] (capacity 4); gn_kernel_name(i) names the
+ * slots.  A slot whose kernel is not launched for this shape (the separate
+ * finalize, when the statistics kernel finishes the groups itself) reads -1.
  * iters must be in [1, 100000]. */
 gn_status gn_profile_rows(const void *x, const float *gamma, const float *beta, void *y,
                           int64_t N, int64_t L, int64_t C, int64_t G,

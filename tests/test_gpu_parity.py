@@ -313,14 +313,19 @@ def test_side_stream(gn, dev, oracle):
 
 def test_profile_helper(gn, dev):
     from gn_inputs import WORKLOADS, make_inputs
-    w = WORKLOADS[1]
+    w = WORKLOADS[2]
     x_bits, gamma, beta = make_inputs(w)
     x = to_dev_bits(x_bits, dev).reshape(w.N, w.L, w.C)
     y = torch.empty_like(x)
     ms = gn.profile_rows(x, w.G, torch.from_numpy(gamma).to(dev), torch.from_numpy(beta).to(dev),
                          w.eps, True, y, 3)
-    assert set(ms) == {"gn_partial_stats", "gn_finalize_stats", "gn_apply"}
+    # G = 32: the statistics kernel finishes the groups itself (no finalize launch)
+    assert set(ms) == {"gn_partial_stats", "gn_apply"}
     assert all(v > 0 for v in ms.values())
+    x2 = to_dev_bits(make_inputs(w)[0][: 4 * 16384 * 512], dev).reshape(4, 16384, 512)
+    ms2 = gn.profile_rows(x2, 512, None, None, w.eps, True, torch.empty_like(x2), 2)
+    # G = 512 > 256 threads: a separate finalize kernel
+    assert set(ms2) == {"gn_partial_stats", "gn_finalize_stats", "gn_apply"}
 
 
 # ------------------------------------------------------ unsupported contract
@@ -366,3 +371,29 @@ def test_extent_one_dims_accept_any_stride(gn, dev, oracle):
     torch.cuda.synchronize()
     compare(from_dev_bits(y), oracle.gn_silu(x_bits, gamma, beta, N, H * W, C, G, 1e-6, 1),
             "extent-1 strides")
+
+
+def test_sample_count_changes_on_one_stream(gn, dev, oracle):
+    """The per-sample arrival counters live at the front of the stream's
+    scratch and only grow; calls whose N rises and falls on the same stream
+    must each see cleared counters (a stale counter would skip or repeat the
+    finalize of a sample)."""
+    from gn_inputs import make_custom
+    L, C, G = 3000, 64, 16
+    for N in (1, 9, 3, 40, 2, 40, 1):
+        x_bits, gamma, beta = make_custom(N, L, C, seed=100 + N, mean_range=(-2, 2))
+        for rep in range(2):
+            y = run_rows(gn, dev, x_bits, gamma, beta, N, L, C, G, 1e-6, 1)
+            compare(y, oracle.gn_silu(x_bits, gamma, beta, N, L, C, G, 1e-6, 1),
+                    "N=%d rep %d" % (N, rep))
+
+
+def test_many_samples_one_workgroup_each(gn, dev, oracle):
+    """N above the statistics workgroup target: one workgroup per sample, each
+    of which is also the last to arrive for its sample."""
+    from gn_inputs import make_custom
+    N, L, C, G = 300, 64, 32, 8
+    x_bits, gamma, beta = make_custom(N, L, C, seed=300, mean_range=(-3, 3))
+    assert gn.plan_rows(N, L, C, G)["K1"] == 1
+    y = run_rows(gn, dev, x_bits, gamma, beta, N, L, C, G, 1e-6, 1)
+    compare(y, oracle.gn_silu(x_bits, gamma, beta, N, L, C, G, 1e-6, 1), "N=300")

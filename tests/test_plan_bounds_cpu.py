@@ -97,10 +97,20 @@ def test_plan_keeps_every_access_in_bounds(N, L, C, G):
     check_streaming_pass(N, E, vec, p["tiles"], p["full"], p["tpc2"], p["K2"])
     # pivot reads x[n, 0, g*Cg] lie in row 0 of the sample
     assert (G - 1) * (C // G) < E
-    # partial-sum slots (n*G + g)*K1 + k and the scratch that holds them
+    # partial-sum slots (n*K1 + k)*G + g, written by step 1 and read by the
+    # finalize (fused tail: thread g + G*j reads k = j, j + 256/G, ...)
     nparts = N * G * p["K1"]
-    assert (N * G - 1) * p["K1"] + p["K1"] - 1 < nparts
-    assert p["scratch_bytes"] == 4 * (2 * nparts + 2 * N * G)
+    assert ((N - 1) * p["K1"] + p["K1"] - 1) * G + G - 1 < nparts
+    if G <= THREADS:
+        tpg = THREADS // G
+        for j in range(tpg):
+            ks = range(j, p["K1"], tpg)
+            assert all(((N - 1) * p["K1"] + k) * G + (G - 1) < nparts for k in ks)
+        # every chunk of every group is read exactly once by the tail
+        seen = sorted(k for j in range(tpg) for k in range(j, p["K1"], tpg))
+        assert seen == list(range(p["K1"]))
+    counters = -(-4 * N // 256) * 256
+    assert p["scratch_bytes"] == counters + 4 * (2 * nparts + 2 * N * G)
     assert N * G < 2 ** 24
     if C * 8 <= 65536:
         lds_slots(C, G, vec)
@@ -113,9 +123,14 @@ def test_plan_is_shape_only_and_bounded():
     # statistics workgroups stay near the target, so partials stay small
     for N, L, C, G in SHAPES:
         p = gn.plan_rows(N, L, C, G)
-        assert N * p["K1"] <= 2048 + N
-        assert N * p["K2"] <= 4096 + N
+        total = N * p["tiles"]
+        assert p["tpc1"] <= 1024                       # each lane's sequential run
+        assert N * p["K1"] <= max(256, -(-total // 1024)) + N
+        assert N * p["K2"] <= 2048 + N
         assert p == gn.plan_rows(N, L, C, G)
+    # the decoder shapes: one statistics workgroup per CU of an MI355X
+    for N, L, C, G in SHAPES[:5]:
+        assert gn.plan_rows(N, L, C, G)["K1"] == 256
 
 
 def test_plan_declines_like_the_entry_points():
