@@ -186,24 +186,23 @@ gn_status zero_counters(unsigned *p, int64_t n, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? GN_OK : GN_DEVICE_ERROR;
 }
 
-// Caller holds scratch_mutex().  Returns the counters (>= n of them, all zero
-// in stream order) and the payload (>= payload bytes).  Grows the buffer when
-// needed; the old one is released only after the stream has drained the work
-// that used it.
+// Caller holds scratch_mutex().  Returns the arrival counters (>= n of them,
+// all zero in stream order) and the payload (>= payload bytes).  Grows the
+// buffer when needed; the old one is released only after the stream has
+// drained the work that used it.
 gn_status scratch_for(int dev, hipStream_t s, int64_t n, size_t payload, unsigned **counters,
                       char **payload_ptr) {
     Scratch &sc = scratch_map()[{dev, reinterpret_cast<uintptr_t>(s)}];
     const int64_t want_arrivals = std::max(sc.arrivals, n);
     const size_t head = arrivals_bytes(want_arrivals);
     const size_t need = head + payload;
-    int64_t zero_from = sc.arrivals;
+    bool clear = want_arrivals > sc.arrivals;  // the counter region grows
     if (sc.bytes < need) {
         if (sc.ptr != nullptr) {
             if (hipStreamSynchronize(s) != hipSuccess) return GN_DEVICE_ERROR;
             (void)hipFree(sc.ptr);
             sc.ptr = nullptr;
             sc.bytes = 0;
-            sc.arrivals = 0;
         }
         size_t sz = size_t{1} << 16;
         while (sz < need) sz <<= 1;
@@ -214,12 +213,13 @@ gn_status scratch_for(int dev, hipStream_t s, int64_t n, size_t payload, unsigne
         }
         sc.ptr = static_cast<char *>(p);
         sc.bytes = sz;
-        zero_from = 0;
+        clear = true;  // fresh memory
     }
-    if (want_arrivals > zero_from) {
-        // Counters beyond the old region may hold stale payload bytes.
-        const gn_status st = zero_counters(reinterpret_cast<unsigned *>(sc.ptr) + zero_from,
-                                           want_arrivals - zero_from, s);
+    if (clear) {
+        // Counters beyond the old region may hold stale payload bytes: clear
+        // the region, in stream order, before this call's kernels.
+        const gn_status st =
+            zero_counters(reinterpret_cast<unsigned *>(sc.ptr), want_arrivals, s);
         if (st != GN_OK) return st;
     }
     sc.arrivals = want_arrivals;
@@ -364,6 +364,7 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
         for (auto &h : e.ev)
             if (hipEventCreate(&h) != hipSuccess) return GN_DEVICE_ERROR;
     double sum_ms[kSlots] = {0.0, 0.0, 0.0};
+    auto launched = [&](int k) { return !(k == kSlotFinalize && p.fused); };
     st = GN_OK;
     for (int done = 0; done < iters && st == GN_OK;) {
         const int nb = std::min(kBatch, iters - done);
@@ -375,7 +376,7 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
         if (st == GN_OK && hipStreamSynchronize(c.stream) != hipSuccess) st = GN_DEVICE_ERROR;
         for (int i = 0; i < nb && st == GN_OK; ++i)
             for (int k = 0; k < kSlots; ++k) {
-                if (k == kSlotFinalize && p.fused) continue;
+                if (!launched(k)) continue;
                 float ms = 0.0f;
                 if (hipEventElapsedTime(&ms, evs[i].ev[2 * k], evs[i].ev[2 * k + 1]) != hipSuccess)
                     st = GN_DEVICE_ERROR;
@@ -387,8 +388,7 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
         for (auto &h : e.ev) (void)hipEventDestroy(h);
     if (st != GN_OK) return st;
     for (int k = 0; k < kSlots; ++k)
-        kernel_ms[k] = (k == kSlotFinalize && p.fused) ? -1.0f
-                                                       : static_cast<float>(sum_ms[k] / iters);
+        kernel_ms[k] = launched(k) ? static_cast<float>(sum_ms[k] / iters) : -1.0f;
     return GN_OK;
 }
 
@@ -524,6 +524,6 @@ const char *gn_status_string(gn_status s) {
     return "unknown gn_status";
 }
 
-int gn_version(void) { return 200; }
+int gn_version(void) { return 300; }
 
 }  // extern "C"

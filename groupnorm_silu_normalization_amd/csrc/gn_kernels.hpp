@@ -160,33 +160,16 @@ __device__ __forceinline__ void store_partial(float *p, float v) {
 }
 
 // ---------------------------------------------------------------------------
-// Step 1: partial statistics.  One workgroup per (sample n, chunk k); writes
-// the pivot-shifted sum and sum of squares of each group over its chunk to
-// part_s / part_q at [(n*K + k)*G + g].
-// FUSED (requires G <= kThreads): the last workgroup of sample n to finish,
-// found with an agent-scope atomic counter, also performs step 2 for that
-// sample -- a fixed-order reduction over the K chunk partials of each group,
-// whichever workgroup happens to be last -- and resets the counter to zero.
-// Ordering: every lane waits for its write-through partial stores to
-// complete (s_waitcnt vmcnt(0)), the workgroup barrier follows, and only then
-// is the arrival counted; the last workgroup reads the partials with
-// agent-scope (coherent) loads.
+// Pieces of steps 1-3, kept as functions so the order of every
+// floating-point operation is written down once.
 // ---------------------------------------------------------------------------
-template <int VEC, int UNROLL, bool NTL, bool FUSED>
-__global__ __launch_bounds__(kThreads) void gn_partial_stats(
-    const uint16_t *__restrict__ x, Geometry geo, StatsOut out) {
-    constexpr int TILE = kThreads * VEC;
-    __shared__ float red_s[TILE];
-    __shared__ float red_q[TILE];
 
-    const int tid = threadIdx.x;
-    const int64_t wg = blockIdx.x;
-    const int64_t n = wg / geo.K;
-    const int64_t k = wg - n * geo.K;
-    const uint16_t *xs = x + n * geo.E;
+// Pivots p_g of the lane's VEC channel slots; zeroed running sums.
+template <int VEC>
+__device__ __forceinline__ void init_slots(const uint16_t *xs, const Geometry &geo, int tid,
+                                           float (&piv)[VEC], float (&s)[VEC],
+                                           float (&q)[VEC]) {
     const int cmask = geo.C - 1;
-
-    float piv[VEC], s[VEC], q[VEC];
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
         const int c = (tid * VEC + j) & cmask;
@@ -194,62 +177,50 @@ __global__ __launch_bounds__(kThreads) void gn_partial_stats(
         s[j] = 0.0f;
         q[j] = 0.0f;
     }
+}
 
-    const int64_t t_begin = k * geo.tpc;
-    const int64_t t_end = t_begin + geo.tpc < geo.tiles ? t_begin + geo.tpc : geo.tiles;
-    const int64_t t_full_end = t_end < geo.full ? t_end : geo.full;
-    const uint16_t *p = xs + t_begin * TILE + tid * VEC;
+template <int VEC>
+__device__ __forceinline__ void accumulate(const Pack<VEC> &v, const float (&piv)[VEC],
+                                           float (&s)[VEC], float (&q)[VEC]) {
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+        const float d = v.get(j) - piv[j];
+        s[j] += d;
+        q[j] = fmaf(d, d, q[j]);
+    }
+}
 
-    int64_t tt = t_begin;
-    for (; tt + UNROLL <= t_full_end; tt += UNROLL) {
-        Pack<VEC> v[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) v[u] = Pack<VEC>::template load<NTL>(p + u * TILE);
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-                const float d = v[u].get(j) - piv[j];
-                s[j] += d;
-                q[j] = fmaf(d, d, q[j]);
-            }
-        }
-        p += UNROLL * TILE;
-    }
-    for (; tt < t_full_end; ++tt) {
-        const Pack<VEC> v = Pack<VEC>::template load<NTL>(p);
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-            const float d = v.get(j) - piv[j];
-            s[j] += d;
-            q[j] = fmaf(d, d, q[j]);
-        }
-        p += TILE;
-    }
-    if (tt < t_end) {
-        // The sample's last tile is partial; E is a multiple of VEC, so each
-        // lane's vector lies wholly inside or wholly outside the sample.
-        const int64_t off = tt * TILE + tid * VEC;
-        if (off < geo.E) {
-            const Pack<VEC> v = Pack<VEC>::template load<NTL>(xs + off);
-#pragma unroll
-            for (int j = 0; j < VEC; ++j) {
-                const float d = v.get(j) - piv[j];
-                s[j] += d;
-                q[j] = fmaf(d, d, q[j]);
-            }
-        }
-    }
+// Tiles [t_begin, t_end) of a chunk; the first t_full_end - t_begin of them
+// lie wholly inside the sample, the one after that (if any) is the sample's
+// partial last tile.
+struct ChunkRange {
+    int64_t t_begin, t_end, t_full_end;
+};
+__device__ __forceinline__ ChunkRange chunk_range(const Geometry &geo, int64_t k) {
+    ChunkRange r;
+    r.t_begin = k * geo.tpc;
+    r.t_end = r.t_begin + geo.tpc < geo.tiles ? r.t_begin + geo.tpc : geo.tiles;
+    r.t_full_end = r.t_end < geo.full ? r.t_end : geo.full;
+    if (r.t_full_end < r.t_begin) r.t_full_end = r.t_begin;
+    return r;
+}
 
-    // Workgroup reduction.  Slot i = tid*VEC + j of red_* holds channel
-    // i mod C; the P = TILE/G slots of group g are i = r*C + g*Cg + u.
+// Workgroup reduction of the lanes' slot sums to per-group partials of chunk
+// k, written to out.part_s / out.part_q at [(n*K + k)*G + g].  Slot
+// i = tid*VEC + j of red_* holds channel i mod C; the P = TILE/G slots of
+// group g are i = r*C + g*Cg + u.
+template <int VEC, bool COHERENT>
+__device__ __forceinline__ void write_group_partials(const float (&s)[VEC], const float (&q)[VEC],
+                                                     float *red_s, float *red_q,
+                                                     const Geometry &geo, int64_t n, int64_t k,
+                                                     const StatsOut &out, int tid) {
+    constexpr int TILE = kThreads * VEC;
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
         red_s[tid * VEC + j] = s[j];
         red_q[tid * VEC + j] = q[j];
     }
     __syncthreads();
-
     const int G = geo.G;
     const int cgm = (1 << geo.cg_shift) - 1;
     if (G <= kThreads) {
@@ -277,8 +248,8 @@ __global__ __launch_bounds__(kThreads) void gn_partial_stats(
         }
         if (part == 0) {
             const int64_t o = (n * geo.K + k) * G + g;
-            store_partial<FUSED>(out.part_s + o, red_s[tid]);
-            store_partial<FUSED>(out.part_q + o, red_q[tid]);
+            store_partial<COHERENT>(out.part_s + o, red_s[tid]);
+            store_partial<COHERENT>(out.part_q + o, red_q[tid]);
         }
     } else {
         const int P = TILE / G;  // < VEC slots per group
@@ -290,69 +261,169 @@ __global__ __launch_bounds__(kThreads) void gn_partial_stats(
                 aq += red_q[i];
             }
             const int64_t o = (n * geo.K + k) * G + g;
-            store_partial<FUSED>(out.part_s + o, as);
-            store_partial<FUSED>(out.part_q + o, aq);
+            store_partial<COHERENT>(out.part_s + o, as);
+            store_partial<COHERENT>(out.part_q + o, aq);
         }
     }
+}
 
+// Counts this workgroup's arrival for sample n once its (write-through)
+// partial stores have completed; true, uniformly, in the last of the K.
+__device__ __forceinline__ bool arrive_is_last(const StatsOut &out, int64_t n, int64_t K,
+                                               int tid) {
+    __shared__ int last;
+    __builtin_amdgcn_s_waitcnt(0);  // this lane's stores have completed ...
+    __syncthreads();                // ... in every lane, before the arrival is counted
+    if (tid == 0) {
+        const unsigned before =
+            __hip_atomic_fetch_add(out.arrivals + n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = (before == static_cast<unsigned>(K - 1));
+    }
+    __syncthreads();
+    return last != 0;
+}
+
+// Step 2 for sample n, run by the last workgroup to arrive (G <= kThreads):
+// thread tid = g + G*j sums the chunks k = j, j + tpg, ... in increasing
+// order (coalesced along g; loads issued kBatch at a time so their round
+// trips overlap -- one round trip for K <= 16*tpg), a fixed tree over j
+// follows, and mean/rstd are written.  The arrival counter is reset to zero
+// for the next call.
+__device__ __forceinline__ void finalize_sample(const uint16_t *xs, const Geometry &geo, int64_t n,
+                                                const StatsOut &out, float *red_s, float *red_q,
+                                                int tid) {
+    const int G = geo.G;
+    const int tpg = kThreads / G;
+    const int g = tid & (G - 1);
+    const int j = tid / G;
+    constexpr int kBatch = 16;
+    const float *ps = out.part_s + n * geo.K * G + g;
+    const float *pq = out.part_q + n * geo.K * G + g;
+    float as = 0.0f, aq = 0.0f;
+    int64_t kk = j;
+    for (; kk + (kBatch - 1) * tpg < geo.K; kk += kBatch * tpg) {
+        float vs[kBatch], vq[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int64_t o = (kk + b * tpg) * G;
+            vs[b] = __hip_atomic_load(ps + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            vq[b] = __hip_atomic_load(pq + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            as += vs[b];
+            aq += vq[b];
+        }
+    }
+    for (; kk < geo.K; kk += tpg) {
+        as += __hip_atomic_load(ps + kk * G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        aq += __hip_atomic_load(pq + kk * G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    red_s[tid] = as;
+    red_q[tid] = aq;
+    __syncthreads();
+    for (int stride = tpg >> 1; stride > 0; stride >>= 1) {
+        if (j < stride) {
+            red_s[tid] += red_s[tid + stride * G];
+            red_q[tid] += red_q[tid + stride * G];
+        }
+        __syncthreads();
+    }
+    if (j == 0) {
+        const float pivot = bf16_bits_to_f32(xs[static_cast<int64_t>(g) << geo.cg_shift]);
+        group_moments(red_s[tid], red_q[tid], pivot, out.inv_m, out.eps, out.mean + n * G + g,
+                      out.rstd + n * G + g);
+    }
+    if (tid == 0)
+        __hip_atomic_store(out.arrivals + n, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// scale = gamma*rstd, shift = beta - mean*scale for the lane's VEC channels.
+template <int VEC>
+__device__ __forceinline__ void fold_affine(const float *mean, const float *rstd,
+                                            const float *gamma, const float *beta,
+                                            const Geometry &geo, int64_t n, int tid,
+                                            float (&sc)[VEC], float (&sh)[VEC]) {
+    const int cmask = geo.C - 1;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+        const int c = (tid * VEC + j) & cmask;
+        const int64_t gi = n * geo.G + (c >> geo.cg_shift);
+        const float ga = gamma ? gamma[c] : 1.0f;
+        const float be = beta ? beta[c] : 0.0f;
+        sc[j] = ga * rstd[gi];
+        sh[j] = fmaf(-mean[gi], sc[j], be);
+    }
+}
+
+template <int VEC, bool SILU>
+__device__ __forceinline__ void transform(const Pack<VEC> &v, const float (&sc)[VEC],
+                                          const float (&sh)[VEC], float (&o)[VEC]) {
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+        const float t = fmaf(v.get(j), sc[j], sh[j]);
+        if constexpr (SILU) {
+            o[j] = silu_f32(t);
+        } else {
+            o[j] = t;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Step 1: partial statistics.  One workgroup per (sample n, chunk k); writes
+// the pivot-shifted sum and sum of squares of each group over its chunk to
+// part_s / part_q at [(n*K + k)*G + g].
+// FUSED (requires G <= kThreads): the last workgroup of sample n to finish,
+// found with an agent-scope atomic counter, also performs step 2 for that
+// sample -- a fixed-order reduction over the K chunk partials of each group,
+// whichever workgroup happens to be last -- and resets the counter to zero.
+// Ordering: every lane waits for its write-through partial stores to
+// complete (s_waitcnt vmcnt(0)), the workgroup barrier follows, and only then
+// is the arrival counted; the last workgroup reads the partials with
+// agent-scope (coherent) loads.
+// ---------------------------------------------------------------------------
+template <int VEC, int UNROLL, bool NTL, bool FUSED>
+__global__ __launch_bounds__(kThreads) void gn_partial_stats(
+    const uint16_t *__restrict__ x, Geometry geo, StatsOut out) {
+    constexpr int TILE = kThreads * VEC;
+    __shared__ float red_s[TILE];
+    __shared__ float red_q[TILE];
+
+    const int tid = threadIdx.x;
+    const int64_t wg = blockIdx.x;
+    const int64_t n = wg / geo.K;
+    const int64_t k = wg - n * geo.K;
+    const uint16_t *xs = x + n * geo.E;
+
+    float piv[VEC], s[VEC], q[VEC];
+    init_slots<VEC>(xs, geo, tid, piv, s, q);
+
+    const ChunkRange cr = chunk_range(geo, k);
+    const uint16_t *p = xs + cr.t_begin * TILE + tid * VEC;
+    int64_t tt = cr.t_begin;
+    for (; tt + UNROLL <= cr.t_full_end; tt += UNROLL) {
+        Pack<VEC> v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) v[u] = Pack<VEC>::template load<NTL>(p + u * TILE);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) accumulate<VEC>(v[u], piv, s, q);
+        p += UNROLL * TILE;
+    }
+    for (; tt < cr.t_full_end; ++tt) {
+        accumulate<VEC>(Pack<VEC>::template load<NTL>(p), piv, s, q);
+        p += TILE;
+    }
+    if (tt < cr.t_end) {
+        // The sample's last tile is partial; E is a multiple of VEC, so each
+        // lane's vector lies wholly inside or wholly outside the sample.
+        const int64_t off = tt * TILE + tid * VEC;
+        if (off < geo.E) accumulate<VEC>(Pack<VEC>::template load<NTL>(xs + off), piv, s, q);
+    }
+
+    write_group_partials<VEC, FUSED>(s, q, red_s, red_q, geo, n, k, out, tid);
     if constexpr (FUSED) {
-        __shared__ int last;
-        __builtin_amdgcn_s_waitcnt(0);  // this lane's partial stores have completed ...
-        __syncthreads();                // ... in every lane, before the arrival is counted
-        if (tid == 0) {
-            const unsigned before = __hip_atomic_fetch_add(
-                out.arrivals + n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            last = (before == static_cast<unsigned>(geo.K - 1));
-        }
-        __syncthreads();
-        if (!last) return;
-        // G <= kThreads: tpg threads per group, thread tid = g + G*j sums the
-        // chunks k = j, j + tpg, ... (coalesced along g), then a tree over j.
-        const int tpg = kThreads / G;
-        const int g = tid & (G - 1);
-        const int j = tid / G;
-        // Loads are issued kBatch at a time so their round trips overlap;
-        // the sums still run over k in increasing order.
-        constexpr int kBatch = 8;
-        const float *ps = out.part_s + n * geo.K * G + g;
-        const float *pq = out.part_q + n * geo.K * G + g;
-        float as = 0.0f, aq = 0.0f;
-        int64_t kk = j;
-        for (; kk + (kBatch - 1) * tpg < geo.K; kk += kBatch * tpg) {
-            float vs[kBatch], vq[kBatch];
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                const int64_t o = (kk + b * tpg) * G;
-                vs[b] = __hip_atomic_load(ps + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                vq[b] = __hip_atomic_load(pq + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                as += vs[b];
-                aq += vq[b];
-            }
-        }
-        for (; kk < geo.K; kk += tpg) {
-            as += __hip_atomic_load(ps + kk * G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            aq += __hip_atomic_load(pq + kk * G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        red_s[tid] = as;
-        red_q[tid] = aq;
-        __syncthreads();
-        for (int stride = tpg >> 1; stride > 0; stride >>= 1) {
-            if (j < stride) {
-                red_s[tid] += red_s[tid + stride * G];
-                red_q[tid] += red_q[tid + stride * G];
-            }
-            __syncthreads();
-        }
-        if (j == 0) {
-            const float pivot = bf16_bits_to_f32(xs[static_cast<int64_t>(g) << geo.cg_shift]);
-            group_moments(red_s[tid], red_q[tid], pivot, out.inv_m, out.eps,
-                          out.mean + n * G + g, out.rstd + n * G + g);
-        }
-        if (tid == 0)
-            __hip_atomic_store(out.arrivals + n, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (arrive_is_last(out, n, geo.K, tid)) finalize_sample(xs, geo, n, out, red_s, red_q, tid);
     }
 }
 
@@ -418,63 +489,37 @@ __global__ __launch_bounds__(kThreads) void gn_apply(
                                : static_cast<int64_t>(blockIdx.x);
     const int64_t n = wg / geo.K;
     const int64_t k = wg - n * geo.K;
-    const int cmask = geo.C - 1;
 
     float sc[VEC], sh[VEC];
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-        const int c = (tid * VEC + j) & cmask;
-        const int64_t gi = n * geo.G + (c >> geo.cg_shift);
-        const float ga = gamma ? gamma[c] : 1.0f;
-        const float be = beta ? beta[c] : 0.0f;
-        sc[j] = ga * rstd[gi];
-        sh[j] = fmaf(-mean[gi], sc[j], be);
-    }
+    fold_affine<VEC>(mean, rstd, gamma, beta, geo, n, tid, sc, sh);
 
     const int64_t base = n * geo.E;
-    const int64_t t_begin = k * geo.tpc;
-    const int64_t t_end = t_begin + geo.tpc < geo.tiles ? t_begin + geo.tpc : geo.tiles;
-    const int64_t t_full_end = t_end < geo.full ? t_end : geo.full;
-    int64_t off = base + t_begin * TILE + tid * VEC;
-
-    auto transform = [&](const Pack<VEC> &v, float (&o)[VEC]) {
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-            const float t = fmaf(v.get(j), sc[j], sh[j]);
-            if constexpr (SILU) {
-                o[j] = silu_f32(t);
-            } else {
-                o[j] = t;
-            }
-        }
-    };
-
-    int64_t tt = t_begin;
-    for (; tt + UNROLL <= t_full_end; tt += UNROLL) {
+    const ChunkRange cr = chunk_range(geo, k);
+    int64_t off = base + cr.t_begin * TILE + tid * VEC;
+    int64_t tt = cr.t_begin;
+    for (; tt + UNROLL <= cr.t_full_end; tt += UNROLL) {
         Pack<VEC> v[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) v[u] = Pack<VEC>::template load<NTL>(x + off + u * TILE);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             float o[VEC];
-            transform(v[u], o);
+            transform<VEC, SILU>(v[u], sc, sh, o);
             Pack<VEC>::template store<NTS>(y + off + u * TILE, o);
         }
         off += UNROLL * TILE;
     }
-    for (; tt < t_full_end; ++tt) {
-        const Pack<VEC> v = Pack<VEC>::template load<NTL>(x + off);
+    for (; tt < cr.t_full_end; ++tt) {
         float o[VEC];
-        transform(v, o);
+        transform<VEC, SILU>(Pack<VEC>::template load<NTL>(x + off), sc, sh, o);
         Pack<VEC>::template store<NTS>(y + off, o);
         off += TILE;
     }
-    if (tt < t_end) {
+    if (tt < cr.t_end) {
         const int64_t rel = tt * TILE + tid * VEC;
         if (rel < geo.E) {
-            const Pack<VEC> v = Pack<VEC>::template load<NTL>(x + base + rel);
             float o[VEC];
-            transform(v, o);
+            transform<VEC, SILU>(Pack<VEC>::template load<NTL>(x + base + rel), sc, sh, o);
             Pack<VEC>::template store<NTS>(y + base + rel, o);
         }
     }

@@ -120,8 +120,9 @@ gn_status gn_apply_rows(const void *x, const float *mean, const float *rstd,
  * pair of HIP events around every kernel launch, synchronises, and writes
  * the mean duration in milliseconds of each kernel slot of the path to
  * kernel_ms[0 .. *n_kernels-1] (capacity 4); gn_kernel_name(i) names the
- * slots.  A slot whose kernel is not launched for this shape (the separate
- * finalize, when the statistics kernel finishes the groups itself) reads -1.
+ * slots: 0 statistics, 1 separate finalize, 2 apply.  A slot whose kernel is
+ * not launched for this shape (the separate finalize, when the statistics
+ * kernel finishes the groups itself) reads -1.
  * iters must be in [1, 100000]. */
 gn_status gn_profile_rows(const void *x, const float *gamma, const float *beta, void *y,
                           int64_t N, int64_t L, int64_t C, int64_t G,

@@ -319,7 +319,7 @@ def test_profile_helper(gn, dev):
     y = torch.empty_like(x)
     ms = gn.profile_rows(x, w.G, torch.from_numpy(gamma).to(dev), torch.from_numpy(beta).to(dev),
                          w.eps, True, y, 3)
-    # G = 32: the statistics kernel finishes the groups itself (no finalize launch)
+    # G = 32, large: the statistics kernel finishes the groups itself (no finalize launch)
     assert set(ms) == {"gn_partial_stats", "gn_apply"}
     assert all(v > 0 for v in ms.values())
     x2 = to_dev_bits(make_inputs(w)[0][: 4 * 16384 * 512], dev).reshape(4, 16384, 512)

@@ -109,7 +109,7 @@ def test_plan_keeps_every_access_in_bounds(N, L, C, G):
         # every chunk of every group is read exactly once by the tail
         seen = sorted(k for j in range(tpg) for k in range(j, p["K1"], tpg))
         assert seen == list(range(p["K1"]))
-    counters = -(-4 * N // 256) * 256
+    counters = -(-4 * N // 256) * 256   # one arrival counter per sample
     assert p["scratch_bytes"] == counters + 4 * (2 * nparts + 2 * N * G)
     assert N * G < 2 ** 24
     if C * 8 <= 65536:
