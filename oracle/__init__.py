@@ -16,7 +16,10 @@ Parity status of each function (what pins it, see ``tests/test_oracle_pins.py``)
     GroupNorm/LayerNorm/InstanceNorm, invariants.
   * ``gn_silu`` -- pinned: exact-arithmetic brute force (Fraction/Decimal),
     torch's fp64 CPU ``group_norm`` + ``silu``, LayerNorm (G=1) and
-    InstanceNorm (G=C) identities, closed-form cases, invariants.
+    InstanceNorm (G=C) identities, closed-form cases, invariants; for fp16
+    and fp32 inputs, torch's fp64 ``group_norm`` on the same values.
+  * ``widen`` -- pinned exhaustively: all 65536 bf16 and all 65536 fp16 bit
+    patterns against numpy's own conversions.
 """
 import ctypes
 import os
@@ -31,11 +34,16 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _as_bits(x_bits):
-    x = np.ascontiguousarray(x_bits)
-    if x.dtype != np.uint16:
-        raise TypeError("oracle input must be bf16 bit patterns (uint16)")
-    return x
+# Input dtypes: uint16 arrays are bf16 bit patterns, float16 and float32
+# arrays are IEEE binary16 / binary32 values.
+_DTYPE_CODE = {np.dtype(np.uint16): 0, np.dtype(np.float16): 1, np.dtype(np.float32): 2}
+
+
+def _as_input(x):
+    x = np.ascontiguousarray(x)
+    if x.dtype not in _DTYPE_CODE:
+        raise TypeError("oracle input must be bf16 bits (uint16), float16 or float32")
+    return x, _DTYPE_CODE[x.dtype]
 
 
 class Oracle:
@@ -45,11 +53,14 @@ class Oracle:
         lib = ctypes.CDLL(lib_path)
         i64 = ctypes.c_int64
         vp = ctypes.c_void_p
-        lib.gno_group_stats.argtypes = [vp, i64, i64, i64, i64, vp, vp]
-        lib.gno_group_stats.restype = ctypes.c_int
-        lib.gno_gn_silu.argtypes = [vp, vp, vp, i64, i64, i64, i64, ctypes.c_double,
-                                    ctypes.c_int, vp, vp, vp, vp]
-        lib.gno_gn_silu.restype = ctypes.c_int
+        ci = ctypes.c_int
+        lib.gno_group_stats_dt.argtypes = [vp, ci, i64, i64, i64, i64, vp, vp]
+        lib.gno_group_stats_dt.restype = ci
+        lib.gno_gn_silu_dt.argtypes = [vp, ci, vp, vp, i64, i64, i64, i64, ctypes.c_double,
+                                       ci, vp, vp, vp, vp]
+        lib.gno_gn_silu_dt.restype = ci
+        lib.gno_widen.argtypes = [vp, ci, i64, vp]
+        lib.gno_widen.restype = ci
         lib.gno_max_threads.argtypes = []
         lib.gno_max_threads.restype = ctypes.c_int
         lib.gno_set_threads.argtypes = [ctypes.c_int]
@@ -63,27 +74,36 @@ class Oracle:
     def set_threads(self, n: int) -> None:
         self.lib.gno_set_threads(int(n))
 
+    def widen(self, x):
+        """The oracle's own fp64 widening of each input element."""
+        x, code = _as_input(x)
+        out = np.empty(max(x.size, 1), np.float64)
+        if self.lib.gno_widen(_ptr(x), code, x.size, _ptr(out)) != 0:
+            raise ValueError("bad dtype")
+        return out[: x.size].reshape(x.shape)
+
     def group_stats(self, x_bits, N, L, C, G):
         """fp64 mean and biased variance per (n, g); arrays of shape (N, G)."""
-        x = _as_bits(x_bits)
+        x, code = _as_input(x_bits)
         if x.size != N * L * C:
             raise ValueError("x has %d elements, expected N*L*C = %d" % (x.size, N * L * C))
         mean = np.empty(max(N * G, 1), np.float64)
         var = np.empty(max(N * G, 1), np.float64)
-        rc = self.lib.gno_group_stats(_ptr(x), N, L, C, G, _ptr(mean), _ptr(var))
+        rc = self.lib.gno_group_stats_dt(_ptr(x), code, N, L, C, G, _ptr(mean), _ptr(var))
         if rc != 0:
             raise ValueError("oracle rejected shape N=%d L=%d C=%d G=%d" % (N, L, C, G))
         return mean[: N * G].reshape(N, G), var[: N * G].reshape(N, G)
 
     def gn_silu(self, x_bits, gamma, beta, N, L, C, G, eps, apply_silu,
                 out_dtype=np.float64, return_stats=False):
-        """GroupNorm(+SiLU) of dense [N, L, C] bf16 bits, computed in fp64.
+        """GroupNorm(+SiLU) of dense [N, L, C] input, computed in fp64.
 
-        ``out_dtype`` float64 returns the fp64 result; float32 returns it
-        rounded once to fp32 (for the largest shapes, to halve host memory).
-        gamma/beta are float32 arrays of length C, or None (ones / zeros).
+        The input is bf16 bits (uint16), float16 or float32.  ``out_dtype``
+        float64 returns the fp64 result; float32 returns it rounded once to
+        fp32 (for the largest shapes, to halve host memory).  gamma/beta are
+        float32 arrays of length C, or None (ones / zeros).
         """
-        x = _as_bits(x_bits)
+        x, code = _as_input(x_bits)
         if x.size != N * L * C:
             raise ValueError("x has %d elements, expected N*L*C = %d" % (x.size, N * L * C))
         g = None if gamma is None else np.ascontiguousarray(gamma, np.float32)
@@ -98,9 +118,9 @@ class Oracle:
         o32 = out if out.dtype == np.float32 else None
         if o64 is None and o32 is None:
             raise TypeError("out_dtype must be float64 or float32")
-        rc = self.lib.gno_gn_silu(_ptr(x), _ptr(g), _ptr(b), N, L, C, G, float(eps),
-                                  1 if apply_silu else 0, _ptr(o64), _ptr(o32),
-                                  _ptr(mean), _ptr(var))
+        rc = self.lib.gno_gn_silu_dt(_ptr(x), code, _ptr(g), _ptr(b), N, L, C, G, float(eps),
+                                     1 if apply_silu else 0, _ptr(o64), _ptr(o32),
+                                     _ptr(mean), _ptr(var))
         if rc != 0:
             raise ValueError("oracle rejected arguments N=%d L=%d C=%d G=%d eps=%r"
                              % (N, L, C, G, eps))
@@ -129,6 +149,10 @@ def max_threads() -> int:
 
 def set_threads(n: int) -> None:
     _get().set_threads(n)
+
+
+def widen(x):
+    return _get().widen(x)
 
 
 def group_stats(x_bits, N, L, C, G):

@@ -29,6 +29,10 @@
  * root; groups are contiguous channel blocks; SiLU comes after the affine;
  * a NULL gamma means all ones and a NULL beta all zeros.
  *
+ * Inputs may be bf16, IEEE binary16 or binary32 (the page's kernel tests
+ * cover fp32 and bf16 activations); every one widens exactly to fp64, so the
+ * arithmetic below is the same for all three.
+ *
  * All arithmetic is IEEE fp64 in the order written above: no blocking, no
  * fused passes, no reassociation.  OpenMP only splits independent groups
  * (statistics) and independent rows (elementwise output) across threads; the
@@ -48,6 +52,38 @@ static double bf16_bits_to_double(uint16_t bits) {
     float f;
     memcpy(&f, &u, sizeof f);
     return (double)f;
+}
+
+/* IEEE binary16 from its definition: 1 sign bit, 5 exponent bits (bias 15),
+ * 10 fraction bits; exponent 0 is zero/subnormal (f * 2^-24), 31 is inf/NaN. */
+static double f16_bits_to_double(uint16_t bits) {
+    const int sign = (bits >> 15) & 1;
+    const int e = (bits >> 10) & 0x1f;
+    const int f = bits & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(f + 1024), e - 25);
+    return sign ? -v : v;
+}
+
+enum { GNO_BF16 = 0, GNO_F16 = 1, GNO_F32 = 2 };
+
+/* Element i of x, widened to fp64. */
+static double load(const void *x, int dtype, int64_t i) {
+    if (dtype == GNO_BF16) return bf16_bits_to_double(((const uint16_t *)x)[i]);
+    if (dtype == GNO_F16) return f16_bits_to_double(((const uint16_t *)x)[i]);
+    return (double)((const float *)x)[i];
+}
+
+/* Widening of n elements (for pinning the decoders against libraries). */
+int gno_widen(const void *x, int dtype, int64_t n, double *out) {
+    if (dtype < GNO_BF16 || dtype > GNO_F32) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = load(x, dtype, i);
+    return 0;
 }
 
 static int check_shape(int64_t N, int64_t L, int64_t C, int64_t G) {
@@ -73,31 +109,36 @@ void gno_set_threads(int n) {
 
 /* Per-(n, g) mean and biased variance, two passes in fp64.
  * mean_out, var_out: N*G doubles, index n*G + g.  Returns 0, or -1 on a bad
- * shape. */
-int gno_group_stats(const uint16_t *x, int64_t N, int64_t L, int64_t C, int64_t G,
-                    double *mean_out, double *var_out) {
-    if (check_shape(N, L, C, G)) return -1;
+ * shape or dtype. */
+int gno_group_stats_dt(const void *x, int dtype, int64_t N, int64_t L, int64_t C, int64_t G,
+                       double *mean_out, double *var_out) {
+    if (check_shape(N, L, C, G) || dtype < GNO_BF16 || dtype > GNO_F32) return -1;
     const int64_t Cg = C / G;
     const int64_t M = L * Cg;
     int64_t ng;
 #pragma omp parallel for schedule(dynamic, 1)
     for (ng = 0; ng < N * G; ++ng) {
         const int64_t n = ng / G, g = ng % G;
-        const uint16_t *xs = x + n * L * C + g * Cg;
+        const int64_t base = n * L * C + g * Cg;
         double sum = 0.0;
         for (int64_t l = 0; l < L; ++l)
-            for (int64_t j = 0; j < Cg; ++j) sum += bf16_bits_to_double(xs[l * C + j]);
+            for (int64_t j = 0; j < Cg; ++j) sum += load(x, dtype, base + l * C + j);
         const double mu = (M > 0) ? sum / (double)M : 0.0;
         double ss = 0.0;
         for (int64_t l = 0; l < L; ++l)
             for (int64_t j = 0; j < Cg; ++j) {
-                const double d = bf16_bits_to_double(xs[l * C + j]) - mu;
+                const double d = load(x, dtype, base + l * C + j) - mu;
                 ss += d * d;
             }
         mean_out[ng] = mu;
         var_out[ng] = (M > 0) ? ss / (double)M : 0.0;
     }
     return 0;
+}
+
+int gno_group_stats(const uint16_t *x, int64_t N, int64_t L, int64_t C, int64_t G,
+                    double *mean_out, double *var_out) {
+    return gno_group_stats_dt(x, GNO_BF16, N, L, C, G, mean_out, var_out);
 }
 
 /* y = SiLU(t) = t * sigmoid(t), written as t / (1 + exp(-t)).  For t far
@@ -108,10 +149,10 @@ static double silu(double t) { return t / (1.0 + exp(-t)); }
  * receives the fp64 result rounded once to fp32 (storage for the large
  * shapes only).  mean_out/var_out (may be NULL) receive the statistics.
  * Returns 0, or -1 on a bad argument. */
-int gno_gn_silu(const uint16_t *x, const float *gamma, const float *beta, int64_t N,
-                int64_t L, int64_t C, int64_t G, double eps, int apply_silu,
-                double *out64, float *out32, double *mean_out, double *var_out) {
-    if (check_shape(N, L, C, G)) return -1;
+int gno_gn_silu_dt(const void *x, int dtype, const float *gamma, const float *beta, int64_t N,
+                   int64_t L, int64_t C, int64_t G, double eps, int apply_silu,
+                   double *out64, float *out32, double *mean_out, double *var_out) {
+    if (check_shape(N, L, C, G) || dtype < GNO_BF16 || dtype > GNO_F32) return -1;
     if ((out64 == NULL) == (out32 == NULL)) return -1;
     if (!(eps >= 0.0)) return -1;
     const int64_t Cg = C / G;
@@ -125,7 +166,7 @@ int gno_gn_silu(const uint16_t *x, const float *gamma, const float *beta, int64_
         mean = heap;
         var = heap + ng;
     }
-    gno_group_stats(x, N, L, C, G, mean, var);
+    gno_group_stats_dt(x, dtype, N, L, C, G, mean, var);
     int64_t row;
 #pragma omp parallel for schedule(static)
     for (row = 0; row < N * L; ++row) {
@@ -136,7 +177,7 @@ int gno_gn_silu(const uint16_t *x, const float *gamma, const float *beta, int64_
             const double rstd = 1.0 / sqrt(var[n * G + g] + eps);
             const double ga = gamma ? (double)gamma[c] : 1.0;
             const double be = beta ? (double)beta[c] : 0.0;
-            const double xv = bf16_bits_to_double(x[row * C + c]);
+            const double xv = load(x, dtype, row * C + c);
             const double t = ga * ((xv - mu) * rstd) + be;
             const double yv = apply_silu ? silu(t) : t;
             if (out64)
@@ -147,4 +188,11 @@ int gno_gn_silu(const uint16_t *x, const float *gamma, const float *beta, int64_
     }
     free(heap);
     return 0;
+}
+
+int gno_gn_silu(const uint16_t *x, const float *gamma, const float *beta, int64_t N,
+                int64_t L, int64_t C, int64_t G, double eps, int apply_silu,
+                double *out64, float *out32, double *mean_out, double *var_out) {
+    return gno_gn_silu_dt(x, GNO_BF16, gamma, beta, N, L, C, G, eps, apply_silu, out64, out32,
+                          mean_out, var_out);
 }

@@ -26,13 +26,19 @@ MUTANTS = {
     "mean added instead of subtracted": ("(xv - mu)", "(xv + mu)"),
     "channel->group map by modulo": ("const int64_t g = c / Cg;", "const int64_t g = c % G;"),
     "SiLU with the wrong sign": ("t / (1.0 + exp(-t))", "t / (1.0 + exp(t))"),
-    "group offset dropped in stats": ("x + n * L * C + g * Cg;", "x + n * L * C + g;"),
+    "group offset dropped in stats": ("const int64_t base = n * L * C + g * Cg;",
+                                      "const int64_t base = n * L * C + g;"),
     "row stride Cg instead of C in the mean": (
-        "sum += bf16_bits_to_double(xs[l * C + j]);",
-        "sum += bf16_bits_to_double(xs[l * Cg + j]);"),
+        "sum += load(x, dtype, base + l * C + j);",
+        "sum += load(x, dtype, base + l * Cg + j);"),
     "second moment not centred": (
-        "const double d = bf16_bits_to_double(xs[l * C + j]) - mu;",
-        "const double d = bf16_bits_to_double(xs[l * C + j]);"),
+        "const double d = load(x, dtype, base + l * C + j) - mu;",
+        "const double d = load(x, dtype, base + l * C + j);"),
+    "fp16 exponent bias off by one": ("ldexp((double)(f + 1024), e - 25)",
+                                      "ldexp((double)(f + 1024), e - 24)"),
+    "fp16 subnormal scale wrong": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
+    "fp16 implicit bit dropped": ("ldexp((double)(f + 1024), e - 25)",
+                                  "ldexp((double)f, e - 25)"),
     "sample index ignored": ("const int64_t n = row / L;", "const int64_t n = 0;"),
 }
 
@@ -46,6 +52,8 @@ def battery():
         ("closed_affine_silu", pins.test_closed_form_affine_and_silu),
         ("moments", lambda o: pins.test_normalised_moments(o, 8.0)),
         ("constant_group", pins.test_constant_group_gives_beta),
+        ("widen_f16", pins.test_widen_f16_exhaustive),
+        ("torch_gn_f16", lambda o: pins.test_torch_group_norm_other_dtypes(o, "float16")),
     ]
 
 

@@ -282,3 +282,48 @@ def test_input_generator_recipe():
     # exactly torch's bf16 rounding
     t = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(bits, t)
+
+
+def test_widen_bf16_exhaustive(oracle):
+    """All 65536 bf16 patterns widen exactly as torch's bf16 -> float64."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle.widen(bits)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all()
+    assert (np.signbit(got) == np.signbit(want))[~np.isnan(want)].all()
+
+
+def test_widen_f16_exhaustive(oracle):
+    """All 65536 binary16 patterns (subnormals, infinities, NaNs included)
+    widen exactly as numpy's float16 -> float64."""
+    vals = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    got = oracle.widen(vals)
+    want = vals.astype(np.float64)
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all()
+    assert (np.signbit(got) == np.signbit(want))[~np.isnan(want)].all()
+
+
+def test_widen_f32_is_identity(oracle):
+    v = np.random.default_rng(1).normal(0, 1e3, 4096).astype(np.float32)
+    v[:4] = [np.inf, -np.inf, 1e-45, -0.0]
+    assert np.array_equal(oracle.widen(v), v.astype(np.float64))
+
+
+@pytest.mark.parametrize("dtype", ["float16", "float32"])
+def test_torch_group_norm_other_dtypes(oracle, dtype):
+    """fp16 and fp32 inputs: the same fp64 GroupNorm(+SiLU) as torch's."""
+    rng = np.random.default_rng(123)
+    for (N, L, C, G) in ((2, 37, 64, 8), (1, 100, 128, 32), (3, 9, 6, 3)):
+        x = (rng.normal(0, 2, (N, L, C)) + rng.uniform(-5, 5, C)).astype(dtype)
+        gamma = rng.normal(1, 0.2, C).astype(np.float32)
+        beta = rng.normal(0, 0.2, C).astype(np.float32)
+        for silu in (False, True):
+            y = oracle.gn_silu(x, gamma, beta, N, L, C, G, 1e-5, silu)
+            xt = torch.from_numpy(x.astype(np.float64)).permute(0, 2, 1).contiguous()
+            ref = F.group_norm(xt, G, torch.from_numpy(gamma.astype(np.float64)),
+                               torch.from_numpy(beta.astype(np.float64)), 1e-5)
+            if silu:
+                ref = F.silu(ref)
+            np.testing.assert_allclose(y, ref.permute(0, 2, 1).numpy(), rtol=1e-11, atol=1e-11)
