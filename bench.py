@@ -16,7 +16,8 @@ Prints ONE JSON line.  Besides the contract fields it carries
   cpu_baseline -- the fp64 oracle (test infrastructure) timed on the host's
                   cores on the same tensor;
   kernels_ms   -- mean duration of each kernel from the same events;
-  other_shapes -- us/call of the other four decoder shapes (context).
+  other_shapes -- us/call of the other four decoder shapes (context);
+  other_dtypes -- the headline shape with fp16 and fp32 input/output.
 """
 import argparse
 import ctypes
@@ -123,6 +124,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--no-other-shapes", action="store_true")
+    ap.add_argument("--no-other-dtypes", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -206,6 +208,37 @@ def main():
             }
             del ox, oy
 
+    dtypes = {}
+    if not args.no_other_dtypes:
+        for dname, tdt, esize in (("f16", torch.float16, 2), ("f32", torch.float32, 4)):
+            log("headline shape in %s" % dname)
+            dx_np, dg, dbeta = make_inputs(w, dtype=dname)
+            dx = torch.from_numpy(dx_np).to(dev).reshape(w.N, w.L, w.C)
+            assert dx.dtype == tdt
+            dy = torch.empty_like(dx)
+            dgt, dbt = torch.from_numpy(dg).to(dev), torch.from_numpy(dbeta).to(dev)
+            code_dt = int(gn.dtype_code(tdt))
+            dxp, dyp = ctypes.c_void_p(dx.data_ptr()), ctypes.c_void_p(dy.data_ptr())
+            dgp, dbp = ctypes.c_void_p(dgt.data_ptr()), ctypes.c_void_p(dbt.data_ptr())
+
+            def dstep(dxp=dxp, dyp=dyp, dgp=dgp, dbp=dbp, code_dt=code_dt):
+                code = gn.gn_silu_nhwc_dtype(dxp, dgp, dbp, dyp, w.N, w.H, w.W, w.C, w.G, w.eps,
+                                             1, code_dt, sh)
+                if code != 0:
+                    raise RuntimeError(gn.status_text(code))
+
+            dms, _ = time_calls(torch, dstep, args.steps, args.warmup, stream)
+            dk = gn.profile_rows(dx, w.G, dgt, dbt, w.eps, True, dy, args.steps)
+            dbytes = 3 * esize * w.numel
+            dtypes[dname] = {
+                "us_per_call": round(dms * 1e3, 2),
+                "bytes_per_call": dbytes,
+                "GB_s": round(dbytes / (dms * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "kernels_us": {k: round(v * 1e3, 2) for k, v in dk.items()},
+            }
+            del dx, dy, dx_np
+
     if args.copy_calibration:
         log("copy calibration: 512 MiB device-to-device copy x5")
         src = torch.empty(256 * 1024 * 1024, dtype=torch.int16, device=dev).fill_(1)
@@ -263,6 +296,7 @@ def main():
         "kernels_ms": {k: round(v, 5) for k, v in kms.items()},
         "cpu_baseline": cpu,
         "other_shapes": other,
+        "other_dtypes": dtypes,
         "wall_s_timed_region": round(wall, 4),
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},

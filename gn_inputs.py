@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for channels-last GroupNorm(+SiLU).
 
 This module is the only thing the GPU path's tests and the fp64 oracle share.
-It draws random numbers and rounds them to bf16; it holds none of the
+It draws random numbers and rounds them to bf16 (or fp16); it holds none of the
 normalisation arithmetic.
 
 The five workload shapes are the FLUX.2 VAE decoder norm shapes of the kernel
@@ -109,8 +109,24 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def make_inputs(w: Workload, seed=None):
-    """Returns (x_bits uint16 [N*H*W*C] in NHWC order, gamma f32[C], beta f32[C])."""
+def _finish(z, dtype):
+    """The float32 draws rounded to the requested element type: bf16 bit
+    patterns (uint16), IEEE float16 (round to nearest even) or float32."""
+    if dtype == "bf16":
+        return f32_to_bf16_bits(z)
+    if dtype == "f16":
+        return z.astype(np.float16)
+    if dtype == "f32":
+        return z
+    raise ValueError("dtype must be bf16, f16 or f32")
+
+
+def make_inputs(w: Workload, seed=None, dtype="bf16"):
+    """Returns (x [N*H*W*C] in NHWC order, gamma f32[C], beta f32[C]).
+
+    x holds bf16 bit patterns (uint16) by default, or float16 / float32
+    values for dtype "f16" / "f32" (the same float32 draws, rounded once).
+    """
     rng = np.random.default_rng(w.seed if seed is None else seed)
     C = w.C
     m = _draw(rng, w.mean_dist, C, 0.0)
@@ -121,17 +137,17 @@ def make_inputs(w: Workload, seed=None):
     z2 = z.reshape(-1, C)
     z2 *= s
     z2 += m
-    x_bits = f32_to_bf16_bits(z)
-    del z, z2
-    return x_bits, gamma, beta
+    x = _finish(z, dtype)
+    del z2
+    return x, gamma, beta
 
 
 def make_custom(N, L, C, seed, mean_range=(0.0, 0.0), std_range=(1.0, 1.0),
-                affine=True):
+                affine=True, dtype="bf16"):
     """Seeded [N, L, C] input of any shape for parity sweeps.
 
     Per-channel mean ~ U(mean_range), std ~ U(std_range), then the same
-    gamma/beta/z draws as ``make_inputs``.
+    gamma/beta/z draws as ``make_inputs``; x in the element type `dtype`.
     """
     rng = np.random.default_rng(seed)
     m = rng.uniform(mean_range[0], mean_range[1], C).astype(np.float32)
@@ -143,7 +159,7 @@ def make_custom(N, L, C, seed, mean_range=(0.0, 0.0), std_range=(1.0, 1.0),
         z2 = z.reshape(-1, C)
         z2 *= s
         z2 += m
-    x_bits = f32_to_bf16_bits(z)
+    x = _finish(z, dtype)
     if not affine:
         gamma = beta = None
-    return x_bits, gamma, beta
+    return x, gamma, beta

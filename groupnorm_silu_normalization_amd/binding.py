@@ -12,15 +12,17 @@ quality=high", Modifications section 1 "Kernel"):
     group_norm_silu_4d(x, num_groups, weight, bias, eps, apply_silu, out)
     group_norm_silu_rows(x, num_groups, weight, bias, eps, apply_silu, out)
 
-Each returns the output tensor, or None when the input is outside the
-supported set so the caller falls back: not a GPU tensor, autograd enabled,
-not bf16, C not a power of two, C > 2048, not channels-last (4-D) / not
-contiguous rows, fp32 weight/bias missing.  Arguments no GroupNorm accepts
+x may be bf16, fp16 or fp32 (y has the same type).  Each returns the output
+tensor, or None when the input is outside the supported set so the caller
+falls back: not a GPU tensor, autograd enabled, another dtype, C not a power
+of two, C > 2048, not channels-last (4-D) / not contiguous rows, weight/bias
+not fp32 on the same device.  Arguments no GroupNorm accepts
 raise ValueError; a failed HIP call raises RuntimeError.
 
 The raw C entry points are re-exported under their C names (gn_silu_nhwc,
 gn_silu_rows, gn_silu_nhwc_strided, gn_stats_rows, gn_apply_rows,
-gn_profile_rows, gn_plan_rows, gn_kernel_name, gn_status_string, gn_version).
+gn_profile_rows, gn_plan_rows, their *_dtype forms, gn_kernel_name,
+gn_status_string, gn_version).
 """
 import ctypes
 import enum
@@ -73,8 +75,23 @@ lib.gn_stats_rows.argtypes = [_vp, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp]
 lib.gn_apply_rows.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _vp]
 lib.gn_profile_rows.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _vp,
                                 _int, ctypes.POINTER(_f32), ctypes.POINTER(_int)]
+lib.gn_silu_nhwc_dtype.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _int,
+                                   _int, _vp]
+lib.gn_silu_rows_dtype.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _int,
+                                   _vp]
+lib.gn_silu_nhwc_strided_dtype.argtypes = [_vp, _i64p, _vp, _vp, _vp, _i64p, _i64, _i64, _i64,
+                                           _i64, _i64, _f32, _int, _int, _vp]
+lib.gn_stats_rows_dtype.argtypes = [_vp, _i64, _i64, _i64, _i64, _f32, _int, _vp, _vp, _vp]
+lib.gn_apply_rows_dtype.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int,
+                                    _int, _vp]
+lib.gn_profile_rows_dtype.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int,
+                                      _int, _vp, _int, ctypes.POINTER(_f32),
+                                      ctypes.POINTER(_int)]
+lib.gn_plan_rows_dtype.argtypes = [_i64, _i64, _i64, _i64, _int, _i64p]
 for _name in ("gn_silu_nhwc", "gn_silu_rows", "gn_silu_nhwc_strided", "gn_stats_rows",
-              "gn_apply_rows", "gn_profile_rows"):
+              "gn_apply_rows", "gn_profile_rows", "gn_silu_nhwc_dtype", "gn_silu_rows_dtype",
+              "gn_silu_nhwc_strided_dtype", "gn_stats_rows_dtype", "gn_apply_rows_dtype",
+              "gn_profile_rows_dtype", "gn_plan_rows_dtype"):
     getattr(lib, _name).restype = _int
 lib.gn_plan_rows.argtypes = [_i64, _i64, _i64, _i64, _i64p]
 lib.gn_plan_rows.restype = _int
@@ -94,10 +111,32 @@ gn_apply_rows = lib.gn_apply_rows
 gn_profile_rows = lib.gn_profile_rows
 gn_kernel_name = lib.gn_kernel_name
 gn_plan_rows = lib.gn_plan_rows
+gn_silu_nhwc_dtype = lib.gn_silu_nhwc_dtype
+gn_silu_rows_dtype = lib.gn_silu_rows_dtype
+gn_silu_nhwc_strided_dtype = lib.gn_silu_nhwc_strided_dtype
+gn_stats_rows_dtype = lib.gn_stats_rows_dtype
+gn_apply_rows_dtype = lib.gn_apply_rows_dtype
+gn_profile_rows_dtype = lib.gn_profile_rows_dtype
+gn_plan_rows_dtype = lib.gn_plan_rows_dtype
 gn_status_string = lib.gn_status_string
 gn_version = lib.gn_version
 
 MAX_CHANNELS = 2048
+
+
+class GnDtype(enum.IntEnum):
+    BF16 = 0
+    F16 = 1
+    F32 = 2
+
+
+_TORCH_DTYPE = {torch.bfloat16: GnDtype.BF16, torch.float16: GnDtype.F16,
+                torch.float32: GnDtype.F32}
+
+
+def dtype_code(dt):
+    """gn_dtype of a torch dtype, or None if the library does not take it."""
+    return _TORCH_DTYPE.get(dt)
 
 
 class GnStatus(enum.IntEnum):
@@ -146,7 +185,7 @@ def _common_checks(x, weight, bias, C):
         return False
     if torch.is_grad_enabled():
         return False
-    if x.dtype != torch.bfloat16:
+    if dtype_code(x.dtype) is None:
         return False
     if C <= 0 or (C & (C - 1)) != 0 or C > MAX_CHANNELS:
         return False
@@ -186,9 +225,10 @@ def group_norm_silu_4d(x, num_groups, weight=None, bias=None, eps=1e-6, apply_si
         out = torch.empty_like(x, memory_format=torch.channels_last)
     elif out.shape != x.shape or out.dtype != x.dtype or out.device != x.device:
         raise ValueError("out must match x in shape, dtype and device")
-    code = lib.gn_silu_nhwc_strided(
+    code = lib.gn_silu_nhwc_strided_dtype(
         _ptr(x), _i64x4(*x.stride()), _ptr(weight), _ptr(bias), _ptr(out), _i64x4(*out.stride()),
-        N, H, W, C, num_groups, float(eps), 1 if apply_silu else 0, _stream_handle(x))
+        N, H, W, C, num_groups, float(eps), 1 if apply_silu else 0, dtype_code(x.dtype),
+        _stream_handle(x))
     return _result(code, out)
 
 
@@ -209,42 +249,52 @@ def group_norm_silu_rows(x, num_groups, weight=None, bias=None, eps=1e-6, apply_
     elif (out.shape != x.shape or out.dtype != x.dtype or out.device != x.device
           or not out.is_contiguous()):
         raise ValueError("out must be a contiguous tensor matching x")
-    code = lib.gn_silu_rows(_ptr(x), _ptr(weight), _ptr(bias), _ptr(out), N, L, C, num_groups,
-                            float(eps), 1 if apply_silu else 0, _stream_handle(x))
+    code = lib.gn_silu_rows_dtype(_ptr(x), _ptr(weight), _ptr(bias), _ptr(out), N, L, C,
+                                  num_groups, float(eps), 1 if apply_silu else 0,
+                                  dtype_code(x.dtype), _stream_handle(x))
     return _result(code, out)
 
 
 def group_stats_rows(x, num_groups, eps=1e-6):
-    """Per-(n, g) fp32 mean and rstd of contiguous (N, L, C) bf16 rows (steps one and two)."""
+    """Per-(n, g) fp32 mean and rstd of contiguous (N, L, C) rows (steps one and two)."""
     torch = _torch()
     N, L, C = x.shape
     mean = torch.empty((N, num_groups), dtype=torch.float32, device=x.device)
     rstd = torch.empty_like(mean)
-    code = lib.gn_stats_rows(_ptr(x), N, L, C, num_groups, float(eps), _ptr(mean), _ptr(rstd),
-                             _stream_handle(x))
+    code = lib.gn_stats_rows_dtype(_ptr(x), N, L, C, num_groups, float(eps),
+                                   _dtype_arg(x), _ptr(mean), _ptr(rstd), _stream_handle(x))
     r = _result(code, (mean, rstd))
     return r
 
 
 def apply_rows(x, mean, rstd, weight=None, bias=None, apply_silu=True, out=None):
-    """Step three alone on contiguous (N, L, C) bf16 rows, given per-(n, g) mean/rstd."""
+    """Step three alone on contiguous (N, L, C) rows, given per-(n, g) mean/rstd."""
     torch = _torch()
     N, L, C = x.shape
     G = mean.shape[-1]
     if out is None:
         out = torch.empty_like(x)
-    code = lib.gn_apply_rows(_ptr(x), _ptr(mean), _ptr(rstd), _ptr(weight), _ptr(bias),
-                             _ptr(out), N, L, C, G, 1 if apply_silu else 0, _stream_handle(x))
+    code = lib.gn_apply_rows_dtype(_ptr(x), _ptr(mean), _ptr(rstd), _ptr(weight), _ptr(bias),
+                                   _ptr(out), N, L, C, G, 1 if apply_silu else 0, _dtype_arg(x),
+                                   _stream_handle(x))
     return _result(code, out)
 
 
-PLAN_FIELDS = ("vec", "tiles", "full", "tpc1", "K1", "tpc2", "K2", "scratch_bytes")
+PLAN_FIELDS = ("vec", "tiles", "full", "tpc1", "K1", "tpc2", "K2", "scratch_bytes",
+               "apply_nontemporal_loads")
 
 
-def plan_rows(N, L, C, G):
+def _dtype_arg(x):
+    code = dtype_code(x.dtype)
+    if code is None:
+        raise TypeError("unsupported dtype %s" % x.dtype)
+    return int(code)
+
+
+def plan_rows(N, L, C, G, dtype=GnDtype.BF16):
     """The library's launch plan for a rows shape (dict), or None if declined."""
-    buf = (_i64 * 8)()
-    code = lib.gn_plan_rows(N, L, C, G, buf)
+    buf = (_i64 * 9)()
+    code = lib.gn_plan_rows_dtype(N, L, C, G, int(dtype), buf)
     r = _result(code, True)
     if r is None:
         return None
@@ -256,9 +306,10 @@ def profile_rows(x, num_groups, weight, bias, eps, apply_silu, out, iters):
     N, L, C = x.shape
     ms = (_f32 * 4)()
     nk = _int(0)
-    code = lib.gn_profile_rows(_ptr(x), _ptr(weight), _ptr(bias), _ptr(out), N, L, C, num_groups,
-                               float(eps), 1 if apply_silu else 0, _stream_handle(x), int(iters),
-                               ms, ctypes.byref(nk))
+    code = lib.gn_profile_rows_dtype(_ptr(x), _ptr(weight), _ptr(bias), _ptr(out), N, L, C,
+                                     num_groups, float(eps), 1 if apply_silu else 0,
+                                     _dtype_arg(x), _stream_handle(x), int(iters), ms,
+                                     ctypes.byref(nk))
     if code != GnStatus.OK:
         _result(code, None)
         raise RuntimeError("profiling declined: " + status_text(code))

@@ -47,10 +47,16 @@ inline int ilog2(int64_t v) {
 }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+inline bool valid_dtype(int dtype) {
+    return dtype == GN_DTYPE_BF16 || dtype == GN_DTYPE_F16 || dtype == GN_DTYPE_F32;
+}
+inline int64_t elem_bytes(int dtype) { return dtype == GN_DTYPE_F32 ? 4 : 2; }
+
 struct Plan {
     int vec;          // 8: 16-byte lanes; 1: 2-byte lanes (C < 8 with L*C not a multiple of 8)
     bool fused;       // step 2 runs in the tail of step 1 (G <= kThreads)
     bool apply_ntl;   // step 3 reads x with nontemporal loads
+    int dtype;        // gn_dtype of x and y
     Geometry stats;   // chunking of steps 1 and 2
     Geometry apply;   // chunking of step 3
     int64_t N;
@@ -59,13 +65,14 @@ struct Plan {
 
 // The plan depends on the shape only, never on the device, so the order of
 // every floating-point reduction is fixed by (N, L, C, G).
-Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G) {
+Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G, int dtype) {
     Plan p;
     p.N = N;
+    p.dtype = dtype;
     const int64_t E = L * C;
     p.vec = (E % 8 == 0) ? 8 : 1;
     p.fused = G <= kThreads;
-    p.apply_ntl = N * E * 2 > kCacheResidentBytes;
+    p.apply_ntl = N * E * elem_bytes(dtype) > kCacheResidentBytes;
     const int64_t tile = int64_t{kThreads} * p.vec;
     Geometry g;
     g.E = E;
@@ -101,13 +108,14 @@ size_t payload_bytes(const Plan &p, bool with_stats) {
 
 // Checks with no HIP call.  INVALID before UNSUPPORTED.
 gn_status check_shape(const void *x, const void *y, int64_t N, int64_t L, int64_t C, int64_t G,
-                      float eps, int apply_silu, bool need_y) {
+                      float eps, int apply_silu, bool need_y, int dtype) {
+    if (!valid_dtype(dtype)) return GN_INVALID_ARGUMENT;
     if (x == nullptr || (need_y && y == nullptr)) return GN_INVALID_ARGUMENT;
     if (N < 0 || L < 0 || C <= 0 || G <= 0 || C % G != 0) return GN_INVALID_ARGUMENT;
     if (!(eps >= 0.0f) || std::isinf(eps)) return GN_INVALID_ARGUMENT;
     if (apply_silu != 0 && apply_silu != 1) return GN_INVALID_ARGUMENT;
     if (L > 0 && N > INT64_MAX / L) return GN_INVALID_ARGUMENT;
-    if (N * L > 0 && C > INT64_MAX / (N * L)) return GN_INVALID_ARGUMENT;
+    if (N * L > 0 && C > INT64_MAX / (N * L) / 4) return GN_INVALID_ARGUMENT;
     if (!is_pow2(C) || C > GN_MAX_CHANNELS) return GN_UNSUPPORTED;
     if ((reinterpret_cast<uintptr_t>(x) & 15u) != 0) return GN_UNSUPPORTED;
     if (need_y && (reinterpret_cast<uintptr_t>(y) & 15u) != 0) return GN_UNSUPPORTED;
@@ -237,60 +245,92 @@ struct Events {
     hipEvent_t ev[2 * kSlots];  // start/stop per slot
 };
 
-void launch_stats(const Plan &p, const uint16_t *x, const StatsOut &o, hipStream_t s,
-                  const Events *ev) {
+template <class D>
+void launch_stats_t(const Plan &p, const void *xv, const StatsOut &o, hipStream_t s,
+                    const Events *ev) {
+    using T = typename D::storage;
+    const T *x = static_cast<const T *>(xv);
     const dim3 block(kThreads);
     const dim3 grid1(static_cast<unsigned>(p.N * p.stats.K));
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotStats], s);
     if (p.vec == 8) {
         if (p.fused)
-            gn_partial_stats<8, kUnrollStats, false, true><<<grid1, block, 0, s>>>(x, p.stats, o);
+            gn_partial_stats<D, 8, kUnrollStats, false, true><<<grid1, block, 0, s>>>(x, p.stats, o);
         else
-            gn_partial_stats<8, kUnrollStats, false, false><<<grid1, block, 0, s>>>(x, p.stats, o);
+            gn_partial_stats<D, 8, kUnrollStats, false, false><<<grid1, block, 0, s>>>(x, p.stats, o);
     } else {
         if (p.fused)
-            gn_partial_stats<1, kUnrollStats, false, true><<<grid1, block, 0, s>>>(x, p.stats, o);
+            gn_partial_stats<D, 1, kUnrollStats, false, true><<<grid1, block, 0, s>>>(x, p.stats, o);
         else
-            gn_partial_stats<1, kUnrollStats, false, false><<<grid1, block, 0, s>>>(x, p.stats, o);
+            gn_partial_stats<D, 1, kUnrollStats, false, false><<<grid1, block, 0, s>>>(x, p.stats, o);
     }
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotStats + 1], s);
     if (!p.fused) {
         const dim3 grid2(static_cast<unsigned>(p.N * p.stats.G));
         if (ev) (void)hipEventRecord(ev->ev[2 * kSlotFinalize], s);
-        gn_finalize_stats<<<grid2, block, 0, s>>>(x, p.stats, o);
+        gn_finalize_stats<D><<<grid2, block, 0, s>>>(x, p.stats, o);
         if (ev) (void)hipEventRecord(ev->ev[2 * kSlotFinalize + 1], s);
     }
 }
 
-template <int VEC, bool SILU>
-void launch_apply_t(const Plan &p, const uint16_t *x, uint16_t *y, const float *mean,
-                    const float *rstd, const float *gamma, const float *beta, hipStream_t s) {
+template <class D, int VEC, bool SILU>
+void launch_apply_vs(const Plan &p, const void *xv, void *yv, const float *mean, const float *rstd,
+                     const float *gamma, const float *beta, hipStream_t s) {
+    using T = typename D::storage;
+    const T *x = static_cast<const T *>(xv);
+    T *y = static_cast<T *>(yv);
     const dim3 block(kThreads);
     const dim3 grid(static_cast<unsigned>(p.N * p.apply.K));
     if (p.apply_ntl)
-        gn_apply<VEC, kUnrollApply, SILU, true, true><<<grid, block, 0, s>>>(
+        gn_apply<D, VEC, kUnrollApply, SILU, true, true><<<grid, block, 0, s>>>(
             x, y, p.apply, 0, mean, rstd, gamma, beta);
     else
-        gn_apply<VEC, kUnrollApply, SILU, false, true><<<grid, block, 0, s>>>(
+        gn_apply<D, VEC, kUnrollApply, SILU, false, true><<<grid, block, 0, s>>>(
             x, y, p.apply, 0, mean, rstd, gamma, beta);
 }
 
-void launch_apply(const Plan &p, const uint16_t *x, uint16_t *y, const float *mean,
-                  const float *rstd, const float *gamma, const float *beta, int silu,
-                  hipStream_t s, const Events *ev) {
+template <class D>
+void launch_apply_t(const Plan &p, const void *x, void *y, const float *mean, const float *rstd,
+                    const float *gamma, const float *beta, int silu, hipStream_t s,
+                    const Events *ev) {
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotApply], s);
     if (p.vec == 8) {
         if (silu)
-            launch_apply_t<8, true>(p, x, y, mean, rstd, gamma, beta, s);
+            launch_apply_vs<D, 8, true>(p, x, y, mean, rstd, gamma, beta, s);
         else
-            launch_apply_t<8, false>(p, x, y, mean, rstd, gamma, beta, s);
+            launch_apply_vs<D, 8, false>(p, x, y, mean, rstd, gamma, beta, s);
     } else {
         if (silu)
-            launch_apply_t<1, true>(p, x, y, mean, rstd, gamma, beta, s);
+            launch_apply_vs<D, 1, true>(p, x, y, mean, rstd, gamma, beta, s);
         else
-            launch_apply_t<1, false>(p, x, y, mean, rstd, gamma, beta, s);
+            launch_apply_vs<D, 1, false>(p, x, y, mean, rstd, gamma, beta, s);
     }
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotApply + 1], s);
+}
+
+void launch_stats(const Plan &p, const void *x, const StatsOut &o, hipStream_t s,
+                  const Events *ev) {
+    switch (p.dtype) {
+        case GN_DTYPE_F16: launch_stats_t<Fp16>(p, x, o, s, ev); break;
+        case GN_DTYPE_F32: launch_stats_t<F32>(p, x, o, s, ev); break;
+        default: launch_stats_t<Bf16>(p, x, o, s, ev); break;
+    }
+}
+
+void launch_apply(const Plan &p, const void *x, void *y, const float *mean, const float *rstd,
+                  const float *gamma, const float *beta, int silu, hipStream_t s,
+                  const Events *ev) {
+    switch (p.dtype) {
+        case GN_DTYPE_F16:
+            launch_apply_t<Fp16>(p, x, y, mean, rstd, gamma, beta, silu, s, ev);
+            break;
+        case GN_DTYPE_F32:
+            launch_apply_t<F32>(p, x, y, mean, rstd, gamma, beta, silu, s, ev);
+            break;
+        default:
+            launch_apply_t<Bf16>(p, x, y, mean, rstd, gamma, beta, silu, s, ev);
+            break;
+    }
 }
 
 // Everything a compute entry point needs after its argument checks.
@@ -318,9 +358,9 @@ gn_status finish_launch() {
 
 // The full path, optionally with events around each kernel (iters > 0).
 gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y, int64_t N,
-                   int64_t L, int64_t C, int64_t G, float eps, int apply_silu, void *stream,
-                   int iters, float *kernel_ms) {
-    gn_status st = check_shape(x, y, N, L, C, G, eps, apply_silu, true);
+                   int64_t L, int64_t C, int64_t G, float eps, int apply_silu, int dtype,
+                   void *stream, int iters, float *kernel_ms) {
+    gn_status st = check_shape(x, y, N, L, C, G, eps, apply_silu, true, dtype);
     if (st != GN_OK) return st;
     if (N * L == 0) {
         if (kernel_ms)
@@ -331,7 +371,7 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
     st = begin_call(stream, {x, y, gamma, beta}, &c);
     if (st != GN_OK) return st;
 
-    const Plan p = make_plan(N, L, C, G);
+    const Plan p = make_plan(N, L, C, G, dtype);
     const size_t nparts = partial_floats(p);
     const size_t nstats = static_cast<size_t>(N) * G;
 
@@ -348,8 +388,8 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
     o.arrivals = counters;
     o.inv_m = p.inv_m;
     o.eps = eps;
-    const uint16_t *xb = static_cast<const uint16_t *>(x);
-    uint16_t *yb = static_cast<uint16_t *>(y);
+    const void *xb = x;
+    void *yb = y;
 
     if (iters <= 0) {
         launch_stats(p, xb, o, c.stream, nullptr);
@@ -409,45 +449,69 @@ using namespace gnsilu;
 
 extern "C" {
 
+gn_status gn_silu_rows_dtype(const void *x, const float *gamma, const float *beta, void *y,
+                             int64_t N, int64_t L, int64_t C, int64_t G, float eps,
+                             int apply_silu, int dtype, void *stream) {
+    return run_rows(x, gamma, beta, y, N, L, C, G, eps, apply_silu, dtype, stream, 0, nullptr);
+}
+
 gn_status gn_silu_rows(const void *x, const float *gamma, const float *beta, void *y, int64_t N,
                        int64_t L, int64_t C, int64_t G, float eps, int apply_silu,
                        void *stream) {
-    return run_rows(x, gamma, beta, y, N, L, C, G, eps, apply_silu, stream, 0, nullptr);
+    return gn_silu_rows_dtype(x, gamma, beta, y, N, L, C, G, eps, apply_silu, GN_DTYPE_BF16,
+                              stream);
+}
+
+gn_status gn_silu_nhwc_dtype(const void *x, const float *gamma, const float *beta, void *y,
+                             int64_t N, int64_t H, int64_t W, int64_t C, int64_t G, float eps,
+                             int apply_silu, int dtype, void *stream) {
+    if (H < 0 || W < 0) return GN_INVALID_ARGUMENT;
+    if (W > 0 && H > INT64_MAX / W) return GN_INVALID_ARGUMENT;
+    return gn_silu_rows_dtype(x, gamma, beta, y, N, H * W, C, G, eps, apply_silu, dtype, stream);
 }
 
 gn_status gn_silu_nhwc(const void *x, const float *gamma, const float *beta, void *y, int64_t N,
                        int64_t H, int64_t W, int64_t C, int64_t G, float eps, int apply_silu,
                        void *stream) {
+    return gn_silu_nhwc_dtype(x, gamma, beta, y, N, H, W, C, G, eps, apply_silu, GN_DTYPE_BF16,
+                              stream);
+}
+
+gn_status gn_silu_nhwc_strided_dtype(const void *x, const int64_t x_strides[4],
+                                     const float *gamma, const float *beta, void *y,
+                                     const int64_t y_strides[4], int64_t N, int64_t H, int64_t W,
+                                     int64_t C, int64_t G, float eps, int apply_silu, int dtype,
+                                     void *stream) {
+    if (x_strides == nullptr || y_strides == nullptr) return GN_INVALID_ARGUMENT;
     if (H < 0 || W < 0) return GN_INVALID_ARGUMENT;
     if (W > 0 && H > INT64_MAX / W) return GN_INVALID_ARGUMENT;
-    return gn_silu_rows(x, gamma, beta, y, N, H * W, C, G, eps, apply_silu, stream);
+    // Argument errors take precedence over layout refusals.
+    gn_status st = check_shape(x, y, N, H * W, C, G, eps, apply_silu, true, dtype);
+    if (st == GN_INVALID_ARGUMENT) return st;
+    if (!dense_nhwc(x_strides, N, H, W, C) || !dense_nhwc(y_strides, N, H, W, C))
+        return GN_UNSUPPORTED;
+    return gn_silu_rows_dtype(x, gamma, beta, y, N, H * W, C, G, eps, apply_silu, dtype, stream);
 }
 
 gn_status gn_silu_nhwc_strided(const void *x, const int64_t x_strides[4], const float *gamma,
                                const float *beta, void *y, const int64_t y_strides[4],
                                int64_t N, int64_t H, int64_t W, int64_t C, int64_t G,
                                float eps, int apply_silu, void *stream) {
-    if (x_strides == nullptr || y_strides == nullptr) return GN_INVALID_ARGUMENT;
-    if (H < 0 || W < 0) return GN_INVALID_ARGUMENT;
-    if (W > 0 && H > INT64_MAX / W) return GN_INVALID_ARGUMENT;
-    // Argument errors take precedence over layout refusals.
-    gn_status st = check_shape(x, y, N, H * W, C, G, eps, apply_silu, true);
-    if (st == GN_INVALID_ARGUMENT) return st;
-    if (!dense_nhwc(x_strides, N, H, W, C) || !dense_nhwc(y_strides, N, H, W, C))
-        return GN_UNSUPPORTED;
-    return gn_silu_rows(x, gamma, beta, y, N, H * W, C, G, eps, apply_silu, stream);
+    return gn_silu_nhwc_strided_dtype(x, x_strides, gamma, beta, y, y_strides, N, H, W, C, G,
+                                      eps, apply_silu, GN_DTYPE_BF16, stream);
 }
 
-gn_status gn_stats_rows(const void *x, int64_t N, int64_t L, int64_t C, int64_t G, float eps,
-                        float *mean_out, float *rstd_out, void *stream) {
+gn_status gn_stats_rows_dtype(const void *x, int64_t N, int64_t L, int64_t C, int64_t G,
+                              float eps, int dtype, float *mean_out, float *rstd_out,
+                              void *stream) {
     if (mean_out == nullptr || rstd_out == nullptr) return GN_INVALID_ARGUMENT;
-    gn_status st = check_shape(x, nullptr, N, L, C, G, eps, 0, false);
+    gn_status st = check_shape(x, nullptr, N, L, C, G, eps, 0, false, dtype);
     if (st != GN_OK) return st;
     if (N * L == 0) return GN_OK;
     Call c;
     st = begin_call(stream, {x, mean_out, rstd_out}, &c);
     if (st != GN_OK) return st;
-    const Plan p = make_plan(N, L, C, G);
+    const Plan p = make_plan(N, L, C, G, dtype);
     const size_t nparts = partial_floats(p);
     std::lock_guard<std::mutex> lock(scratch_mutex());
     unsigned *counters = nullptr;
@@ -462,45 +526,68 @@ gn_status gn_stats_rows(const void *x, int64_t N, int64_t L, int64_t C, int64_t 
     o.rstd = rstd_out;
     o.inv_m = p.inv_m;
     o.eps = eps;
-    launch_stats(p, static_cast<const uint16_t *>(x), o, c.stream, nullptr);
+    launch_stats(p, x, o, c.stream, nullptr);
+    return finish_launch();
+}
+
+gn_status gn_stats_rows(const void *x, int64_t N, int64_t L, int64_t C, int64_t G, float eps,
+                        float *mean_out, float *rstd_out, void *stream) {
+    return gn_stats_rows_dtype(x, N, L, C, G, eps, GN_DTYPE_BF16, mean_out, rstd_out, stream);
+}
+
+gn_status gn_apply_rows_dtype(const void *x, const float *mean, const float *rstd,
+                              const float *gamma, const float *beta, void *y, int64_t N,
+                              int64_t L, int64_t C, int64_t G, int apply_silu, int dtype,
+                              void *stream) {
+    if (mean == nullptr || rstd == nullptr) return GN_INVALID_ARGUMENT;
+    gn_status st = check_shape(x, y, N, L, C, G, 0.0f, apply_silu, true, dtype);
+    if (st != GN_OK) return st;
+    if (N * L == 0) return GN_OK;
+    Call c;
+    st = begin_call(stream, {x, y, mean, rstd, gamma, beta}, &c);
+    if (st != GN_OK) return st;
+    const Plan p = make_plan(N, L, C, G, dtype);
+    launch_apply(p, x, y, mean, rstd, gamma, beta, apply_silu, c.stream, nullptr);
     return finish_launch();
 }
 
 gn_status gn_apply_rows(const void *x, const float *mean, const float *rstd, const float *gamma,
                         const float *beta, void *y, int64_t N, int64_t L, int64_t C, int64_t G,
                         int apply_silu, void *stream) {
-    if (mean == nullptr || rstd == nullptr) return GN_INVALID_ARGUMENT;
-    gn_status st = check_shape(x, y, N, L, C, G, 0.0f, apply_silu, true);
-    if (st != GN_OK) return st;
-    if (N * L == 0) return GN_OK;
-    Call c;
-    st = begin_call(stream, {x, y, mean, rstd, gamma, beta}, &c);
-    if (st != GN_OK) return st;
-    const Plan p = make_plan(N, L, C, G);
-    launch_apply(p, static_cast<const uint16_t *>(x), static_cast<uint16_t *>(y), mean, rstd,
-                 gamma, beta, apply_silu, c.stream, nullptr);
-    return finish_launch();
+    return gn_apply_rows_dtype(x, mean, rstd, gamma, beta, y, N, L, C, G, apply_silu,
+                               GN_DTYPE_BF16, stream);
+}
+
+gn_status gn_profile_rows_dtype(const void *x, const float *gamma, const float *beta, void *y,
+                                int64_t N, int64_t L, int64_t C, int64_t G, float eps,
+                                int apply_silu, int dtype, void *stream, int iters,
+                                float *kernel_ms, int *n_kernels) {
+    if (kernel_ms == nullptr || n_kernels == nullptr || iters < 1 || iters > 100000)
+        return GN_INVALID_ARGUMENT;
+    *n_kernels = kSlots;
+    return run_rows(x, gamma, beta, y, N, L, C, G, eps, apply_silu, dtype, stream, iters,
+                    kernel_ms);
 }
 
 gn_status gn_profile_rows(const void *x, const float *gamma, const float *beta, void *y,
                           int64_t N, int64_t L, int64_t C, int64_t G, float eps, int apply_silu,
                           void *stream, int iters, float *kernel_ms, int *n_kernels) {
-    if (kernel_ms == nullptr || n_kernels == nullptr || iters < 1 || iters > 100000)
-        return GN_INVALID_ARGUMENT;
-    *n_kernels = kSlots;
-    return run_rows(x, gamma, beta, y, N, L, C, G, eps, apply_silu, stream, iters, kernel_ms);
+    return gn_profile_rows_dtype(x, gamma, beta, y, N, L, C, G, eps, apply_silu, GN_DTYPE_BF16,
+                                 stream, iters, kernel_ms, n_kernels);
 }
 
-gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_out[8]) {
+gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dtype,
+                             int64_t plan_out[9]) {
     if (plan_out == nullptr) return GN_INVALID_ARGUMENT;
     static const uint16_t aligned_probe[8] __attribute__((aligned(16))) = {};
-    const gn_status st = check_shape(aligned_probe, aligned_probe, N, L, C, G, 0.0f, 0, true);
+    const gn_status st =
+        check_shape(aligned_probe, aligned_probe, N, L, C, G, 0.0f, 0, true, dtype);
     if (st != GN_OK) return st;
     if (N * L == 0) {
-        for (int i = 0; i < 8; ++i) plan_out[i] = 0;
+        for (int i = 0; i < 9; ++i) plan_out[i] = 0;
         return GN_OK;
     }
-    const Plan p = make_plan(N, L, C, G);
+    const Plan p = make_plan(N, L, C, G, dtype);
     plan_out[0] = p.vec;
     plan_out[1] = p.stats.tiles;
     plan_out[2] = p.stats.full;
@@ -509,7 +596,17 @@ gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_
     plan_out[5] = p.apply.tpc;
     plan_out[6] = p.apply.K;
     plan_out[7] = static_cast<int64_t>(arrivals_bytes(N) + payload_bytes(p, true));
+    plan_out[8] = p.apply_ntl ? 1 : 0;
     return GN_OK;
+}
+
+gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_out[8]) {
+    if (plan_out == nullptr) return GN_INVALID_ARGUMENT;
+    int64_t full[9] = {};
+    const gn_status st = gn_plan_rows_dtype(N, L, C, G, GN_DTYPE_BF16, full);
+    if (st == GN_OK)
+        for (int i = 0; i < 8; ++i) plan_out[i] = full[i];
+    return st;
 }
 
 const char *gn_kernel_name(int i) { return (i >= 0 && i < kSlots) ? kKernelNames[i] : nullptr; }

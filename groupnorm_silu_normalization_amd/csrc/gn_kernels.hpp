@@ -1,17 +1,25 @@
 // gn_kernels.hpp -- gfx950 (CDNA4) kernels of the channels-last GroupNorm(+SiLU)
-// path: partial statistics, finalize, fused apply (+SiLU).
+// path: partial statistics (with the finalize fused into its tail), a
+// separate finalize for many groups, and the fused apply (+SiLU).
 //
 // The three steps are the ones of "FLUX.2 VAE decoder fast path behind
 // quality=high", Modifications section 1 "Kernel"; the kernels below are a
 // fresh design for wave64 CDNA4, not a translation of the Triton kernel the
 // pages describe.
 //
-// Data layout: one sample is E = L*C bf16 values, channel fastest.  A "tile"
-// is kThreads*VEC consecutive elements of a sample (2048 for VEC = 8).  C is
-// a power of two <= 2048, so every tile starts on a row boundary and thread
-// `tid` always sees the same VEC channels, (tid*VEC + j) mod C: its channel
-// parameters and partial sums stay in registers for the whole chunk.  A
-// 16-byte load per lane gives 1 KiB per wave instruction, fully coalesced.
+// Element types: bf16, IEEE fp16 or fp32 in and out (the same type for x and
+// y); all arithmetic is fp32, and y is rounded once to its type (round to
+// nearest even).
+//
+// Data layout: one sample is E = L*C values, channel fastest.  A "tile" is
+// kThreads*VEC consecutive elements of a sample (2048 for VEC = 8).  Lane
+// `tid` owns VEC slots of every tile at fixed offsets o(tid, j) (Pack::
+// slot_offset): 8*tid + j for 16-bit types, whose 8 values are one 16-byte
+// access; 4*tid + j and 1024 + 4*tid + (j - 4) for fp32, two 16-byte
+// accesses, so that each wave instruction still covers 1 KiB of contiguous
+// memory.  C is a power of two <= 2048, so every tile starts on a row
+// boundary and slot j always holds channel o(tid, j) mod C: the lane's
+// channel parameters and partial sums stay in registers for the whole chunk.
 //
 // Numerics: each thread accumulates x - p_g, where the pivot p_g is the first
 // element of its group in row 0 of the sample (x[n, 0, g*Cg]).  Shifting by a
@@ -31,21 +39,55 @@ constexpr int kThreads = 256;  // 4 waves of 64
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
-    return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
+// ---- element types ---------------------------------------------------------
+// storage: the in-memory type; to_f32 widens exactly; pack2 rounds two fp32
+// values to the type (round to nearest even: v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32 on gfx950) and packs them, lower address first.
+struct Bf16 {
+    using storage = uint16_t;
+    __device__ __forceinline__ static float to_f32(uint16_t b) {
+        return __uint_as_float(static_cast<uint32_t>(b) << 16);
+    }
+    __device__ __forceinline__ static float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    __device__ __forceinline__ static float hi(uint32_t w) {
+        return __uint_as_float(w & 0xffff0000u);
+    }
+    __device__ __forceinline__ static uint32_t pack2(float a, float b) {
+        f32x2 v = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    }
+    __device__ __forceinline__ static uint16_t from_f32(float f) {
+        return static_cast<uint16_t>(pack2(f, 0.0f) & 0xffffu);
+    }
+};
 
-// Two fp32 -> two bf16, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    f32x2 v = {lo, hi};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-    return static_cast<uint16_t>(pack_bf16x2(f, 0.0f) & 0xffffu);
-}
+struct Fp16 {
+    using storage = uint16_t;
+    __device__ __forceinline__ static float to_f32(uint16_t b) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, b));
+    }
+    __device__ __forceinline__ static float lo(uint32_t w) {
+        return to_f32(static_cast<uint16_t>(w & 0xffffu));
+    }
+    __device__ __forceinline__ static float hi(uint32_t w) {
+        return to_f32(static_cast<uint16_t>(w >> 16));
+    }
+    __device__ __forceinline__ static uint32_t pack2(float a, float b) {
+        f32x2 v = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+    }
+    __device__ __forceinline__ static uint16_t from_f32(float f) {
+        return static_cast<uint16_t>(pack2(f, 0.0f) & 0xffffu);
+    }
+};
+
+struct F32 {
+    using storage = float;
+    __device__ __forceinline__ static float to_f32(float v) { return v; }
+    __device__ __forceinline__ static float from_f32(float f) { return f; }
+};
 
 // SiLU(t) = t * sigmoid(t) = t / (1 + e^-t), with e^-t = 2^(-t*log2 e):
 // one v_exp_f32 and one v_rcp_f32.  t << 0 gives 2^(+big) = inf, 1/inf = 0,
@@ -55,60 +97,110 @@ __device__ __forceinline__ float silu_f32(float t) {
     return t * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// VEC consecutive bf16 values of one lane.
-template <int VEC> struct Pack;
-
+// ---- a lane's VEC consecutive values ----------------------------------------
 // NT: the access carries the nontemporal hint (streaming cache policy), for
-// data this pass touches once.
-template <> struct Pack<8> {
+// data the pass touches once.
+template <bool NT, class T>
+__device__ __forceinline__ T ld(const T *p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(p);
+    else
+        return *p;
+}
+template <bool NT, class T>
+__device__ __forceinline__ void st(T *p, T v) {
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, p);
+    else
+        *p = v;
+}
+
+template <class D, int VEC> struct Pack;
+
+// Each Pack is loaded from / stored to a tile (its first element) by lane
+// `tid`; slot_offset(tid, j) is the element of the tile held in slot j.
+
+// 16-bit types: 8 values in one 16-byte access.
+template <class D> struct Pack16 {
     u32x4 w;
-    template <bool NT = false>
-    __device__ __forceinline__ static Pack load(const uint16_t *p) {
-        Pack v;
-        const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
-        if constexpr (NT)
-            v.w = __builtin_nontemporal_load(q);
-        else
-            v.w = *q;
-        return v;
-    }
+    __device__ __forceinline__ static int slot_offset(int tid, int j) { return tid * 8 + j; }
     __device__ __forceinline__ float get(int j) const {
         const uint32_t word = w[j >> 1];
-        return (j & 1) ? bf16_hi(word) : bf16_lo(word);
+        return (j & 1) ? D::hi(word) : D::lo(word);
     }
     template <bool NT = false>
-    __device__ __forceinline__ static void store(uint16_t *p, const float (&o)[8]) {
+    __device__ __forceinline__ static void store(uint16_t *tile, int tid, const float (&o)[8]) {
         u32x4 v;
-        v[0] = pack_bf16x2(o[0], o[1]);
-        v[1] = pack_bf16x2(o[2], o[3]);
-        v[2] = pack_bf16x2(o[4], o[5]);
-        v[3] = pack_bf16x2(o[6], o[7]);
-        u32x4 *q = reinterpret_cast<u32x4 *>(p);
-        if constexpr (NT)
-            __builtin_nontemporal_store(v, q);
-        else
-            *q = v;
+        v[0] = D::pack2(o[0], o[1]);
+        v[1] = D::pack2(o[2], o[3]);
+        v[2] = D::pack2(o[4], o[5]);
+        v[3] = D::pack2(o[6], o[7]);
+        st<NT>(reinterpret_cast<u32x4 *>(tile + tid * 8), v);
+    }
+};
+template <> struct Pack<Bf16, 8> : Pack16<Bf16> {
+    template <bool NT = false>
+    __device__ __forceinline__ static Pack load(const uint16_t *tile, int tid) {
+        Pack v;
+        v.w = ld<NT>(reinterpret_cast<const u32x4 *>(tile + tid * 8));
+        return v;
+    }
+};
+template <> struct Pack<Fp16, 8> : Pack16<Fp16> {
+    template <bool NT = false>
+    __device__ __forceinline__ static Pack load(const uint16_t *tile, int tid) {
+        Pack v;
+        v.w = ld<NT>(reinterpret_cast<const u32x4 *>(tile + tid * 8));
+        return v;
     }
 };
 
-template <> struct Pack<1> {
-    uint16_t b;
+// fp32: slots 0-3 are elements 4*tid .. 4*tid+3 of the tile, slots 4-7 the
+// same four one half-tile (kThreads*4 elements) further on.
+template <> struct Pack<F32, 8> {
+    static constexpr int kHalf = kThreads * 4;
+    u32x4 a, b;
+    __device__ __forceinline__ static int slot_offset(int tid, int j) {
+        return (j < 4 ? 0 : kHalf - 4) + tid * 4 + j;
+    }
     template <bool NT = false>
-    __device__ __forceinline__ static Pack load(const uint16_t *p) {
+    __device__ __forceinline__ static Pack load(const float *tile, int tid) {
         Pack v;
-        if constexpr (NT)
-            v.b = __builtin_nontemporal_load(p);
-        else
-            v.b = *p;
+        v.a = ld<NT>(reinterpret_cast<const u32x4 *>(tile + tid * 4));
+        v.b = ld<NT>(reinterpret_cast<const u32x4 *>(tile + kHalf + tid * 4));
         return v;
     }
-    __device__ __forceinline__ float get(int) const { return bf16_bits_to_f32(b); }
+    __device__ __forceinline__ float get(int j) const {
+        return __uint_as_float(j < 4 ? a[j] : b[j - 4]);
+    }
     template <bool NT = false>
-    __device__ __forceinline__ static void store(uint16_t *p, const float (&o)[1]) {
-        if constexpr (NT)
-            __builtin_nontemporal_store(f32_to_bf16_bits(o[0]), p);
-        else
-            *p = f32_to_bf16_bits(o[0]);
+    __device__ __forceinline__ static void store(float *tile, int tid, const float (&o)[8]) {
+        u32x4 va, vb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            va[j] = __float_as_uint(o[j]);
+            vb[j] = __float_as_uint(o[j + 4]);
+        }
+        st<NT>(reinterpret_cast<u32x4 *>(tile + tid * 4), va);
+        st<NT>(reinterpret_cast<u32x4 *>(tile + kHalf + tid * 4), vb);
+    }
+};
+
+// One value per lane (C < 8 with L*C not a multiple of 8).
+template <class D> struct Pack<D, 1> {
+    typename D::storage b;
+    __device__ __forceinline__ static int slot_offset(int tid, int) { return tid; }
+    template <bool NT = false>
+    __device__ __forceinline__ static Pack load(const typename D::storage *tile, int tid) {
+        Pack v;
+        v.b = ld<NT>(tile + tid);
+        return v;
+    }
+    __device__ __forceinline__ float get(int) const { return D::to_f32(b); }
+    template <bool NT = false>
+    __device__ __forceinline__ static void store(typename D::storage *tile, int tid,
+                                                 const float (&o)[1]) {
+        st<NT>(tile + tid, D::from_f32(o[0]));
     }
 };
 
@@ -165,22 +257,22 @@ __device__ __forceinline__ void store_partial(float *p, float v) {
 // ---------------------------------------------------------------------------
 
 // Pivots p_g of the lane's VEC channel slots; zeroed running sums.
-template <int VEC>
-__device__ __forceinline__ void init_slots(const uint16_t *xs, const Geometry &geo, int tid,
-                                           float (&piv)[VEC], float (&s)[VEC],
+template <class D, int VEC>
+__device__ __forceinline__ void init_slots(const typename D::storage *xs, const Geometry &geo,
+                                           int tid, float (&piv)[VEC], float (&s)[VEC],
                                            float (&q)[VEC]) {
     const int cmask = geo.C - 1;
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
-        const int c = (tid * VEC + j) & cmask;
-        piv[j] = bf16_bits_to_f32(xs[(c >> geo.cg_shift) << geo.cg_shift]);
+        const int c = Pack<D, VEC>::slot_offset(tid, j) & cmask;
+        piv[j] = D::to_f32(xs[(c >> geo.cg_shift) << geo.cg_shift]);
         s[j] = 0.0f;
         q[j] = 0.0f;
     }
 }
 
-template <int VEC>
-__device__ __forceinline__ void accumulate(const Pack<VEC> &v, const float (&piv)[VEC],
+template <class D, int VEC>
+__device__ __forceinline__ void accumulate(const Pack<D, VEC> &v, const float (&piv)[VEC],
                                            float (&s)[VEC], float (&q)[VEC]) {
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
@@ -188,6 +280,12 @@ __device__ __forceinline__ void accumulate(const Pack<VEC> &v, const float (&piv
         s[j] += d;
         q[j] = fmaf(d, d, q[j]);
     }
+}
+
+__device__ __forceinline__ void accumulate1(float v, float piv, float &s, float &q) {
+    const float d = v - piv;
+    s += d;
+    q = fmaf(d, d, q);
 }
 
 // Tiles [t_begin, t_end) of a chunk; the first t_full_end - t_begin of them
@@ -206,10 +304,10 @@ __device__ __forceinline__ ChunkRange chunk_range(const Geometry &geo, int64_t k
 }
 
 // Workgroup reduction of the lanes' slot sums to per-group partials of chunk
-// k, written to out.part_s / out.part_q at [(n*K + k)*G + g].  Slot
-// i = tid*VEC + j of red_* holds channel i mod C; the P = TILE/G slots of
-// group g are i = r*C + g*Cg + u.
-template <int VEC, bool COHERENT>
+// k, written to out.part_s / out.part_q at [(n*K + k)*G + g].  Slot j of
+// lane tid goes to red_*[i], i = slot_offset(tid, j), which holds channel
+// i mod C; the P = TILE/G entries of group g are i = r*C + g*Cg + u.
+template <class D, int VEC, bool COHERENT>
 __device__ __forceinline__ void write_group_partials(const float (&s)[VEC], const float (&q)[VEC],
                                                      float *red_s, float *red_q,
                                                      const Geometry &geo, int64_t n, int64_t k,
@@ -217,8 +315,9 @@ __device__ __forceinline__ void write_group_partials(const float (&s)[VEC], cons
     constexpr int TILE = kThreads * VEC;
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
-        red_s[tid * VEC + j] = s[j];
-        red_q[tid * VEC + j] = q[j];
+        const int i = Pack<D, VEC>::slot_offset(tid, j);
+        red_s[i] = s[j];
+        red_q[i] = q[j];
     }
     __syncthreads();
     const int G = geo.G;
@@ -289,7 +388,9 @@ __device__ __forceinline__ bool arrive_is_last(const StatsOut &out, int64_t n, i
 // trips overlap -- one round trip for K <= 16*tpg), a fixed tree over j
 // follows, and mean/rstd are written.  The arrival counter is reset to zero
 // for the next call.
-__device__ __forceinline__ void finalize_sample(const uint16_t *xs, const Geometry &geo, int64_t n,
+template <class D>
+__device__ __forceinline__ void finalize_sample(const typename D::storage *xs,
+                                                const Geometry &geo, int64_t n,
                                                 const StatsOut &out, float *red_s, float *red_q,
                                                 int tid) {
     const int G = geo.G;
@@ -330,7 +431,7 @@ __device__ __forceinline__ void finalize_sample(const uint16_t *xs, const Geomet
         __syncthreads();
     }
     if (j == 0) {
-        const float pivot = bf16_bits_to_f32(xs[static_cast<int64_t>(g) << geo.cg_shift]);
+        const float pivot = D::to_f32(xs[static_cast<int64_t>(g) << geo.cg_shift]);
         group_moments(red_s[tid], red_q[tid], pivot, out.inv_m, out.eps, out.mean + n * G + g,
                       out.rstd + n * G + g);
     }
@@ -339,7 +440,7 @@ __device__ __forceinline__ void finalize_sample(const uint16_t *xs, const Geomet
 }
 
 // scale = gamma*rstd, shift = beta - mean*scale for the lane's VEC channels.
-template <int VEC>
+template <class D, int VEC>
 __device__ __forceinline__ void fold_affine(const float *mean, const float *rstd,
                                             const float *gamma, const float *beta,
                                             const Geometry &geo, int64_t n, int tid,
@@ -347,7 +448,7 @@ __device__ __forceinline__ void fold_affine(const float *mean, const float *rstd
     const int cmask = geo.C - 1;
 #pragma unroll
     for (int j = 0; j < VEC; ++j) {
-        const int c = (tid * VEC + j) & cmask;
+        const int c = Pack<D, VEC>::slot_offset(tid, j) & cmask;
         const int64_t gi = n * geo.G + (c >> geo.cg_shift);
         const float ga = gamma ? gamma[c] : 1.0f;
         const float be = beta ? beta[c] : 0.0f;
@@ -356,18 +457,21 @@ __device__ __forceinline__ void fold_affine(const float *mean, const float *rstd
     }
 }
 
-template <int VEC, bool SILU>
-__device__ __forceinline__ void transform(const Pack<VEC> &v, const float (&sc)[VEC],
+template <bool SILU>
+__device__ __forceinline__ float transform1(float x, float sc, float sh) {
+    const float t = fmaf(x, sc, sh);
+    if constexpr (SILU) {
+        return silu_f32(t);
+    } else {
+        return t;
+    }
+}
+
+template <class D, int VEC, bool SILU>
+__device__ __forceinline__ void transform(const Pack<D, VEC> &v, const float (&sc)[VEC],
                                           const float (&sh)[VEC], float (&o)[VEC]) {
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-        const float t = fmaf(v.get(j), sc[j], sh[j]);
-        if constexpr (SILU) {
-            o[j] = silu_f32(t);
-        } else {
-            o[j] = t;
-        }
-    }
+    for (int j = 0; j < VEC; ++j) o[j] = transform1<SILU>(v.get(j), sc[j], sh[j]);
 }
 
 // ---------------------------------------------------------------------------
@@ -383,9 +487,9 @@ __device__ __forceinline__ void transform(const Pack<VEC> &v, const float (&sc)[
 // is the arrival counted; the last workgroup reads the partials with
 // agent-scope (coherent) loads.
 // ---------------------------------------------------------------------------
-template <int VEC, int UNROLL, bool NTL, bool FUSED>
+template <class D, int VEC, int UNROLL, bool NTL, bool FUSED>
 __global__ __launch_bounds__(kThreads) void gn_partial_stats(
-    const uint16_t *__restrict__ x, Geometry geo, StatsOut out) {
+    const typename D::storage *__restrict__ x, Geometry geo, StatsOut out) {
     constexpr int TILE = kThreads * VEC;
     __shared__ float red_s[TILE];
     __shared__ float red_q[TILE];
@@ -394,36 +498,40 @@ __global__ __launch_bounds__(kThreads) void gn_partial_stats(
     const int64_t wg = blockIdx.x;
     const int64_t n = wg / geo.K;
     const int64_t k = wg - n * geo.K;
-    const uint16_t *xs = x + n * geo.E;
+    const typename D::storage *xs = x + n * geo.E;
 
     float piv[VEC], s[VEC], q[VEC];
-    init_slots<VEC>(xs, geo, tid, piv, s, q);
+    init_slots<D, VEC>(xs, geo, tid, piv, s, q);
 
     const ChunkRange cr = chunk_range(geo, k);
-    const uint16_t *p = xs + cr.t_begin * TILE + tid * VEC;
+    const typename D::storage *p = xs + cr.t_begin * TILE;  // current tile
     int64_t tt = cr.t_begin;
     for (; tt + UNROLL <= cr.t_full_end; tt += UNROLL) {
-        Pack<VEC> v[UNROLL];
+        Pack<D, VEC> v[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) v[u] = Pack<VEC>::template load<NTL>(p + u * TILE);
+        for (int u = 0; u < UNROLL; ++u)
+            v[u] = Pack<D, VEC>::template load<NTL>(p + u * TILE, tid);
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) accumulate<VEC>(v[u], piv, s, q);
+        for (int u = 0; u < UNROLL; ++u) accumulate<D, VEC>(v[u], piv, s, q);
         p += UNROLL * TILE;
     }
     for (; tt < cr.t_full_end; ++tt) {
-        accumulate<VEC>(Pack<VEC>::template load<NTL>(p), piv, s, q);
+        accumulate<D, VEC>(Pack<D, VEC>::template load<NTL>(p, tid), piv, s, q);
         p += TILE;
     }
     if (tt < cr.t_end) {
-        // The sample's last tile is partial; E is a multiple of VEC, so each
-        // lane's vector lies wholly inside or wholly outside the sample.
-        const int64_t off = tt * TILE + tid * VEC;
-        if (off < geo.E) accumulate<VEC>(Pack<VEC>::template load<NTL>(xs + off), piv, s, q);
+        // The sample's last tile is partial: slot by slot, in bounds only.
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            const int64_t off = tt * TILE + Pack<D, VEC>::slot_offset(tid, j);
+            if (off < geo.E) accumulate1(D::to_f32(xs[off]), piv[j], s[j], q[j]);
+        }
     }
 
-    write_group_partials<VEC, FUSED>(s, q, red_s, red_q, geo, n, k, out, tid);
+    write_group_partials<D, VEC, FUSED>(s, q, red_s, red_q, geo, n, k, out, tid);
     if constexpr (FUSED) {
-        if (arrive_is_last(out, n, geo.K, tid)) finalize_sample(xs, geo, n, out, red_s, red_q, tid);
+        if (arrive_is_last(out, n, geo.K, tid))
+            finalize_sample<D>(xs, geo, n, out, red_s, red_q, tid);
     }
 }
 
@@ -432,8 +540,9 @@ __global__ __launch_bounds__(kThreads) void gn_partial_stats(
 // workgroup to finish quickly): one workgroup per (n, g), a fixed-order tree
 // over the K chunk partials.
 // ---------------------------------------------------------------------------
+template <class D>
 __global__ __launch_bounds__(kThreads) void gn_finalize_stats(
-    const uint16_t *__restrict__ x, Geometry geo, StatsOut out) {
+    const typename D::storage *__restrict__ x, Geometry geo, StatsOut out) {
     __shared__ float rs[kThreads];
     __shared__ float rq[kThreads];
     const int tid = threadIdx.x;
@@ -457,8 +566,7 @@ __global__ __launch_bounds__(kThreads) void gn_finalize_stats(
         __syncthreads();
     }
     if (tid == 0) {
-        const float pivot =
-            bf16_bits_to_f32(x[n * geo.E + (static_cast<int64_t>(g) << geo.cg_shift)]);
+        const float pivot = D::to_f32(x[n * geo.E + (static_cast<int64_t>(g) << geo.cg_shift)]);
         group_moments(rs[0], rq[0], pivot, out.inv_m, out.eps, out.mean + ng, out.rstd + ng);
     }
 }
@@ -474,13 +582,13 @@ __global__ __launch_bounds__(kThreads) void gn_zero_u32(unsigned *p, int64_t n) 
 // Step 3: fused apply.  One workgroup per (n, chunk); each lane folds
 // gamma/beta and the group statistics of its VEC channels into scale/shift
 // registers once (scale = gamma*rstd, shift = beta - mean*scale), then
-// streams its chunk: y = SiLU(x*scale + shift), rounded once to bf16.
+// streams its chunk: y = SiLU(x*scale + shift), rounded once to D.
 // x and y may be the same buffer (each element is read, then written, by one
 // lane), so they carry no __restrict__.
 // ---------------------------------------------------------------------------
-template <int VEC, int UNROLL, bool SILU, bool NTL, bool NTS>
+template <class D, int VEC, int UNROLL, bool SILU, bool NTL, bool NTS>
 __global__ __launch_bounds__(kThreads) void gn_apply(
-    const uint16_t *x, uint16_t *y, Geometry geo, int reverse,
+    const typename D::storage *x, typename D::storage *y, Geometry geo, int reverse,
     const float *__restrict__ mean, const float *__restrict__ rstd,
     const float *__restrict__ gamma, const float *__restrict__ beta) {
     constexpr int TILE = kThreads * VEC;
@@ -491,36 +599,38 @@ __global__ __launch_bounds__(kThreads) void gn_apply(
     const int64_t k = wg - n * geo.K;
 
     float sc[VEC], sh[VEC];
-    fold_affine<VEC>(mean, rstd, gamma, beta, geo, n, tid, sc, sh);
+    fold_affine<D, VEC>(mean, rstd, gamma, beta, geo, n, tid, sc, sh);
 
     const int64_t base = n * geo.E;
     const ChunkRange cr = chunk_range(geo, k);
-    int64_t off = base + cr.t_begin * TILE + tid * VEC;
+    int64_t off = base + cr.t_begin * TILE;  // current tile
     int64_t tt = cr.t_begin;
     for (; tt + UNROLL <= cr.t_full_end; tt += UNROLL) {
-        Pack<VEC> v[UNROLL];
+        Pack<D, VEC> v[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) v[u] = Pack<VEC>::template load<NTL>(x + off + u * TILE);
+        for (int u = 0; u < UNROLL; ++u)
+            v[u] = Pack<D, VEC>::template load<NTL>(x + off + u * TILE, tid);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             float o[VEC];
-            transform<VEC, SILU>(v[u], sc, sh, o);
-            Pack<VEC>::template store<NTS>(y + off + u * TILE, o);
+            transform<D, VEC, SILU>(v[u], sc, sh, o);
+            Pack<D, VEC>::template store<NTS>(y + off + u * TILE, tid, o);
         }
         off += UNROLL * TILE;
     }
     for (; tt < cr.t_full_end; ++tt) {
         float o[VEC];
-        transform<VEC, SILU>(Pack<VEC>::template load<NTL>(x + off), sc, sh, o);
-        Pack<VEC>::template store<NTS>(y + off, o);
+        transform<D, VEC, SILU>(Pack<D, VEC>::template load<NTL>(x + off, tid), sc, sh, o);
+        Pack<D, VEC>::template store<NTS>(y + off, tid, o);
         off += TILE;
     }
     if (tt < cr.t_end) {
-        const int64_t rel = tt * TILE + tid * VEC;
-        if (rel < geo.E) {
-            float o[VEC];
-            transform<VEC, SILU>(Pack<VEC>::template load<NTL>(x + base + rel), sc, sh, o);
-            Pack<VEC>::template store<NTS>(y + base + rel, o);
+        // The sample's last tile is partial: slot by slot, in bounds only.
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) {
+            const int64_t rel = tt * TILE + Pack<D, VEC>::slot_offset(tid, j);
+            if (rel < geo.E)
+                y[base + rel] = D::from_f32(transform1<SILU>(D::to_f32(x[base + rel]), sc[j], sh[j]));
         }
     }
 }

@@ -25,8 +25,10 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * Tensors: x and y hold bf16 values as raw 16-bit patterns (uint16 storage),
- *   dense, element (n, l, c) at offset (n*L + l)*C + c.  gamma and beta are
+ * Tensors: x and y hold bf16 values as raw 16-bit patterns (uint16 storage)
+ *   -- or, through the *_dtype entry points, IEEE fp16 or fp32 values, the
+ *   same type for x and y -- dense, element (n, l, c) at offset
+ *   (n*L + l)*C + c.  gamma and beta are
  *   fp32[C]; either may be NULL (all ones / all zeros, i.e. GroupNorm
  *   without affine).  All tensor pointers are DEVICE pointers on the device
  *   that owns `stream`.  x and y must be 16-byte aligned.
@@ -49,7 +51,8 @@
  * Errors (checked in this order; nothing is enqueued unless GN_OK):
  *   GN_INVALID_ARGUMENT -- input no GroupNorm accepts: x or y NULL; N, L, H
  *     or W negative; C <= 0; G <= 0; C % G != 0; eps negative, infinite or
- *     NaN; apply_silu not 0 or 1; N*L*C overflowing int64.
+ *     NaN; apply_silu not 0 or 1; a dtype outside gn_dtype; the tensor's byte
+ *     size overflowing int64.
  *   GN_UNSUPPORTED -- a valid GroupNorm this library declines, so the caller
  *     falls back: C not a power of two; C > 2048; (strided form) a layout
  *     that is not dense channels-last; x or y not 16-byte aligned; a tensor
@@ -72,6 +75,14 @@ typedef enum gn_status {
     GN_INVALID_ARGUMENT = 2,
     GN_DEVICE_ERROR = 3
 } gn_status;
+
+/* Element type of x and y for the *_dtype entry points.  The page's kernel
+ * tests cover fp32 and bf16 activations (Accuracy section, unit tests). */
+typedef enum gn_dtype {
+    GN_DTYPE_BF16 = 0,
+    GN_DTYPE_F16 = 1,
+    GN_DTYPE_F32 = 2
+} gn_dtype;
 
 /* Largest channel count the library accepts (Modifications section 1). */
 #define GN_MAX_CHANNELS 2048
@@ -142,6 +153,35 @@ gn_status gn_profile_rows(const void *x, const float *gamma, const float *beta, 
  * Returns the status gn_silu_rows would return from its argument checks
  * for 16-byte-aligned pointers. */
 gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_out[8]);
+
+/* The same calls for x and y of element type `dtype` (a gn_dtype value);
+ * the bf16 entry points above are these with dtype = GN_DTYPE_BF16.
+ * gn_plan_rows_dtype writes a ninth value, plan_out[8]: 1 when step 3 reads
+ * x with nontemporal loads (tensors larger than the 256 MB Infinity Cache). */
+gn_status gn_silu_nhwc_dtype(const void *x, const float *gamma, const float *beta, void *y,
+                             int64_t N, int64_t H, int64_t W, int64_t C, int64_t G,
+                             float eps, int apply_silu, int dtype, void *stream);
+gn_status gn_silu_rows_dtype(const void *x, const float *gamma, const float *beta, void *y,
+                             int64_t N, int64_t L, int64_t C, int64_t G,
+                             float eps, int apply_silu, int dtype, void *stream);
+gn_status gn_silu_nhwc_strided_dtype(const void *x, const int64_t x_strides[4],
+                                     const float *gamma, const float *beta,
+                                     void *y, const int64_t y_strides[4],
+                                     int64_t N, int64_t H, int64_t W, int64_t C, int64_t G,
+                                     float eps, int apply_silu, int dtype, void *stream);
+gn_status gn_stats_rows_dtype(const void *x, int64_t N, int64_t L, int64_t C, int64_t G,
+                              float eps, int dtype, float *mean_out, float *rstd_out,
+                              void *stream);
+gn_status gn_apply_rows_dtype(const void *x, const float *mean, const float *rstd,
+                              const float *gamma, const float *beta, void *y,
+                              int64_t N, int64_t L, int64_t C, int64_t G,
+                              int apply_silu, int dtype, void *stream);
+gn_status gn_profile_rows_dtype(const void *x, const float *gamma, const float *beta, void *y,
+                                int64_t N, int64_t L, int64_t C, int64_t G,
+                                float eps, int apply_silu, int dtype, void *stream,
+                                int iters, float *kernel_ms, int *n_kernels);
+gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dtype,
+                             int64_t plan_out[9]);
 
 /* Name of kernel slot i of gn_profile_rows, or NULL. */
 const char *gn_kernel_name(int i);

@@ -89,6 +89,31 @@ def test_empty_input_is_ok_without_gpu(N, L):
     assert gn.gn_silu_nhwc(X, None, None, Y, N, L, 1, 64, 32, 1e-6, 1, None) == GnStatus.OK
 
 
+@pytest.mark.parametrize("dtype", [-1, 3, 7])
+def test_invalid_dtype(dtype):
+    assert gn.gn_silu_rows_dtype(X, None, None, Y, 1, 16, 64, 32, 1e-6, 1, dtype,
+                                 None) == GnStatus.INVALID_ARGUMENT
+    assert gn.gn_stats_rows_dtype(X, 1, 16, 64, 32, 1e-6, dtype, Y, Y,
+                                  None) == GnStatus.INVALID_ARGUMENT
+
+
+def test_dtype_entry_points_share_the_checks():
+    for dt in (0, 1, 2):
+        assert gn.gn_silu_rows_dtype(X, None, None, Y, 1, 16, 96, 32, 1e-6, 1, dt,
+                                     None) == GnStatus.UNSUPPORTED
+        assert gn.gn_silu_rows_dtype(X, None, None, Y, 0, 16, 64, 32, 1e-6, 1, dt,
+                                     None) == GnStatus.OK
+        assert gn.gn_silu_nhwc_dtype(None, None, None, Y, 1, 4, 4, 64, 32, 1e-6, 1, dt,
+                                     None) == GnStatus.INVALID_ARGUMENT
+
+
+def test_plan_uses_element_size_for_the_cache_threshold():
+    # (1,512,512,512): 256 MiB in bf16/fp16 (fits the cache), 512 MiB in fp32
+    assert gn.plan_rows(1, 512 * 512, 512, 32, gn.GnDtype.BF16)["apply_nontemporal_loads"] == 0
+    assert gn.plan_rows(1, 512 * 512, 512, 32, gn.GnDtype.F16)["apply_nontemporal_loads"] == 0
+    assert gn.plan_rows(1, 512 * 512, 512, 32, gn.GnDtype.F32)["apply_nontemporal_loads"] == 1
+
+
 def test_nhwc_checks():
     f = gn.gn_silu_nhwc
     assert f(X, None, None, Y, 1, -1, 4, 64, 32, 1e-6, 1, None) == GnStatus.INVALID_ARGUMENT
@@ -130,6 +155,8 @@ def test_binding_declines_cpu_tensors():
     with torch.no_grad():
         assert gn.group_norm_silu_4d(x, 32) is None
         assert gn.group_norm_silu_rows(torch.zeros(1, 16, 64, dtype=torch.bfloat16), 32) is None
+        for dt in (torch.float16, torch.float32, torch.float64):
+            assert gn.group_norm_silu_4d(x.to(dt), 32) is None
     with pytest.raises(ValueError):
         gn.group_norm_silu_4d(torch.zeros(2, 3, dtype=torch.bfloat16), 1)
     with pytest.raises(TypeError):

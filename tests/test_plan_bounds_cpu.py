@@ -139,3 +139,29 @@ def test_plan_declines_like_the_entry_points():
     with pytest.raises(ValueError):
         gn.plan_rows(1, 16, 64, 3)                    # C % G != 0
     assert gn.plan_rows(0, 16, 64, 32)["K1"] == 0     # empty: nothing launched
+
+
+def test_slot_maps_are_permutations_of_a_tile():
+    """Lane tid's slot j holds element o(tid, j) of each 2048-element tile:
+    8*tid + j for 16-bit types, 4*tid + j and 1024 + 4*tid + (j - 4) for
+    fp32.  Each map must cover the tile exactly once, and each 16-byte access
+    (4 fp32 / 8 16-bit slots) must be contiguous and 16-byte aligned."""
+    def o16(tid, j):
+        return 8 * tid + j
+
+    def o32(tid, j):
+        return (0 if j < 4 else 1024 - 4) + 4 * tid + j
+
+    for o, per_access in ((o16, 8), (o32, 4)):
+        offs = [o(t, j) for t in range(THREADS) for j in range(8)]
+        assert sorted(offs) == list(range(THREADS * 8))
+        for t in range(THREADS):
+            for a in range(0, 8, per_access):
+                run = [o(t, j) for j in range(a, a + per_access)]
+                assert run == list(range(run[0], run[0] + per_access))
+                assert run[0] % per_access == 0
+        # one wave instruction (64 lanes, same access index) covers 1 KiB contiguously
+        for a in range(0, 8, per_access):
+            for w in range(THREADS // 64):
+                starts = sorted(o(t, a) for t in range(64 * w, 64 * w + 64))
+                assert starts == list(range(starts[0], starts[0] + 64 * per_access, per_access))
