@@ -17,7 +17,9 @@ Prints ONE JSON line.  Besides the contract fields it carries
                   cores on the same tensor;
   kernels_ms   -- mean duration of each kernel from the same events;
   other_shapes -- us/call of the other four decoder shapes (context);
-  other_dtypes -- the headline shape with fp16 and fp32 input/output.
+  other_dtypes -- the headline shape with fp16 and fp32 input/output;
+  wide_shapes  -- shapes outside the pages' kernel's support set (C not a
+                  power of two, C > 2048, 5-D NDHWC), measured the same way.
 """
 import argparse
 import ctypes
@@ -125,6 +127,7 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--no-other-shapes", action="store_true")
     ap.add_argument("--no-other-dtypes", action="store_true")
+    ap.add_argument("--no-wide-shapes", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -141,7 +144,7 @@ def main():
     import torch
 
     import groupnorm_silu_normalization_amd as gn
-    from gn_inputs import WORKLOADS, make_inputs
+    from gn_inputs import WIDE_WORKLOADS, WORKLOADS, make_inputs
 
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
@@ -239,6 +242,38 @@ def main():
             }
             del dx, dy, dx_np
 
+    wide = {}
+    if not args.no_wide_shapes:
+        for ww in WIDE_WORKLOADS:
+            log("wide shape %s" % ww.label())
+            wb, wg, wbeta = make_inputs(ww)
+            wx = device_tensor(torch, wb, dev).reshape(ww.N, ww.L, ww.C)
+            wy = torch.empty_like(wx)
+            wgt, wbt = torch.from_numpy(wg).to(dev), torch.from_numpy(wbeta).to(dev)
+            wxp, wyp = ctypes.c_void_p(wx.data_ptr()), ctypes.c_void_p(wy.data_ptr())
+            wgp, wbp = ctypes.c_void_p(wgt.data_ptr()), ctypes.c_void_p(wbt.data_ptr())
+
+            def wstep(ww=ww, wxp=wxp, wyp=wyp, wgp=wgp, wbp=wbp):
+                code = gn.gn_silu_rows(wxp, wgp, wbp, wyp, ww.N, ww.L, ww.C, ww.G, ww.eps, 1, sh)
+                if code != 0:
+                    raise RuntimeError(gn.status_text(code))
+
+            wms, _ = time_calls(torch, wstep, args.steps, args.warmup, stream)
+            wk = gn.profile_rows(wx, ww.G, wgt, wbt, ww.eps, True, wy, args.steps)
+            plan = gn.plan_rows(ww.N, ww.L, ww.C, ww.G)
+            wapply = 4 * ww.numel / (wk["gn_apply"] * 1e-3) / 1e9
+            wide[ww.name] = {
+                "shape": [ww.N, ww.C] + ([ww.D] if ww.D != 1 else []) + [ww.H, ww.W],
+                "layout": "NDHWC" if ww.D != 1 else "NHWC",
+                "us_per_call": round(wms * 1e3, 2),
+                "GB_s": round(ww.algorithmic_bytes / (wms * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(ww.algorithmic_bytes / (wms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "apply_frac_of_peak": round(wapply / HBM_PEAK_GBS, 4),
+                "kernels_us": {k: round(v * 1e3, 2) for k, v in wk.items()},
+                "tile": {"A": plan["A"], "W": plan["W"], "slots": plan["slots"], "T": plan["T"]},
+            }
+            del wx, wy
+
     if args.copy_calibration:
         log("copy calibration: 512 MiB device-to-device copy x5")
         src = torch.empty(256 * 1024 * 1024, dtype=torch.int16, device=dev).fill_(1)
@@ -297,6 +332,7 @@ def main():
         "cpu_baseline": cpu,
         "other_shapes": other,
         "other_dtypes": dtypes,
+        "wide_shapes": wide,
         "wall_s_timed_region": round(wall, 4),
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},

@@ -16,6 +16,14 @@ shapes stand in for them.  Recipe (fixed draw order, one generator per case):
     gamma[C] ~ N(1, 0.1), beta[C] ~ N(0, 0.1)          (float32)
     z[N*H*W*C] standard normal float32, NHWC order
     x = bf16_rne(m[c] + s[c] * z)                        (computed in float32)
+
+WIDE_WORKLOADS are shapes outside the pages' kernel's support set (channel
+counts that are not powers of two or exceed 2048, and a 5-D NDHWC video-VAE
+activation), at sizes of the same order as the decoder shapes.  The pages
+give no workload for them: the channel counts are the widths of common
+diffusion UNets and their skip concatenations (320, 960, 1280, 2560), and
+the 5-D shape is a channels_last_3d activation of D = 9 frames, the kind of
+HunyuanVAE-style call site the pages leave on the older kernel.  Same recipe.
 """
 from dataclasses import dataclass, field
 
@@ -36,14 +44,15 @@ class Workload:
     std_dist: tuple = ("one",)
     seed: int = 0
     note: str = field(default="", compare=False)
+    D: int = 1          # depth (frames) of a 5-D NDHWC activation; 1 for 4-D
 
     @property
     def L(self) -> int:
-        return self.H * self.W
+        return self.D * self.H * self.W
 
     @property
     def numel(self) -> int:
-        return self.N * self.C * self.H * self.W
+        return self.N * self.C * self.L
 
     @property
     def algorithmic_bytes(self) -> int:
@@ -51,6 +60,8 @@ class Workload:
         return 3 * 2 * self.numel
 
     def label(self) -> str:
+        if self.D != 1:
+            return "(%d,%d,%d,%d,%d) G=%d" % (self.N, self.C, self.D, self.H, self.W, self.G)
         return "(%d,%d,%d,%d) G=%d" % (self.N, self.C, self.H, self.W, self.G)
 
 
@@ -72,6 +83,26 @@ WORKLOADS = (
     Workload("gn_silu_1x128x1024x1024", 1, 128, 1024, 1024, seed=1005,
              mean_dist=("uniform", -8.0, 8.0), std_dist=("uniform", 0.25, 1.0),
              note="per-channel mean ~ U(-8,8), std ~ U(0.25,1): fp32 cancellation stress"),
+)
+
+
+# Shapes beyond the pages' support set (see the module docstring).
+WIDE_WORKLOADS = (
+    Workload("gn_silu_1x320x512x512", 1, 320, 512, 512, seed=2001,
+             mean_dist=("normal", 0.0, 1.0), std_dist=("uniform", 0.5, 2.0),
+             note="UNet width 320; per-channel mean ~ N(0,1), std ~ U(0.5,2)"),
+    Workload("gn_silu_1x960x256x256", 1, 960, 256, 256, seed=2002,
+             mean_dist=("zero",), std_dist=("uniform", 0.5, 2.0),
+             note="skip concatenation 640+320"),
+    Workload("gn_silu_1x1280x256x256", 1, 1280, 256, 256, seed=2003,
+             mean_dist=("uniform", -8.0, 8.0), std_dist=("uniform", 0.25, 1.0),
+             note="UNet width 1280; mean ~ U(-8,8), std ~ U(0.25,1): cancellation stress"),
+    Workload("gn_silu_1x2560x128x128", 1, 2560, 128, 128, seed=2004,
+             mean_dist=("zero",), std_dist=("uniform", 0.5, 2.0),
+             note="skip concatenation 1280+1280, C > 2048"),
+    Workload("gn_silu_1x128x9x256x256", 1, 128, 256, 256, D=9, seed=2005,
+             mean_dist=("normal", 0.0, 1.0), std_dist=("uniform", 0.5, 2.0),
+             note="5-D NDHWC, 9 frames"),
 )
 
 

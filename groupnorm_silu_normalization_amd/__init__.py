@@ -17,6 +17,9 @@ from .binding import (  # noqa: F401
     gn_plan_rows_dtype,
     gn_profile_rows,
     gn_profile_rows_dtype,
+    gn_silu_ndhwc,
+    gn_silu_ndhwc_dtype,
+    gn_silu_ndhwc_strided_dtype,
     gn_silu_nhwc,
     gn_silu_nhwc_dtype,
     gn_silu_nhwc_strided,
@@ -28,6 +31,7 @@ from .binding import (  # noqa: F401
     gn_status_string,
     gn_version,
     group_norm_silu_4d,
+    group_norm_silu_5d,
     group_norm_silu_rows,
     group_stats_rows,
     lib,

@@ -12,17 +12,20 @@ quality=high", Modifications section 1 "Kernel"):
     group_norm_silu_4d(x, num_groups, weight, bias, eps, apply_silu, out)
     group_norm_silu_rows(x, num_groups, weight, bias, eps, apply_silu, out)
 
+and the 5-D form group_norm_silu_5d for NDHWC (channels_last_3d) tensors.
 x may be bf16, fp16 or fp32 (y has the same type).  Each returns the output
 tensor, or None when the input is outside the supported set so the caller
-falls back: not a GPU tensor, autograd enabled, another dtype, C not a power
-of two, C > 2048, not channels-last (4-D) / not contiguous rows, weight/bias
-not fp32 on the same device.  Arguments no GroupNorm accepts
-raise ValueError; a failed HIP call raises RuntimeError.
+falls back: not a GPU tensor, autograd enabled, another dtype, a channel
+count the library declines (GN_UNSUPPORTED: see the supported set in
+gnsilu.h; every C <= 256, every multiple of 8 up to 2048 and more), not
+channels-last (4-D / 5-D) / not contiguous rows, weight/bias not fp32 on the
+same device.  Arguments no GroupNorm accepts raise ValueError; a failed HIP
+call raises RuntimeError.
 
 The raw C entry points are re-exported under their C names (gn_silu_nhwc,
-gn_silu_rows, gn_silu_nhwc_strided, gn_stats_rows, gn_apply_rows,
-gn_profile_rows, gn_plan_rows, their *_dtype forms, gn_kernel_name,
-gn_status_string, gn_version).
+gn_silu_rows, gn_silu_nhwc_strided, gn_silu_ndhwc, gn_stats_rows,
+gn_apply_rows, gn_profile_rows, gn_plan_rows, their *_dtype forms,
+gn_kernel_name, gn_status_string, gn_version).
 """
 import ctypes
 import enum
@@ -65,6 +68,7 @@ _vp = ctypes.c_void_p
 _f32 = ctypes.c_float
 _int = ctypes.c_int
 _i64x4 = ctypes.c_int64 * 4
+_i64x5 = ctypes.c_int64 * 5
 
 lib.gn_silu_nhwc.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _int, _vp]
 lib.gn_silu_rows.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _vp]
@@ -81,6 +85,12 @@ lib.gn_silu_rows_dtype.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _
                                    _vp]
 lib.gn_silu_nhwc_strided_dtype.argtypes = [_vp, _i64p, _vp, _vp, _vp, _i64p, _i64, _i64, _i64,
                                            _i64, _i64, _f32, _int, _int, _vp]
+lib.gn_silu_ndhwc.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f32, _int,
+                              _vp]
+lib.gn_silu_ndhwc_dtype.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f32,
+                                    _int, _int, _vp]
+lib.gn_silu_ndhwc_strided_dtype.argtypes = [_vp, _i64p, _vp, _vp, _vp, _i64p, _i64, _i64, _i64,
+                                            _i64, _i64, _i64, _f32, _int, _int, _vp]
 lib.gn_stats_rows_dtype.argtypes = [_vp, _i64, _i64, _i64, _i64, _f32, _int, _vp, _vp, _vp]
 lib.gn_apply_rows_dtype.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int,
                                     _int, _vp]
@@ -91,7 +101,8 @@ lib.gn_plan_rows_dtype.argtypes = [_i64, _i64, _i64, _i64, _int, _i64p]
 for _name in ("gn_silu_nhwc", "gn_silu_rows", "gn_silu_nhwc_strided", "gn_stats_rows",
               "gn_apply_rows", "gn_profile_rows", "gn_silu_nhwc_dtype", "gn_silu_rows_dtype",
               "gn_silu_nhwc_strided_dtype", "gn_stats_rows_dtype", "gn_apply_rows_dtype",
-              "gn_profile_rows_dtype", "gn_plan_rows_dtype"):
+              "gn_profile_rows_dtype", "gn_plan_rows_dtype", "gn_silu_ndhwc",
+              "gn_silu_ndhwc_dtype", "gn_silu_ndhwc_strided_dtype"):
     getattr(lib, _name).restype = _int
 lib.gn_plan_rows.argtypes = [_i64, _i64, _i64, _i64, _i64p]
 lib.gn_plan_rows.restype = _int
@@ -114,6 +125,9 @@ gn_plan_rows = lib.gn_plan_rows
 gn_silu_nhwc_dtype = lib.gn_silu_nhwc_dtype
 gn_silu_rows_dtype = lib.gn_silu_rows_dtype
 gn_silu_nhwc_strided_dtype = lib.gn_silu_nhwc_strided_dtype
+gn_silu_ndhwc = lib.gn_silu_ndhwc
+gn_silu_ndhwc_dtype = lib.gn_silu_ndhwc_dtype
+gn_silu_ndhwc_strided_dtype = lib.gn_silu_ndhwc_strided_dtype
 gn_stats_rows_dtype = lib.gn_stats_rows_dtype
 gn_apply_rows_dtype = lib.gn_apply_rows_dtype
 gn_profile_rows_dtype = lib.gn_profile_rows_dtype
@@ -121,7 +135,7 @@ gn_plan_rows_dtype = lib.gn_plan_rows_dtype
 gn_status_string = lib.gn_status_string
 gn_version = lib.gn_version
 
-MAX_CHANNELS = 2048
+MAX_CHANNELS = 8192
 
 
 class GnDtype(enum.IntEnum):
@@ -187,7 +201,7 @@ def _common_checks(x, weight, bias, C):
         return False
     if dtype_code(x.dtype) is None:
         return False
-    if C <= 0 or (C & (C - 1)) != 0 or C > MAX_CHANNELS:
+    if C > MAX_CHANNELS:
         return False
     if not _affine_ok(weight, C, x.device, "weight") or not _affine_ok(bias, C, x.device, "bias"):
         return False
@@ -211,7 +225,7 @@ def _check_groups(C, num_groups):
 
 def group_norm_silu_4d(x, num_groups, weight=None, bias=None, eps=1e-6, apply_silu=True,
                        out=None):
-    """GroupNorm(+SiLU) of a channels-last bf16 tensor of logical shape (N, C, H, W)."""
+    """GroupNorm(+SiLU) of a channels-last tensor of logical shape (N, C, H, W)."""
     torch = _torch()
     if isinstance(x, torch.Tensor) and x.dim() != 4:
         raise ValueError("group_norm_silu_4d expects a 4-D tensor, got %d-D" % x.dim())
@@ -232,9 +246,32 @@ def group_norm_silu_4d(x, num_groups, weight=None, bias=None, eps=1e-6, apply_si
     return _result(code, out)
 
 
+def group_norm_silu_5d(x, num_groups, weight=None, bias=None, eps=1e-6, apply_silu=True,
+                       out=None):
+    """GroupNorm(+SiLU) of a channels_last_3d tensor of logical shape (N, C, D, H, W)."""
+    torch = _torch()
+    if isinstance(x, torch.Tensor) and x.dim() != 5:
+        raise ValueError("group_norm_silu_5d expects a 5-D tensor, got %d-D" % x.dim())
+    N, C, D, H, W = x.shape if isinstance(x, torch.Tensor) else (0, 0, 0, 0, 0)
+    if not _common_checks(x, weight, bias, C):
+        return None
+    _check_groups(C, num_groups)
+    if not x.is_contiguous(memory_format=torch.channels_last_3d):
+        return None
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.channels_last_3d)
+    elif out.shape != x.shape or out.dtype != x.dtype or out.device != x.device:
+        raise ValueError("out must match x in shape, dtype and device")
+    code = lib.gn_silu_ndhwc_strided_dtype(
+        _ptr(x), _i64x5(*x.stride()), _ptr(weight), _ptr(bias), _ptr(out), _i64x5(*out.stride()),
+        N, D, H, W, C, num_groups, float(eps), 1 if apply_silu else 0, dtype_code(x.dtype),
+        _stream_handle(x))
+    return _result(code, out)
+
+
 def group_norm_silu_rows(x, num_groups, weight=None, bias=None, eps=1e-6, apply_silu=True,
                          out=None):
-    """GroupNorm(+SiLU) of contiguous bf16 rows of shape (N, L, C), C innermost."""
+    """GroupNorm(+SiLU) of contiguous rows of shape (N, L, C), C innermost."""
     torch = _torch()
     if isinstance(x, torch.Tensor) and x.dim() != 3:
         raise ValueError("group_norm_silu_rows expects a 3-D (N, L, C) tensor, got %d-D" % x.dim())
@@ -280,8 +317,8 @@ def apply_rows(x, mean, rstd, weight=None, bias=None, apply_silu=True, out=None)
     return _result(code, out)
 
 
-PLAN_FIELDS = ("vec", "tiles", "full", "tpc1", "K1", "tpc2", "K2", "scratch_bytes",
-               "apply_nontemporal_loads")
+PLAN_FIELDS = ("slots", "tiles", "full", "tpc1", "K1", "tpc2", "K2", "scratch_bytes",
+               "apply_nontemporal_loads", "W", "A", "T", "stats_plain_tail")
 
 
 def _dtype_arg(x):
@@ -293,7 +330,7 @@ def _dtype_arg(x):
 
 def plan_rows(N, L, C, G, dtype=GnDtype.BF16):
     """The library's launch plan for a rows shape (dict), or None if declined."""
-    buf = (_i64 * 9)()
+    buf = (_i64 * len(PLAN_FIELDS))()
     code = lib.gn_plan_rows_dtype(N, L, C, G, int(dtype), buf)
     r = _result(code, True)
     if r is None:

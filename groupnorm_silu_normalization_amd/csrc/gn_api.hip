@@ -4,9 +4,14 @@
 //
 // The contract follows "FLUX.2 VAE decoder fast path behind quality=high",
 // Modifications section 1 "Kernel": group_norm_silu_4d / group_norm_silu_rows
-// return a result, or decline inputs outside the supported set (C not a power
-// of two, C > 2048, not channels-last) so that the caller falls back.  Here
-// "decline" is the status GN_UNSUPPORTED.
+// return a result, or decline inputs outside the supported set so that the
+// caller falls back; here "decline" is the status GN_UNSUPPORTED.  The
+// pages' kernel declines C that is not a power of two and C > 2048; this
+// library takes any C for which a tile layout exists (choose_layout below),
+// which covers every C <= 2048 that is a multiple of 8 and 16-bit C up to
+// 8192 that is a multiple of 32, and it also takes 5-D NDHWC activations
+// through the rows form.  A layout that is not channels-last is still
+// declined.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -14,6 +19,7 @@
 #include <cstdint>
 #include <map>
 #include <mutex>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -29,21 +35,24 @@ constexpr int kUnrollStats = 8;             // 16-byte loads in flight per lane,
 constexpr int kUnrollApply = 4;             // 16-byte loads in flight per lane, step 3
 constexpr int64_t kStatsBlocks = 256;       // step-1 workgroups in total: one per CU
 constexpr int64_t kStatsMaxTiles = 1024;    // caps each lane's sequential fp32 run
-constexpr int64_t kApplyTilesPerBlock = 16; // step-3 workgroups: total tiles / 16 ...
+constexpr int64_t kApplyElemsPerBlock = 16 * 2048;  // step-3 workgroups: elements / 32768 ...
 constexpr int64_t kApplyMinBlocks = 256;    // ... clamped to [256, 2048]
 constexpr int64_t kApplyMaxBlocks = 2048;
-// Step 1 reads x with ordinary loads, so the tail of x it read last is still
-// in the Infinity Cache when step 3 reads it again; step 3 writes y with
-// nontemporal stores so y does not evict it.  A tensor larger than the cache
-// cannot be served from it, and step 3 then streams x with nontemporal loads.
+// Step 1 reads the last cache's worth of x with ordinary loads (the rest with
+// nontemporal ones), so that part of x is still in the 256 MB Infinity Cache
+// when step 3 reads it again; step 3 writes y with nontemporal stores so y
+// does not evict it.  A tensor larger than the cache cannot be served from it
+// whole, and step 3 then streams x with nontemporal loads.
 constexpr int64_t kCacheResidentBytes = int64_t{256} << 20;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
-inline int ilog2(int64_t v) {
-    int r = 0;
-    while ((int64_t{1} << r) < v) ++r;
-    return r;
+inline int64_t gcd64(int64_t a, int64_t b) {
+    while (b != 0) {
+        const int64_t t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
 }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -52,8 +61,49 @@ inline bool valid_dtype(int dtype) {
 }
 inline int64_t elem_bytes(int dtype) { return dtype == GN_DTYPE_F32 ? 4 : 2; }
 
+// How a tile is laid over the lanes (see gn_kernels.hpp): R whole rows,
+// T = R*C = A*W*NV elements; the first A lanes each make NV accesses of W
+// consecutive elements.
+struct Layout {
+    int w;      // elements per access: a 16-byte access (8 of a 16-bit type, 4 fp32), or 1
+    int nv;     // accesses per lane and tile: 1, 2 or 4
+    int a;      // active lanes, <= kThreads
+    int64_t t;  // elements per tile
+};
+
+// The tile layout for a sample of E = L*C elements.  16-byte accesses need
+// every sample to start on a 16-byte boundary, i.e. E a multiple of W;
+// otherwise W = 1.  A tile must be a whole number of rows, so C must divide
+// A*W*NV: A is the largest multiple of m = C / gcd(C, W*NV) not above
+// kThreads.  The smallest NV keeping at least half of the lanes busy is taken,
+// else the NV with the most active lanes: measured on MI355X, fewer accesses
+// per lane beat more active lanes (C = 1280: NV = 1 with 160 lanes runs the
+// path 8% faster than NV = 2 with 240; C = 2560: NV = 2 with 160 lanes 22%
+// faster than NV = 4 with 240), because each extra access costs 2*W*NV
+// registers of scale/shift and sums per lane, and with them occupancy and
+// loads in flight.  fp32 starts at NV = 2 so that a lane moves 32 bytes per
+// tile, as a 16-bit lane moves 16.  No NV with m <= kThreads: no layout, and
+// the shape is declined.
+bool choose_layout(int64_t E, int64_t C, int dtype, Layout *out) {
+    const int w16 = static_cast<int>(16 / elem_bytes(dtype));
+    const int w = (E % w16 == 0) ? w16 : 1;
+    const int nv_min = (w == 4) ? 2 : 1;
+    bool found = false;
+    for (int nv = nv_min; nv <= 4; nv *= 2) {
+        const int64_t m = C / gcd64(C, static_cast<int64_t>(w) * nv);
+        if (m > kThreads) continue;
+        const int a = static_cast<int>((kThreads / m) * m);
+        if (!found || a > out->a) {
+            *out = Layout{w, nv, a, static_cast<int64_t>(a) * w * nv};
+            found = true;
+        }
+        if (2 * out->a >= kThreads) break;
+    }
+    return found;
+}
+
 struct Plan {
-    int vec;          // 8: 16-byte lanes; 1: 2-byte lanes (C < 8 with L*C not a multiple of 8)
+    Layout lay;       // tile layout
     bool fused;       // step 2 runs in the tail of step 1 (G <= kThreads)
     bool apply_ntl;   // step 3 reads x with nontemporal loads
     int dtype;        // gn_dtype of x and y
@@ -70,24 +120,39 @@ Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G, int dtype) {
     p.N = N;
     p.dtype = dtype;
     const int64_t E = L * C;
-    p.vec = (E % 8 == 0) ? 8 : 1;
+    (void)choose_layout(E, C, dtype, &p.lay);  // check_shape has accepted the shape
     p.fused = G <= kThreads;
     p.apply_ntl = N * E * elem_bytes(dtype) > kCacheResidentBytes;
-    const int64_t tile = int64_t{kThreads} * p.vec;
     Geometry g;
     g.E = E;
-    g.tiles = ceil_div(E, tile);
-    g.full = E / tile;
+    g.T = p.lay.t;
+    g.tiles = ceil_div(E, g.T);
+    g.full = E / g.T;
     g.C = static_cast<int>(C);
-    g.cg_shift = ilog2(C / G);
     g.G = static_cast<int>(G);
+    g.Cg = static_cast<int>(C / G);
+    g.A = p.lay.a;
+    g.cg_shift = 0;
+    while ((int64_t{1} << g.cg_shift) < C / G) ++g.cg_shift;
+    if (p.lay.a != kThreads) g.cg_shift = 0;  // only the power-of-two kernels use it
+    g.plain_tail = 0;
     const int64_t total = N * g.tiles;
     p.stats = g;
     p.stats.tpc = std::min(kStatsMaxTiles, std::max<int64_t>(1, ceil_div(total, kStatsBlocks)));
     p.stats.K = ceil_div(g.tiles, p.stats.tpc);
+    // Step 1's plain-load tail: the fraction cache / tensor of every chunk (all
+    // of it when the tensor fits), so about one cache's worth of x is read
+    // last with allocating loads.  Measured on MI355X over the whole path:
+    // 512 MiB bf16 -1.7%, 1 GiB -3.7%; a smaller plain fraction slows step 3
+    // by more than it saves in step 1.
+    const int64_t bytes = N * E * elem_bytes(dtype);
+    p.stats.plain_tail =
+        bytes <= kCacheResidentBytes
+            ? p.stats.tpc
+            : std::max<int64_t>(1, ceil_div(p.stats.tpc * kCacheResidentBytes, bytes));
     p.apply = g;
-    const int64_t apply_blocks =
-        std::min(kApplyMaxBlocks, std::max(kApplyMinBlocks, total / kApplyTilesPerBlock));
+    const int64_t apply_blocks = std::min(
+        kApplyMaxBlocks, std::max(kApplyMinBlocks, total * g.T / kApplyElemsPerBlock));
     p.apply.tpc = std::max<int64_t>(1, ceil_div(total, apply_blocks));
     p.apply.K = ceil_div(g.tiles, p.apply.tpc);
     p.inv_m = 1.0 / (static_cast<double>(L) * static_cast<double>(C / G));
@@ -116,7 +181,9 @@ gn_status check_shape(const void *x, const void *y, int64_t N, int64_t L, int64_
     if (apply_silu != 0 && apply_silu != 1) return GN_INVALID_ARGUMENT;
     if (L > 0 && N > INT64_MAX / L) return GN_INVALID_ARGUMENT;
     if (N * L > 0 && C > INT64_MAX / (N * L) / 4) return GN_INVALID_ARGUMENT;
-    if (!is_pow2(C) || C > GN_MAX_CHANNELS) return GN_UNSUPPORTED;
+    if (C > GN_MAX_CHANNELS) return GN_UNSUPPORTED;
+    Layout lay;
+    if (!choose_layout(L * C, C, dtype, &lay)) return GN_UNSUPPORTED;
     if ((reinterpret_cast<uintptr_t>(x) & 15u) != 0) return GN_UNSUPPORTED;
     if (need_y && (reinterpret_cast<uintptr_t>(y) & 15u) != 0) return GN_UNSUPPORTED;
     // Grid extents: a dispatch holds at most 2^32 work-items, i.e. 2^24
@@ -125,7 +192,7 @@ gn_status check_shape(const void *x, const void *y, int64_t N, int64_t L, int64_
     // separate finalize N*G.
     if (N > (int64_t{1} << 24) - 2 * kApplyMaxBlocks || N * G >= (int64_t{1} << 24))
         return GN_UNSUPPORTED;
-    if (L > 0 && N * ceil_div(L * C, kThreads) / kStatsMaxTiles > (int64_t{1} << 23))
+    if (L > 0 && N * ceil_div(L * C, lay.t) / kStatsMaxTiles > (int64_t{1} << 23))
         return GN_UNSUPPORTED;
     return GN_OK;
 }
@@ -245,6 +312,41 @@ struct Events {
     hipEvent_t ev[2 * kSlots];  // start/stop per slot
 };
 
+template <int V> using IC = std::integral_constant<int, V>;
+
+// Calls f(IC<W>, IC<NV>, IC<POW2>) with the plan's layout as compile-time
+// constants; POW2 = all 256 lanes busy, which happens exactly when C is a
+// power of two.
+template <class D, class F>
+void with_layout(const Plan &p, F &&f) {
+    constexpr int W16 = static_cast<int>(16 / sizeof(typename D::storage));
+    auto by_pow2 = [&](auto wc, auto nvc) {
+        if (p.lay.a == kThreads)
+            f(wc, nvc, IC<1>{});
+        else
+            f(wc, nvc, IC<0>{});
+    };
+    if (p.lay.w == 1) {
+        switch (p.lay.nv) {
+            case 1: by_pow2(IC<1>{}, IC<1>{}); break;
+            case 2: by_pow2(IC<1>{}, IC<2>{}); break;
+            default: by_pow2(IC<1>{}, IC<4>{}); break;
+        }
+    } else {
+        switch (p.lay.nv) {
+            case 1:
+                if constexpr (W16 != 4) by_pow2(IC<W16>{}, IC<1>{});  // fp32 starts at NV = 2
+                break;
+            case 2: by_pow2(IC<W16>{}, IC<2>{}); break;
+            default: by_pow2(IC<W16>{}, IC<4>{}); break;
+        }
+    }
+}
+
+// Loads in flight per lane: kUnroll* tiles of up to two accesses, half as
+// many tiles of four.
+constexpr int unroll_for(int base, int nv) { return nv <= 2 ? base : base / 4; }
+
 template <class D>
 void launch_stats_t(const Plan &p, const void *xv, const StatsOut &o, hipStream_t s,
                     const Events *ev) {
@@ -253,17 +355,16 @@ void launch_stats_t(const Plan &p, const void *xv, const StatsOut &o, hipStream_
     const dim3 block(kThreads);
     const dim3 grid1(static_cast<unsigned>(p.N * p.stats.K));
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotStats], s);
-    if (p.vec == 8) {
+    with_layout<D>(p, [&](auto wc, auto nvc, auto pc) {
+        constexpr int W = decltype(wc)::value;
+        constexpr int NV = decltype(nvc)::value;
+        constexpr bool P2 = decltype(pc)::value != 0;
+        constexpr int U = unroll_for(kUnrollStats, NV);
         if (p.fused)
-            gn_partial_stats<D, 8, kUnrollStats, false, true><<<grid1, block, 0, s>>>(x, p.stats, o);
+            gn_partial_stats<D, W, NV, P2, U, true><<<grid1, block, 0, s>>>(x, p.stats, o);
         else
-            gn_partial_stats<D, 8, kUnrollStats, false, false><<<grid1, block, 0, s>>>(x, p.stats, o);
-    } else {
-        if (p.fused)
-            gn_partial_stats<D, 1, kUnrollStats, false, true><<<grid1, block, 0, s>>>(x, p.stats, o);
-        else
-            gn_partial_stats<D, 1, kUnrollStats, false, false><<<grid1, block, 0, s>>>(x, p.stats, o);
-    }
+            gn_partial_stats<D, W, NV, P2, U, false><<<grid1, block, 0, s>>>(x, p.stats, o);
+    });
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotStats + 1], s);
     if (!p.fused) {
         const dim3 grid2(static_cast<unsigned>(p.N * p.stats.G));
@@ -273,20 +374,26 @@ void launch_stats_t(const Plan &p, const void *xv, const StatsOut &o, hipStream_
     }
 }
 
-template <class D, int VEC, bool SILU>
-void launch_apply_vs(const Plan &p, const void *xv, void *yv, const float *mean, const float *rstd,
-                     const float *gamma, const float *beta, hipStream_t s) {
+template <class D, bool SILU>
+void launch_apply_s(const Plan &p, const void *xv, void *yv, const float *mean, const float *rstd,
+                    const float *gamma, const float *beta, hipStream_t s) {
     using T = typename D::storage;
     const T *x = static_cast<const T *>(xv);
     T *y = static_cast<T *>(yv);
     const dim3 block(kThreads);
     const dim3 grid(static_cast<unsigned>(p.N * p.apply.K));
-    if (p.apply_ntl)
-        gn_apply<D, VEC, kUnrollApply, SILU, true, true><<<grid, block, 0, s>>>(
-            x, y, p.apply, 0, mean, rstd, gamma, beta);
-    else
-        gn_apply<D, VEC, kUnrollApply, SILU, false, true><<<grid, block, 0, s>>>(
-            x, y, p.apply, 0, mean, rstd, gamma, beta);
+    with_layout<D>(p, [&](auto wc, auto nvc, auto pc) {
+        constexpr int W = decltype(wc)::value;
+        constexpr int NV = decltype(nvc)::value;
+        constexpr bool P2 = decltype(pc)::value != 0;
+        constexpr int U = unroll_for(kUnrollApply, NV);
+        if (p.apply_ntl)
+            gn_apply<D, W, NV, P2, U, SILU, true, true><<<grid, block, 0, s>>>(
+                x, y, p.apply, mean, rstd, gamma, beta);
+        else
+            gn_apply<D, W, NV, P2, U, SILU, false, true><<<grid, block, 0, s>>>(
+                x, y, p.apply, mean, rstd, gamma, beta);
+    });
 }
 
 template <class D>
@@ -294,17 +401,10 @@ void launch_apply_t(const Plan &p, const void *x, void *y, const float *mean, co
                     const float *gamma, const float *beta, int silu, hipStream_t s,
                     const Events *ev) {
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotApply], s);
-    if (p.vec == 8) {
-        if (silu)
-            launch_apply_vs<D, 8, true>(p, x, y, mean, rstd, gamma, beta, s);
-        else
-            launch_apply_vs<D, 8, false>(p, x, y, mean, rstd, gamma, beta, s);
-    } else {
-        if (silu)
-            launch_apply_vs<D, 1, true>(p, x, y, mean, rstd, gamma, beta, s);
-        else
-            launch_apply_vs<D, 1, false>(p, x, y, mean, rstd, gamma, beta, s);
-    }
+    if (silu)
+        launch_apply_s<D, true>(p, x, y, mean, rstd, gamma, beta, s);
+    else
+        launch_apply_s<D, false>(p, x, y, mean, rstd, gamma, beta, s);
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotApply + 1], s);
 }
 
@@ -432,14 +532,47 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
     return GN_OK;
 }
 
-// Dense channels-last check for logical (N, C, H, W) strides.  A dimension
-// of extent 1 may carry any stride, as in torch's channels_last test.
-bool dense_nhwc(const int64_t st[4], int64_t N, int64_t H, int64_t W, int64_t C) {
-    const int64_t ext[4] = {N, C, H, W};
-    const int64_t want[4] = {H * W * C, 1, W * C, C};
-    for (int d = 0; d < 4; ++d)
-        if (ext[d] > 1 && st[d] != want[d]) return false;
+// Dense channels-last check for the strides of logical (N, C, S1, ..., Sk)
+// dimensions (k = 2: NHWC, k = 3: NDHWC): the dense strides are
+// (S1*...*Sk*C, 1, S2*...*Sk*C, ..., C).  A dimension of extent 1 may carry
+// any stride, as in torch's channels_last tests.
+bool dense_channels_last(const int64_t *st, int64_t N, int64_t C, const int64_t *sp, int k) {
+    int64_t inner = C;  // dense stride of the innermost spatial dimension
+    for (int d = k - 1; d >= 0; --d) {
+        if (sp[d] > 1 && st[2 + d] != inner) return false;
+        inner *= sp[d];
+    }
+    if (N > 1 && st[0] != inner) return false;
+    if (C > 1 && st[1] != 1) return false;
     return true;
+}
+
+// L = product of the k spatial extents, or -1 if one is negative or the
+// product overflows int64.
+int64_t spatial_rows(const int64_t *sp, int k) {
+    int64_t L = 1;
+    for (int d = 0; d < k; ++d) {
+        if (sp[d] < 0) return -1;
+        if (sp[d] > 0 && L > INT64_MAX / sp[d]) return -1;
+        L *= sp[d];
+    }
+    return L;
+}
+
+// The strided 4-D and 5-D forms: argument errors first, then the layout.
+gn_status run_strided(const void *x, const int64_t *x_strides, const float *gamma,
+                      const float *beta, void *y, const int64_t *y_strides, int64_t N,
+                      const int64_t *sp, int k, int64_t C, int64_t G, float eps, int apply_silu,
+                      int dtype, void *stream) {
+    if (x_strides == nullptr || y_strides == nullptr) return GN_INVALID_ARGUMENT;
+    const int64_t L = spatial_rows(sp, k);
+    if (L < 0) return GN_INVALID_ARGUMENT;
+    const gn_status st = check_shape(x, y, N, L, C, G, eps, apply_silu, true, dtype);
+    if (st == GN_INVALID_ARGUMENT) return st;
+    if (!dense_channels_last(x_strides, N, C, sp, k) ||
+        !dense_channels_last(y_strides, N, C, sp, k))
+        return GN_UNSUPPORTED;
+    return run_rows(x, gamma, beta, y, N, L, C, G, eps, apply_silu, dtype, stream, 0, nullptr);
 }
 
 }  // namespace
@@ -482,15 +615,35 @@ gn_status gn_silu_nhwc_strided_dtype(const void *x, const int64_t x_strides[4],
                                      const int64_t y_strides[4], int64_t N, int64_t H, int64_t W,
                                      int64_t C, int64_t G, float eps, int apply_silu, int dtype,
                                      void *stream) {
-    if (x_strides == nullptr || y_strides == nullptr) return GN_INVALID_ARGUMENT;
-    if (H < 0 || W < 0) return GN_INVALID_ARGUMENT;
-    if (W > 0 && H > INT64_MAX / W) return GN_INVALID_ARGUMENT;
-    // Argument errors take precedence over layout refusals.
-    gn_status st = check_shape(x, y, N, H * W, C, G, eps, apply_silu, true, dtype);
-    if (st == GN_INVALID_ARGUMENT) return st;
-    if (!dense_nhwc(x_strides, N, H, W, C) || !dense_nhwc(y_strides, N, H, W, C))
-        return GN_UNSUPPORTED;
-    return gn_silu_rows_dtype(x, gamma, beta, y, N, H * W, C, G, eps, apply_silu, dtype, stream);
+    const int64_t sp[2] = {H, W};
+    return run_strided(x, x_strides, gamma, beta, y, y_strides, N, sp, 2, C, G, eps, apply_silu,
+                       dtype, stream);
+}
+
+gn_status gn_silu_ndhwc_dtype(const void *x, const float *gamma, const float *beta, void *y,
+                              int64_t N, int64_t D, int64_t H, int64_t W, int64_t C, int64_t G,
+                              float eps, int apply_silu, int dtype, void *stream) {
+    const int64_t sp[3] = {D, H, W};
+    const int64_t L = spatial_rows(sp, 3);
+    if (L < 0) return GN_INVALID_ARGUMENT;
+    return gn_silu_rows_dtype(x, gamma, beta, y, N, L, C, G, eps, apply_silu, dtype, stream);
+}
+
+gn_status gn_silu_ndhwc(const void *x, const float *gamma, const float *beta, void *y, int64_t N,
+                        int64_t D, int64_t H, int64_t W, int64_t C, int64_t G, float eps,
+                        int apply_silu, void *stream) {
+    return gn_silu_ndhwc_dtype(x, gamma, beta, y, N, D, H, W, C, G, eps, apply_silu,
+                               GN_DTYPE_BF16, stream);
+}
+
+gn_status gn_silu_ndhwc_strided_dtype(const void *x, const int64_t x_strides[5],
+                                      const float *gamma, const float *beta, void *y,
+                                      const int64_t y_strides[5], int64_t N, int64_t D,
+                                      int64_t H, int64_t W, int64_t C, int64_t G, float eps,
+                                      int apply_silu, int dtype, void *stream) {
+    const int64_t sp[3] = {D, H, W};
+    return run_strided(x, x_strides, gamma, beta, y, y_strides, N, sp, 3, C, G, eps, apply_silu,
+                       dtype, stream);
 }
 
 gn_status gn_silu_nhwc_strided(const void *x, const int64_t x_strides[4], const float *gamma,
@@ -577,18 +730,18 @@ gn_status gn_profile_rows(const void *x, const float *gamma, const float *beta, 
 }
 
 gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dtype,
-                             int64_t plan_out[9]) {
+                             int64_t plan_out[13]) {
     if (plan_out == nullptr) return GN_INVALID_ARGUMENT;
     static const uint16_t aligned_probe[8] __attribute__((aligned(16))) = {};
     const gn_status st =
         check_shape(aligned_probe, aligned_probe, N, L, C, G, 0.0f, 0, true, dtype);
     if (st != GN_OK) return st;
     if (N * L == 0) {
-        for (int i = 0; i < 9; ++i) plan_out[i] = 0;
+        for (int i = 0; i < 13; ++i) plan_out[i] = 0;
         return GN_OK;
     }
     const Plan p = make_plan(N, L, C, G, dtype);
-    plan_out[0] = p.vec;
+    plan_out[0] = static_cast<int64_t>(p.lay.w) * p.lay.nv;
     plan_out[1] = p.stats.tiles;
     plan_out[2] = p.stats.full;
     plan_out[3] = p.stats.tpc;
@@ -597,12 +750,16 @@ gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dty
     plan_out[6] = p.apply.K;
     plan_out[7] = static_cast<int64_t>(arrivals_bytes(N) + payload_bytes(p, true));
     plan_out[8] = p.apply_ntl ? 1 : 0;
+    plan_out[9] = p.lay.w;
+    plan_out[10] = p.lay.a;
+    plan_out[11] = p.lay.t;
+    plan_out[12] = p.stats.plain_tail;
     return GN_OK;
 }
 
 gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_out[8]) {
     if (plan_out == nullptr) return GN_INVALID_ARGUMENT;
-    int64_t full[9] = {};
+    int64_t full[13] = {};
     const gn_status st = gn_plan_rows_dtype(N, L, C, G, GN_DTYPE_BF16, full);
     if (st == GN_OK)
         for (int i = 0; i < 8; ++i) plan_out[i] = full[i];
@@ -621,6 +778,6 @@ const char *gn_status_string(gn_status s) {
     return "unknown gn_status";
 }
 
-int gn_version(void) { return 300; }
+int gn_version(void) { return 400; }
 
 }  // extern "C"

@@ -12,21 +12,25 @@
 // nearest even).
 //
 // Data layout: one sample is E = L*C values, channel fastest.  A "tile" is
-// kThreads*VEC consecutive elements of a sample (2048 for VEC = 8).  Lane
-// `tid` owns VEC slots of every tile at fixed offsets o(tid, j) (Pack::
-// slot_offset): 8*tid + j for 16-bit types, whose 8 values are one 16-byte
-// access; 4*tid + j and 1024 + 4*tid + (j - 4) for fp32, two 16-byte
-// accesses, so that each wave instruction still covers 1 KiB of contiguous
-// memory.  C is a power of two <= 2048, so every tile starts on a row
-// boundary and slot j always holds channel o(tid, j) mod C: the lane's
-// channel parameters and partial sums stay in registers for the whole chunk.
+// R whole rows, T = R*C elements, worked by the first A lanes of a 256-lane
+// workgroup; lane `tid` owns S = W*NV slots of every tile, NV accesses of W
+// consecutive elements (W = 8 for 16-bit types and W = 4 for fp32: one
+// 16-byte access; W = 1 when rows are not 16-byte multiples).  Access a of
+// lane tid covers elements (a*A + tid)*W .. +W-1, so each wave instruction
+// covers contiguous memory, and slot j sits at the fixed offset
+// o(tid, j) = ((j / W)*A + tid)*W + j % W.  Because a tile starts on a row
+// boundary, slot j always holds channel o(tid, j) mod C: the lane's channel
+// parameters and partial sums stay in registers for the whole chunk.  The
+// host picks (W, NV, R) with A*S = T; for power-of-two C <= 2048 in 16-bit
+// types that is W = 8, NV = 1, T = 2048, A = 256.
 //
 // Numerics: each thread accumulates x - p_g, where the pivot p_g is the first
 // element of its group in row 0 of the sample (x[n, 0, g*Cg]).  Shifting by a
 // value of the group keeps the fp32 sum of squares from cancelling when a
 // group's mean is large against its spread; in exact arithmetic the result is
 // unchanged (mean = p + S/M, var = Q/M - (S/M)^2).  Every reduction runs in an
-// order fixed by (N, L, C, G) alone, so results are bitwise reproducible.
+// order fixed by (N, L, C, G) and the element type alone, so results are
+// bitwise reproducible.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -97,7 +101,6 @@ __device__ __forceinline__ float silu_f32(float t) {
     return t * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// ---- a lane's VEC consecutive values ----------------------------------------
 // NT: the access carries the nontemporal hint (streaming cache policy), for
 // data the pass touches once.
 template <bool NT, class T>
@@ -115,105 +118,134 @@ __device__ __forceinline__ void st(T *p, T v) {
         *p = v;
 }
 
-template <class D, int VEC> struct Pack;
+// ---- one access of W consecutive elements -----------------------------------
+template <class D, int W> struct Vec;
 
-// Each Pack is loaded from / stored to a tile (its first element) by lane
-// `tid`; slot_offset(tid, j) is the element of the tile held in slot j.
-
-// 16-bit types: 8 values in one 16-byte access.
-template <class D> struct Pack16 {
+template <class D> struct Vec16x8 {  // 8 16-bit values, one 16-byte access
     u32x4 w;
-    __device__ __forceinline__ static int slot_offset(int tid, int j) { return tid * 8 + j; }
     __device__ __forceinline__ float get(int j) const {
         const uint32_t word = w[j >> 1];
         return (j & 1) ? D::hi(word) : D::lo(word);
     }
-    template <bool NT = false>
-    __device__ __forceinline__ static void store(uint16_t *tile, int tid, const float (&o)[8]) {
+    template <bool NT>
+    __device__ __forceinline__ void load(const uint16_t *p) {
+        w = ld<NT>(reinterpret_cast<const u32x4 *>(p));
+    }
+    template <bool NT>
+    __device__ __forceinline__ static void store(uint16_t *p, const float *o) {
         u32x4 v;
         v[0] = D::pack2(o[0], o[1]);
         v[1] = D::pack2(o[2], o[3]);
         v[2] = D::pack2(o[4], o[5]);
         v[3] = D::pack2(o[6], o[7]);
-        st<NT>(reinterpret_cast<u32x4 *>(tile + tid * 8), v);
+        st<NT>(reinterpret_cast<u32x4 *>(p), v);
     }
 };
-template <> struct Pack<Bf16, 8> : Pack16<Bf16> {
-    template <bool NT = false>
-    __device__ __forceinline__ static Pack load(const uint16_t *tile, int tid) {
-        Pack v;
-        v.w = ld<NT>(reinterpret_cast<const u32x4 *>(tile + tid * 8));
-        return v;
-    }
-};
-template <> struct Pack<Fp16, 8> : Pack16<Fp16> {
-    template <bool NT = false>
-    __device__ __forceinline__ static Pack load(const uint16_t *tile, int tid) {
-        Pack v;
-        v.w = ld<NT>(reinterpret_cast<const u32x4 *>(tile + tid * 8));
-        return v;
-    }
-};
+template <> struct Vec<Bf16, 8> : Vec16x8<Bf16> {};
+template <> struct Vec<Fp16, 8> : Vec16x8<Fp16> {};
 
-// fp32: slots 0-3 are elements 4*tid .. 4*tid+3 of the tile, slots 4-7 the
-// same four one half-tile (kThreads*4 elements) further on.
-template <> struct Pack<F32, 8> {
-    static constexpr int kHalf = kThreads * 4;
-    u32x4 a, b;
-    __device__ __forceinline__ static int slot_offset(int tid, int j) {
-        return (j < 4 ? 0 : kHalf - 4) + tid * 4 + j;
+template <> struct Vec<F32, 4> {  // 4 fp32 values, one 16-byte access
+    u32x4 w;
+    __device__ __forceinline__ float get(int j) const { return __uint_as_float(w[j]); }
+    template <bool NT>
+    __device__ __forceinline__ void load(const float *p) {
+        w = ld<NT>(reinterpret_cast<const u32x4 *>(p));
     }
-    template <bool NT = false>
-    __device__ __forceinline__ static Pack load(const float *tile, int tid) {
-        Pack v;
-        v.a = ld<NT>(reinterpret_cast<const u32x4 *>(tile + tid * 4));
-        v.b = ld<NT>(reinterpret_cast<const u32x4 *>(tile + kHalf + tid * 4));
-        return v;
-    }
-    __device__ __forceinline__ float get(int j) const {
-        return __uint_as_float(j < 4 ? a[j] : b[j - 4]);
-    }
-    template <bool NT = false>
-    __device__ __forceinline__ static void store(float *tile, int tid, const float (&o)[8]) {
-        u32x4 va, vb;
+    template <bool NT>
+    __device__ __forceinline__ static void store(float *p, const float *o) {
+        u32x4 v;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            va[j] = __float_as_uint(o[j]);
-            vb[j] = __float_as_uint(o[j + 4]);
-        }
-        st<NT>(reinterpret_cast<u32x4 *>(tile + tid * 4), va);
-        st<NT>(reinterpret_cast<u32x4 *>(tile + kHalf + tid * 4), vb);
+        for (int j = 0; j < 4; ++j) v[j] = __float_as_uint(o[j]);
+        st<NT>(reinterpret_cast<u32x4 *>(p), v);
     }
 };
 
-// One value per lane (C < 8 with L*C not a multiple of 8).
-template <class D> struct Pack<D, 1> {
+template <class D> struct Vec<D, 1> {  // one value
     typename D::storage b;
-    __device__ __forceinline__ static int slot_offset(int tid, int) { return tid; }
-    template <bool NT = false>
-    __device__ __forceinline__ static Pack load(const typename D::storage *tile, int tid) {
-        Pack v;
-        v.b = ld<NT>(tile + tid);
-        return v;
-    }
     __device__ __forceinline__ float get(int) const { return D::to_f32(b); }
-    template <bool NT = false>
-    __device__ __forceinline__ static void store(typename D::storage *tile, int tid,
-                                                 const float (&o)[1]) {
-        st<NT>(tile + tid, D::from_f32(o[0]));
+    template <bool NT>
+    __device__ __forceinline__ void load(const typename D::storage *p) { b = ld<NT>(p); }
+    template <bool NT>
+    __device__ __forceinline__ static void store(typename D::storage *p, const float *o) {
+        st<NT>(p, D::from_f32(o[0]));
+    }
+};
+
+// ---- a lane's S = W*NV slots of one tile -------------------------------------
+template <class D, int W, int NV> struct Lane {
+    static constexpr int kSlots = W * NV;
+    using T = typename D::storage;
+    Vec<D, W> v[NV];
+    __device__ __forceinline__ static int slot_offset(int A, int tid, int j) {
+        return ((j / W) * A + tid) * W + j % W;
+    }
+    template <bool NT>
+    __device__ __forceinline__ static Lane load(const T *tile, int A, int tid) {
+        Lane l;
+#pragma unroll
+        for (int a = 0; a < NV; ++a) l.v[a].template load<NT>(tile + (a * A + tid) * W);
+        return l;
+    }
+    __device__ __forceinline__ float get(int j) const { return v[j / W].get(j % W); }
+    template <bool NT>
+    __device__ __forceinline__ static void store(T *tile, int A, int tid, const float (&o)[kSlots]) {
+#pragma unroll
+        for (int a = 0; a < NV; ++a) Vec<D, W>::template store<NT>(tile + (a * A + tid) * W, o + a * W);
     }
 };
 
 // Arguments shared by the kernels; the host fills it from the plan.
 struct Geometry {
-    int64_t E;         // elements per sample, L*C
-    int64_t tiles;     // tiles per sample, ceil(E / tile)
-    int64_t full;      // tiles per sample lying entirely inside the sample
-    int64_t tpc;       // tiles per chunk (one workgroup's share)
-    int64_t K;         // chunks per sample
-    int C;             // channels (power of two)
-    int cg_shift;      // log2(C / G)
-    int G;             // groups
+    int64_t E;      // elements per sample, L*C
+    int64_t T;      // elements per tile: R whole rows, a multiple of C (T = A*S)
+    int64_t tiles;  // tiles per sample, ceil(E / T)
+    int64_t full;   // tiles per sample lying entirely inside the sample
+    int64_t tpc;    // tiles per chunk (one workgroup's share)
+    int64_t K;      // chunks per sample
+    int C;          // channels
+    int G;          // groups
+    int Cg;         // channels per group, C / G
+    int A;          // active lanes per tile (<= kThreads)
+    int cg_shift;   // log2(Cg) when C is a power of two, else 0
+    int64_t plain_tail;  // step 1: the last plain_tail tiles of each chunk use plain
+                         // loads, the tiles before them nontemporal ones
+};
+
+// The tile geometry as one kernel sees it.  All 256 lanes are busy exactly
+// when C is a power of two (A is the largest multiple of C / gcd(C, W*NV)
+// not above 256, and W*NV is a power of two).  POW2 kernels are compiled for
+// that case: the tile is the compile-time 256*S elements, and channel and
+// group indices are masks and shifts; the general kernels take T and A from
+// the plan and divide.
+template <bool POW2, int S> struct TileGeo {
+    int64_t T_;
+    int A_, C, Cg, cg_shift;
+    __device__ __forceinline__ explicit TileGeo(const Geometry &g)
+        : T_(g.T), A_(g.A), C(g.C), Cg(g.Cg), cg_shift(g.cg_shift) {}
+    __device__ __forceinline__ int64_t tile() const {
+        if constexpr (POW2)
+            return int64_t{kThreads} * S;
+        else
+            return T_;
+    }
+    __device__ __forceinline__ int lanes() const {
+        if constexpr (POW2)
+            return kThreads;
+        else
+            return A_;
+    }
+    __device__ __forceinline__ int channel(int o) const {  // o mod C
+        if constexpr (POW2)
+            return o & (C - 1);
+        else
+            return o % C;
+    }
+    __device__ __forceinline__ int group_of(int c) const {  // c / Cg
+        if constexpr (POW2)
+            return c >> cg_shift;
+        else
+            return c / Cg;
+    }
 };
 
 // Where the statistics go.
@@ -251,31 +283,35 @@ __device__ __forceinline__ void store_partial(float *p, float v) {
         *p = v;
 }
 
+// Fixed-order tree over the `count` entries red[base + i*step], i < count,
+// whatever count is: strides halve from the power of two below count, entry
+// i adds entry i + stride when that exists; entry 0 ends up holding the sum.
+// Every thread of the workgroup calls it (it contains barriers, and count is
+// uniform); `idx` is the calling thread's i, or -1 for a thread that holds no
+// entry.
+__device__ __forceinline__ void tree_sum(float *red_s, float *red_q, int base, int step, int idx,
+                                         int count) {
+    int p2 = 1;
+    while (p2 < count) p2 <<= 1;
+    for (int stride = p2 >> 1; stride > 0; stride >>= 1) {
+        if (idx >= 0 && idx < stride && idx + stride < count) {
+            red_s[base + idx * step] += red_s[base + (idx + stride) * step];
+            red_q[base + idx * step] += red_q[base + (idx + stride) * step];
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Pieces of steps 1-3, kept as functions so the order of every
 // floating-point operation is written down once.
 // ---------------------------------------------------------------------------
 
-// Pivots p_g of the lane's VEC channel slots; zeroed running sums.
-template <class D, int VEC>
-__device__ __forceinline__ void init_slots(const typename D::storage *xs, const Geometry &geo,
-                                           int tid, float (&piv)[VEC], float (&s)[VEC],
-                                           float (&q)[VEC]) {
-    const int cmask = geo.C - 1;
+template <class L>
+__device__ __forceinline__ void accumulate(const L &v, const float (&piv)[L::kSlots],
+                                           float (&s)[L::kSlots], float (&q)[L::kSlots]) {
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-        const int c = Pack<D, VEC>::slot_offset(tid, j) & cmask;
-        piv[j] = D::to_f32(xs[(c >> geo.cg_shift) << geo.cg_shift]);
-        s[j] = 0.0f;
-        q[j] = 0.0f;
-    }
-}
-
-template <class D, int VEC>
-__device__ __forceinline__ void accumulate(const Pack<D, VEC> &v, const float (&piv)[VEC],
-                                           float (&s)[VEC], float (&q)[VEC]) {
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) {
+    for (int j = 0; j < L::kSlots; ++j) {
         const float d = v.get(j) - piv[j];
         s[j] += d;
         q[j] = fmaf(d, d, q[j]);
@@ -305,59 +341,77 @@ __device__ __forceinline__ ChunkRange chunk_range(const Geometry &geo, int64_t k
 
 // Workgroup reduction of the lanes' slot sums to per-group partials of chunk
 // k, written to out.part_s / out.part_q at [(n*K + k)*G + g].  Slot j of
-// lane tid goes to red_*[i], i = slot_offset(tid, j), which holds channel
-// i mod C; the P = TILE/G entries of group g are i = r*C + g*Cg + u.
-template <class D, int VEC, bool COHERENT>
-__device__ __forceinline__ void write_group_partials(const float (&s)[VEC], const float (&q)[VEC],
-                                                     float *red_s, float *red_q,
-                                                     const Geometry &geo, int64_t n, int64_t k,
-                                                     const StatsOut &out, int tid) {
-    constexpr int TILE = kThreads * VEC;
+// active lane tid goes to red_*[i], i = o(tid, j), which holds channel
+// i mod C; the P = R*Cg entries of group g are i = r*C + g*Cg + u.
+// G <= kThreads: tg = kThreads / G threads per group, thread (g, part) sums
+// the entries e = part, part + tg, ... of its group, then a fixed tree over
+// the parts.  G > kThreads: each thread sums whole groups.
+template <class L, bool POW2, bool COHERENT>
+__device__ __forceinline__ void write_group_partials(const float (&s)[L::kSlots],
+                                                     const float (&q)[L::kSlots], float *red_s,
+                                                     float *red_q, const Geometry &geo,
+                                                     const TileGeo<POW2, L::kSlots> &tg_,
+                                                     int64_t n, int64_t k, const StatsOut &out,
+                                                     int tid) {
+    const int A = tg_.lanes();
+    if (tid < A) {
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-        const int i = Pack<D, VEC>::slot_offset(tid, j);
-        red_s[i] = s[j];
-        red_q[i] = q[j];
+        for (int j = 0; j < L::kSlots; ++j) {
+            const int i = L::slot_offset(A, tid, j);
+            red_s[i] = s[j];
+            red_q[i] = q[j];
+        }
     }
     __syncthreads();
-    const int G = geo.G;
-    const int cgm = (1 << geo.cg_shift) - 1;
+    const int G = geo.G, C = geo.C, Cg = geo.Cg;
+    const int P = static_cast<int>(tg_.tile() / G);  // entries of one group in the tile
     if (G <= kThreads) {
-        const int tg = kThreads / G;  // threads per group
-        const int g = tid / tg;
-        const int part = tid - g * tg;
+        // tg threads per group; thread (g, part) sums the contiguous entries
+        // e in [part*per, (part+1)*per) of its group, a fixed tree over the
+        // parts follows.
+        const int tg = kThreads / G;
+        const int per = (P + tg - 1) / tg;
+        const bool has = tid < tg * G;
+        const int g = has ? tid / tg : 0;
+        const int part = has ? tid - g * tg : 0;
         float as = 0.0f, aq = 0.0f;
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-            const int e = part * VEC + j;
-            const int i = (e >> geo.cg_shift) * geo.C + (g << geo.cg_shift) + (e & cgm);
-            as += red_s[i];
-            aq += red_q[i];
+        if (has) {
+            const int e0 = part * per;
+            const int e1 = e0 + per < P ? e0 + per : P;
+            int r = tg_.group_of(e0), u = e0 - r * Cg;  // entry e = row r, channel g*Cg + u
+            for (int e = e0; e < e1; ++e) {
+                const int i = r * C + g * Cg + u;
+                as += red_s[i];
+                aq += red_q[i];
+                if (++u == Cg) {
+                    u = 0;
+                    ++r;
+                }
+            }
         }
         __syncthreads();
         red_s[tid] = as;
         red_q[tid] = aq;
         __syncthreads();
-        for (int stride = tg >> 1; stride > 0; stride >>= 1) {
-            if (part < stride) {
-                red_s[tid] += red_s[tid + stride];
-                red_q[tid] += red_q[tid + stride];
-            }
-            __syncthreads();
-        }
-        if (part == 0) {
+        tree_sum(red_s, red_q, g * tg, 1, has ? part : -1, tg);
+        if (has && part == 0) {
             const int64_t o = (n * geo.K + k) * G + g;
             store_partial<COHERENT>(out.part_s + o, red_s[tid]);
             store_partial<COHERENT>(out.part_q + o, red_q[tid]);
         }
     } else {
-        const int P = TILE / G;  // < VEC slots per group
+        // Each thread sums whole groups, entries in increasing order.
         for (int g = tid; g < G; g += kThreads) {
             float as = 0.0f, aq = 0.0f;
+            int r = 0, u = 0;
             for (int e = 0; e < P; ++e) {
-                const int i = (e >> geo.cg_shift) * geo.C + (g << geo.cg_shift) + (e & cgm);
+                const int i = r * C + g * Cg + u;
                 as += red_s[i];
                 aq += red_q[i];
+                if (++u == Cg) {
+                    u = 0;
+                    ++r;
+                }
             }
             const int64_t o = (n * geo.K + k) * G + g;
             store_partial<COHERENT>(out.part_s + o, as);
@@ -383,11 +437,11 @@ __device__ __forceinline__ bool arrive_is_last(const StatsOut &out, int64_t n, i
 }
 
 // Step 2 for sample n, run by the last workgroup to arrive (G <= kThreads):
-// thread tid = g + G*j sums the chunks k = j, j + tpg, ... in increasing
-// order (coalesced along g; loads issued kBatch at a time so their round
-// trips overlap -- one round trip for K <= 16*tpg), a fixed tree over j
-// follows, and mean/rstd are written.  The arrival counter is reset to zero
-// for the next call.
+// tpg = kThreads / G threads per group; thread tid = g + G*j (j < tpg) sums
+// the chunks k = j, j + tpg, ... in increasing order (coalesced along g;
+// loads issued kBatch at a time so their round trips overlap), a fixed tree
+// over j follows, and mean/rstd are written.  The arrival counter is reset
+// to zero for the next call.
 template <class D>
 __device__ __forceinline__ void finalize_sample(const typename D::storage *xs,
                                                 const Geometry &geo, int64_t n,
@@ -395,43 +449,40 @@ __device__ __forceinline__ void finalize_sample(const typename D::storage *xs,
                                                 int tid) {
     const int G = geo.G;
     const int tpg = kThreads / G;
-    const int g = tid & (G - 1);
+    const bool has = tid < tpg * G;
+    const int g = tid % G;
     const int j = tid / G;
     constexpr int kBatch = 16;
-    const float *ps = out.part_s + n * geo.K * G + g;
-    const float *pq = out.part_q + n * geo.K * G + g;
     float as = 0.0f, aq = 0.0f;
-    int64_t kk = j;
-    for (; kk + (kBatch - 1) * tpg < geo.K; kk += kBatch * tpg) {
-        float vs[kBatch], vq[kBatch];
+    if (has) {
+        const float *ps = out.part_s + n * geo.K * G + g;
+        const float *pq = out.part_q + n * geo.K * G + g;
+        int64_t kk = j;
+        for (; kk + (kBatch - 1) * tpg < geo.K; kk += kBatch * tpg) {
+            float vs[kBatch], vq[kBatch];
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int64_t o = (kk + b * tpg) * G;
-            vs[b] = __hip_atomic_load(ps + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            vq[b] = __hip_atomic_load(pq + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+            for (int b = 0; b < kBatch; ++b) {
+                const int64_t o = (kk + b * tpg) * G;
+                vs[b] = __hip_atomic_load(ps + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                vq[b] = __hip_atomic_load(pq + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            as += vs[b];
-            aq += vq[b];
+            for (int b = 0; b < kBatch; ++b) {
+                as += vs[b];
+                aq += vq[b];
+            }
         }
-    }
-    for (; kk < geo.K; kk += tpg) {
-        as += __hip_atomic_load(ps + kk * G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        aq += __hip_atomic_load(pq + kk * G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (; kk < geo.K; kk += tpg) {
+            as += __hip_atomic_load(ps + kk * G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            aq += __hip_atomic_load(pq + kk * G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     red_s[tid] = as;
     red_q[tid] = aq;
     __syncthreads();
-    for (int stride = tpg >> 1; stride > 0; stride >>= 1) {
-        if (j < stride) {
-            red_s[tid] += red_s[tid + stride * G];
-            red_q[tid] += red_q[tid + stride * G];
-        }
-        __syncthreads();
-    }
-    if (j == 0) {
-        const float pivot = D::to_f32(xs[static_cast<int64_t>(g) << geo.cg_shift]);
+    tree_sum(red_s, red_q, g, G, has ? j : -1, tpg);
+    if (has && j == 0) {
+        const float pivot = D::to_f32(xs[static_cast<int64_t>(g) * geo.Cg]);
         group_moments(red_s[tid], red_q[tid], pivot, out.inv_m, out.eps, out.mean + n * G + g,
                       out.rstd + n * G + g);
     }
@@ -439,17 +490,18 @@ __device__ __forceinline__ void finalize_sample(const typename D::storage *xs,
         __hip_atomic_store(out.arrivals + n, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// scale = gamma*rstd, shift = beta - mean*scale for the lane's VEC channels.
-template <class D, int VEC>
+// scale = gamma*rstd, shift = beta - mean*scale for the lane's slots.
+template <class L, bool POW2>
 __device__ __forceinline__ void fold_affine(const float *mean, const float *rstd,
                                             const float *gamma, const float *beta,
-                                            const Geometry &geo, int64_t n, int tid,
-                                            float (&sc)[VEC], float (&sh)[VEC]) {
-    const int cmask = geo.C - 1;
+                                            const Geometry &geo,
+                                            const TileGeo<POW2, L::kSlots> &tg_, int64_t n,
+                                            int tid, float (&sc)[L::kSlots],
+                                            float (&sh)[L::kSlots]) {
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-        const int c = Pack<D, VEC>::slot_offset(tid, j) & cmask;
-        const int64_t gi = n * geo.G + (c >> geo.cg_shift);
+    for (int j = 0; j < L::kSlots; ++j) {
+        const int c = tg_.channel(L::slot_offset(tg_.lanes(), tid, j));
+        const int64_t gi = n * geo.G + tg_.group_of(c);
         const float ga = gamma ? gamma[c] : 1.0f;
         const float be = beta ? beta[c] : 0.0f;
         sc[j] = ga * rstd[gi];
@@ -467,17 +519,16 @@ __device__ __forceinline__ float transform1(float x, float sc, float sh) {
     }
 }
 
-template <class D, int VEC, bool SILU>
-__device__ __forceinline__ void transform(const Pack<D, VEC> &v, const float (&sc)[VEC],
-                                          const float (&sh)[VEC], float (&o)[VEC]) {
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) o[j] = transform1<SILU>(v.get(j), sc[j], sh[j]);
-}
-
 // ---------------------------------------------------------------------------
 // Step 1: partial statistics.  One workgroup per (sample n, chunk k); writes
 // the pivot-shifted sum and sum of squares of each group over its chunk to
 // part_s / part_q at [(n*K + k)*G + g].
+// Cache policy: step 3 reads x again, and whatever of x is still in the
+// 256 MB Infinity Cache when step 3 starts is served from there.  The last
+// geo.plain_tail tiles of every chunk -- together about one cache's worth,
+// the part read last -- use plain loads, which allocate in that cache; the
+// tiles before them use nontemporal loads, which would only be evicted again
+// before step 3 and cost bandwidth to allocate.
 // FUSED (requires G <= kThreads): the last workgroup of sample n to finish,
 // found with an agent-scope atomic counter, also performs step 2 for that
 // sample -- a fixed-order reduction over the K chunk partials of each group,
@@ -487,48 +538,70 @@ __device__ __forceinline__ void transform(const Pack<D, VEC> &v, const float (&s
 // is the arrival counted; the last workgroup reads the partials with
 // agent-scope (coherent) loads.
 // ---------------------------------------------------------------------------
-template <class D, int VEC, int UNROLL, bool NTL, bool FUSED>
+template <class D, int W, int NV, bool POW2, int UNROLL, bool FUSED>
 __global__ __launch_bounds__(kThreads) void gn_partial_stats(
     const typename D::storage *__restrict__ x, Geometry geo, StatsOut out) {
-    constexpr int TILE = kThreads * VEC;
-    __shared__ float red_s[TILE];
-    __shared__ float red_q[TILE];
+    using L = Lane<D, W, NV>;
+    constexpr int S = L::kSlots;
+    __shared__ float red_s[kThreads * S];
+    __shared__ float red_q[kThreads * S];
 
+    const TileGeo<POW2, S> tg(geo);
+    const int64_t T = tg.tile();
+    const int A = tg.lanes();
     const int tid = threadIdx.x;
     const int64_t wg = blockIdx.x;
     const int64_t n = wg / geo.K;
     const int64_t k = wg - n * geo.K;
     const typename D::storage *xs = x + n * geo.E;
+    const bool active = tid < A;
 
-    float piv[VEC], s[VEC], q[VEC];
-    init_slots<D, VEC>(xs, geo, tid, piv, s, q);
+    float piv[S], s[S], q[S];
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+        const int c = tg.channel(L::slot_offset(A, active ? tid : 0, j));
+        piv[j] = D::to_f32(xs[tg.group_of(c) * geo.Cg]);
+        s[j] = 0.0f;
+        q[j] = 0.0f;
+    }
 
     const ChunkRange cr = chunk_range(geo, k);
-    const typename D::storage *p = xs + cr.t_begin * TILE;  // current tile
-    int64_t tt = cr.t_begin;
-    for (; tt + UNROLL <= cr.t_full_end; tt += UNROLL) {
-        Pack<D, VEC> v[UNROLL];
+    if (active) {
+        const typename D::storage *p = xs + cr.t_begin * T;  // current tile
+        int64_t tt = cr.t_begin;
+        int64_t t_plain = cr.t_end - geo.plain_tail;  // first tile read with plain loads
+        if (t_plain > cr.t_full_end) t_plain = cr.t_full_end;
+        for (; tt + UNROLL <= t_plain; tt += UNROLL) {
+            L v[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-            v[u] = Pack<D, VEC>::template load<NTL>(p + u * TILE, tid);
+            for (int u = 0; u < UNROLL; ++u) v[u] = L::template load<true>(p + u * T, A, tid);
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) accumulate<D, VEC>(v[u], piv, s, q);
-        p += UNROLL * TILE;
-    }
-    for (; tt < cr.t_full_end; ++tt) {
-        accumulate<D, VEC>(Pack<D, VEC>::template load<NTL>(p, tid), piv, s, q);
-        p += TILE;
-    }
-    if (tt < cr.t_end) {
-        // The sample's last tile is partial: slot by slot, in bounds only.
+            for (int u = 0; u < UNROLL; ++u) accumulate<L>(v[u], piv, s, q);
+            p += UNROLL * T;
+        }
+        for (; tt + UNROLL <= cr.t_full_end; tt += UNROLL) {
+            L v[UNROLL];
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-            const int64_t off = tt * TILE + Pack<D, VEC>::slot_offset(tid, j);
-            if (off < geo.E) accumulate1(D::to_f32(xs[off]), piv[j], s[j], q[j]);
+            for (int u = 0; u < UNROLL; ++u) v[u] = L::template load<false>(p + u * T, A, tid);
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) accumulate<L>(v[u], piv, s, q);
+            p += UNROLL * T;
+        }
+        for (; tt < cr.t_full_end; ++tt) {
+            accumulate<L>(L::template load<false>(p, A, tid), piv, s, q);
+            p += T;
+        }
+        if (tt < cr.t_end) {
+            // The sample's last tile is partial: slot by slot, in bounds only.
+#pragma unroll
+            for (int j = 0; j < S; ++j) {
+                const int64_t off = tt * T + L::slot_offset(A, tid, j);
+                if (off < geo.E) accumulate1(D::to_f32(xs[off]), piv[j], s[j], q[j]);
+            }
         }
     }
 
-    write_group_partials<D, VEC, FUSED>(s, q, red_s, red_q, geo, n, k, out, tid);
+    write_group_partials<L, POW2, FUSED>(s, q, red_s, red_q, geo, tg, n, k, out, tid);
     if constexpr (FUSED) {
         if (arrive_is_last(out, n, geo.K, tid))
             finalize_sample<D>(xs, geo, n, out, red_s, red_q, tid);
@@ -566,7 +639,7 @@ __global__ __launch_bounds__(kThreads) void gn_finalize_stats(
         __syncthreads();
     }
     if (tid == 0) {
-        const float pivot = D::to_f32(x[n * geo.E + (static_cast<int64_t>(g) << geo.cg_shift)]);
+        const float pivot = D::to_f32(x[n * geo.E + static_cast<int64_t>(g) * geo.Cg]);
         group_moments(rs[0], rq[0], pivot, out.inv_m, out.eps, out.mean + ng, out.rstd + ng);
     }
 }
@@ -579,56 +652,63 @@ __global__ __launch_bounds__(kThreads) void gn_zero_u32(unsigned *p, int64_t n) 
 }
 
 // ---------------------------------------------------------------------------
-// Step 3: fused apply.  One workgroup per (n, chunk); each lane folds
-// gamma/beta and the group statistics of its VEC channels into scale/shift
+// Step 3: fused apply.  One workgroup per (n, chunk); each active lane folds
+// gamma/beta and the group statistics of its slots into scale/shift
 // registers once (scale = gamma*rstd, shift = beta - mean*scale), then
 // streams its chunk: y = SiLU(x*scale + shift), rounded once to D.
 // x and y may be the same buffer (each element is read, then written, by one
 // lane), so they carry no __restrict__.
 // ---------------------------------------------------------------------------
-template <class D, int VEC, int UNROLL, bool SILU, bool NTL, bool NTS>
+template <class D, int W, int NV, bool POW2, int UNROLL, bool SILU, bool NTL, bool NTS>
 __global__ __launch_bounds__(kThreads) void gn_apply(
-    const typename D::storage *x, typename D::storage *y, Geometry geo, int reverse,
+    const typename D::storage *x, typename D::storage *y, Geometry geo,
     const float *__restrict__ mean, const float *__restrict__ rstd,
     const float *__restrict__ gamma, const float *__restrict__ beta) {
-    constexpr int TILE = kThreads * VEC;
+    using L = Lane<D, W, NV>;
+    constexpr int S = L::kSlots;
+    const TileGeo<POW2, S> tg(geo);
+    const int64_t T = tg.tile();
+    const int A = tg.lanes();
     const int tid = threadIdx.x;
-    const int64_t wg = reverse ? static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x
-                               : static_cast<int64_t>(blockIdx.x);
+    if (tid >= A) return;
+    const int64_t wg = blockIdx.x;
     const int64_t n = wg / geo.K;
     const int64_t k = wg - n * geo.K;
 
-    float sc[VEC], sh[VEC];
-    fold_affine<D, VEC>(mean, rstd, gamma, beta, geo, n, tid, sc, sh);
+    float sc[S], sh[S];
+    fold_affine<L, POW2>(mean, rstd, gamma, beta, geo, tg, n, tid, sc, sh);
 
     const int64_t base = n * geo.E;
     const ChunkRange cr = chunk_range(geo, k);
-    int64_t off = base + cr.t_begin * TILE;  // current tile
+    int64_t off = base + cr.t_begin * T;  // current tile
     int64_t tt = cr.t_begin;
     for (; tt + UNROLL <= cr.t_full_end; tt += UNROLL) {
-        Pack<D, VEC> v[UNROLL];
+        L v[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
-            v[u] = Pack<D, VEC>::template load<NTL>(x + off + u * TILE, tid);
+            v[u] = L::template load<NTL>(x + off + u * T, A, tid);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            float o[VEC];
-            transform<D, VEC, SILU>(v[u], sc, sh, o);
-            Pack<D, VEC>::template store<NTS>(y + off + u * TILE, tid, o);
+            float o[S];
+#pragma unroll
+            for (int j = 0; j < S; ++j) o[j] = transform1<SILU>(v[u].get(j), sc[j], sh[j]);
+            L::template store<NTS>(y + off + u * T, A, tid, o);
         }
-        off += UNROLL * TILE;
+        off += UNROLL * T;
     }
     for (; tt < cr.t_full_end; ++tt) {
-        float o[VEC];
-        transform<D, VEC, SILU>(Pack<D, VEC>::template load<NTL>(x + off, tid), sc, sh, o);
-        Pack<D, VEC>::template store<NTS>(y + off, tid, o);
-        off += TILE;
+        const L v = L::template load<NTL>(x + off, A, tid);
+        float o[S];
+#pragma unroll
+        for (int j = 0; j < S; ++j) o[j] = transform1<SILU>(v.get(j), sc[j], sh[j]);
+        L::template store<NTS>(y + off, A, tid, o);
+        off += T;
     }
     if (tt < cr.t_end) {
         // The sample's last tile is partial: slot by slot, in bounds only.
 #pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-            const int64_t rel = tt * TILE + Pack<D, VEC>::slot_offset(tid, j);
+        for (int j = 0; j < S; ++j) {
+            const int64_t rel = tt * T + L::slot_offset(A, tid, j);
             if (rel < geo.E)
                 y[base + rel] = D::from_f32(transform1<SILU>(D::to_f32(x[base + rel]), sc[j], sh[j]));
         }

@@ -10,8 +10,12 @@
  * with gamma/beta folded into per-(batch, channel) scale/shift, and a fused
  * elementwise apply with an optional SiLU.  The same section gives the
  * public pair group_norm_silu_4d / group_norm_silu_rows and the inputs for
- * which they decline ("callers must fall back"): C not a power of two,
- * C > 2048, a layout that is not channels-last.
+ * which that kernel declines, leaving the caller to fall back: C not a power
+ * of two, C > 2048, a layout that is not channels-last.  This library keeps
+ * the decline for layouts that are not channels-last but widens the channel
+ * counts it takes (see "Supported set" below), and also takes 5-D NDHWC
+ * activations through the rows form (L = D*H*W): the HunyuanVAE-style 5-D
+ * call sites, which the same section leaves on the older general kernel.
  *
  * For each sample n and group g (channels g*Cg .. g*Cg+Cg-1, Cg = C/G),
  * over the M = L*Cg elements of the group:
@@ -46,17 +50,26 @@
  *   caller's next synchronisation (gn_profile_rows excepted, which
  *   synchronises).
  * Aliasing: y == x (in place) is allowed.  Any other overlap is undefined.
- * Determinism: the reduction order is a pure function of (N, L, C, G), so
- *   the same input gives bitwise-identical output on every call.
+ * Determinism: the reduction order is a pure function of (N, L, C, G) and
+ *   the dtype, so the same input gives bitwise-identical output on every
+ *   call.
+ * Supported set: C <= GN_MAX_CHANNELS for which a tile layout exists.  Let
+ *   Wd = 8 for 16-bit types and 4 for fp32, W = Wd when L*C % Wd == 0 and 1
+ *   otherwise; a layout exists when C / gcd(C, W*NV) <= 256 for some NV in
+ *   {1, 2, 4} (NV in {2, 4} for fp32 with W = 4).  In particular every
+ *   C <= 256; every multiple of 8 up to 2048 (16-bit) or of 4 up to 1024
+ *   (fp32) with L*C % Wd == 0; and multiples of 32 up to 8192 (16-bit) or of
+ *   16 up to 4096 (fp32) with L*C % Wd == 0.  gn_plan_rows_dtype reports
+ *   whether a shape is in the set without touching the GPU.
  * Errors (checked in this order; nothing is enqueued unless GN_OK):
  *   GN_INVALID_ARGUMENT -- input no GroupNorm accepts: x or y NULL; N, L, H
  *     or W negative; C <= 0; G <= 0; C % G != 0; eps negative, infinite or
  *     NaN; apply_silu not 0 or 1; a dtype outside gn_dtype; the tensor's byte
  *     size overflowing int64.
  *   GN_UNSUPPORTED -- a valid GroupNorm this library declines, so the caller
- *     falls back: C not a power of two; C > 2048; (strided form) a layout
- *     that is not dense channels-last; x or y not 16-byte aligned; a tensor
- *     pointer that is not device memory of the stream's device.
+ *     falls back: C outside the supported set below; (strided forms) a
+ *     layout that is not dense channels-last; x or y not 16-byte aligned; a
+ *     tensor pointer that is not device memory of the stream's device.
  *   GN_OK is returned without touching the GPU when N*L == 0.
  *   GN_DEVICE_ERROR -- a HIP call failed (scratch allocation, launch).
  */
@@ -84,8 +97,9 @@ typedef enum gn_dtype {
     GN_DTYPE_F32 = 2
 } gn_dtype;
 
-/* Largest channel count the library accepts (Modifications section 1). */
-#define GN_MAX_CHANNELS 2048
+/* Largest channel count the library accepts.  The pages' kernel stops at
+ * 2048 (Modifications section 1); the tile layout here reaches 8192. */
+#define GN_MAX_CHANNELS 8192
 
 /* group_norm_silu_4d: NHWC 4-D activation of logical shape (N, C, H, W)
  * stored channels-last, i.e. the rows form with L = H*W (the "free permute
@@ -110,6 +124,15 @@ gn_status gn_silu_nhwc_strided(const void *x, const int64_t x_strides[4],
                                void *y, const int64_t y_strides[4],
                                int64_t N, int64_t H, int64_t W, int64_t C, int64_t G,
                                float eps, int apply_silu, void *stream);
+
+/* NDHWC 5-D activation of logical shape (N, C, D, H, W) stored channels-last
+ * (torch.channels_last_3d): the rows form with L = D*H*W.  The same
+ * normalisation applies, each group's statistics taken over all D*H*W
+ * positions (Modifications section 1 names 5-D call sites such as the
+ * HunyuanVAE decoder). */
+gn_status gn_silu_ndhwc(const void *x, const float *gamma, const float *beta, void *y,
+                        int64_t N, int64_t D, int64_t H, int64_t W, int64_t C, int64_t G,
+                        float eps, int apply_silu, void *stream);
 
 /* Steps one and two alone: writes the fp32 per-(n, g) mean and rstd, index
  * n*G + g, to the device buffers mean_out / rstd_out (N*G floats each) --
@@ -142,8 +165,9 @@ gn_status gn_profile_rows(const void *x, const float *gamma, const float *beta, 
 
 /* Launch plan of the rows path for a shape, for inspection and tests; no
  * HIP call.  Writes 8 values to plan_out:
- *   [0] VEC     bf16 values per lane access (8, or 1 when L*C % 8 != 0)
- *   [1] tiles   tiles of 256*VEC elements per sample (last one may be partial)
+ *   [0] slots   values each active lane holds per tile (W*NV)
+ *   [1] tiles   tiles per sample (last one may be partial); a tile is whole
+ *               rows, T elements (plan_out[11] of gn_plan_rows_dtype)
  *   [2] full    tiles per sample lying wholly inside the sample
  *   [3] tpc1    tiles per workgroup, statistics pass
  *   [4] K1      workgroups per sample, statistics pass (N*K1 launched)
@@ -156,8 +180,18 @@ gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_
 
 /* The same calls for x and y of element type `dtype` (a gn_dtype value);
  * the bf16 entry points above are these with dtype = GN_DTYPE_BF16.
- * gn_plan_rows_dtype writes a ninth value, plan_out[8]: 1 when step 3 reads
- * x with nontemporal loads (tensors larger than the 256 MB Infinity Cache). */
+ * gn_plan_rows_dtype writes 13 values, the 8 above and
+ *   [8]  1 when step 3 reads x with nontemporal loads (tensors larger than
+ *        the 256 MB Infinity Cache), else 0
+ *   [9]  W, elements per lane access (16 bytes' worth, or 1)
+ *   [10] A, lanes of the 256-lane workgroup that hold slots
+ *   [11] T, elements per tile (= A*W*NV, a multiple of C)
+ *   [12] the last tiles of each statistics chunk read with plain loads (the
+ *        rest nontemporal): all of the chunk when the tensor fits the
+ *        Infinity Cache, else the chunk's share of one cache's worth
+ * gn_silu_ndhwc_strided_dtype is the strided form for 5-D: strides of the
+ * logical (N, C, D, H, W) dimensions, dense channels-last only
+ * ((D*H*W*C, 1, H*W*C, W*C, C), extent-1 dimensions free). */
 gn_status gn_silu_nhwc_dtype(const void *x, const float *gamma, const float *beta, void *y,
                              int64_t N, int64_t H, int64_t W, int64_t C, int64_t G,
                              float eps, int apply_silu, int dtype, void *stream);
@@ -169,6 +203,15 @@ gn_status gn_silu_nhwc_strided_dtype(const void *x, const int64_t x_strides[4],
                                      void *y, const int64_t y_strides[4],
                                      int64_t N, int64_t H, int64_t W, int64_t C, int64_t G,
                                      float eps, int apply_silu, int dtype, void *stream);
+gn_status gn_silu_ndhwc_dtype(const void *x, const float *gamma, const float *beta, void *y,
+                              int64_t N, int64_t D, int64_t H, int64_t W, int64_t C, int64_t G,
+                              float eps, int apply_silu, int dtype, void *stream);
+gn_status gn_silu_ndhwc_strided_dtype(const void *x, const int64_t x_strides[5],
+                                      const float *gamma, const float *beta,
+                                      void *y, const int64_t y_strides[5],
+                                      int64_t N, int64_t D, int64_t H, int64_t W, int64_t C,
+                                      int64_t G, float eps, int apply_silu, int dtype,
+                                      void *stream);
 gn_status gn_stats_rows_dtype(const void *x, int64_t N, int64_t L, int64_t C, int64_t G,
                               float eps, int dtype, float *mean_out, float *rstd_out,
                               void *stream);
@@ -181,7 +224,7 @@ gn_status gn_profile_rows_dtype(const void *x, const float *gamma, const float *
                                 float eps, int apply_silu, int dtype, void *stream,
                                 int iters, float *kernel_ms, int *n_kernels);
 gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dtype,
-                             int64_t plan_out[9]);
+                             int64_t plan_out[13]);
 
 /* Name of kernel slot i of gn_profile_rows, or NULL. */
 const char *gn_kernel_name(int i);

@@ -3,10 +3,12 @@
 * libgnsilu.so loads and exports every function include/gnsilu.h declares.
 * The status matrix of the argument checks, which run before any HIP call:
   GN_INVALID_ARGUMENT for input no GroupNorm accepts, GN_UNSUPPORTED for the
-  inputs the pages' kernel declines (C not a power of two, C > 2048, not
-  channels-last -- "FLUX.2 VAE decoder fast path behind quality=high",
-  Modifications section 1), GN_OK for empty input.  The pointers passed here
-  are never dereferenced: every case returns before the library touches HIP.
+  inputs the library declines (a channel count with no tile layout, C above
+  GN_MAX_CHANNELS, a layout that is not channels-last -- the decline contract
+  of "FLUX.2 VAE decoder fast path behind quality=high", Modifications
+  section 1, over a wider supported set), GN_OK for empty input.  The
+  pointers passed here are never dereferenced: every case returns before the
+  library touches HIP.
 * The Python binding's None contract for inputs it declines on the host.
 """
 import ctypes
@@ -27,6 +29,10 @@ from groupnorm_silu_normalization_amd import GnStatus  # noqa: E402
 X = ctypes.c_void_p(0x10000)
 Y = ctypes.c_void_p(0x20000)
 I64x4 = ctypes.c_int64 * 4
+I64x5 = ctypes.c_int64 * 5
+# Channel counts used below that the library declines: 257 (prime), 2056
+# (8*257) and 3000 (8*375) have no tile layout; 8200 and 16384 exceed
+# GN_MAX_CHANNELS.
 
 
 def declared_functions():
@@ -38,7 +44,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ("gn_silu_nhwc", "gn_silu_rows", "gn_silu_nhwc_strided", "gn_stats_rows",
-                 "gn_apply_rows", "gn_profile_rows", "gn_status_string"):
+                 "gn_apply_rows", "gn_profile_rows", "gn_status_string", "gn_silu_ndhwc",
+                 "gn_silu_ndhwc_strided_dtype"):
         assert must in names
 
 
@@ -76,8 +83,8 @@ def test_invalid_arguments(kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(C=96, G=32), dict(C=4096, G=32), dict(C=24, G=8), dict(C=3000, G=1),
-    dict(x=ctypes.c_void_p(0x10002)), dict(y=ctypes.c_void_p(0x20008)),
+    dict(C=257, G=1), dict(C=2056, G=8), dict(C=3000, G=1), dict(C=16384, G=32),
+    dict(C=8200, G=8), dict(x=ctypes.c_void_p(0x10002)), dict(y=ctypes.c_void_p(0x20008)),
 ])
 def test_unsupported_inputs(kw):
     assert rows(**kw) == GnStatus.UNSUPPORTED
@@ -99,8 +106,10 @@ def test_invalid_dtype(dtype):
 
 def test_dtype_entry_points_share_the_checks():
     for dt in (0, 1, 2):
-        assert gn.gn_silu_rows_dtype(X, None, None, Y, 1, 16, 96, 32, 1e-6, 1, dt,
+        assert gn.gn_silu_rows_dtype(X, None, None, Y, 1, 16, 3000, 8, 1e-6, 1, dt,
                                      None) == GnStatus.UNSUPPORTED
+        assert gn.gn_silu_ndhwc_dtype(X, None, None, Y, 1, 2, 2, 4, 3000, 8, 1e-6, 1, dt,
+                                      None) == GnStatus.UNSUPPORTED
         assert gn.gn_silu_rows_dtype(X, None, None, Y, 0, 16, 64, 32, 1e-6, 1, dt,
                                      None) == GnStatus.OK
         assert gn.gn_silu_nhwc_dtype(None, None, None, Y, 1, 4, 4, 64, 32, 1e-6, 1, dt,
@@ -118,8 +127,36 @@ def test_nhwc_checks():
     f = gn.gn_silu_nhwc
     assert f(X, None, None, Y, 1, -1, 4, 64, 32, 1e-6, 1, None) == GnStatus.INVALID_ARGUMENT
     assert f(X, None, None, Y, 1, 4, -1, 64, 32, 1e-6, 1, None) == GnStatus.INVALID_ARGUMENT
-    assert f(X, None, None, Y, 1, 4, 4, 96, 32, 1e-6, 1, None) == GnStatus.UNSUPPORTED
+    assert f(X, None, None, Y, 1, 4, 4, 2056, 8, 1e-6, 1, None) == GnStatus.UNSUPPORTED
     assert f(X, None, None, Y, 1, 2 ** 40, 2 ** 40, 8, 1, 1e-6, 1, None) == GnStatus.INVALID_ARGUMENT
+
+
+def test_ndhwc_checks():
+    f = gn.gn_silu_ndhwc
+    for D, H, W in ((-1, 4, 4), (4, -1, 4), (4, 4, -1), (2 ** 30, 2 ** 30, 2 ** 30)):
+        assert f(X, None, None, Y, 1, D, H, W, 64, 32, 1e-6, 1, None) == GnStatus.INVALID_ARGUMENT
+    assert f(X, None, None, Y, 1, 2, 4, 4, 3000, 8, 1e-6, 1, None) == GnStatus.UNSUPPORTED
+    assert f(X, None, None, Y, 1, 0, 4, 4, 64, 32, 1e-6, 1, None) == GnStatus.OK
+    assert f(X, None, None, Y, 2, 3, 0, 4, 64, 32, 1e-6, 1, None) == GnStatus.OK
+
+
+def test_ndhwc_strided_rejects_ncdhw_and_other_layouts():
+    N, C, D, H, W = 2, 64, 3, 5, 7
+    cl = I64x5(D * H * W * C, 1, H * W * C, W * C, C)
+    ncdhw = I64x5(C * D * H * W, D * H * W, H * W, W, 1)
+    swapped = I64x5(D * H * W * C, 1, W * C, D * W * C, C)  # H and D exchanged
+    f = gn.gn_silu_ndhwc_strided_dtype
+    for xs, ys in ((ncdhw, cl), (cl, ncdhw), (swapped, cl)):
+        assert f(X, xs, None, None, Y, ys, N, D, H, W, C, 32, 1e-6, 1, 0,
+                 None) == GnStatus.UNSUPPORTED
+    assert f(X, ncdhw, None, None, Y, cl, N, D, H, W, C, 7, 1e-6, 1, 0,
+             None) == GnStatus.INVALID_ARGUMENT
+    assert f(X, None, None, None, Y, cl, N, D, H, W, C, 32, 1e-6, 1, 0,
+             None) == GnStatus.INVALID_ARGUMENT
+    assert f(X, cl, None, None, Y, cl, 0, D, H, W, C, 32, 1e-6, 1, 0, None) == GnStatus.OK
+    # extent-1 dimensions may carry any stride
+    one = I64x5(999, 1, 5, 7 * C, C)
+    assert f(X, one, None, None, Y, one, 1, 1, 0, W, C, 32, 1e-6, 1, 0, None) == GnStatus.OK
 
 
 def test_strided_rejects_nchw_and_other_layouts():
@@ -141,7 +178,7 @@ def test_strided_rejects_nchw_and_other_layouts():
 def test_stats_apply_profile_argument_checks():
     assert gn.gn_stats_rows(X, 1, 16, 64, 32, 1e-6, None, Y, None) == GnStatus.INVALID_ARGUMENT
     assert gn.gn_stats_rows(X, 1, 16, 64, 32, 1e-6, Y, None, None) == GnStatus.INVALID_ARGUMENT
-    assert gn.gn_stats_rows(X, 1, 16, 96, 32, 1e-6, Y, Y, None) == GnStatus.UNSUPPORTED
+    assert gn.gn_stats_rows(X, 1, 16, 2056, 8, 1e-6, Y, Y, None) == GnStatus.UNSUPPORTED
     assert gn.gn_apply_rows(X, None, Y, None, None, Y, 1, 16, 64, 32, 1, None) == GnStatus.INVALID_ARGUMENT
     ms = (ctypes.c_float * 4)()
     nk = ctypes.c_int(0)
@@ -165,8 +202,8 @@ def test_binding_declines_cpu_tensors():
 
 def test_header_limits_match_binding():
     text = open(HEADER).read()
-    assert "#define GN_MAX_CHANNELS 2048" in text
-    assert gn.MAX_CHANNELS == 2048 and math.log2(gn.MAX_CHANNELS).is_integer()
+    assert "#define GN_MAX_CHANNELS 8192" in text
+    assert gn.MAX_CHANNELS == 8192 and math.log2(gn.MAX_CHANNELS).is_integer()
 
 
 def test_one_hip_runtime_whatever_the_import_order():

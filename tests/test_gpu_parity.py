@@ -337,10 +337,10 @@ def test_unsupported_inputs_return_none(gn, dev):
         xc = x.to(memory_format=torch.channels_last)
         assert gn.group_norm_silu_4d(xc, 32, g, g) is not None
         assert gn.group_norm_silu_4d(xc.half(), 32, g.half(), g.half()) is None    # fp16
-        x96 = torch.randn(1, 96, 4, 4, device=dev).to(torch.bfloat16).to(memory_format=torch.channels_last)
-        assert gn.group_norm_silu_4d(x96, 32) is None                              # C not pow2
-        x4k = torch.randn(1, 4096, 2, 2, device=dev).to(torch.bfloat16).to(memory_format=torch.channels_last)
-        assert gn.group_norm_silu_4d(x4k, 32) is None                              # C > 2048
+        x3k = torch.randn(1, 3000, 4, 4, device=dev).to(torch.bfloat16).to(memory_format=torch.channels_last)
+        assert gn.group_norm_silu_4d(x3k, 8) is None                               # no tile layout
+        x16k = torch.randn(1, 16384, 2, 2, device=dev).to(torch.bfloat16).to(memory_format=torch.channels_last)
+        assert gn.group_norm_silu_4d(x16k, 32) is None                             # C > 8192
         assert gn.group_norm_silu_4d(xc, 32, g.cpu(), g.cpu()) is None             # host affine
         with pytest.raises(ValueError):
             gn.group_norm_silu_4d(xc, 7)                                           # C % G != 0

@@ -1,47 +1,95 @@
 """Host-side proof that every kernel access stays in bounds, on the CPU.
 
-For each shape the library's own launch plan (gn_plan_rows) is read back, and
-the kernels' index arithmetic is replayed here: the element range each
-workgroup of the statistics and apply passes touches, the partial tile at the
-end of a sample, the pivot reads, the partial-sum slots, the LDS slots of the
-workgroup reduction and the grid sizes.  It also checks that the chunks tile
-each sample exactly once, so no element is skipped or counted twice.
+For each shape the library's own launch plan (gn_plan_rows_dtype) is read
+back, and the kernels' index arithmetic is replayed here: the lane->element
+slot map of a tile, the element range each workgroup of the statistics and
+apply passes touches, the partial tile at the end of a sample, the pivot
+reads, the partial-sum slots, the LDS slots of the workgroup reduction and
+the grid sizes.  It also checks that the chunks tile each sample exactly
+once, so no element is skipped or counted twice, and that every slot of a
+lane holds one fixed channel.
 """
+from math import gcd
+
 import numpy as np
 import pytest
 
 gn = pytest.importorskip("groupnorm_silu_normalization_amd")
 
 THREADS = 256
+BF16, F16, F32 = 0, 1, 2
+WIDE = {BF16: 8, F16: 8, F32: 4}   # elements per 16-byte access
+
 SHAPES = [
     # the five decoder shapes (N, L, C, G)
     (1, 64 * 64, 128, 32), (1, 128 * 128, 512, 32), (1, 512 * 512, 512, 32),
     (1, 1024 * 1024, 256, 32), (1, 1024 * 1024, 128, 32),
-    # rows case, ragged tails, small and extreme channel counts
+    # rows case, ragged tails, small and extreme power-of-two channel counts
     (1, 16384, 512, 32), (3, 70001, 128, 32), (2, 5000, 64, 8), (2, 1, 8, 8),
     (1, 1, 1, 1), (1, 3, 2, 1), (2, 7, 4, 2), (4, 5, 2, 2), (1, 257, 2048, 2048),
     (1, 257, 2048, 1), (2, 129, 1024, 512), (2, 33, 512, 256), (7, 3, 16, 4),
     (64, 100, 32, 32), (1, 2 ** 22, 512, 32), (2 ** 12, 1, 8, 1), (1, 9999, 1, 1),
     (2, 131072, 64, 8), (5, 6, 4, 4),
 ]
+# channel counts that are not powers of two, or above 2048 (UNet widths and
+# their concatenations, odd and prime counts, ragged row counts)
+WIDE_SHAPES = [
+    (2, 4096, 320, 32), (1, 1024, 640, 32), (2, 257, 960, 32), (1, 4097, 1280, 32),
+    (1, 999, 1920, 32), (2, 513, 2560, 32), (1, 129, 4096, 32), (1, 65, 8192, 32),
+    (3, 77, 96, 32), (2, 33, 24, 8), (1, 5, 3, 1), (2, 7, 3, 3), (1, 11, 5, 5),
+    (4, 9, 300, 30), (1, 1, 300, 300), (2, 17, 250, 10), (1, 1000, 6144, 32),
+    (1, 100, 1536, 48), (2, 31, 768, 24), (1, 1, 2560, 2560), (2, 3, 1000, 1000),
+]
+DTYPES = (BF16, F16, F32)
 
 
-def log2(v):
-    return int(v).bit_length() - 1
+def lane_offsets(p):
+    """o[tid, j] for the active lanes."""
+    A, W, S = p["A"], p["W"], p["slots"]
+    tid = np.arange(A)[:, None]
+    j = np.arange(S)[None, :]
+    return ((j // W) * A + tid) * W + j % W
 
 
-def chunks(plan_tiles, full, tpc, K):
+def check_layout(p, E, C, dtype):
+    A, W, S, T = p["A"], p["W"], p["slots"], p["T"]
+    NV = S // W
+    assert W in (1, WIDE[dtype]) and S % W == 0 and NV in (1, 2, 4)
+    assert W == 1 or (dtype == F32 and NV >= 2) or dtype != F32
+    assert E % W == 0, "a 16-byte access must not straddle two samples"
+    assert 0 < A <= THREADS and T == A * S
+    assert T % C == 0, "a tile must be whole rows so each slot keeps one channel"
+    # the kernels take masks and shifts for channel and group indices when all
+    # 256 lanes are busy: that must happen exactly for power-of-two C
+    assert (A == THREADS) == (C & (C - 1) == 0)
+    o = lane_offsets(p)
+    # the slot map is a permutation of the tile
+    assert np.array_equal(np.sort(o.ravel()), np.arange(T))
+    # each access of W slots is contiguous and W-aligned; one wave instruction
+    # (64 lanes, same access) covers 64*W contiguous elements
+    for a in range(NV):
+        blk = o[:, a * W:(a + 1) * W]
+        assert np.all(blk[:, 0] % W == 0)
+        assert np.all(np.diff(blk, axis=1) == 1)
+        for w0 in range(0, A, 64):
+            starts = blk[w0:w0 + 64, 0]
+            assert np.array_equal(starts, starts[0] + W * np.arange(starts.size))
+    return o
+
+
+def chunks(tiles, full, tpc, K):
     out = []
     for k in range(K):
         t_begin = k * tpc
-        t_end = min(t_begin + tpc, plan_tiles)
-        out.append((t_begin, t_end, min(t_end, full)))
+        t_end = min(t_begin + tpc, tiles)
+        out.append((t_begin, t_end, max(min(t_end, full), t_begin)))
     return out
 
 
-def check_streaming_pass(N, E, vec, tiles, full, tpc, K):
-    TILE = THREADS * vec
+def check_streaming_pass(N, E, p, o, tpc, K):
+    T, tiles, full = p["T"], p["tiles"], p["full"]
     assert N * K < 2 ** 24, "grid too large"
+    assert tiles == -(-E // T) and full == E // T
     cs = chunks(tiles, full, tpc, K)
     # the chunks cover tiles [0, tiles) once, in order
     assert cs[0][0] == 0 and cs[-1][1] == tiles
@@ -49,80 +97,169 @@ def check_streaming_pass(N, E, vec, tiles, full, tpc, K):
         assert a[1] == b[0] and a[0] < a[1]
     for t_begin, t_end, t_full_end in cs:
         assert t_begin < tiles
-        if t_full_end > t_begin:
-            assert t_full_end * TILE <= E            # whole tiles inside the sample
-        if t_end > max(t_full_end, t_begin):         # the partial last tile
-            tt = max(t_full_end, t_begin)
-            offs = tt * TILE + np.arange(THREADS) * vec
+        assert t_full_end * T <= E                   # whole tiles inside the sample
+        if t_end > t_full_end:                       # the partial last tile
+            assert t_end == t_full_end + 1 == tiles
+            offs = t_full_end * T + o.ravel()
             live = offs[offs < E]
-            assert live.size == 0 or live.max() + vec - 1 < E
-            covered = live.size * vec
-            assert tt * TILE + covered == E          # every tail element read once
-    assert full * TILE <= E <= tiles * TILE and tiles == -(-E // TILE)
+            # the in-bounds slots are exactly the tail elements, once each
+            assert np.array_equal(np.sort(live), np.arange(t_full_end * T, E))
 
 
-def lds_slots(C, G, vec):
-    TILE = THREADS * vec
-    cg_shift = log2(C // G)
-    cgm = (1 << cg_shift) - 1
-    seen = np.zeros(TILE, np.int64)
+def check_lds(p, C, G):
+    """The workgroup reduction of step 1: slot (tid, j) goes to LDS entry
+    o(tid, j) < T <= 256*slots; group g's P = T/G entries are read back."""
+    T, S = p["T"], p["slots"]
+    Cg = C // G
+    P = T // G
+    assert T <= THREADS * S
+    seen = np.zeros(T, np.int64)
     if G <= THREADS:
         tg = THREADS // G
-        for tid in range(THREADS):
-            g, part = divmod(tid, tg)
-            for j in range(vec):
-                e = part * vec + j
-                i = (e >> cg_shift) * C + (g << cg_shift) + (e & cgm)
-                assert 0 <= i < TILE and (i % C) // (C // G) == g
-                seen[i] += 1
+        per = -(-P // tg)
+        for g in range(G):
+            for part in range(tg):
+                for e in range(part * per, min(P, (part + 1) * per)):
+                    i = (e // Cg) * C + g * Cg + e % Cg
+                    assert 0 <= i < T and (i % C) // Cg == g
+                    seen[i] += 1
+        # the tree over the tg parts of group g stays inside [g*tg, g*tg + tg)
+        assert G * tg <= THREADS
     else:
-        P = TILE // G
         for g in range(G):
             for e in range(P):
-                i = (e >> cg_shift) * C + (g << cg_shift) + (e & cgm)
-                assert 0 <= i < TILE and (i % C) // (C // G) == g
+                i = (e // Cg) * C + g * Cg + e % Cg
+                assert 0 <= i < T and (i % C) // Cg == g
                 seen[i] += 1
     assert np.all(seen == 1), "each LDS slot is summed into exactly one group once"
 
 
-@pytest.mark.parametrize("N,L,C,G", SHAPES)
-def test_plan_keeps_every_access_in_bounds(N, L, C, G):
-    p = gn.plan_rows(N, L, C, G)
-    assert p is not None
+def check_plan(N, L, C, G, dtype):
+    p = gn.plan_rows(N, L, C, G, dtype)
+    assert p is not None, (N, L, C, G, dtype)
     E = L * C
-    vec = p["vec"]
-    assert vec in (1, 8) and E % vec == 0
-    assert THREADS * vec % C == 0, "a tile must start on a row boundary"
-    check_streaming_pass(N, E, vec, p["tiles"], p["full"], p["tpc1"], p["K1"])
-    check_streaming_pass(N, E, vec, p["tiles"], p["full"], p["tpc2"], p["K2"])
+    o = check_layout(p, E, C, dtype)
+    check_streaming_pass(N, E, p, o, p["tpc1"], p["K1"])
+    check_streaming_pass(N, E, p, o, p["tpc2"], p["K2"])
+    # each lane slot keeps one channel across tiles: o mod C, and its group
+    ch = o % C
+    assert np.all((ch // (C // G)) < G)
     # pivot reads x[n, 0, g*Cg] lie in row 0 of the sample
     assert (G - 1) * (C // G) < E
     # partial-sum slots (n*K1 + k)*G + g, written by step 1 and read by the
-    # finalize (fused tail: thread g + G*j reads k = j, j + 256/G, ...)
+    # finalize (fused tail: thread g + G*j, j < 256//G, reads k = j, j + 256//G, ...)
     nparts = N * G * p["K1"]
     assert ((N - 1) * p["K1"] + p["K1"] - 1) * G + G - 1 < nparts
     if G <= THREADS:
         tpg = THREADS // G
-        for j in range(tpg):
-            ks = range(j, p["K1"], tpg)
-            assert all(((N - 1) * p["K1"] + k) * G + (G - 1) < nparts for k in ks)
-        # every chunk of every group is read exactly once by the tail
+        assert tpg * G <= THREADS
         seen = sorted(k for j in range(tpg) for k in range(j, p["K1"], tpg))
         assert seen == list(range(p["K1"]))
     counters = -(-4 * N // 256) * 256   # one arrival counter per sample
     assert p["scratch_bytes"] == counters + 4 * (2 * nparts + 2 * N * G)
     assert N * G < 2 ** 24
-    if C * 8 <= 65536:
-        lds_slots(C, G, vec)
-    # the reverse walk of the apply pass is a bijection on its workgroups
-    nb = N * p["K2"]
-    assert sorted(nb - 1 - b for b in range(min(nb, 5000))) == list(range(nb - min(nb, 5000), nb))
+    check_lds(p, C, G)
+    # step 1's plain-load tail: the whole chunk when the tensor fits the
+    # 256 MiB cache, else the chunk's share of one cache's worth (at least 1)
+    nbytes = N * E * (4 if dtype == F32 else 2)
+    cache = 256 << 20
+    want = p["tpc1"] if nbytes <= cache else max(1, -(-p["tpc1"] * cache // nbytes))
+    assert p["stats_plain_tail"] == want
+    return p
+
+
+@pytest.mark.parametrize("N,L,C,G", SHAPES)
+def test_plan_keeps_every_access_in_bounds(N, L, C, G):
+    for dtype in DTYPES:
+        check_plan(N, L, C, G, dtype)
+
+
+@pytest.mark.parametrize("N,L,C,G", WIDE_SHAPES)
+def test_wide_plan_keeps_every_access_in_bounds(N, L, C, G):
+    for dtype in DTYPES:
+        if supported(L * C, C, dtype):
+            check_plan(N, L, C, G, dtype)
+        else:
+            assert gn.plan_rows(N, L, C, G, dtype) is None
+
+
+def supported(E, C, dtype):
+    """The supported set as the header states it."""
+    if C > 8192:
+        return False
+    Wd = WIDE[dtype]
+    W = Wd if E % Wd == 0 else 1
+    nvs = (2, 4) if W == 4 else (1, 2, 4)
+    return any(C // gcd(C, W * nv) <= THREADS for nv in nvs)
+
+
+def test_power_of_two_layout_is_the_2048_element_tile():
+    # 16-bit types: one 16-byte access per lane; fp32: two; every lane busy
+    for C in (8, 16, 64, 128, 256, 512, 1024, 2048):
+        for dtype in DTYPES:
+            if dtype == F32 and C > 2048:
+                continue
+            p = gn.plan_rows(1, 4096, C, 8 if C >= 8 else 1, dtype)
+            assert (p["A"], p["T"], p["slots"]) == (256, 2048, 8)
+            assert p["W"] == WIDE[dtype]
+
+
+def expected_layout(E, C, dtype):
+    """(W, NV, A) by the plan's rule: the smallest NV with at least half of
+    the 256 lanes busy, else the NV with the most busy lanes."""
+    Wd = WIDE[dtype]
+    W = Wd if E % Wd == 0 else 1
+    best = None
+    for nv in ((2, 4) if W == 4 else (1, 2, 4)):
+        m = C // gcd(C, W * nv)
+        if m > THREADS:
+            continue
+        A = (THREADS // m) * m
+        if best is None or A > best[2]:
+            best = (W, nv, A)
+        if 2 * best[2] >= THREADS:
+            break
+    return best
+
+
+def test_wide_layouts_follow_the_rule():
+    for C in (320, 640, 960, 1280, 1920, 2560, 4096, 8192, 96, 24, 3, 300, 1000, 6144):
+        for L in (1, 8, 4096):
+            for dtype in DTYPES:
+                want = expected_layout(L * C, C, dtype)
+                p = gn.plan_rows(1, L, C, 1, dtype)
+                if want is None:
+                    assert p is None
+                    continue
+                assert (p["W"], p["slots"] // p["W"], p["A"]) == want, (C, L, dtype, p)
+    # UNet channel counts in bf16: one 16-byte access per lane where half the
+    # lanes suffice (1280: 160 lanes), two for 2560 (160 lanes)
+    assert [gn.plan_rows(1, 4096, C, 32)["slots"] for C in (320, 1280, 2560, 8192)] == \
+        [8, 8, 16, 32]
+    assert [gn.plan_rows(1, 4096, C, 32)["A"] for C in (320, 1280, 2560, 8192)] == \
+        [240, 160, 160, 256]
+
+
+def test_supported_set_matches_the_header_rule():
+    Ls = (1, 3, 8, 16)
+    for C in list(range(1, 300)) + [320, 640, 960, 1000, 1028, 1280, 1920, 2056, 2560, 3000,
+                                    4096, 4100, 5120, 6144, 8192, 8200, 16384]:
+        for L in Ls:
+            for dtype in DTYPES:
+                got = gn.plan_rows(1, L, C, 1, dtype) is not None
+                assert got == supported(L * C, C, dtype), (C, L, dtype)
+    # every C <= 256, and multiples of 8 up to 2048 in 16-bit types
+    assert all(gn.plan_rows(1, 3, C, 1) is not None for C in range(1, 257))
+    assert all(gn.plan_rows(1, 8, C, 1) is not None for C in range(8, 2049, 8))
+    assert all(gn.plan_rows(1, 8, C, 1, F32) is not None for C in range(4, 1025, 4))
 
 
 def test_plan_is_shape_only_and_bounded():
     # statistics workgroups stay near the target, so partials stay small
-    for N, L, C, G in SHAPES:
+    for N, L, C, G in SHAPES + WIDE_SHAPES:
         p = gn.plan_rows(N, L, C, G)
+        if p is None:
+            continue
         total = N * p["tiles"]
         assert p["tpc1"] <= 1024                       # each lane's sequential run
         assert N * p["K1"] <= max(256, -(-total // 1024)) + N
@@ -134,34 +271,11 @@ def test_plan_is_shape_only_and_bounded():
 
 
 def test_plan_declines_like_the_entry_points():
-    assert gn.plan_rows(1, 16, 96, 32) is None        # C not a power of two
-    assert gn.plan_rows(1, 16, 4096, 32) is None      # C > 2048
+    assert gn.plan_rows(1, 16, 257, 1) is None        # prime above 256: no layout
+    assert gn.plan_rows(1, 16, 3000, 1) is None       # 8*375: no layout
+    assert gn.plan_rows(1, 16, 16384, 32) is None     # C > GN_MAX_CHANNELS
+    assert gn.plan_rows(1, 16, 96, 32) is not None    # widened: not a power of two
+    assert gn.plan_rows(1, 16, 4096, 32) is not None  # widened: C > 2048
     with pytest.raises(ValueError):
         gn.plan_rows(1, 16, 64, 3)                    # C % G != 0
     assert gn.plan_rows(0, 16, 64, 32)["K1"] == 0     # empty: nothing launched
-
-
-def test_slot_maps_are_permutations_of_a_tile():
-    """Lane tid's slot j holds element o(tid, j) of each 2048-element tile:
-    8*tid + j for 16-bit types, 4*tid + j and 1024 + 4*tid + (j - 4) for
-    fp32.  Each map must cover the tile exactly once, and each 16-byte access
-    (4 fp32 / 8 16-bit slots) must be contiguous and 16-byte aligned."""
-    def o16(tid, j):
-        return 8 * tid + j
-
-    def o32(tid, j):
-        return (0 if j < 4 else 1024 - 4) + 4 * tid + j
-
-    for o, per_access in ((o16, 8), (o32, 4)):
-        offs = [o(t, j) for t in range(THREADS) for j in range(8)]
-        assert sorted(offs) == list(range(THREADS * 8))
-        for t in range(THREADS):
-            for a in range(0, 8, per_access):
-                run = [o(t, j) for j in range(a, a + per_access)]
-                assert run == list(range(run[0], run[0] + per_access))
-                assert run[0] % per_access == 0
-        # one wave instruction (64 lanes, same access index) covers 1 KiB contiguously
-        for a in range(0, 8, per_access):
-            for w in range(THREADS // 64):
-                starts = sorted(o(t, a) for t in range(64 * w, 64 * w + 64))
-                assert starts == list(range(starts[0], starts[0] + 64 * per_access, per_access))
