@@ -20,6 +20,12 @@ Parity status of each function (what pins it, see ``tests/test_oracle_pins.py``)
     and fp32 inputs, torch's fp64 ``group_norm`` on the same values.
   * ``widen`` -- pinned exhaustively: all 65536 bf16 and all 65536 fp16 bit
     patterns against numpy's own conversions.
+  * ``conv3x3`` -- pinned: torch's fp64 CPU ``conv2d`` (padding 1), exact
+    rational brute force on tiny inputs, identity / shift / linearity
+    invariants that fix the tap orientation, the padding and the weight
+    layout.
+  * ``gn_silu_conv3x3`` -- composition of the pinned ``gn_silu``,
+    ``conv3x3`` and ``group_stats`` (fp64 input), nothing else.
 """
 import ctypes
 import os
@@ -35,14 +41,16 @@ def _ptr(a):
 
 
 # Input dtypes: uint16 arrays are bf16 bit patterns, float16 and float32
-# arrays are IEEE binary16 / binary32 values.
-_DTYPE_CODE = {np.dtype(np.uint16): 0, np.dtype(np.float16): 1, np.dtype(np.float32): 2}
+# arrays are IEEE binary16 / binary32 values (float64 for the statistics of
+# an fp64 tensor).
+_DTYPE_CODE = {np.dtype(np.uint16): 0, np.dtype(np.float16): 1, np.dtype(np.float32): 2,
+               np.dtype(np.float64): 3}
 
 
 def _as_input(x):
     x = np.ascontiguousarray(x)
     if x.dtype not in _DTYPE_CODE:
-        raise TypeError("oracle input must be bf16 bits (uint16), float16 or float32")
+        raise TypeError("oracle input must be bf16 bits (uint16), float16, float32 or float64")
     return x, _DTYPE_CODE[x.dtype]
 
 
@@ -65,6 +73,8 @@ class Oracle:
         lib.gno_max_threads.restype = ctypes.c_int
         lib.gno_set_threads.argtypes = [ctypes.c_int]
         lib.gno_set_threads.restype = None
+        lib.gno_conv3x3_nhwc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp]
+        lib.gno_conv3x3_nhwc.restype = ci
         self.lib = lib
         self.path = lib_path
 
@@ -73,6 +83,53 @@ class Oracle:
 
     def set_threads(self, n: int) -> None:
         self.lib.gno_set_threads(int(n))
+
+    def conv3x3(self, inp, wt, bias, N, H, W, Ci, Co, res=None, return_abs=False):
+        """3x3 convolution, zero padding 1, stride 1, NHWC, in fp64.
+
+        inp: [N, H, W, Ci] values (any input dtype; widened exactly);
+        wt: [Co, 3, 3, Ci] values; bias: [Co] or None; res: [N, H, W, Co] or
+        None (added to the output).  Returns out [N, H, W, Co] float64, and
+        with ``return_abs`` also the per-output sum of absolute terms.
+        """
+        def f64(a, n, name):
+            if a is None:
+                return None
+            a = self.widen(a).reshape(-1) if np.asarray(a).dtype != np.float64 else \
+                np.ascontiguousarray(a, np.float64).reshape(-1)
+            if a.size != n:
+                raise ValueError("%s has %d elements, expected %d" % (name, a.size, n))
+            return a
+        i64 = f64(inp, N * H * W * Ci, "inp")
+        w64 = f64(wt, Co * 9 * Ci, "wt")
+        b64 = f64(bias, Co, "bias")
+        r64 = f64(res, N * H * W * Co, "res")
+        out = np.empty(max(N * H * W * Co, 1), np.float64)
+        mag = np.empty_like(out) if return_abs else None
+        rc = self.lib.gno_conv3x3_nhwc(_ptr(i64), _ptr(w64), _ptr(b64), _ptr(r64), N, H, W, Ci,
+                                       Co, _ptr(out), _ptr(mag))
+        if rc != 0:
+            raise ValueError("oracle rejected conv shape")
+        out = out[: N * H * W * Co].reshape(N, H, W, Co)
+        if return_abs:
+            return out, mag[: N * H * W * Co].reshape(N, H, W, Co)
+        return out
+
+    def gn_silu_conv3x3(self, x, gamma, beta, G, eps, apply_silu, wt, bias, N, H, W, Ci, Co,
+                        res=None, G2=None):
+        """conv3x3(GroupNorm(+SiLU)(x)) + bias (+ res), in fp64, plus the
+        per-output magnitude sums and, when G2 is given, the fp64 mean and
+        biased variance of each of the output's G2 groups per sample.
+
+        Returns (z [N,H,W,Co], mag [N,H,W,Co], mean2 [N,G2] or None,
+        var2 [N,G2] or None).
+        """
+        y = self.gn_silu(x, gamma, beta, N, H * W, Ci, G, eps, apply_silu)
+        z, mag = self.conv3x3(y, wt, bias, N, H, W, Ci, Co, res=res, return_abs=True)
+        mean2 = var2 = None
+        if G2 is not None:
+            mean2, var2 = self.group_stats(z, N, H * W, Co, G2)
+        return z, mag, mean2, var2
 
     def widen(self, x):
         """The oracle's own fp64 widening of each input element."""
@@ -153,6 +210,16 @@ def set_threads(n: int) -> None:
 
 def widen(x):
     return _get().widen(x)
+
+
+def conv3x3(inp, wt, bias, N, H, W, Ci, Co, res=None, return_abs=False):
+    return _get().conv3x3(inp, wt, bias, N, H, W, Ci, Co, res=res, return_abs=return_abs)
+
+
+def gn_silu_conv3x3(x, gamma, beta, G, eps, apply_silu, wt, bias, N, H, W, Ci, Co, res=None,
+                    G2=None):
+    return _get().gn_silu_conv3x3(x, gamma, beta, G, eps, apply_silu, wt, bias, N, H, W, Ci, Co,
+                                  res=res, G2=G2)
 
 
 def group_stats(x_bits, N, L, C, G):

@@ -37,6 +37,18 @@
  * fused passes, no reassociation.  OpenMP only splits independent groups
  * (statistics) and independent rows (elementwise output) across threads; the
  * order of every sum is the plain sequential one.
+ *
+ * The neighbouring convolution (for the fused GroupNorm -> SiLU -> conv of
+ * the decoder's ResnetBlock2D, named in the same page's Modifications
+ * section 2: "ResnetBlock2D norm1/norm2 + SiLU chains", and its
+ * "Conv2d(3x3, p1)"): a 3x3 cross-correlation with zero padding 1 and
+ * stride 1 over NHWC activations, the plain definition
+ *
+ *   out[n,h,w,co] = bias[co] + res[n,h,w,co]
+ *                 + sum_{kh,kw in 0..2} sum_{ci} wt[co,kh,kw,ci] * in[n,h+kh-1,w+kw-1,ci]
+ *
+ * with in = 0 outside the image, weights stored [Co][3][3][Ci] (the
+ * channels-last layout of a [Co, Ci, 3, 3] weight), bias and res optional.
  */
 #include <math.h>
 #include <stdint.h>
@@ -70,12 +82,13 @@ static double f16_bits_to_double(uint16_t bits) {
     return sign ? -v : v;
 }
 
-enum { GNO_BF16 = 0, GNO_F16 = 1, GNO_F32 = 2 };
+enum { GNO_BF16 = 0, GNO_F16 = 1, GNO_F32 = 2, GNO_F64 = 3 };
 
 /* Element i of x, widened to fp64. */
 static double load(const void *x, int dtype, int64_t i) {
     if (dtype == GNO_BF16) return bf16_bits_to_double(((const uint16_t *)x)[i]);
     if (dtype == GNO_F16) return f16_bits_to_double(((const uint16_t *)x)[i]);
+    if (dtype == GNO_F64) return ((const double *)x)[i];
     return (double)((const float *)x)[i];
 }
 
@@ -112,7 +125,7 @@ void gno_set_threads(int n) {
  * shape or dtype. */
 int gno_group_stats_dt(const void *x, int dtype, int64_t N, int64_t L, int64_t C, int64_t G,
                        double *mean_out, double *var_out) {
-    if (check_shape(N, L, C, G) || dtype < GNO_BF16 || dtype > GNO_F32) return -1;
+    if (check_shape(N, L, C, G) || dtype < GNO_BF16 || dtype > GNO_F64) return -1;
     const int64_t Cg = C / G;
     const int64_t M = L * Cg;
     int64_t ng;
@@ -195,4 +208,50 @@ int gno_gn_silu(const uint16_t *x, const float *gamma, const float *beta, int64_
                 double *out64, float *out32, double *mean_out, double *var_out) {
     return gno_gn_silu_dt(x, GNO_BF16, gamma, beta, N, L, C, G, eps, apply_silu, out64, out32,
                           mean_out, var_out);
+}
+
+/* The 3x3 convolution above, in fp64.  in: [N][H][W][Ci]; wt: [Co][3][3][Ci];
+ * bias: [Co] or NULL; res: [N][H][W][Co] or NULL; out: [N][H][W][Co].
+ * abs_out (may be NULL) receives, per output, the same sum taken over the
+ * absolute values of every term (|bias| + |res| + sum |wt * in|): the scale
+ * against which rounding errors of the operands are bounded.  Every output
+ * sums its terms in the order bias, res, then kh, kw, ci ascending.
+ * Returns 0, or -1 on a bad shape. */
+int gno_conv3x3_nhwc(const double *in, const double *wt, const double *bias, const double *res,
+                     int64_t N, int64_t H, int64_t W, int64_t Ci, int64_t Co, double *out,
+                     double *abs_out) {
+    if (N < 0 || H < 0 || W < 0 || Ci <= 0 || Co <= 0) return -1;
+    int64_t pix;
+#pragma omp parallel for schedule(static)
+    for (pix = 0; pix < N * H * W; ++pix) {
+        const int64_t n = pix / (H * W);
+        const int64_t h = (pix / W) % H;
+        const int64_t w = pix % W;
+        for (int64_t co = 0; co < Co; ++co) {
+            double acc = bias ? bias[co] : 0.0;
+            double mag = bias ? fabs(bias[co]) : 0.0;
+            if (res) {
+                acc += res[pix * Co + co];
+                mag += fabs(res[pix * Co + co]);
+            }
+            for (int64_t kh = 0; kh < 3; ++kh) {
+                const int64_t ih = h + kh - 1;
+                if (ih < 0 || ih >= H) continue;
+                for (int64_t kw = 0; kw < 3; ++kw) {
+                    const int64_t iw = w + kw - 1;
+                    if (iw < 0 || iw >= W) continue;
+                    const double *ip = in + ((n * H + ih) * W + iw) * Ci;
+                    const double *wp = wt + ((co * 3 + kh) * 3 + kw) * Ci;
+                    for (int64_t ci = 0; ci < Ci; ++ci) {
+                        const double term = wp[ci] * ip[ci];
+                        acc += term;
+                        mag += fabs(term);
+                    }
+                }
+            }
+            out[pix * Co + co] = acc;
+            if (abs_out) abs_out[pix * Co + co] = mag;
+        }
+    }
+    return 0;
 }

@@ -11,6 +11,7 @@ import subprocess
 import pytest
 
 import oracle as oracle_pkg
+import test_oracle_conv_pins as cpins
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle_pkg.__file__), "gn_oracle.c")
@@ -40,6 +41,17 @@ MUTANTS = {
     "fp16 implicit bit dropped": ("ldexp((double)(f + 1024), e - 25)",
                                   "ldexp((double)f, e - 25)"),
     "sample index ignored": ("const int64_t n = row / L;", "const int64_t n = 0;"),
+    "conv: true convolution (taps flipped)": ("const int64_t ih = h + kh - 1;",
+                                              "const int64_t ih = h - kh + 1;"),
+    "conv: column offset off by one": ("const int64_t iw = w + kw - 1;",
+                                       "const int64_t iw = w + kw - 2;"),
+    "conv: weight taps transposed": ("wt + ((co * 3 + kh) * 3 + kw) * Ci",
+                                     "wt + ((co * 3 + kw) * 3 + kh) * Ci"),
+    "conv: bias dropped": ("double acc = bias ? bias[co] : 0.0;", "double acc = 0.0;"),
+    "conv: residual dropped": ("acc += res[pix * Co + co];", "acc += 0.0;"),
+    "conv: magnitude of negative terms lost": ("mag += fabs(term);", "mag += term;"),
+    "fp64 statistics read as fp32": ("if (dtype == GNO_F64) return ((const double *)x)[i];",
+                                     "if (dtype == GNO_F64) return ((const float *)x)[i];"),
 }
 
 
@@ -54,6 +66,14 @@ def battery():
         ("constant_group", pins.test_constant_group_gives_beta),
         ("widen_f16", pins.test_widen_f16_exhaustive),
         ("torch_gn_f16", lambda o: pins.test_torch_group_norm_other_dtypes(o, "float16")),
+        ("conv_torch", lambda o: cpins.test_conv_against_torch_fp64(o, 1, 9, 4, 8, 16, True,
+                                                                    True)),
+        ("conv_exact", cpins.test_conv_exact_integer_bruteforce),
+        ("conv_shift", lambda o: cpins.test_conv_off_centre_tap_is_a_shift_with_zero_fill(
+            o, 0, 2)),
+        ("conv_layout", cpins.test_conv_weight_layout_maps_input_to_output_channels),
+        ("conv_abs", cpins.test_conv_magnitude_sum_is_conv_of_absolute_values),
+        ("stats_f64", cpins.test_group_stats_of_fp64_input),
     ]
 
 
