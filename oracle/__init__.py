@@ -24,6 +24,8 @@ Parity status of each function (what pins it, see ``tests/test_oracle_pins.py``)
     rational brute force on tiny inputs, identity / shift / linearity
     invariants that fix the tap orientation, the padding and the weight
     layout.
+  * ``conv3x3_at`` -- the same per-pixel sum as ``conv3x3`` at selected
+    pixels; pinned equal to ``conv3x3`` there.
   * ``gn_silu_conv3x3`` -- composition of the pinned ``gn_silu``,
     ``conv3x3`` and ``group_stats`` (fp64 input), nothing else.
 """
@@ -75,6 +77,9 @@ class Oracle:
         lib.gno_set_threads.restype = None
         lib.gno_conv3x3_nhwc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp]
         lib.gno_conv3x3_nhwc.restype = ci
+        lib.gno_conv3x3_nhwc_at.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, i64,
+                                            vp, vp]
+        lib.gno_conv3x3_nhwc_at.restype = ci
         self.lib = lib
         self.path = lib_path
 
@@ -114,6 +119,31 @@ class Oracle:
         if return_abs:
             return out, mag[: N * H * W * Co].reshape(N, H, W, Co)
         return out
+
+    def conv3x3_at(self, inp, wt, bias, N, H, W, Ci, Co, pix, res=None):
+        """The convolution at selected output pixels: pix holds linear pixel
+        indices (n*H + h)*W + w; returns (out, mag), each [len(pix), Co]."""
+        def f64(a, n):
+            if a is None:
+                return None
+            a = np.ascontiguousarray(a)
+            a = a.reshape(-1).astype(np.float64) if a.dtype == np.float64 else \
+                self.widen(a).reshape(-1)
+            if a.size != n:
+                raise ValueError("size mismatch")
+            return a
+        i64 = f64(inp, N * H * W * Ci)
+        w64 = f64(wt, Co * 9 * Ci)
+        b64 = f64(bias, Co)
+        r64 = f64(res, N * H * W * Co)
+        pix = np.ascontiguousarray(pix, np.int64)
+        out = np.empty((max(pix.size, 1), Co), np.float64)
+        mag = np.empty_like(out)
+        rc = self.lib.gno_conv3x3_nhwc_at(_ptr(i64), _ptr(w64), _ptr(b64), _ptr(r64), N, H, W,
+                                          Ci, Co, _ptr(pix), pix.size, _ptr(out), _ptr(mag))
+        if rc != 0:
+            raise ValueError("oracle rejected conv shape or pixel list")
+        return out[: pix.size], mag[: pix.size]
 
     def gn_silu_conv3x3(self, x, gamma, beta, G, eps, apply_silu, wt, bias, N, H, W, Ci, Co,
                         res=None, G2=None):
@@ -214,6 +244,10 @@ def widen(x):
 
 def conv3x3(inp, wt, bias, N, H, W, Ci, Co, res=None, return_abs=False):
     return _get().conv3x3(inp, wt, bias, N, H, W, Ci, Co, res=res, return_abs=return_abs)
+
+
+def conv3x3_at(inp, wt, bias, N, H, W, Ci, Co, pix, res=None):
+    return _get().conv3x3_at(inp, wt, bias, N, H, W, Ci, Co, pix, res=res)
 
 
 def gn_silu_conv3x3(x, gamma, beta, G, eps, apply_silu, wt, bias, N, H, W, Ci, Co, res=None,

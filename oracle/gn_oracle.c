@@ -210,6 +210,40 @@ int gno_gn_silu(const uint16_t *x, const float *gamma, const float *beta, int64_
                           mean_out, var_out);
 }
 
+/* One output pixel (n, h, w) of the convolution below, all Co channels. */
+static void conv_pixel(const double *in, const double *wt, const double *bias, const double *res,
+                       int64_t H, int64_t W, int64_t Ci, int64_t Co, int64_t pix, double *out,
+                       double *abs_out) {
+    const int64_t n = pix / (H * W);
+    const int64_t h = (pix / W) % H;
+    const int64_t w = pix % W;
+    for (int64_t co = 0; co < Co; ++co) {
+        double acc = bias ? bias[co] : 0.0;
+        double mag = bias ? fabs(bias[co]) : 0.0;
+        if (res) {
+            acc += res[pix * Co + co];
+            mag += fabs(res[pix * Co + co]);
+        }
+        for (int64_t kh = 0; kh < 3; ++kh) {
+            const int64_t ih = h + kh - 1;
+            if (ih < 0 || ih >= H) continue;
+            for (int64_t kw = 0; kw < 3; ++kw) {
+                const int64_t iw = w + kw - 1;
+                if (iw < 0 || iw >= W) continue;
+                const double *ip = in + ((n * H + ih) * W + iw) * Ci;
+                const double *wp = wt + ((co * 3 + kh) * 3 + kw) * Ci;
+                for (int64_t ci = 0; ci < Ci; ++ci) {
+                    const double term = wp[ci] * ip[ci];
+                    acc += term;
+                    mag += fabs(term);
+                }
+            }
+        }
+        out[co] = acc;
+        if (abs_out) abs_out[co] = mag;
+    }
+}
+
 /* The 3x3 convolution above, in fp64.  in: [N][H][W][Ci]; wt: [Co][3][3][Ci];
  * bias: [Co] or NULL; res: [N][H][W][Co] or NULL; out: [N][H][W][Co].
  * abs_out (may be NULL) receives, per output, the same sum taken over the
@@ -223,35 +257,26 @@ int gno_conv3x3_nhwc(const double *in, const double *wt, const double *bias, con
     if (N < 0 || H < 0 || W < 0 || Ci <= 0 || Co <= 0) return -1;
     int64_t pix;
 #pragma omp parallel for schedule(static)
-    for (pix = 0; pix < N * H * W; ++pix) {
-        const int64_t n = pix / (H * W);
-        const int64_t h = (pix / W) % H;
-        const int64_t w = pix % W;
-        for (int64_t co = 0; co < Co; ++co) {
-            double acc = bias ? bias[co] : 0.0;
-            double mag = bias ? fabs(bias[co]) : 0.0;
-            if (res) {
-                acc += res[pix * Co + co];
-                mag += fabs(res[pix * Co + co]);
-            }
-            for (int64_t kh = 0; kh < 3; ++kh) {
-                const int64_t ih = h + kh - 1;
-                if (ih < 0 || ih >= H) continue;
-                for (int64_t kw = 0; kw < 3; ++kw) {
-                    const int64_t iw = w + kw - 1;
-                    if (iw < 0 || iw >= W) continue;
-                    const double *ip = in + ((n * H + ih) * W + iw) * Ci;
-                    const double *wp = wt + ((co * 3 + kh) * 3 + kw) * Ci;
-                    for (int64_t ci = 0; ci < Ci; ++ci) {
-                        const double term = wp[ci] * ip[ci];
-                        acc += term;
-                        mag += fabs(term);
-                    }
-                }
-            }
-            out[pix * Co + co] = acc;
-            if (abs_out) abs_out[pix * Co + co] = mag;
-        }
-    }
+    for (pix = 0; pix < N * H * W; ++pix)
+        conv_pixel(in, wt, bias, res, H, W, Ci, Co, pix, out + pix * Co,
+                   abs_out ? abs_out + pix * Co : NULL);
+    return 0;
+}
+
+/* The same convolution at npix selected output pixels only (linear pixel
+ * indices (n*H + h)*W + w in pix[]): out and abs_out are [npix][Co].  For
+ * checking sampled outputs of tensors too large for the full sum. */
+int gno_conv3x3_nhwc_at(const double *in, const double *wt, const double *bias,
+                        const double *res, int64_t N, int64_t H, int64_t W, int64_t Ci,
+                        int64_t Co, const int64_t *pix, int64_t npix, double *out,
+                        double *abs_out) {
+    if (N < 0 || H < 0 || W < 0 || Ci <= 0 || Co <= 0 || npix < 0) return -1;
+    for (int64_t i = 0; i < npix; ++i)
+        if (pix[i] < 0 || pix[i] >= N * H * W) return -1;
+    int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < npix; ++i)
+        conv_pixel(in, wt, bias, res, H, W, Ci, Co, pix[i], out + i * Co,
+                   abs_out ? abs_out + i * Co : NULL);
     return 0;
 }

@@ -157,3 +157,17 @@ def test_composition_is_conv_of_gn_silu(oracle):
     assert np.array_equal(z, oracle.conv3x3(y, w, b, N, H, W, Ci, Co))
     m, v = oracle.group_stats(z.reshape(-1).copy(), N, H * W, Co, G2)
     assert np.array_equal(m2, m) and np.array_equal(v2, v)
+
+
+def test_conv_at_selected_pixels_equals_full_conv(oracle):
+    rng = np.random.default_rng(8)
+    N, H, W, Ci, Co = 2, 5, 6, 7, 3
+    x = rng.standard_normal((N, H, W, Ci))
+    w = rng.standard_normal((Co, 3, 3, Ci))
+    b = rng.standard_normal(Co)
+    r = rng.standard_normal((N, H, W, Co))
+    z, mag = oracle.conv3x3(x, w, b, N, H, W, Ci, Co, res=r, return_abs=True)
+    pix = np.array([0, 5, 29, 30, 59, 17])
+    zs, ms = oracle.conv3x3_at(x, w, b, N, H, W, Ci, Co, pix, res=r)
+    assert np.array_equal(zs, z.reshape(-1, Co)[pix])
+    assert np.array_equal(ms, mag.reshape(-1, Co)[pix])
