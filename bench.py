@@ -19,7 +19,13 @@ Prints ONE JSON line.  Besides the contract fields it carries
   other_shapes -- us/call of the other four decoder shapes (context);
   other_dtypes -- the headline shape with fp16 and fp32 input/output;
   wide_shapes  -- shapes outside the pages' kernel's support set (C not a
-                  power of two, C > 2048, 5-D NDHWC), measured the same way.
+                  power of two, C > 2048, 5-D NDHWC), measured the same way;
+  resnet_block -- the decoder's ResnetBlock2D (GroupNorm -> SiLU -> conv3x3 ->
+                  GroupNorm -> SiLU -> conv3x3 + shortcut) with the GroupNorms
+                  fused into the convolutions, against the same block run as
+                  separate GroupNorm and convolution calls (ours, and with the
+                  convolutions from torch / MIOpen), plus the fused
+                  convolution's matrix-core roofline.
 """
 import argparse
 import ctypes
@@ -34,6 +40,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E, published peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak, published
+RESNET_SHAPES = ((1, 512, 128, 128), (1, 512, 256, 256), (1, 256, 512, 512))
 H200_US = {                        # the pages' new-kernel column (H200), context only
     "gn_silu_1x512x128x128": 76.0,
     "gn_silu_1x512x512x512": 311.1,
@@ -118,6 +126,110 @@ def cpu_baseline(w, x_bits, gamma, beta, budget_s):
     }
 
 
+def time_events(torch, fn, steps, warmup, stream):
+    """Mean ms of fn over `steps` calls between two events on `stream`."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def resnet_block(torch, gn, dev, shp, args):
+    """ResnetBlock2D of the decoder at logical shape (N, C, H, W), C -> C, G=32.
+
+    fused:    statistics of x; conv1 with GroupNorm1+SiLU in its prologue and
+              the statistics for GroupNorm2 in its epilogue; conv2 with
+              GroupNorm2+SiLU in its prologue and the shortcut x added in its
+              epilogue.  Two full-tensor convolutions, one statistics pass.
+    unfused:  GroupNorm1+SiLU; conv1; GroupNorm2+SiLU; conv2 + shortcut (our
+              kernels, the same convolution kernel without the fusion).
+    torch_conv: the unfused block with torch's conv2d (MIOpen) for the two
+              convolutions and the shortcut added by torch.
+    Seeded synthetic activations and weights (1/sqrt(9C)-scaled normal); the
+    convolution FLOPs are 2*N*H*W*C*9*C per conv.
+    """
+    N, C, H, W = shp
+    G = 32
+    g = torch.Generator(device="cpu").manual_seed(C * 7 + H)
+    x = (torch.randn(N, C, H, W, generator=g) * 1.5 + 0.3).to(dev).bfloat16() \
+        .contiguous(memory_format=torch.channels_last)
+    ws = [(torch.randn(C, C, 3, 3, generator=g) / (9 * C) ** 0.5).to(dev).bfloat16()
+          .contiguous(memory_format=torch.channels_last) for _ in range(2)]
+    bs = [(torch.randn(C, generator=g) * 0.1).to(dev) for _ in range(2)]
+    gam = [(1 + 0.1 * torch.randn(C, generator=g)).to(dev) for _ in range(2)]
+    bet = [(0.1 * torch.randn(C, generator=g)).to(dev) for _ in range(2)]
+    rows = x.permute(0, 2, 3, 1).reshape(N, H * W, C)
+    stream = torch.cuda.current_stream(dev)
+
+    def fused():
+        m1, r1 = gn.group_stats_rows(rows, G, 1e-6)
+        h, m2, r2 = gn.conv3x3(x, ws[0], bs[0], norm=(m1, r1, gam[0], bet[0]), apply_silu=True,
+                               next_groups=G)
+        return gn.conv3x3(h, ws[1], bs[1], norm=(m2, r2, gam[1], bet[1]), apply_silu=True,
+                          residual=x)
+
+    def unfused():
+        y1 = gn.group_norm_silu_4d(x, G, gam[0], bet[0], 1e-6)
+        h = gn.conv3x3(y1, ws[0], bs[0])
+        y2 = gn.group_norm_silu_4d(h, G, gam[1], bet[1], 1e-6)
+        return gn.conv3x3(y2, ws[1], bs[1], residual=x)
+
+    bb = [b.bfloat16() for b in bs]
+
+    def torch_conv():
+        y1 = gn.group_norm_silu_4d(x, G, gam[0], bet[0], 1e-6)
+        h = torch.nn.functional.conv2d(y1, ws[0], bb[0], padding=1)
+        y2 = gn.group_norm_silu_4d(h, G, gam[1], bet[1], 1e-6)
+        return torch.nn.functional.conv2d(y2, ws[1], bb[1], padding=1) + x
+
+    m1, r1 = gn.group_stats_rows(rows, G, 1e-6)
+
+    def conv1_fused():
+        return gn.conv3x3(x, ws[0], bs[0], norm=(m1, r1, gam[0], bet[0]), apply_silu=True,
+                          next_groups=G)
+
+    def conv_plain():
+        return gn.conv3x3(x, ws[0], bs[0])
+
+    steps = max(5, min(args.steps, 30))
+    with torch.no_grad():
+        for f in (fused, unfused, torch_conv):
+            if f() is None:
+                raise RuntimeError("resnet block declined")
+        t_f = time_events(torch, fused, steps, 3, stream)
+        t_u = time_events(torch, unfused, steps, 3, stream)
+        t_t = time_events(torch, torch_conv, steps, 3, stream)
+        t_c1 = time_events(torch, conv1_fused, steps, 3, stream)
+        t_cp = time_events(torch, conv_plain, steps, 3, stream)
+        t_tc = time_events(torch, lambda: torch.nn.functional.conv2d(x, ws[0], bb[0], padding=1),
+                           steps, 3, stream)
+    flops = 2.0 * N * H * W * C * 9 * C
+    tf = flops / (t_c1 * 1e-3) / 1e12
+    return {
+        "shape_nchw": [N, C, H, W],
+        "fused_us": round(t_f * 1e3, 1),
+        "unfused_us": round(t_u * 1e3, 1),
+        "torch_conv_us": round(t_t * 1e3, 1),
+        "fused_speedup_vs_unfused": round(t_u / t_f, 3),
+        "fused_speedup_vs_torch_conv": round(t_t / t_f, 3),
+        "conv_fused_prologue_stats_us": round(t_c1 * 1e3, 1),
+        "conv_plain_us": round(t_cp * 1e3, 1),
+        "torch_conv2d_us": round(t_tc * 1e3, 1),
+        "conv_roofline": {"kernel": "gn_conv3x3 (GroupNorm+SiLU prologue, statistics epilogue)",
+                          "bound": "mfma", "achieved": round(tf, 1),
+                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                          "flops_per_launch": flops},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -128,6 +240,7 @@ def main():
     ap.add_argument("--no-other-shapes", action="store_true")
     ap.add_argument("--no-other-dtypes", action="store_true")
     ap.add_argument("--no-wide-shapes", action="store_true")
+    ap.add_argument("--no-resnet-block", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -274,6 +387,12 @@ def main():
             }
             del wx, wy
 
+    resnet = {}
+    if not args.no_resnet_block:
+        for shp in RESNET_SHAPES:
+            log("resnet block %s" % (shp,))
+            resnet["x".join(str(v) for v in shp)] = resnet_block(torch, gn, dev, shp, args)
+
     if args.copy_calibration:
         log("copy calibration: 512 MiB device-to-device copy x5")
         src = torch.empty(256 * 1024 * 1024, dtype=torch.int16, device=dev).fill_(1)
@@ -333,6 +452,7 @@ def main():
         "other_shapes": other,
         "other_dtypes": dtypes,
         "wide_shapes": wide,
+        "resnet_block": resnet,
         "wall_s_timed_region": round(wall, 4),
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},

@@ -9,9 +9,13 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     MAX_CHANNELS,
     apply_rows,
+    conv3x3,
+    conv_plan,
     dtype_code,
     gn_apply_rows,
     gn_apply_rows_dtype,
+    gn_conv3x3_nhwc,
+    gn_conv3x3_plan,
     gn_kernel_name,
     gn_plan_rows,
     gn_plan_rows_dtype,

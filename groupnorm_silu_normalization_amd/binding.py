@@ -91,6 +91,9 @@ lib.gn_silu_ndhwc_dtype.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, 
                                     _int, _int, _vp]
 lib.gn_silu_ndhwc_strided_dtype.argtypes = [_vp, _i64p, _vp, _vp, _vp, _i64p, _i64, _i64, _i64,
                                             _i64, _i64, _i64, _f32, _int, _int, _vp]
+lib.gn_conv3x3_nhwc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _int, _vp, _vp, _vp, _vp, _i64,
+                                 _i64, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp]
+lib.gn_conv3x3_plan.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i64p]
 lib.gn_stats_rows_dtype.argtypes = [_vp, _i64, _i64, _i64, _i64, _f32, _int, _vp, _vp, _vp]
 lib.gn_apply_rows_dtype.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int,
                                     _int, _vp]
@@ -102,7 +105,8 @@ for _name in ("gn_silu_nhwc", "gn_silu_rows", "gn_silu_nhwc_strided", "gn_stats_
               "gn_apply_rows", "gn_profile_rows", "gn_silu_nhwc_dtype", "gn_silu_rows_dtype",
               "gn_silu_nhwc_strided_dtype", "gn_stats_rows_dtype", "gn_apply_rows_dtype",
               "gn_profile_rows_dtype", "gn_plan_rows_dtype", "gn_silu_ndhwc",
-              "gn_silu_ndhwc_dtype", "gn_silu_ndhwc_strided_dtype"):
+              "gn_silu_ndhwc_dtype", "gn_silu_ndhwc_strided_dtype", "gn_conv3x3_nhwc",
+              "gn_conv3x3_plan"):
     getattr(lib, _name).restype = _int
 lib.gn_plan_rows.argtypes = [_i64, _i64, _i64, _i64, _i64p]
 lib.gn_plan_rows.restype = _int
@@ -128,6 +132,8 @@ gn_silu_nhwc_strided_dtype = lib.gn_silu_nhwc_strided_dtype
 gn_silu_ndhwc = lib.gn_silu_ndhwc
 gn_silu_ndhwc_dtype = lib.gn_silu_ndhwc_dtype
 gn_silu_ndhwc_strided_dtype = lib.gn_silu_ndhwc_strided_dtype
+gn_conv3x3_nhwc = lib.gn_conv3x3_nhwc
+gn_conv3x3_plan = lib.gn_conv3x3_plan
 gn_stats_rows_dtype = lib.gn_stats_rows_dtype
 gn_apply_rows_dtype = lib.gn_apply_rows_dtype
 gn_profile_rows_dtype = lib.gn_profile_rows_dtype
@@ -353,3 +359,80 @@ def profile_rows(x, num_groups, weight, bias, eps, apply_silu, out, iters):
     # a negative slot is a kernel not launched for this shape (finalize fused
     # into the statistics kernel)
     return {lib.gn_kernel_name(i).decode(): float(ms[i]) for i in range(nk.value) if ms[i] >= 0}
+
+
+def conv3x3(x, weight, bias=None, *, norm=None, apply_silu=False, residual=None,
+            next_groups=None, next_eps=1e-6, out=None):
+    """3x3 convolution (padding 1, stride 1) of a channels-last bf16 tensor,
+    with the GroupNorm(+SiLU) of its input in the prologue and, optionally,
+    the statistics of its output for the next GroupNorm (gn_conv3x3_nhwc).
+
+    x: (N, Ci, H, W) bf16, channels_last.  weight: (Co, Ci, 3, 3) bf16 in
+    channels_last memory format (element [co, ci, kh, kw] at
+    ((co*3 + kh)*3 + kw)*Ci + ci).  bias: fp32 (Co,) or None.  norm: None, or
+    (mean, rstd, gamma, beta) with fp32 mean/rstd of shape (N, G) (as from
+    ``group_stats_rows``) and fp32 gamma/beta of shape (Ci,) or None.
+    residual: (N, Co, H, W) bf16 channels_last or None.  next_groups: G2 for
+    the output statistics, or None.
+
+    Returns z, or (z, mean2, rstd2) when next_groups is given; None when the
+    library declines the input (the caller falls back).
+    """
+    torch = _torch()
+    if not isinstance(x, torch.Tensor) or x.dim() != 4:
+        raise ValueError("conv3x3 expects a 4-D (N, Ci, H, W) tensor")
+    N, Ci, H, W = x.shape
+    if weight.dim() != 4 or tuple(weight.shape[1:]) != (Ci, 3, 3):
+        raise ValueError("weight must have shape (Co, Ci, 3, 3)")
+    Co = weight.shape[0]
+    if (x.device.type != "cuda" or torch.is_grad_enabled() or x.dtype != torch.bfloat16
+            or weight.dtype != torch.bfloat16 or weight.device != x.device):
+        return None
+    if not x.is_contiguous(memory_format=torch.channels_last):
+        return None
+    if not weight.is_contiguous(memory_format=torch.channels_last):
+        return None
+    if bias is not None and (bias.dtype != torch.float32 or bias.numel() != Co
+                             or bias.device != x.device):
+        return None
+    if residual is not None:
+        if (tuple(residual.shape) != (N, Co, H, W) or residual.dtype != torch.bfloat16
+                or not residual.is_contiguous(memory_format=torch.channels_last)):
+            return None
+    nm = nr = ga = be = None
+    G = 0
+    if norm is not None:
+        nm, nr, ga, be = norm
+        G = nm.shape[-1]
+        for t in (nm, nr):
+            if t.dtype != torch.float32 or t.device != x.device or not t.is_contiguous():
+                return None
+        if not _affine_ok(ga, Ci, x.device, "gamma") or not _affine_ok(be, Ci, x.device, "beta"):
+            return None
+    if out is None:
+        out = torch.empty((N, Co, H, W), dtype=torch.bfloat16, device=x.device,
+                          memory_format=torch.channels_last)
+    m2 = r2 = None
+    G2 = 0
+    if next_groups is not None:
+        G2 = int(next_groups)
+        m2 = torch.empty((N, G2), dtype=torch.float32, device=x.device)
+        r2 = torch.empty_like(m2)
+    code = lib.gn_conv3x3_nhwc(
+        _ptr(x), _ptr(nm), _ptr(nr), _ptr(ga), _ptr(be), G, 1 if apply_silu else 0,
+        _ptr(weight), _ptr(bias), _ptr(residual), _ptr(out), N, H, W, Ci, Co, G2,
+        float(next_eps), _ptr(m2), _ptr(r2), _stream_handle(x))
+    r = _result(code, out)
+    if r is None:
+        return None
+    return (out, m2, r2) if next_groups is not None else out
+
+
+CONV_PLAN_FIELDS = ("tiles_h", "tiles_w", "nb", "xcd_map", "blocks", "grid")
+
+
+def conv_plan(N, H, W, Ci, Co, G2=0):
+    """The library's launch shape for gn_conv3x3_nhwc (dict), or None if declined."""
+    buf = (_i64 * 6)()
+    r = _result(lib.gn_conv3x3_plan(N, H, W, Ci, Co, G2, buf), True)
+    return None if r is None else dict(zip(CONV_PLAN_FIELDS, list(buf)))

@@ -23,6 +23,7 @@
 #include <utility>
 #include <vector>
 
+#include "gn_conv.hpp"
 #include "gn_kernels.hpp"
 #include "gnsilu.h"
 
@@ -576,6 +577,81 @@ gn_status run_strided(const void *x, const int64_t *x_strides, const float *gamm
 }
 
 }  // namespace
+// ---- fused GroupNorm(+SiLU) -> 3x3 convolution (-> statistics) -------------
+
+// Launch shape of gn_conv3x3 for a problem: real workgroups, grid size and
+// whether the XCD-aware block order applies.
+struct ConvPlan {
+    int tiles_h, tiles_w, nb, xcd_map;
+    int64_t blocks, grid;
+};
+
+ConvPlan make_conv_plan(int64_t N, int64_t H, int64_t W, int64_t Co) {
+    ConvPlan c;
+    c.tiles_h = static_cast<int>(ceil_div(H, gnconv::TH));
+    c.tiles_w = static_cast<int>(ceil_div(W, gnconv::TW));
+    c.nb = static_cast<int>(Co / gnconv::BN);
+    const int64_t tiles = N * c.tiles_h * c.tiles_w;
+    c.blocks = tiles * c.nb;
+    c.xcd_map = (8 % c.nb == 0) ? 1 : 0;
+    // xcd_map: workgroup b runs output-channel block (b % 8) % nb on tile
+    // (b / 8) * (8 / nb) + (b % 8) / nb; the grid covers every tile once per
+    // block and is a multiple of 8 (the surplus exits at once).
+    c.grid = c.xcd_map ? 8 * ceil_div(tiles, 8 / c.nb) : c.blocks;
+    return c;
+}
+
+gn_status check_conv(const void *x, const float *nmean, const float *nrstd, int64_t G,
+                     int apply_silu, const void *wt, const void *res, const void *z, int64_t N,
+                     int64_t H, int64_t W, int64_t Ci, int64_t Co, int64_t G2, float eps2,
+                     const float *mean2, const float *rstd2) {
+    if (x == nullptr || wt == nullptr || z == nullptr) return GN_INVALID_ARGUMENT;
+    if (N < 0 || H < 0 || W < 0 || Ci <= 0 || Co <= 0) return GN_INVALID_ARGUMENT;
+    if ((nmean == nullptr) != (nrstd == nullptr)) return GN_INVALID_ARGUMENT;
+    if (nmean != nullptr && (G <= 0 || Ci % G != 0)) return GN_INVALID_ARGUMENT;
+    if (apply_silu != 0 && apply_silu != 1) return GN_INVALID_ARGUMENT;
+    if ((mean2 == nullptr) != (rstd2 == nullptr)) return GN_INVALID_ARGUMENT;
+    if (mean2 != nullptr) {
+        if (G2 <= 0 || Co % G2 != 0) return GN_INVALID_ARGUMENT;
+        if (!(eps2 >= 0.0f) || std::isinf(eps2)) return GN_INVALID_ARGUMENT;
+    }
+    if (W > 0 && H > INT64_MAX / W) return GN_INVALID_ARGUMENT;
+    if (H * W > 0 && N > INT64_MAX / (H * W)) return GN_INVALID_ARGUMENT;
+    const int64_t pix = N * H * W;
+    const int64_t cmax = Ci > Co ? Ci : Co;
+    if (pix > 0 && cmax > INT64_MAX / pix / 4) return GN_INVALID_ARGUMENT;
+    // the kernel's tile shapes
+    if (Ci % gnconv::BK != 0 || Ci > gnconv::kMaxCi || Co % gnconv::BN != 0) return GN_UNSUPPORTED;
+    if (mean2 != nullptr && 64 % (Co / G2) != 0) return GN_UNSUPPORTED;  // groups within 64 ch
+    for (const void *p : {x, wt, res, z})
+        if (p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) != 0) return GN_UNSUPPORTED;
+    // grid and 32-bit index limits of the kernel
+    if (H > (1 << 20) || W > (1 << 20) || N > (1 << 20)) return GN_UNSUPPORTED;
+    if (pix > 0) {
+        const ConvPlan c = make_conv_plan(N, H, W, Co);
+        if (c.grid >= (int64_t{1} << 31) || int64_t{c.tiles_h} * c.tiles_w >= (int64_t{1} << 31))
+            return GN_UNSUPPORTED;
+    }
+    return GN_OK;
+}
+
+template <bool PRO, bool SILU>
+void launch_conv_ps(const gnconv::ConvArgs &a, int64_t grid, bool stats, hipStream_t s) {
+    const dim3 g(static_cast<unsigned>(grid)), b(gnconv::kThreads);
+    const bool res = a.res != nullptr;
+    if (stats) {
+        if (res)
+            gnconv::gn_conv3x3<PRO, SILU, true, true><<<g, b, 0, s>>>(a);
+        else
+            gnconv::gn_conv3x3<PRO, SILU, true, false><<<g, b, 0, s>>>(a);
+    } else {
+        if (res)
+            gnconv::gn_conv3x3<PRO, SILU, false, true><<<g, b, 0, s>>>(a);
+        else
+            gnconv::gn_conv3x3<PRO, SILU, false, false><<<g, b, 0, s>>>(a);
+    }
+}
+
 }  // namespace gnsilu
 
 using namespace gnsilu;
@@ -764,6 +840,93 @@ gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_
     if (st == GN_OK)
         for (int i = 0; i < 8; ++i) plan_out[i] = full[i];
     return st;
+}
+
+gn_status gn_conv3x3_nhwc(const void *x, const float *norm_mean, const float *norm_rstd,
+                          const float *gamma, const float *beta, int64_t G, int apply_silu,
+                          const void *wt, const float *bias, const void *res, void *z, int64_t N,
+                          int64_t H, int64_t W, int64_t Ci, int64_t Co, int64_t G2, float eps2,
+                          float *mean2_out, float *rstd2_out, void *stream) {
+    gn_status st = check_conv(x, norm_mean, norm_rstd, G, apply_silu, wt, res, z, N, H, W, Ci,
+                              Co, G2, eps2, mean2_out, rstd2_out);
+    if (st != GN_OK) return st;
+    if (N * H * W == 0) return GN_OK;
+    Call c;
+    st = begin_call(stream, {x, norm_mean, norm_rstd, gamma, beta, wt, bias, res, z, mean2_out,
+                             rstd2_out},
+                    &c);
+    if (st != GN_OK) return st;
+    const ConvPlan cp = make_conv_plan(N, H, W, Co);
+    gnconv::ConvArgs a;
+    a.x = static_cast<const uint16_t *>(x);
+    a.mean = norm_mean;
+    a.rstd = norm_rstd;
+    a.gamma = gamma;
+    a.beta = beta;
+    a.wt = static_cast<const uint16_t *>(wt);
+    a.bias = bias;
+    a.res = static_cast<const uint16_t *>(res);
+    a.z = static_cast<uint16_t *>(z);
+    a.part = nullptr;
+    a.N = static_cast<int>(N);
+    a.H = static_cast<int>(H);
+    a.W = static_cast<int>(W);
+    a.Ci = static_cast<int>(Ci);
+    a.Co = static_cast<int>(Co);
+    a.G = norm_mean ? static_cast<int>(G) : 1;
+    a.G2 = mean2_out ? static_cast<int>(G2) : 1;
+    a.tiles_h = cp.tiles_h;
+    a.tiles_w = cp.tiles_w;
+    a.nb = cp.nb;
+    a.xcd_map = cp.xcd_map;
+    a.blocks = cp.blocks;
+    const bool stats = mean2_out != nullptr;
+    const int64_t tiles_per_sample = int64_t{cp.tiles_h} * cp.tiles_w;
+
+    std::unique_lock<std::mutex> lock(scratch_mutex(), std::defer_lock);
+    if (stats) {
+        lock.lock();
+        unsigned *counters = nullptr;
+        char *payload = nullptr;
+        const size_t bytes = sizeof(float) * 4 * static_cast<size_t>(N * tiles_per_sample * G2);
+        st = scratch_for(c.dev, c.stream, 0, bytes, &counters, &payload);
+        if (st != GN_OK) return st;
+        a.part = reinterpret_cast<float *>(payload);
+    }
+    const bool pro = norm_mean != nullptr || apply_silu;
+    if (pro && apply_silu)
+        launch_conv_ps<true, true>(a, cp.grid, stats, c.stream);
+    else if (pro)
+        launch_conv_ps<true, false>(a, cp.grid, stats, c.stream);
+    else
+        launch_conv_ps<false, false>(a, cp.grid, stats, c.stream);
+    if (stats)
+        gnconv::gn_conv_stats_finalize<<<static_cast<unsigned>(N * G2), gnconv::kThreads, 0,
+                                         c.stream>>>(a.part, static_cast<int>(tiles_per_sample),
+                                                     static_cast<int>(G2), eps2, mean2_out,
+                                                     rstd2_out);
+    return finish_launch();
+}
+
+gn_status gn_conv3x3_plan(int64_t N, int64_t H, int64_t W, int64_t Ci, int64_t Co, int64_t G2,
+                          int64_t plan_out[6]) {
+    if (plan_out == nullptr) return GN_INVALID_ARGUMENT;
+    static const uint16_t probe[8] __attribute__((aligned(16))) = {};
+    static float fprobe[4];
+    const gn_status st = check_conv(probe, nullptr, nullptr, 0, 0, probe, nullptr, probe, N, H,
+                                    W, Ci, Co, G2, 0.0f, G2 > 0 ? fprobe : nullptr,
+                                    G2 > 0 ? fprobe : nullptr);
+    if (st != GN_OK) return st;
+    for (int i = 0; i < 6; ++i) plan_out[i] = 0;
+    if (N * H * W == 0) return GN_OK;
+    const ConvPlan c = make_conv_plan(N, H, W, Co);
+    plan_out[0] = c.tiles_h;
+    plan_out[1] = c.tiles_w;
+    plan_out[2] = c.nb;
+    plan_out[3] = c.xcd_map;
+    plan_out[4] = c.blocks;
+    plan_out[5] = c.grid;
+    return GN_OK;
 }
 
 const char *gn_kernel_name(int i) { return (i >= 0 && i < kSlots) ? kKernelNames[i] : nullptr; }

@@ -1,0 +1,464 @@
+// gn_conv.hpp -- gfx950 (CDNA4) 3x3 NHWC convolution with the GroupNorm(+SiLU)
+// of its input fused into the prologue and the statistics of its output for
+// the next GroupNorm fused into the epilogue.
+//
+// The fusion is the one the decoder's ResnetBlock2D invites ("FLUX.2 VAE
+// decoder fast path behind quality=high", Modifications section 2: the
+// ResnetBlock2D norm1/norm2 + SiLU chains around its Conv2d(3x3, p1)): the
+// normalised activation y = SiLU(GroupNorm(x)) exists only in LDS, on its way
+// into the matrix cores, and the output's per-group moments are taken while
+// the output tile is still on chip, so the two elementwise passes of the
+// GroupNorm between two convolutions disappear.
+//
+//   z[n,h,w,co] = bias[co] + res[n,h,w,co]
+//               + sum_{kh,kw,ci} wt[co,kh,kw,ci] * y[n,h+kh-1,w+kw-1,ci]   (y = 0 outside)
+//   y = SiLU?(gamma[ci] * (x - mean[n,g]) * rstd[n,g] + beta[ci])          (or y = x)
+//
+// Implicit GEMM on the matrix cores: M = output pixels, N = output channels,
+// K = 9 taps x Ci.  A workgroup of 256 lanes owns an 8 x 16 pixel x 128
+// channel output tile; each of its four waves owns 64 pixels x 64 channels as
+// 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.  Per chunk of 32 input channels:
+//   * the 10 x 18 pixel halo of the tile is loaded once, normalised (+SiLU)
+//     with per-channel scale/shift held in LDS, rounded to bf16 and stored to
+//     LDS -- every input value is transformed once per chunk, not once per
+//     tap;
+//   * the nine taps run against it, each with its 128 x 32 weight tile in one
+//     of two LDS buffers; the next tap's weights are loaded from global memory
+//     into registers while the current tap's MFMAs run.
+// LDS rows are 80 bytes (32 bf16 + 8 padding), so the 16-byte fragment reads
+// of 16 consecutive lanes fall on distinct banks.
+//
+// Epilogue: the accumulators (+ bias) are staged as fp32 through LDS, 64
+// output channels at a time, so that every lane adds the residual and writes
+// z with 16-byte accesses; the bf16-rounded values (what the next GroupNorm
+// reads) give, per tile and per output group, the count, mean and sum of
+// squared deviations (M2), in a fixed order.  gn_conv_stats_finalize merges
+// the tiles of each (n, group) with the parallel-variance formula in fp64, in
+// a fixed order, so the statistics are reproducible bit for bit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gnconv {
+
+constexpr int kThreads = 256;
+constexpr int TH = 8, TW = 16;                 // output tile, pixels
+constexpr int HH = TH + 2, HWD = TW + 2;       // halo tile
+constexpr int BM = TH * TW;                    // 128 output pixels
+constexpr int BN = 128;                        // output channels per workgroup
+constexpr int BK = 32;                         // input channels per chunk
+constexpr int KS = BK + 8;                     // LDS row stride of A and B, bf16 elements
+constexpr int A_ELEMS = HH * HWD * KS;         // 7200 bf16
+constexpr int B_ELEMS = BN * KS;               // 5120 bf16 per tap buffer
+constexpr int OS = 72;                         // epilogue fp32 row stride (64 + 8)
+constexpr int kMaxCi = 1024;                   // scale/shift table in LDS
+constexpr int kLdsBytesMain = (A_ELEMS + 2 * B_ELEMS) * 2;   // 34880
+constexpr int kLdsBytesEpi = BM * OS * 4;                    // 36864
+constexpr int kLdsBytes = kLdsBytesMain > kLdsBytesEpi ? kLdsBytesMain : kLdsBytesEpi;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct ConvArgs {
+    const uint16_t *x;      // [N][H][W][Ci] bf16
+    const float *mean;      // [N][G] or null: no normalisation (y = SiLU?(x))
+    const float *rstd;      // [N][G]
+    const float *gamma;     // [Ci] or null (ones)
+    const float *beta;      // [Ci] or null (zeros)
+    const uint16_t *wt;     // [Co][3][3][Ci] bf16
+    const float *bias;      // [Co] or null
+    const uint16_t *res;    // [N][H][W][Co] bf16 or null
+    uint16_t *z;            // [N][H][W][Co] bf16
+    float *part;            // [N][tiles][G2][4]: count, mean, M2, 0 (statistics only)
+    int N, H, W, Ci, Co, G, G2;
+    int tiles_h, tiles_w;   // ceil(H/8), ceil(W/16)
+    int nb;                 // Co / 128 output-channel blocks
+    int xcd_map;            // 1: XCD-aware block order (nb divides 8)
+    int64_t blocks;         // N * tiles_h * tiles_w * nb (real workgroups)
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ float silu(float t) {
+    const float e = __builtin_amdgcn_exp2f(t * -1.4426950408889634f);
+    return t * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Workgroup -> (sample, tile, output-channel block).  Dispatch hands
+// consecutive workgroups to the 8 XCDs in turn; with xcd_map, the XCDs are
+// split into nb sets, each set working on one output-channel block (so each
+// XCD's L2 holds one 128-channel slice of the weights) and all sets walking
+// the pixel tiles in the same order (so the nb reads of an input tile fall
+// close together in time and share the Infinity Cache).
+__device__ __forceinline__ bool map_block(const ConvArgs &a, int64_t b, int64_t *tile,
+                                          int *cb) {
+    if (a.xcd_map) {
+        const int xcd = static_cast<int>(b & 7);
+        const int64_t j = b >> 3;
+        const int reps = 8 / a.nb;  // XCDs per output-channel block
+        *cb = xcd % a.nb;
+        *tile = j * reps + xcd / a.nb;
+        return *tile < a.blocks / a.nb;
+    }
+    *cb = static_cast<int>(b % a.nb);
+    *tile = b / a.nb;
+    return b < a.blocks;
+}
+
+// ---------------------------------------------------------------------------
+// PRO: normalise (+SILU) the input on its way into LDS; STATS: output
+// moments; RES: add the residual.
+// ---------------------------------------------------------------------------
+template <bool PRO, bool SILU, bool STATS, bool RES>
+__global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
+    __shared__ float s_scale[PRO ? kMaxCi : 1];
+    __shared__ float s_shift[PRO ? kMaxCi : 1];
+    uint16_t *sA = reinterpret_cast<uint16_t *>(smem);
+    uint16_t *sB = sA + A_ELEMS;  // two tap buffers of B_ELEMS
+    float *sO = reinterpret_cast<float *>(smem);
+
+    int64_t tile;
+    int cb;
+    if (!map_block(a, blockIdx.x, &tile, &cb)) return;  // padding workgroup: uniform exit
+    const int tiles_per_sample = a.tiles_h * a.tiles_w;
+    const int n = static_cast<int>(tile / tiles_per_sample);
+    const int tin = static_cast<int>(tile - static_cast<int64_t>(n) * tiles_per_sample);
+    const int h0 = (tin / a.tiles_w) * TH;
+    const int w0 = (tin % a.tiles_w) * TW;
+    const int co0 = cb * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int Ci = a.Ci;
+
+    if constexpr (PRO) {
+        if (a.mean) {
+            const int Cg = Ci / a.G;
+            for (int c = tid; c < Ci; c += kThreads) {
+                const int gi = n * a.G + c / Cg;
+                const float sc = (a.gamma ? a.gamma[c] : 1.0f) * a.rstd[gi];
+                s_scale[c] = sc;
+                s_shift[c] = fmaf(-a.mean[gi], sc, a.beta ? a.beta[c] : 0.0f);
+            }
+        } else {
+            for (int c = tid; c < Ci; c += kThreads) {
+                s_scale[c] = 1.0f;
+                s_shift[c] = 0.0f;
+            }
+        }
+        __syncthreads();
+    }
+
+    // B (weights) of one tap and chunk: 128 rows of 32 bf16 = 512 16-byte
+    // pieces, two per lane: piece v -> row v / 4, quarter v % 4.
+    const uint16_t *wbase = a.wt + static_cast<int64_t>(co0) * 9 * Ci;
+    auto load_b = [&](int tap, int ci0, u32x4 (&r)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int v = tid + i * kThreads;
+            const int row = v >> 2, q = v & 3;
+            const uint16_t *src = wbase + (static_cast<int64_t>(row) * 9 + tap) * Ci + ci0 + 8 * q;
+            r[i] = *reinterpret_cast<const u32x4 *>(src);
+        }
+    };
+    auto store_b = [&](int buf, const u32x4 (&r)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int v = tid + i * kThreads;
+            const int row = v >> 2, q = v & 3;
+            *reinterpret_cast<u32x4 *>(sB + buf * B_ELEMS + row * KS + 8 * q) = r[i];
+        }
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nchunks = Ci / BK;
+    int buf = 0;
+    {
+        u32x4 r[2];
+        load_b(0, 0, r);
+        store_b(0, r);
+    }
+    // Lane constants of the fragment reads: pixel p = lane % 32 of a 32-pixel
+    // block (2 rows of 16), k offset 8 * (lane / 32).
+    const int fp = lane & 31, fk = 8 * (lane >> 5);
+    const int frow = fp >> 4, fcol = fp & 15;
+
+    for (int k = 0; k < nchunks; ++k) {
+        const int ci0 = k * BK;
+        // ---- the halo tile of this chunk: 180 pixels x 4 pieces of 8 channels
+        {
+            constexpr int kPieces = HH * HWD * 4;  // 720
+            u32x4 raw[3];
+            bool inside[3];
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const int v = tid + i * kThreads;
+                inside[i] = false;
+                raw[i] = u32x4{0u, 0u, 0u, 0u};
+                if (v < kPieces) {
+                    const int p = v >> 2, q = v & 3;
+                    const int ih = h0 - 1 + p / HWD, iw = w0 - 1 + p % HWD;
+                    if (ih >= 0 && ih < a.H && iw >= 0 && iw < a.W) {
+                        inside[i] = true;
+                        raw[i] = *reinterpret_cast<const u32x4 *>(
+                            a.x + ((static_cast<int64_t>(n) * a.H + ih) * a.W + iw) * Ci + ci0 +
+                            8 * q);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const int v = tid + i * kThreads;
+                if (v < kPieces) {
+                    const int p = v >> 2, q = v & 3;
+                    u32x4 out = u32x4{0u, 0u, 0u, 0u};  // zero padding of y
+                    if (inside[i]) {
+                        if constexpr (PRO) {
+                            const int c = ci0 + 8 * q;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                float lo = bf16_to_f32(raw[i][e] & 0xffffu);
+                                float hi = bf16_to_f32(raw[i][e] >> 16);
+                                lo = fmaf(lo, s_scale[c + 2 * e], s_shift[c + 2 * e]);
+                                hi = fmaf(hi, s_scale[c + 2 * e + 1], s_shift[c + 2 * e + 1]);
+                                if constexpr (SILU) {
+                                    lo = silu(lo);
+                                    hi = silu(hi);
+                                }
+                                out[e] = pack_bf16x2(lo, hi);
+                            }
+                        } else {
+                            out = raw[i];
+                        }
+                    }
+                    *reinterpret_cast<u32x4 *>(sA + p * KS + 8 * q) = out;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- nine taps
+        for (int t = 0; t < 9; ++t) {
+            const bool more = (t < 8) || (k + 1 < nchunks);
+            u32x4 nb[2];
+            if (more) load_b(t < 8 ? t + 1 : 0, t < 8 ? ci0 : ci0 + BK, nb);
+            const int kh = t / 3, kw = t % 3;
+            const uint16_t *b_cur = sB + buf * B_ELEMS;
+#pragma unroll
+            for (int kk = 0; kk < BK; kk += 16) {
+                bf16x8 af[2], bfr[2];
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi) {
+                    const int r0 = wm * 4 + mi * 2;
+                    const int hp = (r0 + frow + kh) * HWD + fcol + kw;
+                    af[mi] = *reinterpret_cast<const bf16x8 *>(sA + hp * KS + kk + fk);
+                }
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni) {
+                    const int col = wn * 64 + ni * 32 + fp;
+                    bfr[ni] = *reinterpret_cast<const bf16x8 *>(b_cur + col * KS + kk + fk);
+                }
+#pragma unroll
+                for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < 2; ++ni)
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni],
+                                                                             acc[mi][ni], 0, 0, 0);
+            }
+            if (more) store_b(buf ^ 1, nb);
+            __syncthreads();
+            buf ^= 1;
+        }
+    }
+
+    // ---- epilogue, 64 output channels at a time
+    const int q = tid & 7;          // 8-channel piece of the half
+    const int prow = tid >> 3;      // pixels prow + 32 * i
+    float vals[4][8];
+    bool valid[4];
+    int cnt = 0;                    // valid pixels of the tile
+    {
+        const int rows = min(TH, a.H - h0), cols = min(TW, a.W - w0);
+        cnt = rows * cols;
+    }
+    const int Cg2 = STATS ? a.Co / a.G2 : 1;
+    for (int half = 0; half < 2; ++half) {
+        if (wn == half) {
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni) {
+                    const int cl = ni * 32 + fp;  // channel within the half
+                    const float bv = a.bias ? a.bias[co0 + half * 64 + cl] : 0.0f;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                        const int pix = wm * 64 + mi * 32 + m;
+                        sO[pix * OS + cl] = acc[mi][ni][r] + bv;
+                    }
+                }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int pix = prow + 32 * i;
+            const int oh = h0 + pix / TW, ow = w0 + pix % TW;
+            valid[i] = oh < a.H && ow < a.W;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = sO[pix * OS + 8 * q + e];
+            const int64_t off = ((static_cast<int64_t>(n) * a.H + oh) * a.W + ow) * a.Co + co0 +
+                                half * 64 + 8 * q;
+            if (valid[i]) {
+                if constexpr (RES) {
+                    const u32x4 rr = *reinterpret_cast<const u32x4 *>(a.res + off);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        v[2 * e] += bf16_to_f32(rr[e] & 0xffffu);
+                        v[2 * e + 1] += bf16_to_f32(rr[e] >> 16);
+                    }
+                }
+                u32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+                    // the stored (rounded) values, for the statistics
+                    vals[i][2 * e] = bf16_to_f32(o[e] & 0xffffu);
+                    vals[i][2 * e + 1] = bf16_to_f32(o[e] >> 16);
+                }
+                *reinterpret_cast<u32x4 *>(a.z + off) = o;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vals[i][e] = 0.0f;
+            }
+        }
+        __syncthreads();  // sO fully read: free for the next half or the statistics
+
+        if constexpr (STATS) {
+            // Per channel: sum over this lane's pixels, then over the 32 lanes
+            // of the same piece in order; per group: over its channels.
+            float *red = sO;                 // [32][64]
+            float *gmean = sO + 32 * 64;     // [64]: mean of the group of each channel
+            float s8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float s = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s += valid[i] ? vals[i][e] : 0.0f;
+                s8[e] = s;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[prow * 64 + 8 * q + e] = s8[e];
+            __syncthreads();
+            if (tid < 64) {
+                float s = 0.0f;
+                for (int r = 0; r < 32; ++r) s += red[r * 64 + tid];
+                red[tid] = s;  // row 0 is read only by this lane below it
+            }
+            __syncthreads();
+            const int ngroups = 64 / Cg2;
+            if (tid < ngroups) {
+                float s = 0.0f;
+                for (int c = 0; c < Cg2; ++c) s += red[tid * Cg2 + c];
+                const float mg = s / static_cast<float>(cnt * Cg2);
+                for (int c = 0; c < Cg2; ++c) gmean[tid * Cg2 + c] = mg;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float mg = gmean[8 * q + e];
+                float s = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float d = vals[i][e] - mg;
+                    s = valid[i] ? fmaf(d, d, s) : s;
+                }
+                s8[e] = s;
+            }
+            __syncthreads();  // gmean read by every lane before red is reused
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[prow * 64 + 8 * q + e] = s8[e];
+            __syncthreads();
+            if (tid < 64) {
+                float s = 0.0f;
+                for (int r = 0; r < 32; ++r) s += red[r * 64 + tid];
+                red[tid] = s;
+            }
+            __syncthreads();
+            if (tid < ngroups) {
+                float m2 = 0.0f;
+                for (int c = 0; c < Cg2; ++c) m2 += red[tid * Cg2 + c];
+                const int g2 = (co0 + half * 64) / Cg2 + tid;
+                float *dst = a.part + ((static_cast<int64_t>(n) * tiles_per_sample + tin) *
+                                           a.G2 + g2) * 4;
+                dst[0] = static_cast<float>(cnt * Cg2);
+                dst[1] = gmean[tid * Cg2];
+                dst[2] = m2;
+                dst[3] = 0.0f;
+            }
+            __syncthreads();  // red and gmean free for the next half
+        }
+    }
+}
+
+// Merge of the per-tile (count, mean, M2) of each (n, group) into fp32 mean
+// and rstd: thread j folds tiles j, j + 256, ... in increasing order with the
+// parallel-variance update in fp64, then a fixed tree over the 256 threads.
+__global__ __launch_bounds__(kThreads) void gn_conv_stats_finalize(const float *part, int tiles,
+                                                                   int G2, float eps, float *mean,
+                                                                   float *rstd) {
+    __shared__ double sn[kThreads], sm[kThreads], sq[kThreads];
+    const int ng = blockIdx.x;
+    const int n = ng / G2, g = ng % G2;
+    const int tid = threadIdx.x;
+    double cn = 0.0, cm = 0.0, cq = 0.0;
+    for (int t = tid; t < tiles; t += kThreads) {
+        const float *p = part + ((static_cast<int64_t>(n) * tiles + t) * G2 + g) * 4;
+        const double bn = p[0], bm = p[1], bq = p[2];
+        const double tn = cn + bn;
+        const double d = bm - cm;
+        cm += d * (bn / tn);
+        cq += bq + d * d * (cn * bn / tn);
+        cn = tn;
+    }
+    sn[tid] = cn;
+    sm[tid] = cm;
+    sq[tid] = cq;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+        if (tid < s && sn[tid + s] > 0.0) {
+            const double an = sn[tid], bn = sn[tid + s];
+            const double tn = an + bn;
+            const double d = sm[tid + s] - sm[tid];
+            sm[tid] += d * (bn / tn);
+            sq[tid] += sq[tid + s] + d * d * (an * bn / tn);
+            sn[tid] = tn;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const double var = sn[0] > 0.0 ? sq[0] / sn[0] : 0.0;
+        mean[ng] = static_cast<float>(sm[0]);
+        rstd[ng] = static_cast<float>(1.0 / sqrt((var > 0.0 ? var : 0.0) + static_cast<double>(eps)));
+    }
+}
+
+}  // namespace gnconv

@@ -226,6 +226,54 @@ gn_status gn_profile_rows_dtype(const void *x, const float *gamma, const float *
 gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dtype,
                              int64_t plan_out[13]);
 
+/* The GroupNorm(+SiLU) fused into the neighbouring 3x3 convolution of the
+ * decoder's ResnetBlock2D (Modifications section 2: "ResnetBlock2D
+ * norm1/norm2 + SiLU chains" around Conv2d(3x3, p1)):
+ *
+ *   y = apply_silu ? SiLU(t) : t,   t = gamma[c]*(x - mean[n,g])*rstd[n,g] + beta[c]
+ *       (t = x when norm_mean is NULL)
+ *   z[n,h,w,co] = bias[co] + res[n,h,w,co]
+ *               + sum_{kh,kw in 0..2} sum_{ci} wt[co,kh,kw,ci] * y[n,h+kh-1,w+kw-1,ci]
+ *   with y = 0 outside the image (zero padding 1, stride 1), and, when
+ *   mean2_out is given, the statistics of z for the next GroupNorm: per
+ *   (n, g2) over the G2 contiguous groups of Co, the fp32 mean and
+ *   1/sqrt(var + eps2) (biased variance) of the stored bf16 values of z.
+ *
+ * x: bf16 [N][H][W][Ci] (NHWC); norm_mean / norm_rstd: fp32 [N][G] as written
+ * by gn_stats_rows (or by the statistics output of a previous call), both or
+ * neither; gamma / beta: fp32 [Ci] or NULL; wt: bf16 [Co][3][3][Ci] (the
+ * channels-last layout of a [Co, Ci, 3, 3] weight); bias: fp32 [Co] or NULL;
+ * res: bf16 [N][H][W][Co] or NULL (added before rounding: the ResnetBlock2D
+ * shortcut); z: bf16 [N][H][W][Co], must not overlap x or res; mean2_out /
+ * rstd2_out: fp32 [N][G2] device buffers, both or neither.  The products are
+ * of bf16 operands (y is rounded once to bf16 on its way to the matrix
+ * cores), accumulated in fp32; z is rounded once to bf16.
+ * Supported: Ci a multiple of 32 up to 1024, Co a multiple of 128, and with
+ * statistics Co/G2 dividing 64; pointers 16-byte aligned; else
+ * GN_UNSUPPORTED.  INVALID as for gn_silu_rows (NULL x/wt/z, negative sizes,
+ * Ci % G, Co % G2, eps2, apply_silu, one of a pointer pair missing).  N*H*W
+ * == 0 enqueues nothing.  With statistics, the library's scratch buffer of
+ * the stream holds per-tile partials (16 bytes per 8x16 pixel tile and
+ * output group) and a second kernel merges them; the result is bitwise
+ * reproducible. */
+gn_status gn_conv3x3_nhwc(const void *x, const float *norm_mean, const float *norm_rstd,
+                          const float *gamma, const float *beta, int64_t G, int apply_silu,
+                          const void *wt, const float *bias, const void *res, void *z,
+                          int64_t N, int64_t H, int64_t W, int64_t Ci, int64_t Co,
+                          int64_t G2, float eps2, float *mean2_out, float *rstd2_out,
+                          void *stream);
+
+/* Launch shape of gn_conv3x3_nhwc for a problem, for inspection and tests;
+ * no HIP call.  G2 > 0 asks for the statistics output.  Writes 6 values:
+ * [0] tiles_h = ceil(H/8), [1] tiles_w = ceil(W/16) (output tiles of 8x16
+ * pixels), [2] nb = Co/128 output-channel blocks, [3] 1 when the XCD-aware
+ * block order is used (nb divides 8), [4] workgroups with work
+ * (N*tiles_h*tiles_w*nb), [5] workgroups launched.  Returns the status
+ * gn_conv3x3_nhwc would return from its argument checks for aligned
+ * pointers. */
+gn_status gn_conv3x3_plan(int64_t N, int64_t H, int64_t W, int64_t Ci, int64_t Co, int64_t G2,
+                          int64_t plan_out[6]);
+
 /* Name of kernel slot i of gn_profile_rows, or NULL. */
 const char *gn_kernel_name(int i);
 

@@ -1,0 +1,108 @@
+"""Host-side proof that the fused conv kernel's accesses stay in bounds.
+
+gn_conv3x3_plan gives the launch shape; the kernel's index arithmetic is
+replayed here with its tile constants (8 x 16 output pixels, 128 output
+channels, chunks of 32 input channels, LDS rows of 40 bf16, epilogue rows of
+72 fp32): the workgroup -> (tile, channel block) map covers every pair once,
+the halo, weight, residual and output addresses stay inside their tensors,
+every LDS index stays inside its array, and the statistics partials stay
+inside their buffer.
+"""
+import numpy as np
+import pytest
+
+gn = pytest.importorskip("groupnorm_silu_normalization_amd")
+
+TH, TW, BN, BK, KS, OS = 8, 16, 128, 32, 40, 72
+HH, HWD = TH + 2, TW + 2
+A_ELEMS, B_ELEMS = HH * HWD * KS, BN * KS
+LDS_MAIN = A_ELEMS + 2 * B_ELEMS            # bf16 elements
+LDS_EPI_FLOATS = TH * TW * OS
+
+SHAPES = [  # N, H, W, Ci, Co, G2
+    (1, 8, 16, 32, 128, 32), (2, 13, 21, 64, 128, 32), (1, 32, 48, 128, 256, 32),
+    (1, 5, 7, 32, 128, 8), (1, 64, 64, 512, 512, 32), (3, 9, 17, 96, 384, 24),
+    (1, 128, 128, 512, 512, 32), (2, 1, 1, 32, 1024, 64), (1, 17, 33, 1024, 128, 32),
+]
+
+
+def block_map(p, b):
+    if p["xcd_map"]:
+        xcd, j = b % 8, b // 8
+        reps = 8 // p["nb"]
+        tile, cb = j * reps + xcd // p["nb"], xcd % p["nb"]
+        return (tile, cb) if tile < p["blocks"] // p["nb"] else None
+    return (b // p["nb"], b % p["nb"]) if b < p["blocks"] else None
+
+
+@pytest.mark.parametrize("N,H,W,Ci,Co,G2", SHAPES)
+def test_conv_plan_and_indices_in_bounds(N, H, W, Ci, Co, G2):
+    p = gn.conv_plan(N, H, W, Ci, Co, G2)
+    assert p is not None
+    assert p["tiles_h"] == -(-H // TH) and p["tiles_w"] == -(-W // TW) and p["nb"] == Co // BN
+    tps = p["tiles_h"] * p["tiles_w"]
+    assert p["blocks"] == N * tps * p["nb"] and p["grid"] < 2 ** 31
+    assert p["xcd_map"] == (8 % p["nb"] == 0)
+    if p["xcd_map"]:
+        assert p["grid"] % 8 == 0
+    seen = set()
+    for b in range(p["grid"]):
+        m = block_map(p, b)
+        if m is not None:
+            assert m not in seen
+            seen.add(m)
+    assert len(seen) == p["blocks"], "every (tile, channel block) runs exactly once"
+    # halo pieces: 180 pixels x 4 pieces of 8 channels, three per lane
+    v = np.arange(256)[:, None] + 256 * np.arange(3)[None, :]
+    live = v < HH * HWD * 4
+    pix, q = v // 4, v % 4
+    assert np.all((pix * KS + 8 * q + 8)[live] <= A_ELEMS)
+    # fragment reads: wave (wm, wn), block mi/ni, lane -> halo pixel, k offset
+    lane = np.arange(64)
+    fp, fk = lane % 32, 8 * (lane // 32)
+    for wm in (0, 1):
+        for mi in (0, 1):
+            for kh in range(3):
+                for kw in range(3):
+                    hp = (wm * 4 + mi * 2 + fp // 16 + kh) * HWD + fp % 16 + kw
+                    assert np.all(hp * KS + 16 + fk + 8 <= A_ELEMS)
+    col = np.arange(128)
+    assert np.all(col * KS + 16 + 8 + 8 <= B_ELEMS)
+    # weight pieces of a tap: 128 rows x 4 pieces, two per lane, inside the block's slice
+    v2 = np.arange(512)
+    row, q2 = v2 // 4, v2 % 4
+    for tap in (0, 8):
+        for ci0 in (0, Ci - BK):
+            off = (row * 9 + tap) * Ci + ci0 + 8 * q2
+            assert off.min() >= 0 and (off + 8).max() <= BN * 9 * Ci
+    # epilogue staging and the statistics scratch in the same LDS
+    r = np.arange(16)
+    m = 8 * (r[:, None] // 4) + 4 * (lane[None, :] // 32) + r[:, None] % 4
+    pixl = 64 * 1 + 32 * 1 + m
+    assert (pixl * OS + 63).max() < LDS_EPI_FLOATS and m.max() < 32
+    assert 32 * 64 + 64 <= LDS_EPI_FLOATS
+    assert max(LDS_MAIN * 2, LDS_EPI_FLOATS * 4) <= 64 * 1024
+    # output / residual pieces of valid pixels, statistics partials
+    for tile in (0, N * tps - 1):
+        n, tin = tile // tps, tile % tps
+        h0, w0 = (tin // p["tiles_w"]) * TH, (tin % p["tiles_w"]) * TW
+        for pixt in range(TH * TW):
+            oh, ow = h0 + pixt // TW, w0 + pixt % TW
+            if oh < H and ow < W:
+                off = ((n * H + oh) * W + ow) * Co + (Co - BN) + 64 + 8 * 7
+                assert off + 8 <= N * H * W * Co
+        if G2:
+            Cg2 = Co // G2
+            assert 64 % Cg2 == 0
+            g2 = (Co - BN + 64) // Cg2 + 64 // Cg2 - 1
+            assert ((n * tps + tin) * G2 + g2) * 4 + 4 <= N * tps * G2 * 4
+
+
+def test_conv_plan_declines():
+    assert gn.conv_plan(1, 8, 8, 48, 128) is None            # Ci not a multiple of 32
+    assert gn.conv_plan(1, 8, 8, 64, 192) is None            # Co not a multiple of 128
+    assert gn.conv_plan(1, 8, 8, 2048, 128) is None          # Ci above 1024
+    assert gn.conv_plan(1, 8, 8, 64, 512, 4) is None         # groups of 128 channels
+    with pytest.raises(ValueError):
+        gn.conv_plan(1, 8, 8, 64, 128, 3)                    # Co % G2 != 0
+    assert gn.conv_plan(0, 8, 8, 64, 128)["grid"] == 0       # empty: nothing launched
