@@ -94,6 +94,8 @@ lib.gn_silu_ndhwc_strided_dtype.argtypes = [_vp, _i64p, _vp, _vp, _vp, _i64p, _i
 lib.gn_conv3x3_nhwc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _int, _vp, _vp, _vp, _vp, _i64,
                                  _i64, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp]
 lib.gn_conv3x3_plan.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i64p]
+lib.gn_conv3x3_pack_weights.argtypes = [_vp, _vp, _i64, _i64, _vp]
+lib.gn_conv3x3_nhwc_packed.argtypes = lib.gn_conv3x3_nhwc.argtypes
 lib.gn_stats_rows_dtype.argtypes = [_vp, _i64, _i64, _i64, _i64, _f32, _int, _vp, _vp, _vp]
 lib.gn_apply_rows_dtype.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int,
                                     _int, _vp]
@@ -106,7 +108,7 @@ for _name in ("gn_silu_nhwc", "gn_silu_rows", "gn_silu_nhwc_strided", "gn_stats_
               "gn_silu_nhwc_strided_dtype", "gn_stats_rows_dtype", "gn_apply_rows_dtype",
               "gn_profile_rows_dtype", "gn_plan_rows_dtype", "gn_silu_ndhwc",
               "gn_silu_ndhwc_dtype", "gn_silu_ndhwc_strided_dtype", "gn_conv3x3_nhwc",
-              "gn_conv3x3_plan"):
+              "gn_conv3x3_plan", "gn_conv3x3_pack_weights", "gn_conv3x3_nhwc_packed"):
     getattr(lib, _name).restype = _int
 lib.gn_plan_rows.argtypes = [_i64, _i64, _i64, _i64, _i64p]
 lib.gn_plan_rows.restype = _int
@@ -134,6 +136,8 @@ gn_silu_ndhwc_dtype = lib.gn_silu_ndhwc_dtype
 gn_silu_ndhwc_strided_dtype = lib.gn_silu_ndhwc_strided_dtype
 gn_conv3x3_nhwc = lib.gn_conv3x3_nhwc
 gn_conv3x3_plan = lib.gn_conv3x3_plan
+gn_conv3x3_pack_weights = lib.gn_conv3x3_pack_weights
+gn_conv3x3_nhwc_packed = lib.gn_conv3x3_nhwc_packed
 gn_stats_rows_dtype = lib.gn_stats_rows_dtype
 gn_apply_rows_dtype = lib.gn_apply_rows_dtype
 gn_profile_rows_dtype = lib.gn_profile_rows_dtype
@@ -361,6 +365,32 @@ def profile_rows(x, num_groups, weight, bias, eps, apply_silu, out, iters):
     return {lib.gn_kernel_name(i).decode(): float(ms[i]) for i in range(nk.value) if ms[i] >= 0}
 
 
+class PackedConv3x3Weight:
+    """A (Co, Ci, 3, 3) bf16 weight packed once into the library's fragment
+    order (gn_conv3x3_pack_weights), for repeated convolutions."""
+
+    def __init__(self, data, Co, Ci, device):
+        self.data, self.Co, self.Ci, self.device = data, Co, Ci, device
+        self.shape = (Co, Ci, 3, 3)
+        self.dtype = _torch().bfloat16
+
+
+def pack_conv3x3_weight(weight):
+    """Packs a channels_last (Co, Ci, 3, 3) bf16 weight; None if declined."""
+    torch = _torch()
+    if (weight.dim() != 4 or tuple(weight.shape[2:]) != (3, 3) or weight.dtype != torch.bfloat16
+            or weight.device.type != "cuda"
+            or not weight.is_contiguous(memory_format=torch.channels_last)):
+        return None
+    Co, Ci = weight.shape[0], weight.shape[1]
+    packed = torch.empty(Co * 9 * Ci, dtype=torch.bfloat16, device=weight.device)
+    code = lib.gn_conv3x3_pack_weights(_ptr(weight), _ptr(packed), Ci, Co,
+                                       _stream_handle(weight))
+    if _result(code, True) is None:
+        return None
+    return PackedConv3x3Weight(packed, Co, Ci, weight.device)
+
+
 def conv3x3(x, weight, bias=None, *, norm=None, apply_silu=False, residual=None,
             next_groups=None, next_eps=1e-6, out=None):
     """3x3 convolution (padding 1, stride 1) of a channels-last bf16 tensor,
@@ -369,7 +399,7 @@ def conv3x3(x, weight, bias=None, *, norm=None, apply_silu=False, residual=None,
 
     x: (N, Ci, H, W) bf16, channels_last.  weight: (Co, Ci, 3, 3) bf16 in
     channels_last memory format (element [co, ci, kh, kw] at
-    ((co*3 + kh)*3 + kw)*Ci + ci).  bias: fp32 (Co,) or None.  norm: None, or
+    ((co*3 + kh)*3 + kw)*Ci + ci), or a ``PackedConv3x3Weight``.  bias: fp32 (Co,) or None.  norm: None, or
     (mean, rstd, gamma, beta) with fp32 mean/rstd of shape (N, G) (as from
     ``group_stats_rows``) and fp32 gamma/beta of shape (Ci,) or None.
     residual: (N, Co, H, W) bf16 channels_last or None.  next_groups: G2 for
@@ -382,7 +412,8 @@ def conv3x3(x, weight, bias=None, *, norm=None, apply_silu=False, residual=None,
     if not isinstance(x, torch.Tensor) or x.dim() != 4:
         raise ValueError("conv3x3 expects a 4-D (N, Ci, H, W) tensor")
     N, Ci, H, W = x.shape
-    if weight.dim() != 4 or tuple(weight.shape[1:]) != (Ci, 3, 3):
+    packed = isinstance(weight, PackedConv3x3Weight)
+    if tuple(weight.shape[1:]) != (Ci, 3, 3):
         raise ValueError("weight must have shape (Co, Ci, 3, 3)")
     Co = weight.shape[0]
     if (x.device.type != "cuda" or torch.is_grad_enabled() or x.dtype != torch.bfloat16
@@ -390,7 +421,7 @@ def conv3x3(x, weight, bias=None, *, norm=None, apply_silu=False, residual=None,
         return None
     if not x.is_contiguous(memory_format=torch.channels_last):
         return None
-    if not weight.is_contiguous(memory_format=torch.channels_last):
+    if not packed and not weight.is_contiguous(memory_format=torch.channels_last):
         return None
     if bias is not None and (bias.dtype != torch.float32 or bias.numel() != Co
                              or bias.device != x.device):
@@ -418,10 +449,11 @@ def conv3x3(x, weight, bias=None, *, norm=None, apply_silu=False, residual=None,
         G2 = int(next_groups)
         m2 = torch.empty((N, G2), dtype=torch.float32, device=x.device)
         r2 = torch.empty_like(m2)
-    code = lib.gn_conv3x3_nhwc(
+    fn = lib.gn_conv3x3_nhwc_packed if packed else lib.gn_conv3x3_nhwc
+    code = fn(
         _ptr(x), _ptr(nm), _ptr(nr), _ptr(ga), _ptr(be), G, 1 if apply_silu else 0,
-        _ptr(weight), _ptr(bias), _ptr(residual), _ptr(out), N, H, W, Ci, Co, G2,
-        float(next_eps), _ptr(m2), _ptr(r2), _stream_handle(x))
+        _ptr(weight.data if packed else weight), _ptr(bias), _ptr(residual), _ptr(out), N, H, W,
+        Ci, Co, G2, float(next_eps), _ptr(m2), _ptr(r2), _stream_handle(x))
     r = _result(code, out)
     if r is None:
         return None

@@ -627,6 +627,9 @@ gn_status check_conv(const void *x, const float *nmean, const float *nrstd, int6
         if (p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) != 0) return GN_UNSUPPORTED;
     // grid and 32-bit index limits of the kernel
     if (H > (1 << 20) || W > (1 << 20) || N > (1 << 20)) return GN_UNSUPPORTED;
+    // per-sample element offsets of the halo loads are 32-bit
+    if (H * W > 0 && (Ci > (INT32_MAX / (H * W)) || Co > (INT32_MAX / (H * W))))
+        return GN_UNSUPPORTED;
     if (pix > 0) {
         const ConvPlan c = make_conv_plan(N, H, W, Co);
         if (c.grid >= (int64_t{1} << 31) || int64_t{c.tiles_h} * c.tiles_w >= (int64_t{1} << 31))
@@ -635,20 +638,20 @@ gn_status check_conv(const void *x, const float *nmean, const float *nrstd, int6
     return GN_OK;
 }
 
-template <bool PRO, bool SILU>
-void launch_conv_ps(const gnconv::ConvArgs &a, int64_t grid, bool stats, hipStream_t s) {
+template <bool SILU>
+void launch_conv_s(const gnconv::ConvArgs &a, int64_t grid, bool stats, hipStream_t s) {
     const dim3 g(static_cast<unsigned>(grid)), b(gnconv::kThreads);
     const bool res = a.res != nullptr;
     if (stats) {
         if (res)
-            gnconv::gn_conv3x3<PRO, SILU, true, true><<<g, b, 0, s>>>(a);
+            gnconv::gn_conv3x3<SILU, true, true><<<g, b, 0, s>>>(a);
         else
-            gnconv::gn_conv3x3<PRO, SILU, true, false><<<g, b, 0, s>>>(a);
+            gnconv::gn_conv3x3<SILU, true, false><<<g, b, 0, s>>>(a);
     } else {
         if (res)
-            gnconv::gn_conv3x3<PRO, SILU, false, true><<<g, b, 0, s>>>(a);
+            gnconv::gn_conv3x3<SILU, false, true><<<g, b, 0, s>>>(a);
         else
-            gnconv::gn_conv3x3<PRO, SILU, false, false><<<g, b, 0, s>>>(a);
+            gnconv::gn_conv3x3<SILU, false, false><<<g, b, 0, s>>>(a);
     }
 }
 
@@ -842,11 +845,34 @@ gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_
     return st;
 }
 
-gn_status gn_conv3x3_nhwc(const void *x, const float *norm_mean, const float *norm_rstd,
-                          const float *gamma, const float *beta, int64_t G, int apply_silu,
-                          const void *wt, const float *bias, const void *res, void *z, int64_t N,
-                          int64_t H, int64_t W, int64_t Ci, int64_t Co, int64_t G2, float eps2,
-                          float *mean2_out, float *rstd2_out, void *stream) {
+gn_status gn_conv3x3_pack_weights(const void *wt, void *packed, int64_t Ci, int64_t Co,
+                                  void *stream) {
+    if (wt == nullptr || packed == nullptr || Ci <= 0 || Co <= 0) return GN_INVALID_ARGUMENT;
+    if (Ci % gnconv::BK != 0 || Ci > gnconv::kMaxCi || Co % gnconv::BN != 0) return GN_UNSUPPORTED;
+    if ((reinterpret_cast<uintptr_t>(wt) & 15u) != 0 ||
+        (reinterpret_cast<uintptr_t>(packed) & 15u) != 0)
+        return GN_UNSUPPORTED;
+    Call c;
+    gn_status st = begin_call(stream, {wt, packed}, &c);
+    if (st != GN_OK) return st;
+    const int64_t pieces = Co * 9 * Ci / 8;
+    gnconv::gn_conv_pack_weights<<<static_cast<unsigned>(ceil_div(pieces, gnconv::kThreads)),
+                                   gnconv::kThreads, 0, c.stream>>>(
+        static_cast<const uint16_t *>(wt), static_cast<uint16_t *>(packed), static_cast<int>(Ci),
+        pieces);
+    return finish_launch();
+}
+
+namespace gnsilu {
+namespace {
+
+// The convolution with weights either in the [Co][3][3][Ci] layout (packed
+// into the stream's scratch first) or already packed.
+gn_status run_conv(const void *x, const float *norm_mean, const float *norm_rstd,
+                   const float *gamma, const float *beta, int64_t G, int apply_silu,
+                   const void *wt, bool wt_packed, const float *bias, const void *res, void *z,
+                   int64_t N, int64_t H, int64_t W, int64_t Ci, int64_t Co, int64_t G2, float eps2,
+                   float *mean2_out, float *rstd2_out, void *stream) {
     gn_status st = check_conv(x, norm_mean, norm_rstd, G, apply_silu, wt, res, z, N, H, W, Ci,
                               Co, G2, eps2, mean2_out, rstd2_out);
     if (st != GN_OK) return st;
@@ -884,28 +910,58 @@ gn_status gn_conv3x3_nhwc(const void *x, const float *norm_mean, const float *no
     const int64_t tiles_per_sample = int64_t{cp.tiles_h} * cp.tiles_w;
 
     std::unique_lock<std::mutex> lock(scratch_mutex(), std::defer_lock);
-    if (stats) {
+    const size_t pack_bytes = wt_packed ? 0 : align_up(static_cast<size_t>(Co * 9 * Ci) * 2, 256);
+    const size_t part_bytes =
+        stats ? sizeof(float) * 4 * static_cast<size_t>(N * tiles_per_sample * G2) : 0;
+    if (pack_bytes + part_bytes > 0) {
         lock.lock();
         unsigned *counters = nullptr;
         char *payload = nullptr;
-        const size_t bytes = sizeof(float) * 4 * static_cast<size_t>(N * tiles_per_sample * G2);
-        st = scratch_for(c.dev, c.stream, 0, bytes, &counters, &payload);
+        st = scratch_for(c.dev, c.stream, 0, pack_bytes + part_bytes, &counters, &payload);
         if (st != GN_OK) return st;
-        a.part = reinterpret_cast<float *>(payload);
+        if (!wt_packed) {
+            const int64_t pieces = Co * 9 * Ci / 8;
+            gnconv::gn_conv_pack_weights<<<static_cast<unsigned>(
+                                               ceil_div(pieces, gnconv::kThreads)),
+                                           gnconv::kThreads, 0, c.stream>>>(
+                static_cast<const uint16_t *>(wt), reinterpret_cast<uint16_t *>(payload),
+                static_cast<int>(Ci), pieces);
+            a.wt = reinterpret_cast<const uint16_t *>(payload);
+        }
+        if (stats) a.part = reinterpret_cast<float *>(payload + pack_bytes);
     }
-    const bool pro = norm_mean != nullptr || apply_silu;
-    if (pro && apply_silu)
-        launch_conv_ps<true, true>(a, cp.grid, stats, c.stream);
-    else if (pro)
-        launch_conv_ps<true, false>(a, cp.grid, stats, c.stream);
+    if (apply_silu)
+        launch_conv_s<true>(a, cp.grid, stats, c.stream);
     else
-        launch_conv_ps<false, false>(a, cp.grid, stats, c.stream);
+        launch_conv_s<false>(a, cp.grid, stats, c.stream);
     if (stats)
         gnconv::gn_conv_stats_finalize<<<static_cast<unsigned>(N * G2), gnconv::kThreads, 0,
                                          c.stream>>>(a.part, static_cast<int>(tiles_per_sample),
                                                      static_cast<int>(G2), eps2, mean2_out,
                                                      rstd2_out);
     return finish_launch();
+}
+
+}  // namespace
+}  // namespace gnsilu
+
+gn_status gn_conv3x3_nhwc(const void *x, const float *norm_mean, const float *norm_rstd,
+                          const float *gamma, const float *beta, int64_t G, int apply_silu,
+                          const void *wt, const float *bias, const void *res, void *z, int64_t N,
+                          int64_t H, int64_t W, int64_t Ci, int64_t Co, int64_t G2, float eps2,
+                          float *mean2_out, float *rstd2_out, void *stream) {
+    return run_conv(x, norm_mean, norm_rstd, gamma, beta, G, apply_silu, wt, false, bias, res, z,
+                    N, H, W, Ci, Co, G2, eps2, mean2_out, rstd2_out, stream);
+}
+
+gn_status gn_conv3x3_nhwc_packed(const void *x, const float *norm_mean, const float *norm_rstd,
+                                 const float *gamma, const float *beta, int64_t G,
+                                 int apply_silu, const void *packed_wt, const float *bias,
+                                 const void *res, void *z, int64_t N, int64_t H, int64_t W,
+                                 int64_t Ci, int64_t Co, int64_t G2, float eps2,
+                                 float *mean2_out, float *rstd2_out, void *stream) {
+    return run_conv(x, norm_mean, norm_rstd, gamma, beta, G, apply_silu, packed_wt, true, bias,
+                    res, z, N, H, W, Ci, Co, G2, eps2, mean2_out, rstd2_out, stream);
 }
 
 gn_status gn_conv3x3_plan(int64_t N, int64_t H, int64_t W, int64_t Ci, int64_t Co, int64_t G2,

@@ -18,13 +18,18 @@
 // K = 9 taps x Ci.  A workgroup of 256 lanes owns an 8 x 16 pixel x 128
 // channel output tile; each of its four waves owns 64 pixels x 64 channels as
 // 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.  Per chunk of 32 input channels:
-//   * the 10 x 18 pixel halo of the tile is loaded once, normalised (+SiLU)
-//     with per-channel scale/shift held in LDS, rounded to bf16 and stored to
-//     LDS -- every input value is transformed once per chunk, not once per
-//     tap;
-//   * the nine taps run against it, each with its 128 x 32 weight tile in one
-//     of two LDS buffers; the next tap's weights are loaded from global memory
-//     into registers while the current tap's MFMAs run.
+//   * the 10 x 18 pixel halo of the tile is normalised (+SiLU) with
+//     per-channel scale/shift held in LDS, rounded to bf16 and stored to one
+//     of two LDS halo buffers -- every input value is transformed once per
+//     chunk, not once per tap.  The next chunk's halo is loaded into
+//     registers when a chunk starts and normalised into the other buffer
+//     half way through its taps, so the loads and the VALU work overlap the
+//     matrix-core work; one barrier per chunk;
+//   * the nine taps run against it.  Each wave reads its weight fragments
+//     straight from global memory (the 128-channel weight slice of a
+//     workgroup stays in its XCD's L2) into a ring of registers, two taps
+//     ahead of their use, so no weight tile passes through LDS and no tap
+//     needs a barrier.
 // LDS rows are 80 bytes (32 bf16 + 8 padding), so the 16-byte fragment reads
 // of 16 consecutive lanes fall on distinct banks.
 //
@@ -49,11 +54,15 @@ constexpr int BM = TH * TW;                    // 128 output pixels
 constexpr int BN = 128;                        // output channels per workgroup
 constexpr int BK = 32;                         // input channels per chunk
 constexpr int KS = BK + 8;                     // LDS row stride of A and B, bf16 elements
-constexpr int A_ELEMS = HH * HWD * KS;         // 7200 bf16
-constexpr int B_ELEMS = BN * KS;               // 5120 bf16 per tap buffer
+constexpr int A_ELEMS = HH * HWD * KS;         // 7200 bf16 per halo buffer
 constexpr int OS = 72;                         // epilogue fp32 row stride (64 + 8)
 constexpr int kMaxCi = 1024;                   // scale/shift table in LDS
-constexpr int kLdsBytesMain = (A_ELEMS + 2 * B_ELEMS) * 2;   // 34880
+// Packed weights: per (output-channel block, step = chunk * 9 + tap) one run
+// of kPackStep bf16 = 2 k-steps x 2 wave columns x 2 block columns x 64 lanes
+// x 8 values; lane l of block column ni, wave column wn, k-step ks holds
+// wt[cb*128 + wn*64 + ni*32 + l%32][tap][chunk*32 + ks*16 + 8*(l/32) + 0..7].
+constexpr int kPackStep = 2 * 2 * 2 * 64 * 8;  // 4096 bf16 = 8 KiB
+constexpr int kLdsBytesMain = 2 * A_ELEMS * 2;              // 28800: two halo buffers
 constexpr int kLdsBytesEpi = BM * OS * 4;                    // 36864
 constexpr int kLdsBytes = kLdsBytesMain > kLdsBytesEpi ? kLdsBytesMain : kLdsBytesEpi;
 
@@ -69,7 +78,7 @@ struct ConvArgs {
     const float *rstd;      // [N][G]
     const float *gamma;     // [Ci] or null (ones)
     const float *beta;      // [Ci] or null (zeros)
-    const uint16_t *wt;     // [Co][3][3][Ci] bf16
+    const uint16_t *wt;     // weights packed by gn_conv_pack_weights (fragment order)
     const float *bias;      // [Co] or null
     const uint16_t *res;    // [N][H][W][Co] bf16 or null
     uint16_t *z;            // [N][H][W][Co] bf16
@@ -115,16 +124,20 @@ __device__ __forceinline__ bool map_block(const ConvArgs &a, int64_t b, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// PRO: normalise (+SILU) the input on its way into LDS; STATS: output
-// moments; RES: add the residual.
+// SILU: apply SiLU after the normalisation; STATS: output moments; RES: add
+// the residual.  The prologue always runs: without statistics it is the
+// identity scale 1, shift 0 (fmaf(x, 1, 0) == x for every finite x), which
+// costs one fma per input value and keeps every variant on the same
+// instruction schedule -- without the transform between the halo load and
+// its LDS store the compiler drains all outstanding loads at each store.
 // ---------------------------------------------------------------------------
-template <bool PRO, bool SILU, bool STATS, bool RES>
+template <bool SILU, bool STATS, bool RES>
 __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
+    constexpr bool PRO = true;
     __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
-    __shared__ float s_scale[PRO ? kMaxCi : 1];
-    __shared__ float s_shift[PRO ? kMaxCi : 1];
-    uint16_t *sA = reinterpret_cast<uint16_t *>(smem);
-    uint16_t *sB = sA + A_ELEMS;  // two tap buffers of B_ELEMS
+    __shared__ float s_scale[kMaxCi];
+    __shared__ float s_shift[kMaxCi];
+    uint16_t *sA = reinterpret_cast<uint16_t *>(smem);  // two halo buffers of A_ELEMS
     float *sO = reinterpret_cast<float *>(smem);
 
     int64_t tile;
@@ -160,25 +173,77 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
         __syncthreads();
     }
 
-    // B (weights) of one tap and chunk: 128 rows of 32 bf16 = 512 16-byte
-    // pieces, two per lane: piece v -> row v / 4, quarter v % 4.
-    const uint16_t *wbase = a.wt + static_cast<int64_t>(co0) * 9 * Ci;
-    auto load_b = [&](int tap, int ci0, u32x4 (&r)[2]) {
+    // Lane constants of the fragment reads: pixel p = lane % 32 of a 32-pixel
+    // block (2 rows of 16), k offset 8 * (lane / 32); output channel
+    // co0 + wn*64 + ni*32 + lane % 32 for the weights.
+    const int fp = lane & 31, fk = 8 * (lane >> 5);
+    const int frow = fp >> 4, fcol = fp & 15;
+    const int nchunks = Ci / BK;
+    const int nsteps = nchunks * 9;  // (chunk, tap) steps
+
+    // Weight fragments come straight from global memory (L2) into registers,
+    // two steps ahead of their use.  The packed layout puts the 64 lanes'
+    // 16-byte fragments of one (block, step, k-step, wave column, block
+    // column) next to each other, so each load is one contiguous 1 KiB.
+    const uint16_t *wwave = a.wt + static_cast<int64_t>(cb) * nsteps * kPackStep +
+                            wn * 2 * 512 + lane * 8;
+    auto load_w = [&](int step, bf16x8 (&w)[2][2]) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int v = tid + i * kThreads;
-            const int row = v >> 2, q = v & 3;
-            const uint16_t *src = wbase + (static_cast<int64_t>(row) * 9 + tap) * Ci + ci0 + 8 * q;
-            r[i] = *reinterpret_cast<const u32x4 *>(src);
-        }
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                w[ks][ni] = *reinterpret_cast<const bf16x8 *>(
+                    wwave + static_cast<int64_t>(step) * kPackStep + ks * 4 * 512 + ni * 512);
     };
-    auto store_b = [&](int buf, const u32x4 (&r)[2]) {
+
+    // The halo tile of a chunk: 180 pixels x 4 pieces of 8 channels, three
+    // pieces per lane (a lane whose third piece would lie past the last one
+    // redoes the last piece: the same value, written twice).  Loaded into
+    // registers, then normalised and stored to one of the two LDS halo
+    // buffers.  No branches: pixels outside the image load from a clamped
+    // address and become zero by a select, so the whole chunk -- taps,
+    // loads and the transform -- is one basic block the scheduler can
+    // interleave with the matrix-core instructions.
+    constexpr int kPieces = HH * HWD * 4;  // 720
+    int hoff[3], hq[3];
+    bool hin[3];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int v = tid + i * kThreads;
-            const int row = v >> 2, q = v & 3;
-            *reinterpret_cast<u32x4 *>(sB + buf * B_ELEMS + row * KS + 8 * q) = r[i];
+    for (int i = 0; i < 3; ++i) {
+        const int v = min(tid + i * kThreads, kPieces - 1);
+        const int p = v >> 2, q = v & 3;
+        const int ih = h0 - 1 + p / HWD, iw = w0 - 1 + p % HWD;
+        hin[i] = ih >= 0 && ih < a.H && iw >= 0 && iw < a.W;
+        const int ihc = min(max(ih, 0), a.H - 1), iwc = min(max(iw, 0), a.W - 1);
+        hoff[i] = p * KS + 8 * q;           // LDS offset
+        hq[i] = (ihc * a.W + iwc) * Ci + 8 * q;  // element offset within the sample
+    }
+    const uint16_t *xs = a.x + static_cast<int64_t>(n) * a.H * a.W * Ci;
+    auto load_halo = [&](int k, u32x4 (&raw)[3]) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+            raw[i] = *reinterpret_cast<const u32x4 *>(xs + hq[i] + k * BK);
+    };
+    auto store_piece = [&](int k, uint16_t *dst, const u32x4 &raw, int i) {
+        u32x4 out;
+        if constexpr (PRO) {
+            const int c = k * BK + (hoff[i] % KS);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float lo = bf16_to_f32(raw[e] & 0xffffu);
+                float hi = bf16_to_f32(raw[e] >> 16);
+                lo = fmaf(lo, s_scale[c + 2 * e], s_shift[c + 2 * e]);
+                hi = fmaf(hi, s_scale[c + 2 * e + 1], s_shift[c + 2 * e + 1]);
+                if constexpr (SILU) {
+                    lo = silu(lo);
+                    hi = silu(hi);
+                }
+                out[e] = pack_bf16x2(lo, hi);
+            }
+        } else {
+            out = raw;
         }
+        const u32x4 zero = u32x4{0u, 0u, 0u, 0u};  // zero padding of y
+        *reinterpret_cast<u32x4 *>(dst + hoff[i]) = hin[i] ? out : zero;
     };
 
     f32x16 acc[2][2];
@@ -189,104 +254,55 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int nchunks = Ci / BK;
-    int buf = 0;
+    bf16x8 wq[3][2][2];  // ring of weight fragments: step s in slot s % 3
     {
-        u32x4 r[2];
-        load_b(0, 0, r);
-        store_b(0, r);
+        u32x4 raw[3];
+        load_halo(0, raw);
+        load_w(0, wq[0]);
+        load_w(min(1, nsteps - 1), wq[1]);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) store_piece(0, sA, raw[i], i);
     }
-    // Lane constants of the fragment reads: pixel p = lane % 32 of a 32-pixel
-    // block (2 rows of 16), k offset 8 * (lane / 32).
-    const int fp = lane & 31, fk = 8 * (lane >> 5);
-    const int frow = fp >> 4, fcol = fp & 15;
+    __syncthreads();
 
     for (int k = 0; k < nchunks; ++k) {
-        const int ci0 = k * BK;
-        // ---- the halo tile of this chunk: 180 pixels x 4 pieces of 8 channels
-        {
-            constexpr int kPieces = HH * HWD * 4;  // 720
-            u32x4 raw[3];
-            bool inside[3];
+        const uint16_t *a_cur = sA + (k & 1) * A_ELEMS;
+        uint16_t *a_next = sA + ((k + 1) & 1) * A_ELEMS;
+        // The next chunk's halo (the last chunk reloads its own: harmless,
+        // it goes to the buffer no one reads again).
+        const int kn = min(k + 1, nchunks - 1);
+        u32x4 raw[3];
+        load_halo(kn, raw);
+        // Keep the loads where they are issued: left to itself the scheduler
+        // sinks them next to their first use to save registers, which turns
+        // the prefetch into a stall.
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                const int v = tid + i * kThreads;
-                inside[i] = false;
-                raw[i] = u32x4{0u, 0u, 0u, 0u};
-                if (v < kPieces) {
-                    const int p = v >> 2, q = v & 3;
-                    const int ih = h0 - 1 + p / HWD, iw = w0 - 1 + p % HWD;
-                    if (ih >= 0 && ih < a.H && iw >= 0 && iw < a.W) {
-                        inside[i] = true;
-                        raw[i] = *reinterpret_cast<const u32x4 *>(
-                            a.x + ((static_cast<int64_t>(n) * a.H + ih) * a.W + iw) * Ci + ci0 +
-                            8 * q);
-                    }
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                const int v = tid + i * kThreads;
-                if (v < kPieces) {
-                    const int p = v >> 2, q = v & 3;
-                    u32x4 out = u32x4{0u, 0u, 0u, 0u};  // zero padding of y
-                    if (inside[i]) {
-                        if constexpr (PRO) {
-                            const int c = ci0 + 8 * q;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                float lo = bf16_to_f32(raw[i][e] & 0xffffu);
-                                float hi = bf16_to_f32(raw[i][e] >> 16);
-                                lo = fmaf(lo, s_scale[c + 2 * e], s_shift[c + 2 * e]);
-                                hi = fmaf(hi, s_scale[c + 2 * e + 1], s_shift[c + 2 * e + 1]);
-                                if constexpr (SILU) {
-                                    lo = silu(lo);
-                                    hi = silu(hi);
-                                }
-                                out[e] = pack_bf16x2(lo, hi);
-                            }
-                        } else {
-                            out = raw[i];
-                        }
-                    }
-                    *reinterpret_cast<u32x4 *>(sA + p * KS + 8 * q) = out;
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- nine taps
         for (int t = 0; t < 9; ++t) {
-            const bool more = (t < 8) || (k + 1 < nchunks);
-            u32x4 nb[2];
-            if (more) load_b(t < 8 ? t + 1 : 0, t < 8 ? ci0 : ci0 + BK, nb);
+            const int s = k * 9 + t;
+            // slots rotate with t; 9 is a multiple of 3, so slot = t % 3.
+            // Past the last step the last step's weights are reloaded.
+            load_w(min(s + 2, nsteps - 1), wq[(t + 2) % 3]);
+            __builtin_amdgcn_sched_barrier(0);
             const int kh = t / 3, kw = t % 3;
-            const uint16_t *b_cur = sB + buf * B_ELEMS;
 #pragma unroll
-            for (int kk = 0; kk < BK; kk += 16) {
-                bf16x8 af[2], bfr[2];
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8 af[2];
 #pragma unroll
                 for (int mi = 0; mi < 2; ++mi) {
-                    const int r0 = wm * 4 + mi * 2;
-                    const int hp = (r0 + frow + kh) * HWD + fcol + kw;
-                    af[mi] = *reinterpret_cast<const bf16x8 *>(sA + hp * KS + kk + fk);
-                }
-#pragma unroll
-                for (int ni = 0; ni < 2; ++ni) {
-                    const int col = wn * 64 + ni * 32 + fp;
-                    bfr[ni] = *reinterpret_cast<const bf16x8 *>(b_cur + col * KS + kk + fk);
+                    const int hp = (wm * 4 + mi * 2 + frow + kh) * HWD + fcol + kw;
+                    af[mi] = *reinterpret_cast<const bf16x8 *>(a_cur + hp * KS + 16 * ks + fk);
                 }
 #pragma unroll
                 for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
                     for (int ni = 0; ni < 2; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni],
-                                                                             acc[mi][ni], 0, 0, 0);
+                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            af[mi], wq[t % 3][ks][ni], acc[mi][ni], 0, 0, 0);
             }
-            if (more) store_b(buf ^ 1, nb);
-            __syncthreads();
-            buf ^= 1;
+            if (t == 2 || t == 4 || t == 6) store_piece(kn, a_next, raw[t / 2 - 1], t / 2 - 1);
         }
+        __syncthreads();  // a_next written by all lanes; a_cur no longer read
     }
 
     // ---- epilogue, 64 output channels at a time
@@ -417,6 +433,32 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
             __syncthreads();  // red and gmean free for the next half
         }
     }
+}
+
+// Packs [Co][3][3][Ci] bf16 weights into the fragment order above: one lane
+// per 16-byte piece of the packed array.
+__global__ __launch_bounds__(kThreads) void gn_conv_pack_weights(const uint16_t *__restrict__ wt,
+                                                                 uint16_t *__restrict__ packed,
+                                                                 int Ci, int64_t pieces) {
+    const int64_t v = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (v >= pieces) return;
+    // v = ((((cb * nsteps + step) * 2 + ks) * 2 + wn) * 2 + ni) * 64 + lane
+    const int lane = static_cast<int>(v & 63);
+    int64_t r = v >> 6;
+    const int ni = static_cast<int>(r & 1);
+    r >>= 1;
+    const int wn = static_cast<int>(r & 1);
+    r >>= 1;
+    const int ks = static_cast<int>(r & 1);
+    r >>= 1;
+    const int nsteps = (Ci / BK) * 9;
+    const int step = static_cast<int>(r % nsteps);
+    const int64_t cb = r / nsteps;
+    const int k = step / 9, t = step % 9;
+    const int64_t co = cb * BN + wn * 64 + ni * 32 + (lane & 31);
+    const int ci = k * BK + ks * 16 + 8 * (lane >> 5);
+    *reinterpret_cast<u32x4 *>(packed + v * 8) =
+        *reinterpret_cast<const u32x4 *>(wt + (co * 9 + t) * Ci + ci);
 }
 
 // Merge of the per-tile (count, mean, M2) of each (n, group) into fp32 mean

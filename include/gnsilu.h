@@ -263,6 +263,25 @@ gn_status gn_conv3x3_nhwc(const void *x, const float *norm_mean, const float *no
                           int64_t G2, float eps2, float *mean2_out, float *rstd2_out,
                           void *stream);
 
+/* The weights of gn_conv3x3_nhwc reach the matrix cores in a packed order
+ * (per 128 output channels, per chunk of 32 input channels and tap, the
+ * 16-byte fragments of each wave next to each other); gn_conv3x3_nhwc packs
+ * them into the stream's scratch buffer on every call (one extra kernel,
+ * 2*Co*9*Ci bytes read and written).  A caller whose weights do not change
+ * packs them once with gn_conv3x3_pack_weights -- wt: bf16 [Co][3][3][Ci],
+ * packed: a device buffer of the same size (Co*9*Ci bf16), 16-byte aligned;
+ * same support checks as the convolution -- and passes the packed buffer to
+ * gn_conv3x3_nhwc_packed, which is gn_conv3x3_nhwc without the packing
+ * step.  The packed order is internal to this library version. */
+gn_status gn_conv3x3_pack_weights(const void *wt, void *packed, int64_t Ci, int64_t Co,
+                                  void *stream);
+gn_status gn_conv3x3_nhwc_packed(const void *x, const float *norm_mean, const float *norm_rstd,
+                                 const float *gamma, const float *beta, int64_t G,
+                                 int apply_silu, const void *packed_wt, const float *bias,
+                                 const void *res, void *z, int64_t N, int64_t H, int64_t W,
+                                 int64_t Ci, int64_t Co, int64_t G2, float eps2,
+                                 float *mean2_out, float *rstd2_out, void *stream);
+
 /* Launch shape of gn_conv3x3_nhwc for a problem, for inspection and tests;
  * no HIP call.  G2 > 0 asks for the statistics output.  Writes 6 values:
  * [0] tiles_h = ceil(H/8), [1] tiles_w = ceil(W/16) (output tiles of 8x16

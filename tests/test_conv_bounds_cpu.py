@@ -2,11 +2,11 @@
 
 gn_conv3x3_plan gives the launch shape; the kernel's index arithmetic is
 replayed here with its tile constants (8 x 16 output pixels, 128 output
-channels, chunks of 32 input channels, LDS rows of 40 bf16, epilogue rows of
-72 fp32): the workgroup -> (tile, channel block) map covers every pair once,
-the halo, weight, residual and output addresses stay inside their tensors,
-every LDS index stays inside its array, and the statistics partials stay
-inside their buffer.
+channels, chunks of 32 input channels, two LDS halo buffers with rows of 40
+bf16, epilogue rows of 72 fp32): the workgroup -> (tile, channel block) map
+covers every pair once, the halo, weight-fragment, residual and output
+addresses stay inside their tensors, every LDS index stays inside its array,
+and the statistics partials stay inside their buffer.
 """
 import numpy as np
 import pytest
@@ -15,8 +15,9 @@ gn = pytest.importorskip("groupnorm_silu_normalization_amd")
 
 TH, TW, BN, BK, KS, OS = 8, 16, 128, 32, 40, 72
 HH, HWD = TH + 2, TW + 2
-A_ELEMS, B_ELEMS = HH * HWD * KS, BN * KS
-LDS_MAIN = A_ELEMS + 2 * B_ELEMS            # bf16 elements
+A_ELEMS = HH * HWD * KS
+PACK_STEP = 2 * 2 * 2 * 64 * 8             # packed weights per (block, step)
+LDS_MAIN = 2 * A_ELEMS                      # bf16 elements: two halo buffers
 LDS_EPI_FLOATS = TH * TW * OS
 
 SHAPES = [  # N, H, W, Ci, Co, G2
@@ -57,24 +58,45 @@ def test_conv_plan_and_indices_in_bounds(N, H, W, Ci, Co, G2):
     live = v < HH * HWD * 4
     pix, q = v // 4, v % 4
     assert np.all((pix * KS + 8 * q + 8)[live] <= A_ELEMS)
-    # fragment reads: wave (wm, wn), block mi/ni, lane -> halo pixel, k offset
+    # halo fragment reads: wave (wm, wn), block mi, lane -> halo pixel, k offset,
+    # in either halo buffer
     lane = np.arange(64)
     fp, fk = lane % 32, 8 * (lane // 32)
-    for wm in (0, 1):
-        for mi in (0, 1):
-            for kh in range(3):
-                for kw in range(3):
-                    hp = (wm * 4 + mi * 2 + fp // 16 + kh) * HWD + fp % 16 + kw
-                    assert np.all(hp * KS + 16 + fk + 8 <= A_ELEMS)
-    col = np.arange(128)
-    assert np.all(col * KS + 16 + 8 + 8 <= B_ELEMS)
-    # weight pieces of a tap: 128 rows x 4 pieces, two per lane, inside the block's slice
-    v2 = np.arange(512)
-    row, q2 = v2 // 4, v2 % 4
-    for tap in (0, 8):
-        for ci0 in (0, Ci - BK):
-            off = (row * 9 + tap) * Ci + ci0 + 8 * q2
-            assert off.min() >= 0 and (off + 8).max() <= BN * 9 * Ci
+    for buf in (0, 1):
+        for wm in (0, 1):
+            for mi in (0, 1):
+                for kh in range(3):
+                    for kw in range(3):
+                        hp = (wm * 4 + mi * 2 + fp // 16 + kh) * HWD + fp % 16 + kw
+                        assert np.all(buf * A_ELEMS + hp * KS + 16 + fk + 8 <= LDS_MAIN)
+                        assert np.all(hp < HH * HWD)
+    # packed weight fragments, read from global memory: block cb, step s,
+    # k-step ks, wave column wn, block column ni, lane -> 8 bf16 at
+    # (cb*nsteps + s)*4096 + ((ks*2 + wn)*2 + ni)*512 + lane*8
+    nsteps = Ci // BK * 9
+    for cb in (0, Co // BN - 1):
+        for wn in (0, 1):
+            for ni in (0, 1):
+                for step in (0, 1, nsteps - 1):
+                    for ks in (0, 1):
+                        off = (cb * nsteps + step) * PACK_STEP + ((ks * 2 + wn) * 2 + ni) * 512 \
+                            + lane * 8
+                        assert off.min() >= 0 and (off + 8).max() <= Co * 9 * Ci
+    # the packing kernel's map is a bijection from packed pieces onto the
+    # weight tensor's 16-byte pieces
+    if Co * 9 * Ci <= 128 * 9 * 1024:
+        v = np.arange(Co * 9 * Ci // 8)
+        lane_, r = v % 64, v // 64
+        ni_, r = r % 2, r // 2
+        wn_, r = r % 2, r // 2
+        ks_, r = r % 2, r // 2
+        step_, cb_ = r % nsteps, r // nsteps
+        k_, t_ = step_ // 9, step_ % 9
+        co = cb_ * BN + wn_ * 64 + ni_ * 32 + lane_ % 32
+        ci = k_ * BK + ks_ * 16 + 8 * (lane_ // 32)
+        src = (co * 9 + t_) * Ci + ci
+        assert src.min() >= 0 and (src + 8).max() <= Co * 9 * Ci
+        assert np.array_equal(np.sort(src // 8), np.arange(Co * 9 * Ci // 8))
     # epilogue staging and the statistics scratch in the same LDS
     r = np.arange(16)
     m = 8 * (r[:, None] // 4) + 4 * (lane[None, :] // 32) + r[:, None] % 4
@@ -106,3 +128,5 @@ def test_conv_plan_declines():
     with pytest.raises(ValueError):
         gn.conv_plan(1, 8, 8, 64, 128, 3)                    # Co % G2 != 0
     assert gn.conv_plan(0, 8, 8, 64, 128)["grid"] == 0       # empty: nothing launched
+    assert gn.conv_plan(1, 2048, 2048, 512, 128) is None      # sample of 2^31 elements
+    assert gn.conv_plan(1, 2048, 1024, 512, 128) is not None  # 2^30: 32-bit offsets hold

@@ -228,6 +228,68 @@ def test_deterministic(gn, dev):
         assert np.array_equal(m2, outs[0][1]) and np.array_equal(r2, outs[0][2])
 
 
+def test_packed_weights_give_the_same_output(gn, dev):
+    """Packing once (gn_conv3x3_pack_weights) and calling the packed entry
+    gives the unpacked entry's output bit for bit."""
+    N, H, W, Ci, Co, G, G2 = 1, 21, 37, 96, 256, 32, 32
+    x, gamma, beta, wb, bias, r = make_problem(N, H, W, Ci, Co, seed=650, res=True)
+    xd = bits_dev(x, (N, H, W, Ci), dev).permute(0, 3, 1, 2)
+    wd = bits_dev(wb, (Co, 3, 3, Ci), dev).permute(0, 3, 1, 2)
+    bd = torch.from_numpy(bias).to(dev)
+    rd = bits_dev(r, (N, H, W, Co), dev).permute(0, 3, 1, 2)
+    with torch.no_grad():
+        mean, rstd = gn.group_stats_rows(xd.permute(0, 2, 3, 1).reshape(N, H * W, Ci), G, 1e-6)
+        nrm = (mean, rstd, torch.from_numpy(gamma).to(dev), torch.from_numpy(beta).to(dev))
+        pw = gn.pack_conv3x3_weight(wd)
+        assert pw is not None
+        a = gn.conv3x3(xd, wd, bd, norm=nrm, apply_silu=True, residual=rd, next_groups=G2)
+        b = gn.conv3x3(xd, pw, bd, norm=nrm, apply_silu=True, residual=rd, next_groups=G2)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+
+
+def test_resnet_block_in_a_hip_graph(gn, dev):
+    """The fused ResnetBlock2D sequence (statistics, conv1 with GroupNorm+SiLU
+    and output statistics, conv2 with GroupNorm+SiLU and the shortcut)
+    captured into a HIP graph: every replay, with eager work of the same
+    library between replays, equals the eager result bit for bit."""
+    N, H, W, C, G = 1, 24, 40, 128, 32
+    x, gamma, beta, wb, bias, _ = make_problem(N, H, W, C, C, seed=800)
+    xd = bits_dev(x, (N, H, W, C), dev).permute(0, 3, 1, 2)
+    wd = bits_dev(wb, (C, 3, 3, C), dev).permute(0, 3, 1, 2)
+    bd = torch.from_numpy(bias).to(dev)
+    ga = torch.from_numpy(gamma).to(dev)
+    be = torch.from_numpy(beta).to(dev)
+    rows = xd.permute(0, 2, 3, 1).reshape(N, H * W, C)
+    stream = torch.cuda.Stream(dev)
+
+    def block():
+        m1, r1 = gn.group_stats_rows(rows, G, 1e-6)
+        h, m2, r2 = gn.conv3x3(xd, pw, bd, norm=(m1, r1, ga, be), apply_silu=True, next_groups=G)
+        return gn.conv3x3(h, pw, bd, norm=(m2, r2, ga, be), apply_silu=True, residual=xd)
+
+    with torch.no_grad():
+        pw = gn.pack_conv3x3_weight(wd)
+        with torch.cuda.stream(stream):
+            ref = block().clone()
+            for _ in range(2):
+                block()
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            out = block()
+        for rep in range(4):
+            with torch.cuda.stream(stream):
+                g.replay()
+            stream.synchronize()
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "replay %d" % rep
+            with torch.cuda.stream(stream):
+                other = block()          # eager work between replays
+            stream.synchronize()
+            assert torch.equal(other.view(torch.int16), ref.view(torch.int16))
+
+
 def test_unsupported_and_invalid(gn, dev):
     x = torch.zeros(1, 48, 8, 8, device=dev, dtype=torch.bfloat16).to(
         memory_format=torch.channels_last)
