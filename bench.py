@@ -53,6 +53,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gn_silu_1x256x1024x1024.j
 KERNEL_SOURCES = [
     os.path.join(ROOT, "groupnorm_silu_normalization_amd", "csrc", "gn_kernels.hpp"),
     os.path.join(ROOT, "groupnorm_silu_normalization_amd", "csrc", "gn_api.hip"),
+    os.path.join(ROOT, "groupnorm_silu_normalization_amd", "csrc", "gn_conv.hpp"),
 ]
 
 
@@ -227,30 +228,42 @@ def resnet_block(torch, gn, dev, shp, args):
 
     steps = max(5, min(args.steps, 30))
     gstream = torch.cuda.Stream(dev)
+
+    def best(fn, s, rounds):
+        return min(time_events(torch, fn, steps, 3, s) for _ in range(rounds))
+
     with torch.no_grad():
         for f in (fused, unfused, torch_conv):
             if f() is None:
                 raise RuntimeError("resnet block declined")
-        t_fe = time_events(torch, fused, steps, 3, stream)
-        t_ue = time_events(torch, unfused, steps, 3, stream)
         g_f = graph_of(torch, fused, gstream)
         g_u = graph_of(torch, unfused, gstream)
+        # clocks up before anything is timed; then each variant twice, in
+        # alternating order, best of the two (no order bias)
         with torch.cuda.stream(gstream):
-            t_f = time_events(torch, g_f.replay, steps, 3, gstream)
-            t_u = time_events(torch, g_u.replay, steps, 3, gstream)
-        t_t = time_events(torch, torch_conv, steps, 3, stream)
-        t_c1 = time_events(torch, conv1_fused, steps, 3, stream)
-        t_cp = time_events(torch, conv_plain, steps, 3, stream)
-        t_cu = time_events(torch, conv_unpacked, steps, 3, stream)
-        t_tc = time_events(torch, lambda: torch.nn.functional.conv2d(x, ws[0], bb[0], padding=1),
-                           steps, 3, stream)
+            for _ in range(30):
+                g_u.replay()
+        gstream.synchronize()
+        t_f = t_u = t_fe = t_ue = float("inf")
+        for _ in range(2):
+            with torch.cuda.stream(gstream):
+                t_f = min(t_f, time_events(torch, g_f.replay, steps, 3, gstream))
+                t_u = min(t_u, time_events(torch, g_u.replay, steps, 3, gstream))
+            t_fe = min(t_fe, time_events(torch, fused, steps, 3, stream))
+            t_ue = min(t_ue, time_events(torch, unfused, steps, 3, stream))
+        t_t = best(torch_conv, stream, 2)
+        t_c1 = best(conv1_fused, stream, 2)
+        t_cp = best(conv_plain, stream, 2)
+        t_cu = best(conv_unpacked, stream, 2)
+        t_tc = best(lambda: torch.nn.functional.conv2d(x, ws[0], bb[0], padding=1), stream, 2)
     flops = 2.0 * N * H * W * C * 9 * C
     tf = flops / (t_c1 * 1e-3) / 1e12
     return {
         "shape_nchw": [N, C, H, W],
         "fused_us": round(t_f * 1e3, 1),
         "unfused_us": round(t_u * 1e3, 1),
-        "timing": "fused_us / unfused_us: HIP-graph replays; *_eager_us: eager calls",
+        "timing": "fused_us / unfused_us: HIP-graph replays; *_eager_us: eager calls; "
+                  "each the best of two rounds in alternating order after a warm-up",
         "fused_eager_us": round(t_fe * 1e3, 1),
         "unfused_eager_us": round(t_ue * 1e3, 1),
         "torch_conv_us": round(t_t * 1e3, 1),

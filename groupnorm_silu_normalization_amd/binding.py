@@ -460,11 +460,11 @@ def conv3x3(x, weight, bias=None, *, norm=None, apply_silu=False, residual=None,
     return (out, m2, r2) if next_groups is not None else out
 
 
-CONV_PLAN_FIELDS = ("tiles_h", "tiles_w", "nb", "xcd_map", "blocks", "grid")
+CONV_PLAN_FIELDS = ("tiles_h", "tiles_w", "nb", "xcd_map", "blocks", "grid", "wn")
 
 
 def conv_plan(N, H, W, Ci, Co, G2=0):
     """The library's launch shape for gn_conv3x3_nhwc (dict), or None if declined."""
-    buf = (_i64 * 6)()
+    buf = (_i64 * len(CONV_PLAN_FIELDS))()
     r = _result(lib.gn_conv3x3_plan(N, H, W, Ci, Co, G2, buf), True)
     return None if r is None else dict(zip(CONV_PLAN_FIELDS, list(buf)))

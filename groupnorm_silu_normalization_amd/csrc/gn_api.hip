@@ -582,15 +582,22 @@ gn_status run_strided(const void *x, const int64_t *x_strides, const float *gamm
 // Launch shape of gn_conv3x3 for a problem: real workgroups, grid size and
 // whether the XCD-aware block order applies.
 struct ConvPlan {
-    int tiles_h, tiles_w, nb, xcd_map;
+    int tiles_h, tiles_w, nb, xcd_map, wn;
     int64_t blocks, grid;
 };
 
+// wn = 2: 128 output channels per workgroup of 256 lanes.  Workgroups of 512
+// lanes over 256 channels (wn = 4, the kernel's other shape) halve the
+// prologue's work per output but measured 7-10% slower on MI355X at the
+// decoder shapes (one 8-wave barrier per chunk, half the workgroups), so the
+// plan does not use them.
 ConvPlan make_conv_plan(int64_t N, int64_t H, int64_t W, int64_t Co) {
     ConvPlan c;
     c.tiles_h = static_cast<int>(ceil_div(H, gnconv::TH));
     c.tiles_w = static_cast<int>(ceil_div(W, gnconv::TW));
-    c.nb = static_cast<int>(Co / gnconv::BN);
+    c.wn = 2;
+    (void)Co;
+    c.nb = static_cast<int>(Co / (64 * c.wn));
     const int64_t tiles = N * c.tiles_h * c.tiles_w;
     c.blocks = tiles * c.nb;
     c.xcd_map = (8 % c.nb == 0) ? 1 : 0;
@@ -638,21 +645,29 @@ gn_status check_conv(const void *x, const float *nmean, const float *nrstd, int6
     return GN_OK;
 }
 
-template <bool SILU>
-void launch_conv_s(const gnconv::ConvArgs &a, int64_t grid, bool stats, hipStream_t s) {
-    const dim3 g(static_cast<unsigned>(grid)), b(gnconv::kThreads);
+template <int WN, bool SILU>
+void launch_conv_ws(const gnconv::ConvArgs &a, int64_t grid, bool stats, hipStream_t s) {
+    const dim3 g(static_cast<unsigned>(grid)), b(128 * WN);
     const bool res = a.res != nullptr;
     if (stats) {
         if (res)
-            gnconv::gn_conv3x3<SILU, true, true><<<g, b, 0, s>>>(a);
+            gnconv::gn_conv3x3<WN, SILU, true, true><<<g, b, 0, s>>>(a);
         else
-            gnconv::gn_conv3x3<SILU, true, false><<<g, b, 0, s>>>(a);
+            gnconv::gn_conv3x3<WN, SILU, true, false><<<g, b, 0, s>>>(a);
     } else {
         if (res)
-            gnconv::gn_conv3x3<SILU, false, true><<<g, b, 0, s>>>(a);
+            gnconv::gn_conv3x3<WN, SILU, false, true><<<g, b, 0, s>>>(a);
         else
-            gnconv::gn_conv3x3<SILU, false, false><<<g, b, 0, s>>>(a);
+            gnconv::gn_conv3x3<WN, SILU, false, false><<<g, b, 0, s>>>(a);
     }
+}
+
+void launch_conv(const gnconv::ConvArgs &a, int64_t grid, bool silu, bool stats,
+                 hipStream_t s) {
+    if (silu)
+        launch_conv_ws<2, true>(a, grid, stats, s);
+    else
+        launch_conv_ws<2, false>(a, grid, stats, s);
 }
 
 }  // namespace gnsilu
@@ -930,10 +945,7 @@ gn_status run_conv(const void *x, const float *norm_mean, const float *norm_rstd
         }
         if (stats) a.part = reinterpret_cast<float *>(payload + pack_bytes);
     }
-    if (apply_silu)
-        launch_conv_s<true>(a, cp.grid, stats, c.stream);
-    else
-        launch_conv_s<false>(a, cp.grid, stats, c.stream);
+    launch_conv(a, cp.grid, apply_silu != 0, stats, c.stream);
     if (stats)
         gnconv::gn_conv_stats_finalize<<<static_cast<unsigned>(N * G2), gnconv::kThreads, 0,
                                          c.stream>>>(a.part, static_cast<int>(tiles_per_sample),
@@ -965,7 +977,7 @@ gn_status gn_conv3x3_nhwc_packed(const void *x, const float *norm_mean, const fl
 }
 
 gn_status gn_conv3x3_plan(int64_t N, int64_t H, int64_t W, int64_t Ci, int64_t Co, int64_t G2,
-                          int64_t plan_out[6]) {
+                          int64_t plan_out[7]) {
     if (plan_out == nullptr) return GN_INVALID_ARGUMENT;
     static const uint16_t probe[8] __attribute__((aligned(16))) = {};
     static float fprobe[4];
@@ -973,7 +985,7 @@ gn_status gn_conv3x3_plan(int64_t N, int64_t H, int64_t W, int64_t Ci, int64_t C
                                     W, Ci, Co, G2, 0.0f, G2 > 0 ? fprobe : nullptr,
                                     G2 > 0 ? fprobe : nullptr);
     if (st != GN_OK) return st;
-    for (int i = 0; i < 6; ++i) plan_out[i] = 0;
+    for (int i = 0; i < 7; ++i) plan_out[i] = 0;
     if (N * H * W == 0) return GN_OK;
     const ConvPlan c = make_conv_plan(N, H, W, Co);
     plan_out[0] = c.tiles_h;
@@ -982,6 +994,7 @@ gn_status gn_conv3x3_plan(int64_t N, int64_t H, int64_t W, int64_t Ci, int64_t C
     plan_out[3] = c.xcd_map;
     plan_out[4] = c.blocks;
     plan_out[5] = c.grid;
+    plan_out[6] = c.wn;
     return GN_OK;
 }
 

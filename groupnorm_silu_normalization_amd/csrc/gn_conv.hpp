@@ -85,7 +85,7 @@ struct ConvArgs {
     float *part;            // [N][tiles][G2][4]: count, mean, M2, 0 (statistics only)
     int N, H, W, Ci, Co, G, G2;
     int tiles_h, tiles_w;   // ceil(H/8), ceil(W/16)
-    int nb;                 // Co / 128 output-channel blocks
+    int nb;                 // Co / (64*WN) output-channel blocks
     int xcd_map;            // 1: XCD-aware block order (nb divides 8)
     int64_t blocks;         // N * tiles_h * tiles_w * nb (real workgroups)
 };
@@ -131,9 +131,18 @@ __device__ __forceinline__ bool map_block(const ConvArgs &a, int64_t b, int64_t 
 // instruction schedule -- without the transform between the halo load and
 // its LDS store the compiler drains all outstanding loads at each store.
 // ---------------------------------------------------------------------------
-template <bool SILU, bool STATS, bool RES>
-__global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
+// WN waves along the output channels: a workgroup of 128*WN lanes owns
+// 64*WN output channels (WN = 2: 128 channels, 4 waves; WN = 4: 256 channels,
+// 8 waves).  Each wave's share is the same 64 x 64 block either way; with
+// WN = 4 the normalised halo of a chunk serves twice as many outputs, so the
+// prologue's loads and transcendentals per output halve.
+template <int WN, bool SILU, bool STATS, bool RES>
+__global__ __launch_bounds__(128 * WN) void gn_conv3x3(ConvArgs a) {
     constexpr bool PRO = true;
+    constexpr int NT = 128 * WN;             // lanes
+    constexpr int BNW = 64 * WN;             // output channels of the workgroup
+    constexpr int ROWS = NT / 8;             // epilogue: lanes per 8-channel piece
+    constexpr int PIX = BM / ROWS;           // epilogue: pixels per lane
     __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
     __shared__ float s_scale[kMaxCi];
     __shared__ float s_shift[kMaxCi];
@@ -148,24 +157,24 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
     const int tin = static_cast<int>(tile - static_cast<int64_t>(n) * tiles_per_sample);
     const int h0 = (tin / a.tiles_w) * TH;
     const int w0 = (tin % a.tiles_w) * TW;
-    const int co0 = cb * BN;
+    const int co0 = cb * BNW;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int Ci = a.Ci;
 
     if constexpr (PRO) {
         if (a.mean) {
             const int Cg = Ci / a.G;
-            for (int c = tid; c < Ci; c += kThreads) {
+            for (int c = tid; c < Ci; c += NT) {
                 const int gi = n * a.G + c / Cg;
                 const float sc = (a.gamma ? a.gamma[c] : 1.0f) * a.rstd[gi];
                 s_scale[c] = sc;
                 s_shift[c] = fmaf(-a.mean[gi], sc, a.beta ? a.beta[c] : 0.0f);
             }
         } else {
-            for (int c = tid; c < Ci; c += kThreads) {
+            for (int c = tid; c < Ci; c += NT) {
                 s_scale[c] = 1.0f;
                 s_shift[c] = 0.0f;
             }
@@ -185,8 +194,9 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
     // two steps ahead of their use.  The packed layout puts the 64 lanes'
     // 16-byte fragments of one (block, step, k-step, wave column, block
     // column) next to each other, so each load is one contiguous 1 KiB.
-    const uint16_t *wwave = a.wt + static_cast<int64_t>(cb) * nsteps * kPackStep +
-                            wn * 2 * 512 + lane * 8;
+    // (packed in 128-channel blocks: wave column wn reads block co0/128 + wn/2)
+    const uint16_t *wwave = a.wt + static_cast<int64_t>(co0 / BN + wn / 2) * nsteps * kPackStep +
+                            (wn % 2) * 2 * 512 + lane * 8;
     auto load_w = [&](int step, bf16x8 (&w)[2][2]) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -196,8 +206,8 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
                     wwave + static_cast<int64_t>(step) * kPackStep + ks * 4 * 512 + ni * 512);
     };
 
-    // The halo tile of a chunk: 180 pixels x 4 pieces of 8 channels, three
-    // pieces per lane (a lane whose third piece would lie past the last one
+    // The halo tile of a chunk: 180 pixels x 4 pieces of 8 channels, PP
+    // pieces per lane (a lane whose last piece would lie past the last one
     // redoes the last piece: the same value, written twice).  Loaded into
     // registers, then normalised and stored to one of the two LDS halo
     // buffers.  No branches: pixels outside the image load from a clamped
@@ -205,11 +215,12 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
     // loads and the transform -- is one basic block the scheduler can
     // interleave with the matrix-core instructions.
     constexpr int kPieces = HH * HWD * 4;  // 720
-    int hoff[3], hq[3];
-    bool hin[3];
+    constexpr int PP = (kPieces + NT - 1) / NT;  // 3 (256 lanes) or 2 (512)
+    int hoff[PP], hq[PP];
+    bool hin[PP];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        const int v = min(tid + i * kThreads, kPieces - 1);
+    for (int i = 0; i < PP; ++i) {
+        const int v = min(tid + i * NT, kPieces - 1);
         const int p = v >> 2, q = v & 3;
         const int ih = h0 - 1 + p / HWD, iw = w0 - 1 + p % HWD;
         hin[i] = ih >= 0 && ih < a.H && iw >= 0 && iw < a.W;
@@ -218,9 +229,9 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
         hq[i] = (ihc * a.W + iwc) * Ci + 8 * q;  // element offset within the sample
     }
     const uint16_t *xs = a.x + static_cast<int64_t>(n) * a.H * a.W * Ci;
-    auto load_halo = [&](int k, u32x4 (&raw)[3]) {
+    auto load_halo = [&](int k, u32x4 (&raw)[PP]) {
 #pragma unroll
-        for (int i = 0; i < 3; ++i)
+        for (int i = 0; i < PP; ++i)
             raw[i] = *reinterpret_cast<const u32x4 *>(xs + hq[i] + k * BK);
     };
     auto store_piece = [&](int k, uint16_t *dst, const u32x4 &raw, int i) {
@@ -256,12 +267,12 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
 
     bf16x8 wq[3][2][2];  // ring of weight fragments: step s in slot s % 3
     {
-        u32x4 raw[3];
+        u32x4 raw[PP];
         load_halo(0, raw);
         load_w(0, wq[0]);
         load_w(min(1, nsteps - 1), wq[1]);
 #pragma unroll
-        for (int i = 0; i < 3; ++i) store_piece(0, sA, raw[i], i);
+        for (int i = 0; i < PP; ++i) store_piece(0, sA, raw[i], i);
     }
     __syncthreads();
 
@@ -271,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
         // The next chunk's halo (the last chunk reloads its own: harmless,
         // it goes to the buffer no one reads again).
         const int kn = min(k + 1, nchunks - 1);
-        u32x4 raw[3];
+        u32x4 raw[PP];
         load_halo(kn, raw);
         // Keep the loads where they are issued: left to itself the scheduler
         // sinks them next to their first use to save registers, which turns
@@ -300,23 +311,29 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             af[mi], wq[t % 3][ks][ni], acc[mi][ni], 0, 0, 0);
             }
-            if (t == 2 || t == 4 || t == 6) store_piece(kn, a_next, raw[t / 2 - 1], t / 2 - 1);
+            // the next chunk's pieces are normalised and stored spread over
+            // the taps: at taps 2, 4, 6 (three pieces) or 3, 6 (two)
+            if constexpr (PP == 3) {
+                if (t == 2 || t == 4 || t == 6) store_piece(kn, a_next, raw[t / 2 - 1], t / 2 - 1);
+            } else {
+                if (t == 3 || t == 6) store_piece(kn, a_next, raw[t / 3 - 1], t / 3 - 1);
+            }
         }
         __syncthreads();  // a_next written by all lanes; a_cur no longer read
     }
 
     // ---- epilogue, 64 output channels at a time
-    const int q = tid & 7;          // 8-channel piece of the half
-    const int prow = tid >> 3;      // pixels prow + 32 * i
-    float vals[4][8];
-    bool valid[4];
+    const int q = tid & 7;          // 8-channel piece of the pass
+    const int prow = tid >> 3;      // pixels prow + ROWS * i
+    float vals[PIX][8];
+    bool valid[PIX];
     int cnt = 0;                    // valid pixels of the tile
     {
         const int rows = min(TH, a.H - h0), cols = min(TW, a.W - w0);
         cnt = rows * cols;
     }
     const int Cg2 = STATS ? a.Co / a.G2 : 1;
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < WN; ++half) {  // passes of 64 channels
         if (wn == half) {
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
@@ -334,8 +351,8 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
         }
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int pix = prow + 32 * i;
+        for (int i = 0; i < PIX; ++i) {
+            const int pix = prow + ROWS * i;
             const int oh = h0 + pix / TW, ow = w0 + pix % TW;
             valid[i] = oh < a.H && ow < a.W;
             float v[8];
@@ -369,16 +386,16 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
         __syncthreads();  // sO fully read: free for the next half or the statistics
 
         if constexpr (STATS) {
-            // Per channel: sum over this lane's pixels, then over the 32 lanes
-            // of the same piece in order; per group: over its channels.
-            float *red = sO;                 // [32][64]
-            float *gmean = sO + 32 * 64;     // [64]: mean of the group of each channel
+            // Per channel: sum over this lane's pixels, then over the ROWS
+            // lanes of the same piece in order; per group: over its channels.
+            float *red = sO;                   // [ROWS][64]
+            float *gmean = sO + ROWS * 64;     // [64]: mean of the group of each channel
             float s8[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 float s = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s += valid[i] ? vals[i][e] : 0.0f;
+                for (int i = 0; i < PIX; ++i) s += valid[i] ? vals[i][e] : 0.0f;
                 s8[e] = s;
             }
 #pragma unroll
@@ -386,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
             __syncthreads();
             if (tid < 64) {
                 float s = 0.0f;
-                for (int r = 0; r < 32; ++r) s += red[r * 64 + tid];
+                for (int r = 0; r < ROWS; ++r) s += red[r * 64 + tid];
                 red[tid] = s;  // row 0 is read only by this lane below it
             }
             __syncthreads();
@@ -403,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
                 const float mg = gmean[8 * q + e];
                 float s = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < PIX; ++i) {
                     const float d = vals[i][e] - mg;
                     s = valid[i] ? fmaf(d, d, s) : s;
                 }
@@ -415,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void gn_conv3x3(ConvArgs a) {
             __syncthreads();
             if (tid < 64) {
                 float s = 0.0f;
-                for (int r = 0; r < 32; ++r) s += red[r * 64 + tid];
+                for (int r = 0; r < ROWS; ++r) s += red[r * 64 + tid];
                 red[tid] = s;
             }
             __syncthreads();

@@ -283,15 +283,17 @@ gn_status gn_conv3x3_nhwc_packed(const void *x, const float *norm_mean, const fl
                                  float *mean2_out, float *rstd2_out, void *stream);
 
 /* Launch shape of gn_conv3x3_nhwc for a problem, for inspection and tests;
- * no HIP call.  G2 > 0 asks for the statistics output.  Writes 6 values:
+ * no HIP call.  G2 > 0 asks for the statistics output.  Writes 7 values:
  * [0] tiles_h = ceil(H/8), [1] tiles_w = ceil(W/16) (output tiles of 8x16
- * pixels), [2] nb = Co/128 output-channel blocks, [3] 1 when the XCD-aware
- * block order is used (nb divides 8), [4] workgroups with work
- * (N*tiles_h*tiles_w*nb), [5] workgroups launched.  Returns the status
+ * pixels), [2] nb = Co/(64*wn) output-channel blocks, [3] 1 when the
+ * XCD-aware block order is used (nb divides 8), [4] workgroups with work
+ * (N*tiles_h*tiles_w*nb), [5] workgroups launched, [6] wn: waves along the
+ * output channels (2: workgroups of 256 lanes over 128 channels).  Returns
+ * the status
  * gn_conv3x3_nhwc would return from its argument checks for aligned
  * pointers. */
 gn_status gn_conv3x3_plan(int64_t N, int64_t H, int64_t W, int64_t Ci, int64_t Co, int64_t G2,
-                          int64_t plan_out[6]);
+                          int64_t plan_out[7]);
 
 /* Name of kernel slot i of gn_profile_rows, or NULL. */
 const char *gn_kernel_name(int i);

@@ -40,7 +40,10 @@ def block_map(p, b):
 def test_conv_plan_and_indices_in_bounds(N, H, W, Ci, Co, G2):
     p = gn.conv_plan(N, H, W, Ci, Co, G2)
     assert p is not None
-    assert p["tiles_h"] == -(-H // TH) and p["tiles_w"] == -(-W // TW) and p["nb"] == Co // BN
+    WN = p["wn"]
+    assert WN == 2
+    NT, BNW = 128 * WN, 64 * WN                  # lanes, output channels per workgroup
+    assert p["tiles_h"] == -(-H // TH) and p["tiles_w"] == -(-W // TW) and p["nb"] == Co // BNW
     tps = p["tiles_h"] * p["tiles_w"]
     assert p["blocks"] == N * tps * p["nb"] and p["grid"] < 2 ** 31
     assert p["xcd_map"] == (8 % p["nb"] == 0)
@@ -53,17 +56,19 @@ def test_conv_plan_and_indices_in_bounds(N, H, W, Ci, Co, G2):
             assert m not in seen
             seen.add(m)
     assert len(seen) == p["blocks"], "every (tile, channel block) runs exactly once"
-    # halo pieces: 180 pixels x 4 pieces of 8 channels, three per lane
-    v = np.arange(256)[:, None] + 256 * np.arange(3)[None, :]
-    live = v < HH * HWD * 4
+    # halo pieces: 180 pixels x 4 pieces of 8 channels, PP per lane, clamped
+    # to the last piece
+    PP = -(-720 // NT)
+    v = np.minimum(np.arange(NT)[:, None] + NT * np.arange(PP)[None, :], 719)
     pix, q = v // 4, v % 4
-    assert np.all((pix * KS + 8 * q + 8)[live] <= A_ELEMS)
+    assert np.all(pix * KS + 8 * q + 8 <= A_ELEMS)
+    assert set(v.ravel().tolist()) == set(range(720)), "every halo piece is written"
     # halo fragment reads: wave (wm, wn), block mi, lane -> halo pixel, k offset,
     # in either halo buffer
     lane = np.arange(64)
     fp, fk = lane % 32, 8 * (lane // 32)
     for buf in (0, 1):
-        for wm in (0, 1):
+        for wm in range(NT // 64 // WN):
             for mi in (0, 1):
                 for kh in range(3):
                     for kw in range(3):
@@ -74,13 +79,14 @@ def test_conv_plan_and_indices_in_bounds(N, H, W, Ci, Co, G2):
     # k-step ks, wave column wn, block column ni, lane -> 8 bf16 at
     # (cb*nsteps + s)*4096 + ((ks*2 + wn)*2 + ni)*512 + lane*8
     nsteps = Ci // BK * 9
-    for cb in (0, Co // BN - 1):
-        for wn in (0, 1):
+    for cb in (0, Co // BNW - 1):
+        for wn in range(WN):
+            blk = cb * BNW // BN + wn // 2           # 128-channel packed block
             for ni in (0, 1):
                 for step in (0, 1, nsteps - 1):
                     for ks in (0, 1):
-                        off = (cb * nsteps + step) * PACK_STEP + ((ks * 2 + wn) * 2 + ni) * 512 \
-                            + lane * 8
+                        off = (blk * nsteps + step) * PACK_STEP \
+                            + ((ks * 2 + wn % 2) * 2 + ni) * 512 + lane * 8
                         assert off.min() >= 0 and (off + 8).max() <= Co * 9 * Ci
     # the packing kernel's map is a bijection from packed pieces onto the
     # weight tensor's 16-byte pieces
@@ -100,9 +106,10 @@ def test_conv_plan_and_indices_in_bounds(N, H, W, Ci, Co, G2):
     # epilogue staging and the statistics scratch in the same LDS
     r = np.arange(16)
     m = 8 * (r[:, None] // 4) + 4 * (lane[None, :] // 32) + r[:, None] % 4
-    pixl = 64 * 1 + 32 * 1 + m
+    pixl = 64 * (NT // 64 // WN - 1) + 32 * 1 + m
     assert (pixl * OS + 63).max() < LDS_EPI_FLOATS and m.max() < 32
-    assert 32 * 64 + 64 <= LDS_EPI_FLOATS
+    ROWS = NT // 8
+    assert ROWS * 64 + 64 <= LDS_EPI_FLOATS and (TH * TW) % ROWS == 0
     assert max(LDS_MAIN * 2, LDS_EPI_FLOATS * 4) <= 64 * 1024
     # output / residual pieces of valid pixels, statistics partials
     for tile in (0, N * tps - 1):
@@ -111,12 +118,12 @@ def test_conv_plan_and_indices_in_bounds(N, H, W, Ci, Co, G2):
         for pixt in range(TH * TW):
             oh, ow = h0 + pixt // TW, w0 + pixt % TW
             if oh < H and ow < W:
-                off = ((n * H + oh) * W + ow) * Co + (Co - BN) + 64 + 8 * 7
+                off = ((n * H + oh) * W + ow) * Co + (Co - BNW) + 64 * (WN - 1) + 8 * 7
                 assert off + 8 <= N * H * W * Co
         if G2:
             Cg2 = Co // G2
             assert 64 % Cg2 == 0
-            g2 = (Co - BN + 64) // Cg2 + 64 // Cg2 - 1
+            g2 = (Co - 64) // Cg2 + 64 // Cg2 - 1
             assert ((n * tps + tin) * G2 + g2) * 4 + 4 <= N * tps * G2 * 4
 
 
