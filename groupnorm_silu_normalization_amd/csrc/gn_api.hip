@@ -34,7 +34,10 @@ namespace {
 // over the full three-step sequence at the decoder shapes.
 constexpr int kUnrollStats = 8;             // 16-byte loads in flight per lane, step 1
 constexpr int kUnrollApply = 4;             // 16-byte loads in flight per lane, step 3
-constexpr int64_t kStatsBlocks = 256;       // step-1 workgroups in total: one per CU
+constexpr int64_t kStatsBlocks = 256;       // step-1 workgroups in total: one per CU ...
+constexpr int64_t kStatsBlocksSmall = 128;  // ... or half that for x up to kStatsSmallBytes,
+constexpr int64_t kStatsSmallBytes = int64_t{16} << 20;  // where latency, not bandwidth, rules
+constexpr int64_t kStatsMinTiles = 8;       // tiles per workgroup, at least
 constexpr int64_t kStatsMaxTiles = 1024;    // caps each lane's sequential fp32 run
 constexpr int64_t kApplyElemsPerBlock = 16 * 2048;  // step-3 workgroups: elements / 32768 ...
 constexpr int64_t kApplyMinBlocks = 256;    // ... clamped to [256, 2048]
@@ -138,15 +141,24 @@ Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G, int dtype) {
     if (p.lay.a != kThreads) g.cg_shift = 0;  // only the power-of-two kernels use it
     g.plain_tail = 0;
     const int64_t total = N * g.tiles;
+    const int64_t bytes = N * E * elem_bytes(dtype);
     p.stats = g;
-    p.stats.tpc = std::min(kStatsMaxTiles, std::max<int64_t>(1, ceil_div(total, kStatsBlocks)));
+    // Step 1 on a small x is a chain of latencies (load batch, LDS reduction,
+    // write-through partials, arrival atomic, finalize), and every extra
+    // workgroup adds an arrival on the same counter line: measured on MI355X
+    // (bf16, stats kernel alone), 0.5-16 MiB shapes take 9.1-12.0 us with at
+    // least 8 tiles per workgroup and at most 128 workgroups, against
+    // 9.9-13.3 us with 256 workgroups of fewer tiles; from 64 MiB up, 256
+    // workgroups are 1-30% faster than 128.
+    const int64_t blocks = bytes <= kStatsSmallBytes ? kStatsBlocksSmall : kStatsBlocks;
+    p.stats.tpc = std::min(kStatsMaxTiles,
+                           std::max(kStatsMinTiles, ceil_div(total, blocks)));
     p.stats.K = ceil_div(g.tiles, p.stats.tpc);
     // Step 1's plain-load tail: the fraction cache / tensor of every chunk (all
     // of it when the tensor fits), so about one cache's worth of x is read
     // last with allocating loads.  Measured on MI355X over the whole path:
     // 512 MiB bf16 -1.7%, 1 GiB -3.7%; a smaller plain fraction slows step 3
     // by more than it saves in step 1.
-    const int64_t bytes = N * E * elem_bytes(dtype);
     p.stats.plain_tail =
         bytes <= kCacheResidentBytes
             ? p.stats.tpc
@@ -165,10 +177,13 @@ size_t partial_floats(const Plan &p) {
 }
 
 // Scratch bytes of a call: the arrival counters (one per sample, at the front,
-// 256-byte aligned), the partials, and -- for the full path -- mean and rstd.
+// 256-byte aligned), the partial sums, the partial squares, the finalize's
+// over-read padding, and -- for the full path -- mean and rstd.  The padding
+// sits right after the partial squares, so a finalize batch that reads past
+// them never touches mean/rstd while another sample writes them.
 size_t arrivals_bytes(int64_t n) { return align_up(static_cast<size_t>(n) * 4, 256); }
 size_t payload_bytes(const Plan &p, bool with_stats) {
-    return sizeof(float) * (2 * partial_floats(p) +
+    return sizeof(float) * (2 * partial_floats(p) + static_cast<size_t>(kFinalizeOverread) +
                             (with_stats ? 2 * static_cast<size_t>(p.N) * p.stats.G : 0));
 }
 
@@ -484,7 +499,7 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
     StatsOut o;
     o.part_s = reinterpret_cast<float *>(payload);
     o.part_q = o.part_s + nparts;
-    o.mean = o.part_q + nparts;
+    o.mean = o.part_q + nparts + kFinalizeOverread;
     o.rstd = o.mean + nstats;
     o.arrivals = counters;
     o.inv_m = p.inv_m;

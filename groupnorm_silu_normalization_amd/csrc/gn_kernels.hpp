@@ -436,6 +436,12 @@ __device__ __forceinline__ bool arrive_is_last(const StatsOut &out, int64_t n, i
     return last != 0;
 }
 
+// Partials the fused finalize loads per thread in one batch, and how far past
+// the end of a partials array a batch may read; the partial squares are
+// followed by that much padding.
+constexpr int kFinalizeBatch = 16;
+constexpr int64_t kFinalizeOverread = int64_t{kFinalizeBatch - 1} * kThreads;
+
 // Step 2 for sample n, run by the last workgroup to arrive (G <= kThreads):
 // tpg = kThreads / G threads per group; thread tid = g + G*j (j < tpg) sums
 // the chunks k = j, j + tpg, ... in increasing order (coalesced along g;
@@ -452,13 +458,18 @@ __device__ __forceinline__ void finalize_sample(const typename D::storage *xs,
     const bool has = tid < tpg * G;
     const int g = tid % G;
     const int j = tid / G;
-    constexpr int kBatch = 16;
+    constexpr int kBatch = kFinalizeBatch;
     float as = 0.0f, aq = 0.0f;
     if (has) {
         const float *ps = out.part_s + n * geo.K * G + g;
         const float *pq = out.part_q + n * geo.K * G + g;
-        int64_t kk = j;
-        for (; kk + (kBatch - 1) * tpg < geo.K; kk += kBatch * tpg) {
+        // Every batch, the last one included, issues all kBatch loads before
+        // the first add, so a short tail costs one round trip, not one per
+        // chunk.  A slot past K reads up to (kBatch-1)*tpg*G floats beyond the
+        // sample's partials -- the next sample's, the partial squares after
+        // the sums, or the kFinalizeOverread floats of padding after the
+        // squares -- and is not added.
+        for (int64_t kk = j; kk < geo.K; kk += kBatch * tpg) {
             float vs[kBatch], vq[kBatch];
 #pragma unroll
             for (int b = 0; b < kBatch; ++b) {
@@ -466,15 +477,14 @@ __device__ __forceinline__ void finalize_sample(const typename D::storage *xs,
                 vs[b] = __hip_atomic_load(ps + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 vq[b] = __hip_atomic_load(pq + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
+            __builtin_amdgcn_sched_barrier(0);  // all loads issued before the adds
 #pragma unroll
             for (int b = 0; b < kBatch; ++b) {
-                as += vs[b];
-                aq += vq[b];
+                if (kk + b * tpg < geo.K) {
+                    as += vs[b];
+                    aq += vq[b];
+                }
             }
-        }
-        for (; kk < geo.K; kk += tpg) {
-            as += __hip_atomic_load(ps + kk * G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            aq += __hip_atomic_load(pq + kk * G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     red_s[tid] = as;
@@ -538,8 +548,14 @@ __device__ __forceinline__ float transform1(float x, float sc, float sh) {
 // is the arrival counted; the last workgroup reads the partials with
 // agent-scope (coherent) loads.
 // ---------------------------------------------------------------------------
+// Step 1 launches about one workgroup per CU, so its occupancy target is one
+// or two waves per SIMD: with that, the compiler keeps a whole batch of
+// UNROLL tiles in flight and starts accumulating as the first arrives, where
+// a higher target made it interleave waits into the loads (fully serialized
+// for 16-bit wide tiles) to save registers.
 template <class D, int W, int NV, bool POW2, int UNROLL, bool FUSED>
-__global__ __launch_bounds__(kThreads) void gn_partial_stats(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void
+gn_partial_stats(
     const typename D::storage *__restrict__ x, Geometry geo, StatsOut out) {
     using L = Lane<D, W, NV>;
     constexpr int S = L::kSlots;
@@ -587,9 +603,18 @@ __global__ __launch_bounds__(kThreads) void gn_partial_stats(
             for (int u = 0; u < UNROLL; ++u) accumulate<L>(v[u], piv, s, q);
             p += UNROLL * T;
         }
-        for (; tt < cr.t_full_end; ++tt) {
-            accumulate<L>(L::template load<false>(p, A, tid), piv, s, q);
-            p += T;
+        if (tt < cr.t_full_end) {
+            // Fewer than UNROLL whole tiles left: one batch all the same, its
+            // surplus loads re-reading the last whole tile and not accumulated.
+            const int rem = static_cast<int>(cr.t_full_end - tt);
+            L v[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                v[u] = L::template load<false>(p + (u < rem ? u : rem - 1) * T, A, tid);
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                if (u < rem) accumulate<L>(v[u], piv, s, q);
+            tt += rem;
         }
         if (tt < cr.t_end) {
             // The sample's last tile is partial: slot by slot, in bounds only.
@@ -696,13 +721,25 @@ __global__ __launch_bounds__(kThreads) void gn_apply(
         }
         off += UNROLL * T;
     }
-    for (; tt < cr.t_full_end; ++tt) {
-        const L v = L::template load<NTL>(x + off, A, tid);
-        float o[S];
+    if (tt < cr.t_full_end) {
+        // Fewer than UNROLL whole tiles left: one batch of loads (the surplus
+        // re-reading the last whole tile, before any store of the batch), and
+        // stores for the real tiles only.
+        const int rem = static_cast<int>(cr.t_full_end - tt);
+        L v[UNROLL];
 #pragma unroll
-        for (int j = 0; j < S; ++j) o[j] = transform1<SILU>(v.get(j), sc[j], sh[j]);
-        L::template store<NTS>(y + off, A, tid, o);
-        off += T;
+        for (int u = 0; u < UNROLL; ++u)
+            v[u] = L::template load<NTL>(x + off + (u < rem ? u : rem - 1) * T, A, tid);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            if (u < rem) {
+                float o[S];
+#pragma unroll
+                for (int j = 0; j < S; ++j) o[j] = transform1<SILU>(v[u].get(j), sc[j], sh[j]);
+                L::template store<NTS>(y + off + u * T, A, tid, o);
+            }
+        }
+        tt += rem;
     }
     if (tt < cr.t_end) {
         // The sample's last tile is partial: slot by slot, in bounds only.

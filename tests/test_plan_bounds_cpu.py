@@ -17,6 +17,7 @@ import pytest
 gn = pytest.importorskip("groupnorm_silu_normalization_amd")
 
 THREADS = 256
+FINALIZE_BATCH = 16   # partials per thread per batch in the fused finalize
 BF16, F16, F32 = 0, 1, 2
 WIDE = {BF16: 8, F16: 8, F32: 4}   # elements per 16-byte access
 
@@ -150,13 +151,22 @@ def check_plan(N, L, C, G, dtype):
     # finalize (fused tail: thread g + G*j, j < 256//G, reads k = j, j + 256//G, ...)
     nparts = N * G * p["K1"]
     assert ((N - 1) * p["K1"] + p["K1"] - 1) * G + G - 1 < nparts
+    pad = (FINALIZE_BATCH - 1) * THREADS   # finalize over-read padding after the squares
     if G <= THREADS:
         tpg = THREADS // G
         assert tpg * G <= THREADS
         seen = sorted(k for j in range(tpg) for k in range(j, p["K1"], tpg))
         assert seen == list(range(p["K1"]))
+        # a fused-finalize batch loads slots kk + b*tpg, b < FINALIZE_BATCH, for
+        # every kk = j + m*FINALIZE_BATCH*tpg < K1, adding only those < K1: the
+        # highest float it reads, relative to the start of the partial squares
+        # of the last sample, stays inside the squares and the padding
+        K = p["K1"]
+        kk_last = max(kk for j in range(tpg) for kk in range(j, K, FINALIZE_BATCH * tpg))
+        top = ((N - 1) * K + kk_last + (FINALIZE_BATCH - 1) * tpg) * G + G - 1
+        assert top < nparts + pad
     counters = -(-4 * N // 256) * 256   # one arrival counter per sample
-    assert p["scratch_bytes"] == counters + 4 * (2 * nparts + 2 * N * G)
+    assert p["scratch_bytes"] == counters + 4 * (2 * nparts + pad + 2 * N * G)
     assert N * G < 2 ** 24
     check_lds(p, C, G)
     # step 1's plain-load tail: the whole chunk when the tensor fits the
@@ -265,9 +275,19 @@ def test_plan_is_shape_only_and_bounded():
         assert N * p["K1"] <= max(256, -(-total // 1024)) + N
         assert N * p["K2"] <= 2048 + N
         assert p == gn.plan_rows(N, L, C, G)
-    # the decoder shapes: one statistics workgroup per CU of an MI355X
-    for N, L, C, G in SHAPES[:5]:
+    # the decoder shapes: one statistics workgroup per CU of an MI355X from
+    # 64 MiB up; below 16 MiB at most 128 workgroups of at least 8 tiles
+    for N, L, C, G in SHAPES[2:5]:
         assert gn.plan_rows(N, L, C, G)["K1"] == 256
+    assert gn.plan_rows(*SHAPES[0])["K1"] == 256 // 8        # 256 tiles
+    assert gn.plan_rows(*SHAPES[1])["K1"] == 128              # 4096 tiles, 16 MiB
+    for N, L, C, G in SHAPES + WIDE_SHAPES:
+        p = gn.plan_rows(N, L, C, G)
+        if p is None or N * L == 0:
+            continue
+        blocks = 128 if N * L * C * 2 <= 16 << 20 else 256
+        assert N * p["K1"] <= max(blocks, -(-N * p["tiles"] // 1024)) + N
+        assert p["tpc1"] >= 8
 
 
 def test_plan_declines_like_the_entry_points():
