@@ -14,12 +14,17 @@ Prints ONE JSON line.  Besides the contract fields it carries
                   launch / its mean duration from HIP events recorded around
                   each launch on the stream it runs on;
   cpu_baseline -- the fp64 oracle (test infrastructure) timed on the host's
-                  cores on the same tensor;
+                  cores on the same tensor, and once on one core;
   kernels_ms   -- mean duration of each kernel from the same events;
   other_shapes -- us/call of the other four decoder shapes (context);
   other_dtypes -- the headline shape with fp16 and fp32 input/output;
   wide_shapes  -- shapes outside the pages' kernel's support set (C not a
                   power of two, C > 2048, 5-D NDHWC), measured the same way;
+  extra_shapes -- (1,512,256,256), rows (1,16384,512) without SiLU, and one
+                  GPU's share (1/8 of the rows) of the headline tensor;
+  per_call     -- the headline call timed call by call: warm (back to back)
+                  and cold (a 1 GiB buffer written, or read, before each call,
+                  so the Infinity Cache holds none of x): mean / median / min;
   resnet_block -- the decoder's ResnetBlock2D (GroupNorm -> SiLU -> conv3x3 ->
                   GroupNorm -> SiLU -> conv3x3 + shortcut) with the GroupNorms
                   fused into the convolutions, against the same block run as
@@ -116,6 +121,16 @@ def cpu_baseline(w, x_bits, gamma, beta, budget_s):
         runs += 1
         del y
     per_call = total / runs
+    # the same call on one core, once (the oracle is the same code either way)
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        y = oracle.gn_silu(x_bits, gamma, beta, w.N, w.L, w.C, w.G, w.eps, w.apply_silu,
+                           out_dtype=np.float32)
+        one = time.perf_counter() - t0
+        del y
+    finally:
+        oracle.set_threads(threads)
     return {
         "value": round(w.algorithmic_bytes / per_call / 1e9, 3),
         "unit": "GB/s",
@@ -124,6 +139,9 @@ def cpu_baseline(w, x_bits, gamma, beta, budget_s):
         "us_per_call": round(per_call * 1e6, 1),
         "sample": "the full %s tensor (%d elements), %d oracle call(s), fp64 two-pass, "
                   "%d OpenMP threads" % (w.label(), w.numel, runs, threads),
+        "one_core": {"value": round(w.algorithmic_bytes / one / 1e9, 3), "unit": "GB/s",
+                     "us_per_call": round(one * 1e6, 1), "cores": 1,
+                     "sample": "the same tensor, one oracle call on one thread"},
     }
 
 
@@ -140,6 +158,32 @@ def time_events(torch, fn, steps, warmup, stream):
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
+
+
+def per_call_us(torch, fn, n, stream, before=None):
+    """Sorted durations (us) of n calls of fn, each between its own pair of
+    events on `stream`; `before`, if given, runs untimed ahead of every call
+    on the same stream."""
+    evs = []
+    for _ in range(n):
+        if before is not None:
+            before()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    return sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+
+
+def call_stats(us, nbytes):
+    med = us[len(us) // 2]
+    return {"calls": len(us), "mean_us": round(sum(us) / len(us), 2), "median_us": round(med, 2),
+            "min_us": round(us[0], 2), "max_us": round(us[-1], 2),
+            "GB_s_median": round(nbytes / (med * 1e-6) / 1e9, 1),
+            "frac_of_peak_median": round(nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def graph_of(torch, fn, stream):
@@ -291,6 +335,7 @@ def main():
     ap.add_argument("--no-other-shapes", action="store_true")
     ap.add_argument("--no-other-dtypes", action="store_true")
     ap.add_argument("--no-wide-shapes", action="store_true")
+    ap.add_argument("--no-extra-shapes", action="store_true")
     ap.add_argument("--no-resnet-block", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (for scaling PMC byte counters)")
@@ -308,7 +353,7 @@ def main():
     import torch
 
     import groupnorm_silu_normalization_amd as gn
-    from gn_inputs import WIDE_WORKLOADS, WORKLOADS, make_inputs
+    from gn_inputs import EXTRA_WORKLOADS, WIDE_WORKLOADS, WORKLOADS, make_inputs
 
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
@@ -342,6 +387,23 @@ def main():
     apply_bytes = 4 * w.numel  # one read and one write of the bf16 tensor
     achieved = apply_bytes / (apply_ms * 1e-3) / 1e9
     traffic = measured_traffic()
+
+    # Each call timed alone: warm (back to back), then cold, with a 1 GiB buffer
+    # touched (untimed, same stream) before every call so the 256 MB Infinity
+    # Cache holds none of x.  Written, the buffer also leaves up to a cache's
+    # worth of dirty lines whose write-back lands in the timed call; read, it
+    # leaves clean lines only.
+    log("per-call events, warm and cold")
+    warm_us = per_call_us(torch, step, max(args.steps, 20), stream)
+    scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cold_w_us = per_call_us(torch, step, 20, stream, before=lambda: scrub.fill_(1.0))
+    cold_r_us = per_call_us(torch, step, 20, stream, before=lambda: scrub.sum())
+    del scrub
+    per_call = {"warm": call_stats(warm_us, w.algorithmic_bytes),
+                "cold_after_write": call_stats(cold_w_us, w.algorithmic_bytes),
+                "cold_after_read": call_stats(cold_r_us, w.algorithmic_bytes),
+                "cold_note": "before each call a 1 GiB buffer is written (cold_after_write) "
+                             "or read (cold_after_read), untimed, on the same stream"}
 
     other = {}
     if not args.no_other_shapes:
@@ -438,6 +500,37 @@ def main():
             }
             del wx, wy
 
+    extra = {}
+    if not args.no_extra_shapes:
+        for ew in EXTRA_WORKLOADS:
+            log("extra shape %s silu=%d" % (ew.label(), ew.apply_silu))
+            eb, eg, ebeta = make_inputs(ew)
+            ex = device_tensor(torch, eb, dev).reshape(ew.N, ew.L, ew.C)
+            ey = torch.empty_like(ex)
+            egt, ebt = torch.from_numpy(eg).to(dev), torch.from_numpy(ebeta).to(dev)
+            exp_, eyp = ctypes.c_void_p(ex.data_ptr()), ctypes.c_void_p(ey.data_ptr())
+            egp, ebp = ctypes.c_void_p(egt.data_ptr()), ctypes.c_void_p(ebt.data_ptr())
+
+            def estep(ew=ew, exp_=exp_, eyp=eyp, egp=egp, ebp=ebp):
+                code = gn.gn_silu_rows(exp_, egp, ebp, eyp, ew.N, ew.L, ew.C, ew.G, ew.eps,
+                                       int(ew.apply_silu), sh)
+                if code != 0:
+                    raise RuntimeError(gn.status_text(code))
+
+            ems, _ = time_calls(torch, estep, args.steps, args.warmup, stream)
+            ek = gn.profile_rows(ex, ew.G, egt, ebt, ew.eps, ew.apply_silu, ey, args.steps)
+            extra[ew.name] = {
+                "shape": [ew.N, ew.C, ew.H, ew.W] if ew.W != 1 else [ew.N, ew.H, ew.C],
+                "layout": "NHWC" if ew.W != 1 else "rows (N, L, C)",
+                "apply_silu": ew.apply_silu,
+                "note": ew.note,
+                "us_per_call": round(ems * 1e3, 2),
+                "GB_s": round(ew.algorithmic_bytes / (ems * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(ew.algorithmic_bytes / (ems * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "kernels_us": {k: round(v * 1e3, 2) for k, v in ek.items()},
+            }
+            del ex, ey
+
     resnet = {}
     if not args.no_resnet_block:
         for shp in RESNET_SHAPES:
@@ -499,14 +592,20 @@ def main():
             "mean_launch_ms": round(apply_ms, 5),
         },
         "kernels_ms": {k: round(v, 5) for k, v in kms.items()},
+        "per_call": per_call,
         "cpu_baseline": cpu,
+        "gpu_over_cpu": None if cpu is None else {
+            "all_cores": round(value / cpu["value"], 1),
+            "one_core": round(value / cpu["one_core"]["value"], 1)},
         "other_shapes": other,
         "other_dtypes": dtypes,
         "wide_shapes": wide,
+        "extra_shapes": extra,
         "resnet_block": resnet,
         "wall_s_timed_region": round(wall, 4),
-        "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "arch": getattr(props, "gcnArchName", "")},
+        "device": dict({"name": props.name, "cus": props.multi_processor_count,
+                        "arch": getattr(props, "gcnArchName", "")},
+                       **gn.device_info(dev.index or 0)),
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(result), flush=True)

@@ -105,6 +105,22 @@ WIDE_WORKLOADS = (
              note="5-D NDHWC, 9 frames"),
 )
 
+# Shapes measured beside the decoder shapes, not part of the metric: the
+# pages' (1,512,256,256) decoder norm shape, the attention-style rows call
+# (N, L, C) = (1, 16384, 512) with SiLU off (H = L, W = 1), and one GPU's share
+# of the (1,256,1024,1024) activation split eight ways along its rows.
+EXTRA_WORKLOADS = (
+    Workload("gn_silu_1x512x256x256", 1, 512, 256, 256, seed=1006,
+             mean_dist=("zero",), std_dist=("uniform", 0.5, 2.0),
+             note="per-channel std ~ U(0.5,2)"),
+    Workload("gn_rows_1x16384x512_nosilu", 1, 512, 16384, 1, apply_silu=False, seed=1007,
+             mean_dist=("normal", 0.0, 1.0), std_dist=("uniform", 0.5, 2.0),
+             note="rows (N, L, C) = (1, 16384, 512), SiLU off"),
+    Workload("gn_silu_1x256x128x1024_shard", 1, 256, 128, 1024, seed=1008,
+             mean_dist=("zero",), std_dist=("uniform", 0.5, 2.0),
+             note="1/8 of the rows of (1,256,1024,1024): one GPU's share"),
+)
+
 
 def _draw(rng, dist, C, default):
     kind = dist[0]

@@ -25,7 +25,7 @@ call raises RuntimeError.
 The raw C entry points are re-exported under their C names (gn_silu_nhwc,
 gn_silu_rows, gn_silu_nhwc_strided, gn_silu_ndhwc, gn_stats_rows,
 gn_apply_rows, gn_profile_rows, gn_plan_rows, their *_dtype forms,
-gn_kernel_name, gn_status_string, gn_version).
+gn_kernel_name, gn_status_string, gn_version, gn_device_info).
 """
 import ctypes
 import enum
@@ -118,6 +118,8 @@ lib.gn_status_string.argtypes = [_int]
 lib.gn_status_string.restype = ctypes.c_char_p
 lib.gn_version.argtypes = []
 lib.gn_version.restype = _int
+lib.gn_device_info.argtypes = [_int, _i64p]
+lib.gn_device_info.restype = _int
 
 # C entry points under their own names.
 gn_silu_nhwc = lib.gn_silu_nhwc
@@ -144,6 +146,7 @@ gn_profile_rows_dtype = lib.gn_profile_rows_dtype
 gn_plan_rows_dtype = lib.gn_plan_rows_dtype
 gn_status_string = lib.gn_status_string
 gn_version = lib.gn_version
+gn_device_info = lib.gn_device_info
 
 MAX_CHANNELS = 8192
 
@@ -468,3 +471,17 @@ def conv_plan(N, H, W, Ci, Co, G2=0):
     buf = (_i64 * len(CONV_PLAN_FIELDS))()
     r = _result(lib.gn_conv3x3_plan(N, H, W, Ci, Co, G2, buf), True)
     return None if r is None else dict(zip(CONV_PLAN_FIELDS, list(buf)))
+
+
+DEVICE_INFO_FIELDS = ("compute_units", "engine_clock_khz", "memory_clock_khz",
+                      "memory_bus_bits", "memory_bytes", "wavefront")
+
+
+def device_info(device=0):
+    """gn_device_info of HIP device `device` as a dict (raises RuntimeError
+    when the query fails)."""
+    out = (ctypes.c_int64 * len(DEVICE_INFO_FIELDS))()
+    code = lib.gn_device_info(int(device), out)
+    if code != GnStatus.OK:
+        raise RuntimeError(status_text(code))
+    return dict(zip(DEVICE_INFO_FIELDS, (int(v) for v in out)))

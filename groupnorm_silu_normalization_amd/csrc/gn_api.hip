@@ -1025,6 +1025,22 @@ const char *gn_status_string(gn_status s) {
     return "unknown gn_status";
 }
 
-int gn_version(void) { return 400; }
+int gn_version(void) { return 401; }
+
+gn_status gn_device_info(int device, int64_t info_out[6]) {
+    if (info_out == nullptr || device < 0) return GN_INVALID_ARGUMENT;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) {
+        (void)hipGetLastError();
+        return GN_DEVICE_ERROR;
+    }
+    info_out[0] = prop.multiProcessorCount;
+    info_out[1] = prop.clockRate;
+    info_out[2] = prop.memoryClockRate;
+    info_out[3] = prop.memoryBusWidth;
+    info_out[4] = static_cast<int64_t>(prop.totalGlobalMem);
+    info_out[5] = prop.warpSize;
+    return GN_OK;
+}
 
 }  // extern "C"

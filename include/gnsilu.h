@@ -304,6 +304,14 @@ const char *gn_status_string(gn_status s);
 /* Library version, major*10000 + minor*100 + patch. */
 int gn_version(void);
 
+/* Facts about HIP device `device` for measurement reports (hipGetDeviceProperties):
+ * info_out[0] compute units, [1] peak engine clock in kHz, [2] peak memory
+ * clock in kHz, [3] memory bus width in bits, [4] device memory in bytes,
+ * [5] wavefront size.  GN_INVALID_ARGUMENT for a null info_out or a negative
+ * device, GN_DEVICE_ERROR when the HIP call fails (no device there).  Writes
+ * nothing on error. */
+gn_status gn_device_info(int device, int64_t info_out[6]);
+
 #ifdef __cplusplus
 }
 #endif

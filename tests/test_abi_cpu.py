@@ -59,6 +59,13 @@ def test_library_exports_every_declared_symbol():
     assert set(names) <= exported
 
 
+def test_device_info_rejects_bad_arguments_without_a_hip_call():
+    out = (ctypes.c_int64 * 6)(*([-7] * 6))
+    assert gn.gn_device_info(0, None) == GnStatus.INVALID_ARGUMENT
+    assert gn.gn_device_info(-1, out) == GnStatus.INVALID_ARGUMENT
+    assert list(out) == [-7] * 6
+
+
 def test_status_strings_and_version():
     for s in GnStatus:
         assert gn.status_text(s).startswith("GN_" + s.name)

@@ -112,6 +112,20 @@ def test_decoder_workload_full_size(gn, dev, oracle, idx):
     compare(y_bits, ref, w.name)
 
 
+@pytest.mark.parametrize("idx", [0, 1, 2])
+def test_extra_workload_full_size(gn, dev, oracle, idx):
+    """The shapes bench.py measures beside the decoder shapes, full size, through
+    the rows entry (the one the rows case uses; NHWC is the same call)."""
+    from gn_inputs import EXTRA_WORKLOADS, make_inputs
+    w = EXTRA_WORKLOADS[idx]
+    print("case %s %s silu=%d" % (w.name, w.label(), w.apply_silu), flush=True)
+    x_bits, gamma, beta = make_inputs(w)
+    y_bits = run_rows(gn, dev, x_bits, gamma, beta, w.N, w.L, w.C, w.G, w.eps, w.apply_silu)
+    ref = oracle.gn_silu(x_bits, gamma, beta, w.N, w.L, w.C, w.G, w.eps, w.apply_silu,
+                         out_dtype=np.float32)
+    compare(y_bits, ref, w.name)
+
+
 @pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
 def test_decoder_workload_statistics(gn, dev, oracle, idx):
     """fp32 mean/rstd against the oracle's fp64 ones.
@@ -397,3 +411,13 @@ def test_many_samples_one_workgroup_each(gn, dev, oracle):
     assert gn.plan_rows(N, L, C, G)["K1"] == 1
     y = run_rows(gn, dev, x_bits, gamma, beta, N, L, C, G, 1e-6, 1)
     compare(y, oracle.gn_silu(x_bits, gamma, beta, N, L, C, G, 1e-6, 1), "N=300")
+
+
+def test_device_info_reports_the_device(gn, dev):
+    info = gn.device_info(dev.index or 0)
+    props = torch.cuda.get_device_properties(dev)
+    assert info["compute_units"] == props.multi_processor_count
+    assert info["wavefront"] == 64
+    assert info["memory_bytes"] == props.total_memory
+    assert info["engine_clock_khz"] > 0 and info["memory_clock_khz"] > 0
+    assert info["memory_bus_bits"] > 0
