@@ -21,15 +21,16 @@
 //   * the 10 x 18 pixel halo of the tile is normalised (+SiLU) with
 //     per-channel scale/shift held in LDS, rounded to bf16 and stored to one
 //     of two LDS halo buffers -- every input value is transformed once per
-//     chunk, not once per tap.  The next chunk's halo is loaded into
-//     registers when a chunk starts and normalised into the other buffer
-//     half way through its taps, so the loads and the VALU work overlap the
-//     matrix-core work; one barrier per chunk;
+//     chunk, not once per tap.  The halo of chunk k+1 is loaded into
+//     registers at tap 4 of chunk k-1 and normalised into the other buffer
+//     at taps 1-3 of chunk k, so the loads have most of a chunk to arrive
+//     and the VALU work overlaps the matrix-core work; one barrier per chunk;
 //   * the nine taps run against it.  Each wave reads its weight fragments
 //     straight from global memory (the 128-channel weight slice of a
 //     workgroup stays in its XCD's L2) into a ring of registers, two taps
 //     ahead of their use, so no weight tile passes through LDS and no tap
-//     needs a barrier.
+//     needs a barrier; its A fragments come from LDS one tap ahead, into
+//     two register sets.
 // LDS rows are 80 bytes (32 bf16 + 8 padding), so the 16-byte fragment reads
 // of 16 consecutive lanes fall on distinct banks.
 //
@@ -266,57 +267,70 @@ __global__ __launch_bounds__(128 * WN) void gn_conv3x3(ConvArgs a) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     bf16x8 wq[3][2][2];  // ring of weight fragments: step s in slot s % 3
-    {
-        u32x4 raw[PP];
-        load_halo(0, raw);
-        load_w(0, wq[0]);
-        load_w(min(1, nsteps - 1), wq[1]);
+    // A fragments of a tap from the current halo buffer: rows of the wave's
+    // 64 pixels shifted by the tap, k-steps ks, pixel blocks mi.
+    bf16x8 afr[2][2][2];  // [tap parity][ks][mi]
+    auto read_a = [&](const uint16_t *abuf, int t, bf16x8 (&af)[2][2]) {
+        const int kh = t / 3, kw = t % 3;
 #pragma unroll
-        for (int i = 0; i < PP; ++i) store_piece(0, sA, raw[i], i);
-    }
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) {
+                const int hp = (wm * 4 + mi * 2 + frow + kh) * HWD + fcol + kw;
+                af[ks][mi] = *reinterpret_cast<const bf16x8 *>(abuf + hp * KS + 16 * ks + fk);
+            }
+    };
+    // raw holds the halo of the chunk after the current one: stored to LDS
+    // early in the current chunk, then reloaded with the chunk after that.
+    u32x4 raw[PP];
+    load_halo(0, raw);
+    load_w(0, wq[0]);
+    load_w(min(1, nsteps - 1), wq[1]);
+#pragma unroll
+    for (int i = 0; i < PP; ++i) store_piece(0, sA, raw[i], i);
+    load_halo(min(1, nchunks - 1), raw);
     __syncthreads();
 
     for (int k = 0; k < nchunks; ++k) {
         const uint16_t *a_cur = sA + (k & 1) * A_ELEMS;
         uint16_t *a_next = sA + ((k + 1) & 1) * A_ELEMS;
-        // The next chunk's halo (the last chunk reloads its own: harmless,
-        // it goes to the buffer no one reads again).
+        // raw holds chunk kn's halo and is reloaded with chunk kl's at tap 4
+        // (past the end the last chunk is reloaded and stored again, to the
+        // buffer no one reads any more: harmless).
         const int kn = min(k + 1, nchunks - 1);
-        u32x4 raw[PP];
-        load_halo(kn, raw);
-        // Keep the loads where they are issued: left to itself the scheduler
-        // sinks them next to their first use to save registers, which turns
-        // the prefetch into a stall.
-        __builtin_amdgcn_sched_barrier(0);
+        const int kl = min(k + 2, nchunks - 1);
+        // A fragments of tap 0; later taps' are read one tap ahead.
+        read_a(a_cur, 0, afr[0]);
 #pragma unroll
         for (int t = 0; t < 9; ++t) {
             const int s = k * 9 + t;
             // slots rotate with t; 9 is a multiple of 3, so slot = t % 3.
             // Past the last step the last step's weights are reloaded.
             load_w(min(s + 2, nsteps - 1), wq[(t + 2) % 3]);
+            if (t < 8) read_a(a_cur, t + 1, afr[(t + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
-            const int kh = t / 3, kw = t % 3;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 af[2];
-#pragma unroll
-                for (int mi = 0; mi < 2; ++mi) {
-                    const int hp = (wm * 4 + mi * 2 + frow + kh) * HWD + fcol + kw;
-                    af[mi] = *reinterpret_cast<const bf16x8 *>(a_cur + hp * KS + 16 * ks + fk);
-                }
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
                     for (int ni = 0; ni < 2; ++ni)
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            af[mi], wq[t % 3][ks][ni], acc[mi][ni], 0, 0, 0);
-            }
-            // the next chunk's pieces are normalised and stored spread over
-            // the taps: at taps 2, 4, 6 (three pieces) or 3, 6 (two)
+                            afr[t & 1][ks][mi], wq[t % 3][ks][ni], acc[mi][ni], 0, 0, 0);
+            // the next chunk's pieces are normalised and stored early, at
+            // taps 1-3 (three pieces) or 1-2 (two), which frees raw for the
+            // reload at tap 4
             if constexpr (PP == 3) {
-                if (t == 2 || t == 4 || t == 6) store_piece(kn, a_next, raw[t / 2 - 1], t / 2 - 1);
+                if (t >= 1 && t <= 3) store_piece(kn, a_next, raw[t - 1], t - 1);
             } else {
-                if (t == 3 || t == 6) store_piece(kn, a_next, raw[t / 3 - 1], t / 3 - 1);
+                if (t >= 1 && t <= 2) store_piece(kn, a_next, raw[t - 1], t - 1);
+            }
+            if (t == 4) {
+                load_halo(kl, raw);
+                // Keep the loads where they are issued: left to itself the
+                // scheduler sinks them next to their first use to save
+                // registers, which turns the prefetch into a stall.
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         __syncthreads();  // a_next written by all lanes; a_cur no longer read
