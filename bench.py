@@ -49,6 +49,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak, published
 RESNET_SHAPES = ((1, 512, 128, 128), (1, 512, 256, 256), (1, 256, 512, 512))
 H200_US = {                        # the pages' new-kernel column (H200), context only
     "gn_silu_1x512x128x128": 76.0,
+    "gn_silu_1x512x256x256": 121.0,
     "gn_silu_1x512x512x512": 311.1,
     "gn_silu_1x256x1024x1024": 913.8,
     "gn_silu_1x128x1024x1024": 307.9,
@@ -528,6 +529,7 @@ def main():
                 "GB_s": round(ew.algorithmic_bytes / (ems * 1e-3) / 1e9, 1),
                 "frac_of_peak": round(ew.algorithmic_bytes / (ems * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "kernels_us": {k: round(v * 1e3, 2) for k, v in ek.items()},
+                "h200_us_context": H200_US.get(ew.name),
             }
             del ex, ey
 
