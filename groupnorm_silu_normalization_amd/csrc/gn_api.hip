@@ -176,12 +176,13 @@ size_t partial_floats(const Plan &p) {
     return static_cast<size_t>(p.N) * p.stats.K * p.stats.G;
 }
 
-// Scratch bytes of a call: the arrival counters (one per sample, at the front,
-// 256-byte aligned), the partial sums, the partial squares, the finalize's
+// Scratch bytes of a call: the arrival counter words (arrival_stride(K1) per
+// sample, at the front, 256-byte aligned), the partial sums, the partial squares, the finalize's
 // over-read padding, and -- for the full path -- mean and rstd.  The padding
 // sits right after the partial squares, so a finalize batch that reads past
 // them never touches mean/rstd while another sample writes them.
-size_t arrivals_bytes(int64_t n) { return align_up(static_cast<size_t>(n) * 4, 256); }
+int64_t arrival_words(const Plan &p) { return p.N * arrival_stride(p.stats.K); }
+size_t arrivals_bytes(int64_t words) { return align_up(static_cast<size_t>(words) * 4, 256); }
 size_t payload_bytes(const Plan &p, bool with_stats) {
     return sizeof(float) * (2 * partial_floats(p) + static_cast<size_t>(kFinalizeOverread) +
                             (with_stats ? 2 * static_cast<size_t>(p.N) * p.stats.G : 0));
@@ -254,7 +255,7 @@ bool on_device(const void *ptr, int dev) {
 }
 
 // ---- scratch buffer per (device, stream) ----------------------------------
-// Layout: [arrival counters: `arrivals` uint32, zero between calls][payload].
+// Layout: [arrival counters: `arrivals` uint32 words, zero between calls][payload].
 // The counter region only grows, so a payload never overlaps a counter.
 struct Scratch {
     char *ptr = nullptr;
@@ -277,8 +278,8 @@ gn_status zero_counters(unsigned *p, int64_t n, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? GN_OK : GN_DEVICE_ERROR;
 }
 
-// Caller holds scratch_mutex().  Returns the arrival counters (>= n of them,
-// all zero in stream order) and the payload (>= payload bytes).  Grows the
+// Caller holds scratch_mutex().  Returns the arrival counter words (>= n of
+// them, all zero in stream order) and the payload (>= payload bytes).  Grows the
 // buffer when needed; the old one is released only after the stream has
 // drained the work that used it.
 gn_status scratch_for(int dev, hipStream_t s, int64_t n, size_t payload, unsigned **counters,
@@ -494,7 +495,8 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
     std::lock_guard<std::mutex> lock(scratch_mutex());
     unsigned *counters = nullptr;
     char *payload = nullptr;
-    st = scratch_for(c.dev, c.stream, N, payload_bytes(p, true), &counters, &payload);
+    st = scratch_for(c.dev, c.stream, arrival_words(p), payload_bytes(p, true), &counters,
+                     &payload);
     if (st != GN_OK) return st;
     StatsOut o;
     o.part_s = reinterpret_cast<float *>(payload);
@@ -778,7 +780,8 @@ gn_status gn_stats_rows_dtype(const void *x, int64_t N, int64_t L, int64_t C, in
     std::lock_guard<std::mutex> lock(scratch_mutex());
     unsigned *counters = nullptr;
     char *payload = nullptr;
-    st = scratch_for(c.dev, c.stream, N, payload_bytes(p, false), &counters, &payload);
+    st = scratch_for(c.dev, c.stream, arrival_words(p), payload_bytes(p, false), &counters,
+                     &payload);
     if (st != GN_OK) return st;
     StatsOut o;
     o.part_s = reinterpret_cast<float *>(payload);
@@ -857,7 +860,7 @@ gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dty
     plan_out[4] = p.stats.K;
     plan_out[5] = p.apply.tpc;
     plan_out[6] = p.apply.K;
-    plan_out[7] = static_cast<int64_t>(arrivals_bytes(N) + payload_bytes(p, true));
+    plan_out[7] = static_cast<int64_t>(arrivals_bytes(arrival_words(p)) + payload_bytes(p, true));
     plan_out[8] = p.apply_ntl ? 1 : 0;
     plan_out[9] = p.lay.w;
     plan_out[10] = p.lay.a;

@@ -252,8 +252,8 @@ template <bool POW2, int S> struct TileGeo {
 struct StatsOut {
     float *part_s;        // [N][K][G] pivot-shifted sum of each group over chunk k
     float *part_q;        // [N][K][G] pivot-shifted sum of squares
-    unsigned *arrivals;   // [N] statistics workgroups of sample n finished (fused
-                          // finalize only); zero between calls
+    unsigned *arrivals;   // [N][arrival_stride(K)] arrival counters of sample n
+                          // (fused finalize only); zero between calls
     float *mean;          // [N][G]
     float *rstd;          // [N][G]
     double inv_m;         // 1 / (L*Cg)
@@ -420,17 +420,52 @@ __device__ __forceinline__ void write_group_partials(const float (&s)[L::kSlots]
     }
 }
 
-// Counts this workgroup's arrival for sample n once its (write-through)
-// partial stores have completed; true, uniformly, in the last of the K.
+// Arrival counters of a sample.  With fewer than kArrivalTwoLevelMinK chunks
+// a sample has one counter word.  With more, the arrivals of its chunks
+// queue at the memory on one word, and a two-level count is faster (measured
+// on MI355X: 1-1.6 us less for step 1 at 32-64 MiB, no change from 256 MiB
+// up): word 0 counts finished groups of chunks, and word kArrivalLine*(1+s),
+// s < kArrivalSubs, the chunks k with k % kArrivalSubs == s, each counter on
+// a 128-byte line of its own.  (A sample with that many chunks is large, so
+// the wider stride costs little scratch.)
+constexpr int kArrivalSubs = 8;
+constexpr int kArrivalLine = 32;  // 32-bit words per 128 bytes
+constexpr int64_t kArrivalTwoLevelMinK = 64;
+__host__ __device__ constexpr int64_t arrival_stride(int64_t K) {
+    return K >= kArrivalTwoLevelMinK ? int64_t{kArrivalSubs + 1} * kArrivalLine : 1;
+}
+
+// Counts this workgroup's arrival (chunk k of sample n) once its
+// (write-through) partial stores have completed; true, uniformly, in the last
+// of the K.  In the two-level count the last arrival of a group of chunks
+// resets that group's counter and counts the group on word 0.
 __device__ __forceinline__ bool arrive_is_last(const StatsOut &out, int64_t n, int64_t K,
-                                               int tid) {
+                                               int64_t k, int tid) {
     __shared__ int last;
     __builtin_amdgcn_s_waitcnt(0);  // this lane's stores have completed ...
     __syncthreads();                // ... in every lane, before the arrival is counted
     if (tid == 0) {
-        const unsigned before =
-            __hip_atomic_fetch_add(out.arrivals + n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = (before == static_cast<unsigned>(K - 1));
+        unsigned *top = out.arrivals + n * arrival_stride(K);
+        if (K < kArrivalTwoLevelMinK) {
+            const unsigned before =
+                __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = (before == static_cast<unsigned>(K - 1));
+        } else {
+            const int sub = static_cast<int>(k % kArrivalSubs);
+            const unsigned in_sub =
+                static_cast<unsigned>((K - sub + kArrivalSubs - 1) / kArrivalSubs);
+            unsigned *sc = top + (1 + sub) * kArrivalLine;
+            const unsigned before =
+                __hip_atomic_fetch_add(sc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            int is_last = 0;
+            if (before == in_sub - 1) {
+                __hip_atomic_store(sc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const unsigned groups =
+                    __hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                is_last = (groups == static_cast<unsigned>(kArrivalSubs - 1));
+            }
+            last = is_last;
+        }
     }
     __syncthreads();
     return last != 0;
@@ -497,7 +532,8 @@ __device__ __forceinline__ void finalize_sample(const typename D::storage *xs,
                       out.rstd + n * G + g);
     }
     if (tid == 0)
-        __hip_atomic_store(out.arrivals + n, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(out.arrivals + n * arrival_stride(geo.K), 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // scale = gamma*rstd, shift = beta - mean*scale for the lane's slots.
@@ -628,7 +664,7 @@ gn_partial_stats(
 
     write_group_partials<L, POW2, FUSED>(s, q, red_s, red_q, geo, tg, n, k, out, tid);
     if constexpr (FUSED) {
-        if (arrive_is_last(out, n, geo.K, tid))
+        if (arrive_is_last(out, n, geo.K, k, tid))
             finalize_sample<D>(xs, geo, n, out, red_s, red_q, tid);
     }
 }

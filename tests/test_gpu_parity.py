@@ -421,3 +421,35 @@ def test_device_info_reports_the_device(gn, dev):
     assert info["memory_bytes"] == props.total_memory
     assert info["engine_clock_khz"] > 0 and info["memory_clock_khz"] > 0
     assert info["memory_bus_bits"] > 0
+
+
+def test_arrival_counters_alternating_modes(gn, dev, oracle):
+    """Shapes whose samples have >= 64 statistics chunks (two-level arrival
+    count) alternate on one stream with shapes that use one counter word per
+    sample: every repeat is bitwise equal to the first call of its shape (a
+    counter left non-zero would misplace the finalize), and the two-level one
+    matches the oracle."""
+    from gn_inputs import make_custom
+    cases = [(3, 70001, 128, 32), (1, 4096, 128, 32), (2, 40000, 256, 32), (64, 100, 32, 32)]
+    ks = [gn.plan_rows(*c)["K1"] for c in cases]
+    assert ks[0] >= 64 and ks[2] >= 64 and ks[1] < 64 and ks[3] < 64
+    data = []
+    for i, (N, L, C, G) in enumerate(cases):
+        x_bits, gamma, beta = make_custom(N, L, C, seed=300 + i)
+        data.append((to_dev_bits(x_bits, dev).reshape(N, L, C), torch.from_numpy(gamma).to(dev),
+                     torch.from_numpy(beta).to(dev), x_bits, gamma, beta))
+    first = {}
+    with torch.no_grad():
+        for rep in range(3):
+            for i, (N, L, C, G) in enumerate(cases):
+                x, g, b = data[i][:3]
+                y = gn.group_norm_silu_rows(x, G, g, b, 1e-6).view(torch.int16).clone()
+                if rep == 0:
+                    first[i] = y
+                else:
+                    assert torch.equal(y, first[i]), (rep, cases[i])
+    torch.cuda.synchronize()
+    N, L, C, G = cases[0]
+    x_bits, gamma, beta = data[0][3:]
+    compare(from_dev_bits(first[0].view(torch.bfloat16)),
+            oracle.gn_silu(x_bits, gamma, beta, N, L, C, G, 1e-6, 1), "two-level arrival")

@@ -165,7 +165,10 @@ def check_plan(N, L, C, G, dtype):
         kk_last = max(kk for j in range(tpg) for kk in range(j, K, FINALIZE_BATCH * tpg))
         top = ((N - 1) * K + kk_last + (FINALIZE_BATCH - 1) * tpg) * G + G - 1
         assert top < nparts + pad
-    counters = -(-4 * N // 256) * 256   # one arrival counter per sample
+    # arrival counters: one word per sample, or a two-level count of 8 groups
+    # plus a total, each on its own 128-byte line, when a sample has >= 64 chunks
+    words = N * ((8 + 1) * 32 if p["K1"] >= 64 else 1)
+    counters = -(-4 * words // 256) * 256
     assert p["scratch_bytes"] == counters + 4 * (2 * nparts + pad + 2 * N * G)
     assert N * G < 2 ** 24
     check_lds(p, C, G)
