@@ -752,56 +752,44 @@ __global__ __launch_bounds__(kThreads) void gn_apply(
             L::template store<NTS>(y + o0 + u * T, A, tid, o);
         }
     };
-    if constexpr (sizeof(typename D::storage) == 2) {
-        // 16-bit data: whole batches software-pipelined in two register sets.
-        // One in-order counter covers loads and stores, so waiting for a
-        // batch's loads also waits for every older store; loading batch i+1
-        // before storing batch i keeps the stores out of that wait.  The last
-        // one or two batches are peeled, so no batch is loaded twice; in place
-        // (x == y) every tile is still loaded before it is stored.  Measured on
-        // MI355X: 2-5% faster step 3 from 32 to 256 MiB, 3-15% on wide tiles,
-        // unchanged at 512 MiB, 2% slower at C = 1280; slower in fp32, which
-        // keeps the plain loop below.
-        const int64_t nb = (cr.t_full_end - tt) / UNROLL;
-        if (nb > 0) {
-            const int64_t step = UNROLL * T;
-            L a[UNROLL], b[UNROLL];
-            auto load_batch = [&](L (&v)[UNROLL], int64_t o0) {
+    // Whole batches, software-pipelined in two register sets.  One in-order
+    // counter covers loads and stores, so waiting for a batch's loads also
+    // waits for every older store; loading batch i+1 before storing batch i
+    // keeps the stores out of that wait.  The last one or two batches are
+    // peeled, so no batch is loaded twice; in place (x == y) every tile is
+    // still loaded before it is stored.  Measured on MI355X against the plain
+    // load-then-store loop: 2-5% faster step 3 for 16-bit data from 32 MiB to
+    // 1 GiB, 3-15% on wide tiles, 0-3% in fp32, 2% slower at C = 1280.
+    const int64_t nb = (cr.t_full_end - tt) / UNROLL;
+    if (nb > 0) {
+        const int64_t step = UNROLL * T;
+        L a[UNROLL], b[UNROLL];
+        auto load_batch = [&](L (&v)[UNROLL], int64_t o0) {
 #pragma unroll
-                for (int u = 0; u < UNROLL; ++u) v[u] = L::template load<NTL>(x + o0 + u * T, A, tid);
-            };
-            load_batch(a, off);
-            int64_t i = 0;
-            for (; i + 3 <= nb; i += 2) {  // batches i, i+1 and i+2 exist
-                load_batch(b, off + step);
-                __builtin_amdgcn_sched_barrier(0);
-                apply_batch(a, off);
-                load_batch(a, off + 2 * step);
-                __builtin_amdgcn_sched_barrier(0);
-                apply_batch(b, off + step);
-                off += 2 * step;
-            }
-            if (i + 2 <= nb) {  // two batches left, the first in a
-                load_batch(b, off + step);
-                __builtin_amdgcn_sched_barrier(0);
-                apply_batch(a, off);
-                apply_batch(b, off + step);
-                off += 2 * step;
-            } else {  // one batch left, in a
-                apply_batch(a, off);
-                off += step;
-            }
-            tt += nb * UNROLL;
+            for (int u = 0; u < UNROLL; ++u) v[u] = L::template load<NTL>(x + o0 + u * T, A, tid);
+        };
+        load_batch(a, off);
+        int64_t i = 0;
+        for (; i + 3 <= nb; i += 2) {  // batches i, i+1 and i+2 exist
+            load_batch(b, off + step);
+            __builtin_amdgcn_sched_barrier(0);
+            apply_batch(a, off);
+            load_batch(a, off + 2 * step);
+            __builtin_amdgcn_sched_barrier(0);
+            apply_batch(b, off + step);
+            off += 2 * step;
         }
-    } else {
-        for (; tt + UNROLL <= cr.t_full_end; tt += UNROLL) {
-            L v[UNROLL];
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u)
-                v[u] = L::template load<NTL>(x + off + u * T, A, tid);
-            apply_batch(v, off);
-            off += UNROLL * T;
+        if (i + 2 <= nb) {  // two batches left, the first in a
+            load_batch(b, off + step);
+            __builtin_amdgcn_sched_barrier(0);
+            apply_batch(a, off);
+            apply_batch(b, off + step);
+            off += 2 * step;
+        } else {  // one batch left, in a
+            apply_batch(a, off);
+            off += step;
         }
+        tt += nb * UNROLL;
     }
     if (tt < cr.t_full_end) {
         // Fewer than UNROLL whole tiles left: one batch of loads (the surplus
