@@ -45,6 +45,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 namespace gnconv {
 
@@ -258,6 +259,14 @@ __global__ __launch_bounds__(128 * WN) void gn_conv3x3(ConvArgs a) {
         *reinterpret_cast<u32x4 *>(dst + hoff[i]) = hin[i] ? out : zero;
     };
 
+    // Bias of the wave's output channels (co0 + wn*64 + ni*32 + lane % 32),
+    // read once here rather than in the epilogue, where each read would wait
+    // behind the stores before it.
+    float bias_v[2];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+        bias_v[ni] = a.bias ? a.bias[co0 + wn * 64 + ni * 32 + (lane & 31)] : 0.0f;
+
     f32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -354,7 +363,7 @@ __global__ __launch_bounds__(128 * WN) void gn_conv3x3(ConvArgs a) {
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni) {
                     const int cl = ni * 32 + fp;  // channel within the half
-                    const float bv = a.bias ? a.bias[co0 + half * 64 + cl] : 0.0f;
+                    const float bv = bias_v[ni];
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int m = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -364,39 +373,61 @@ __global__ __launch_bounds__(128 * WN) void gn_conv3x3(ConvArgs a) {
                 }
         }
         __syncthreads();
+        // Output offsets of the lane's pixels; with a residual, all of its
+        // values are loaded before the first store of z (waiting for a load
+        // also waits for every older store, one counter covering both), and
+        // before any z of the half is written, so res may alias z. A tile
+        // with every pixel inside the image takes a copy of this code with
+        // no per-pixel branch: a load or store inside one makes the compiler
+        // wait for all outstanding memory operations at each store.
+        int64_t offs[PIX];
+        u32x4 rr[PIX];
+        auto emit = [&](auto checked) {
+            constexpr bool CHECK = decltype(checked)::value;
 #pragma unroll
-        for (int i = 0; i < PIX; ++i) {
-            const int pix = prow + ROWS * i;
-            const int oh = h0 + pix / TW, ow = w0 + pix % TW;
-            valid[i] = oh < a.H && ow < a.W;
-            float v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = sO[pix * OS + 8 * q + e];
-            const int64_t off = ((static_cast<int64_t>(n) * a.H + oh) * a.W + ow) * a.Co + co0 +
-                                half * 64 + 8 * q;
-            if (valid[i]) {
+            for (int i = 0; i < PIX; ++i) {
+                const int pix = prow + ROWS * i;
+                const int oh = h0 + pix / TW, ow = w0 + pix % TW;
+                valid[i] = !CHECK || (oh < a.H && ow < a.W);
+                offs[i] = ((static_cast<int64_t>(n) * a.H + oh) * a.W + ow) * a.Co + co0 +
+                          half * 64 + 8 * q;
                 if constexpr (RES) {
-                    const u32x4 rr = *reinterpret_cast<const u32x4 *>(a.res + off);
+                    if (!CHECK || valid[i]) rr[i] = *reinterpret_cast<const u32x4 *>(a.res + offs[i]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < PIX; ++i) {
+                const int pix = prow + ROWS * i;
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = sO[pix * OS + 8 * q + e];
+                if (!CHECK || valid[i]) {
+                    if constexpr (RES) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            v[2 * e] += bf16_to_f32(rr[i][e] & 0xffffu);
+                            v[2 * e + 1] += bf16_to_f32(rr[i][e] >> 16);
+                        }
+                    }
+                    u32x4 o;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        v[2 * e] += bf16_to_f32(rr[e] & 0xffffu);
-                        v[2 * e + 1] += bf16_to_f32(rr[e] >> 16);
+                        o[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+                        // the stored (rounded) values, for the statistics
+                        vals[i][2 * e] = bf16_to_f32(o[e] & 0xffffu);
+                        vals[i][2 * e + 1] = bf16_to_f32(o[e] >> 16);
                     }
-                }
-                u32x4 o;
+                    *reinterpret_cast<u32x4 *>(a.z + offs[i]) = o;
+                } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    o[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-                    // the stored (rounded) values, for the statistics
-                    vals[i][2 * e] = bf16_to_f32(o[e] & 0xffffu);
-                    vals[i][2 * e + 1] = bf16_to_f32(o[e] >> 16);
+                    for (int e = 0; e < 8; ++e) vals[i][e] = 0.0f;
                 }
-                *reinterpret_cast<u32x4 *>(a.z + off) = o;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) vals[i][e] = 0.0f;
             }
-        }
+        };
+        if (cnt == BM)
+            emit(std::false_type{});
+        else
+            emit(std::true_type{});
         __syncthreads();  // sO fully read: free for the next half or the statistics
 
         if constexpr (STATS) {
