@@ -15,9 +15,11 @@
 //   y = SiLU?(gamma[ci] * (x - mean[n,g]) * rstd[n,g] + beta[ci])          (or y = x)
 //
 // Implicit GEMM on the matrix cores: M = output pixels, N = output channels,
-// K = 9 taps x Ci.  A workgroup of 256 lanes owns an 8 x 16 pixel x 128
-// channel output tile; each of its four waves owns 64 pixels x 64 channels as
-// 2 x 2 blocks of v_mfma_f32_32x32x16_bf16.  Per chunk of 32 input channels:
+// K = 9 taps x Ci.  A workgroup of 256 lanes owns an 8 x 16 pixel output tile
+// and 256 output channels, each of its four waves 128 pixels x 64 channels as
+// 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (when Co is not a multiple of 256:
+// 128 channels, each wave 64 pixels x 64 channels as 2 x 2 blocks).  Per
+// chunk of 32 input channels:
 //   * the 10 x 18 pixel halo of the tile is normalised (+SiLU) with
 //     per-channel scale/shift held in LDS, rounded to bf16 and stored to one
 //     of two LDS halo buffers -- every input value is transformed once per
@@ -26,11 +28,13 @@
 //     at taps 1-3 of chunk k, so the loads have most of a chunk to arrive
 //     and the VALU work overlaps the matrix-core work; one barrier per chunk;
 //   * the nine taps run against it.  Each wave reads its weight fragments
-//     straight from global memory (the 128-channel weight slice of a
-//     workgroup stays in its XCD's L2) into a ring of registers, two taps
-//     ahead of their use, so no weight tile passes through LDS and no tap
-//     needs a barrier; its A fragments come from LDS one tap ahead, into
-//     two register sets.
+//     straight from global memory (the weight slice of a workgroup stays in
+//     its XCD's L2) into a ring of registers, two taps ahead of their use, so
+//     no weight tile passes through LDS and no tap needs a barrier; its A
+//     fragments come from LDS one tap ahead (64-pixel waves: into a second
+//     register set; 128-pixel waves: each k-step's right after its products
+//     are issued, which keeps the wave within 256 registers, two waves per
+//     SIMD).
 // LDS rows are 80 bytes (32 bf16 + 8 padding), so the 16-byte fragment reads
 // of 16 consecutive lanes fall on distinct banks.
 //
@@ -133,15 +137,25 @@ __device__ __forceinline__ bool map_block(const ConvArgs &a, int64_t b, int64_t 
 // instruction schedule -- without the transform between the halo load and
 // its LDS store the compiler drains all outstanding loads at each store.
 // ---------------------------------------------------------------------------
-// WN waves along the output channels: a workgroup of 128*WN lanes owns
-// 64*WN output channels (WN = 2: 128 channels, 4 waves; WN = 4: 256 channels,
-// 8 waves).  Each wave's share is the same 64 x 64 block either way; with
-// WN = 4 the normalised halo of a chunk serves twice as many outputs, so the
-// prologue's loads and transcendentals per output halve.
-template <int WN, bool SILU, bool STATS, bool RES>
-__global__ __launch_bounds__(128 * WN) void gn_conv3x3(ConvArgs a) {
+// WM x WN waves: WM along the tile's 128 pixels, WN along the output
+// channels; a workgroup of 64*WM*WN lanes owns 64*WN output channels and each
+// wave 128/WM pixels x 64 channels, as MI x 2 blocks of 32 x 32 (MI = 4/WM).
+// WM = 2, WN = 2: 128 channels, 4 waves of 64 pixels.  WM = 1, WN = 4: 256
+// channels, 4 waves of 128 pixels -- each weight fragment a wave pulls from
+// L2 feeds twice the matrix-core work, and the normalised halo of a chunk
+// serves twice as many outputs, so the prologue's loads and transcendentals
+// per output halve.
+// Two waves per SIMD (at most 256 registers a lane): one wave stalls on its
+// loads while the other keeps the matrix core busy; left to itself the
+// compiler gives the 128-pixel waves 384 registers and one wave per SIMD,
+// measured 5-18% slower at the decoder shapes.
+template <int WM, int WN, bool SILU, bool STATS, bool RES>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+gn_conv3x3(ConvArgs a) {
+    static_assert(WM == 1 || WM == 2, "a wave owns 128 or 64 pixels");
     constexpr bool PRO = true;
-    constexpr int NT = 128 * WN;             // lanes
+    constexpr int MI = 4 / WM;               // 32-pixel blocks per wave
+    constexpr int NT = 64 * WM * WN;         // lanes
     constexpr int BNW = 64 * WN;             // output channels of the workgroup
     constexpr int ROWS = NT / 8;             // epilogue: lanes per 8-channel piece
     constexpr int PIX = BM / ROWS;           // epilogue: pixels per lane
@@ -267,9 +281,9 @@ __global__ __launch_bounds__(128 * WN) void gn_conv3x3(ConvArgs a) {
     for (int ni = 0; ni < 2; ++ni)
         bias_v[ni] = a.bias ? a.bias[co0 + wn * 64 + ni * 32 + (lane & 31)] : 0.0f;
 
-    f32x16 acc[2][2];
+    f32x16 acc[MI][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -277,17 +291,25 @@ __global__ __launch_bounds__(128 * WN) void gn_conv3x3(ConvArgs a) {
 
     bf16x8 wq[3][2][2];  // ring of weight fragments: step s in slot s % 3
     // A fragments of a tap from the current halo buffer: rows of the wave's
-    // 64 pixels shifted by the tap, k-steps ks, pixel blocks mi.
-    bf16x8 afr[2][2][2];  // [tap parity][ks][mi]
-    auto read_a = [&](const uint16_t *abuf, int t, bf16x8 (&af)[2][2]) {
+    // 32*MI pixels shifted by the tap, k-steps ks, pixel blocks mi.
+    // With 64 pixels per wave the next tap's fragments go to a second
+    // register set; with 128 there is one set, and each k-step's fragments of
+    // the next tap are read as soon as that k-step's products are issued.
+    constexpr int ASETS = MI == 2 ? 2 : 1;
+    bf16x8 afr[ASETS][2][MI];  // [tap parity][ks][mi]
+    // (the lane's part of the address is added once; the rest is a constant
+    // offset of the LDS read)
+    const int alane = ((wm * 2 * MI + frow) * HWD + fcol) * KS + fk;
+    auto read_a_ks = [&](const uint16_t *abuf, int t, int ks, bf16x8 (&af)[MI]) {
         const int kh = t / 3, kw = t % 3;
+        const uint16_t *ab = abuf + alane;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int mi = 0; mi < MI; ++mi)
+            af[mi] = *reinterpret_cast<const bf16x8 *>(ab + ((mi * 2 + kh) * HWD + kw) * KS + 16 * ks);
+    };
+    auto read_a = [&](const uint16_t *abuf, int t, bf16x8 (&af)[2][MI]) {
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) {
-                const int hp = (wm * 4 + mi * 2 + frow + kh) * HWD + fcol + kw;
-                af[ks][mi] = *reinterpret_cast<const bf16x8 *>(abuf + hp * KS + 16 * ks + fk);
-            }
+        for (int ks = 0; ks < 2; ++ks) read_a_ks(abuf, t, ks, af[ks]);
     };
     // raw holds the halo of the chunk after the current one: stored to LDS
     // early in the current chunk, then reloaded with the chunk after that.
@@ -316,16 +338,23 @@ __global__ __launch_bounds__(128 * WN) void gn_conv3x3(ConvArgs a) {
             // slots rotate with t; 9 is a multiple of 3, so slot = t % 3.
             // Past the last step the last step's weights are reloaded.
             load_w(min(s + 2, nsteps - 1), wq[(t + 2) % 3]);
-            if (t < 8) read_a(a_cur, t + 1, afr[(t + 1) & 1]);
+            if constexpr (ASETS == 2) {
+                if (t < 8) read_a(a_cur, t + 1, afr[(t + 1) & 1]);
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8 (&af)[MI] = afr[ASETS == 2 ? (t & 1) : 0][ks];
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi)
+                for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                     for (int ni = 0; ni < 2; ++ni)
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            afr[t & 1][ks][mi], wq[t % 3][ks][ni], acc[mi][ni], 0, 0, 0);
+                            af[mi], wq[t % 3][ks][ni], acc[mi][ni], 0, 0, 0);
+                if constexpr (ASETS == 1) {
+                    if (t < 8) read_a_ks(a_cur, t + 1, ks, af);
+                }
+            }
             // the next chunk's pieces are normalised and stored early, at
             // taps 1-3 (three pieces) or 1-2 (two), which frees raw for the
             // reload at tap 4
@@ -359,7 +388,7 @@ __global__ __launch_bounds__(128 * WN) void gn_conv3x3(ConvArgs a) {
     for (int half = 0; half < WN; ++half) {  // passes of 64 channels
         if (wn == half) {
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
+            for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni) {
                     const int cl = ni * 32 + fp;  // channel within the half
@@ -367,7 +396,7 @@ __global__ __launch_bounds__(128 * WN) void gn_conv3x3(ConvArgs a) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int m = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                        const int pix = wm * 64 + mi * 32 + m;
+                        const int pix = wm * 32 * MI + mi * 32 + m;
                         sO[pix * OS + cl] = acc[mi][ni][r] + bv;
                     }
                 }

@@ -288,7 +288,9 @@ gn_status gn_conv3x3_nhwc_packed(const void *x, const float *norm_mean, const fl
  * pixels), [2] nb = Co/(64*wn) output-channel blocks, [3] 1 when the
  * XCD-aware block order is used (nb divides 8), [4] workgroups with work
  * (N*tiles_h*tiles_w*nb), [5] workgroups launched, [6] wn: waves along the
- * output channels (2: workgroups of 256 lanes over 128 channels).  Returns
+ * output channels of a workgroup of 256 lanes (4 when Co is a multiple of
+ * 256: 4 waves of 128 pixels x 64 channels; else 2: 2 x 2 waves of 64 pixels
+ * x 64 channels).  Returns
  * the status
  * gn_conv3x3_nhwc would return from its argument checks for aligned
  * pointers. */

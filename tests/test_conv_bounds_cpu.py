@@ -1,9 +1,11 @@
 """Host-side proof that the fused conv kernel's accesses stay in bounds.
 
 gn_conv3x3_plan gives the launch shape; the kernel's index arithmetic is
-replayed here with its tile constants (8 x 16 output pixels, 128 output
-channels, chunks of 32 input channels, two LDS halo buffers with rows of 40
-bf16, epilogue rows of 72 fp32): the workgroup -> (tile, channel block) map
+replayed here with its tile constants (8 x 16 output pixels; 256 lanes as
+2 x 2 waves of 64 pixels x 64 channels, or as 1 x 4 waves of 128 pixels x 64
+channels when Co is a multiple of 256; chunks of 32 input channels, two LDS
+halo buffers with rows of 40 bf16, epilogue rows of 72 fp32): the workgroup
+-> (tile, channel block) map
 covers every pair once, the halo, weight-fragment, residual and output
 addresses stay inside their tensors, every LDS index stays inside its array,
 and the statistics partials stay inside their buffer.
@@ -24,6 +26,7 @@ SHAPES = [  # N, H, W, Ci, Co, G2
     (1, 8, 16, 32, 128, 32), (2, 13, 21, 64, 128, 32), (1, 32, 48, 128, 256, 32),
     (1, 5, 7, 32, 128, 8), (1, 64, 64, 512, 512, 32), (3, 9, 17, 96, 384, 24),
     (1, 128, 128, 512, 512, 32), (2, 1, 1, 32, 1024, 64), (1, 17, 33, 1024, 128, 32),
+    (1, 9, 20, 64, 768, 48), (2, 7, 40, 32, 256, 16),
 ]
 
 
@@ -41,8 +44,11 @@ def test_conv_plan_and_indices_in_bounds(N, H, W, Ci, Co, G2):
     p = gn.conv_plan(N, H, W, Ci, Co, G2)
     assert p is not None
     WN = p["wn"]
-    assert WN == 2
-    NT, BNW = 128 * WN, 64 * WN                  # lanes, output channels per workgroup
+    assert WN == (4 if Co % 256 == 0 else 2)
+    WM = 4 // WN                                 # waves along the pixels
+    MI = 4 // WM                                 # 32-pixel blocks per wave
+    NT, BNW = 64 * WM * WN, 64 * WN              # lanes, output channels per workgroup
+    assert NT == 256
     assert p["tiles_h"] == -(-H // TH) and p["tiles_w"] == -(-W // TW) and p["nb"] == Co // BNW
     tps = p["tiles_h"] * p["tiles_w"]
     assert p["blocks"] == N * tps * p["nb"] and p["grid"] < 2 ** 31
@@ -68,11 +74,11 @@ def test_conv_plan_and_indices_in_bounds(N, H, W, Ci, Co, G2):
     lane = np.arange(64)
     fp, fk = lane % 32, 8 * (lane // 32)
     for buf in (0, 1):
-        for wm in range(NT // 64 // WN):
-            for mi in (0, 1):
+        for wm in range(WM):
+            for mi in range(MI):
                 for kh in range(3):
                     for kw in range(3):
-                        hp = (wm * 4 + mi * 2 + fp // 16 + kh) * HWD + fp % 16 + kw
+                        hp = (wm * 2 * MI + mi * 2 + fp // 16 + kh) * HWD + fp % 16 + kw
                         assert np.all(buf * A_ELEMS + hp * KS + 16 + fk + 8 <= LDS_MAIN)
                         assert np.all(hp < HH * HWD)
     # packed weight fragments, read from global memory: block cb, step s,
@@ -106,7 +112,7 @@ def test_conv_plan_and_indices_in_bounds(N, H, W, Ci, Co, G2):
     # epilogue staging and the statistics scratch in the same LDS
     r = np.arange(16)
     m = 8 * (r[:, None] // 4) + 4 * (lane[None, :] // 32) + r[:, None] % 4
-    pixl = 64 * (NT // 64 // WN - 1) + 32 * 1 + m
+    pixl = 32 * MI * (WM - 1) + 32 * (MI - 1) + m
     assert (pixl * OS + 63).max() < LDS_EPI_FLOATS and m.max() < 32
     ROWS = NT // 8
     assert ROWS * 64 + 64 <= LDS_EPI_FLOATS and (TH * TW) % ROWS == 0

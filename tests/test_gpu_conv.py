@@ -151,6 +151,7 @@ SHAPES = [  # N, H, W, Ci, Co, G, G2
     (1, 8, 16, 32, 128, 8, 32), (2, 13, 21, 64, 128, 32, 32), (1, 32, 48, 128, 256, 32, 32),
     (1, 5, 7, 32, 128, 4, 8), (3, 9, 17, 96, 384, 24, 24), (1, 17, 33, 1024, 128, 32, 32),
     (2, 1, 1, 32, 1024, 8, 64), (1, 24, 40, 512, 512, 32, 32), (1, 16, 16, 256, 256, 32, 16),
+    (2, 13, 21, 64, 256, 32, 32), (1, 9, 20, 64, 768, 16, 48),
 ]
 
 
@@ -178,7 +179,7 @@ def test_gn_silu_conv_with_statistics(gn, dev, oracle, N, H, W, Ci, Co, G, G2):
     check_stats(m2, r2, ref, tol, N, H * W, Co, G2, 1e-6, "gn+silu+conv")
 
 
-@pytest.mark.parametrize("N,H,W,Ci,Co,G,G2", [SHAPES[1], SHAPES[4], SHAPES[7]])
+@pytest.mark.parametrize("N,H,W,Ci,Co,G,G2", [SHAPES[1], SHAPES[4], SHAPES[7], SHAPES[9]])
 def test_gn_conv_residual_without_silu(gn, dev, oracle, N, H, W, Ci, Co, G, G2):
     x, gamma, beta, wb, bias, r = make_problem(N, H, W, Ci, Co, seed=300 + Co, res=True)
     z, m2, r2 = run_gpu(gn, dev, N, H, W, Ci, Co, x, gamma, beta, wb, bias, r, G, False, True,
