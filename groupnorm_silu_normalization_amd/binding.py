@@ -18,8 +18,8 @@ tensor, or None when the input is outside the supported set so the caller
 falls back: not a GPU tensor, autograd enabled, another dtype, a channel
 count the library declines (GN_UNSUPPORTED: see the supported set in
 gnsilu.h; every C <= 256, every multiple of 8 up to 2048 and more), not
-channels-last (4-D / 5-D) / not contiguous rows, weight/bias not fp32 on the
-same device.  Arguments no GroupNorm accepts raise ValueError; a failed HIP
+channels-last (4-D / 5-D) / not contiguous rows, weight/bias not fp32, bf16 or
+fp16 (both of one type) on the same device.  Arguments no GroupNorm accepts raise ValueError; a failed HIP
 call raises RuntimeError.
 
 The raw C entry points are re-exported under their C names (gn_silu_nhwc,
@@ -166,6 +166,26 @@ def dtype_code(dt):
     return _TORCH_DTYPE.get(dt)
 
 
+# Element type of gamma and beta, or-ed into the dtype argument (GN_AFFINE_*).
+AFFINE_FLAG = {torch.float32: 0x10, torch.bfloat16: 0x20, torch.float16: 0x30}
+
+
+def _affine_flag(weight, bias):
+    """GN_AFFINE_* value for weight and bias, 0 when both are None, None when
+    their types differ."""
+    types = {p.dtype for p in (weight, bias) if p is not None}
+    if len(types) > 1:
+        return None
+    return AFFINE_FLAG[types.pop()] if types else 0
+
+
+def _affine_arg(weight, bias):
+    f = _affine_flag(weight, bias)
+    if f is None:
+        raise TypeError("weight and bias must have the same dtype")
+    return f
+
+
 class GnStatus(enum.IntEnum):
     OK = 0
     UNSUPPORTED = 1
@@ -199,7 +219,7 @@ def _affine_ok(p, C, device, name):
         raise TypeError("%s must be a tensor or None" % name)
     if p.numel() != C:
         raise ValueError("%s must have C=%d elements, got %d" % (name, C, p.numel()))
-    if p.dtype != torch.float32 or p.device != device or not p.is_contiguous():
+    if p.dtype not in AFFINE_FLAG or p.device != device or not p.is_contiguous():
         return False
     return True
 
@@ -218,7 +238,7 @@ def _common_checks(x, weight, bias, C):
         return False
     if not _affine_ok(weight, C, x.device, "weight") or not _affine_ok(bias, C, x.device, "bias"):
         return False
-    return True
+    return _affine_flag(weight, bias) is not None
 
 
 def _result(code, out):
@@ -254,8 +274,8 @@ def group_norm_silu_4d(x, num_groups, weight=None, bias=None, eps=1e-6, apply_si
         raise ValueError("out must match x in shape, dtype and device")
     code = lib.gn_silu_nhwc_strided_dtype(
         _ptr(x), _i64x4(*x.stride()), _ptr(weight), _ptr(bias), _ptr(out), _i64x4(*out.stride()),
-        N, H, W, C, num_groups, float(eps), 1 if apply_silu else 0, dtype_code(x.dtype),
-        _stream_handle(x))
+        N, H, W, C, num_groups, float(eps), 1 if apply_silu else 0,
+        dtype_code(x.dtype) | _affine_flag(weight, bias), _stream_handle(x))
     return _result(code, out)
 
 
@@ -277,8 +297,8 @@ def group_norm_silu_5d(x, num_groups, weight=None, bias=None, eps=1e-6, apply_si
         raise ValueError("out must match x in shape, dtype and device")
     code = lib.gn_silu_ndhwc_strided_dtype(
         _ptr(x), _i64x5(*x.stride()), _ptr(weight), _ptr(bias), _ptr(out), _i64x5(*out.stride()),
-        N, D, H, W, C, num_groups, float(eps), 1 if apply_silu else 0, dtype_code(x.dtype),
-        _stream_handle(x))
+        N, D, H, W, C, num_groups, float(eps), 1 if apply_silu else 0,
+        dtype_code(x.dtype) | _affine_flag(weight, bias), _stream_handle(x))
     return _result(code, out)
 
 
@@ -301,7 +321,8 @@ def group_norm_silu_rows(x, num_groups, weight=None, bias=None, eps=1e-6, apply_
         raise ValueError("out must be a contiguous tensor matching x")
     code = lib.gn_silu_rows_dtype(_ptr(x), _ptr(weight), _ptr(bias), _ptr(out), N, L, C,
                                   num_groups, float(eps), 1 if apply_silu else 0,
-                                  dtype_code(x.dtype), _stream_handle(x))
+                                  dtype_code(x.dtype) | _affine_flag(weight, bias),
+                                  _stream_handle(x))
     return _result(code, out)
 
 
@@ -325,8 +346,8 @@ def apply_rows(x, mean, rstd, weight=None, bias=None, apply_silu=True, out=None)
     if out is None:
         out = torch.empty_like(x)
     code = lib.gn_apply_rows_dtype(_ptr(x), _ptr(mean), _ptr(rstd), _ptr(weight), _ptr(bias),
-                                   _ptr(out), N, L, C, G, 1 if apply_silu else 0, _dtype_arg(x),
-                                   _stream_handle(x))
+                                   _ptr(out), N, L, C, G, 1 if apply_silu else 0,
+                                   _dtype_arg(x) | _affine_arg(weight, bias), _stream_handle(x))
     return _result(code, out)
 
 
@@ -358,7 +379,8 @@ def profile_rows(x, num_groups, weight, bias, eps, apply_silu, out, iters):
     nk = _int(0)
     code = lib.gn_profile_rows_dtype(_ptr(x), _ptr(weight), _ptr(bias), _ptr(out), N, L, C,
                                      num_groups, float(eps), 1 if apply_silu else 0,
-                                     _dtype_arg(x), _stream_handle(x), int(iters), ms,
+                                     _dtype_arg(x) | _affine_arg(weight, bias),
+                                     _stream_handle(x), int(iters), ms,
                                      ctypes.byref(nk))
     if code != GnStatus.OK:
         _result(code, None)
@@ -443,6 +465,8 @@ def conv3x3(x, weight, bias=None, *, norm=None, apply_silu=False, residual=None,
                 return None
         if not _affine_ok(ga, Ci, x.device, "gamma") or not _affine_ok(be, Ci, x.device, "beta"):
             return None
+        if any(t is not None and t.dtype != torch.float32 for t in (ga, be)):
+            return None  # the convolution's prologue takes fp32 gamma and beta
     if out is None:
         out = torch.empty((N, Co, H, W), dtype=torch.bfloat16, device=x.device,
                           memory_format=torch.channels_last)

@@ -60,10 +60,22 @@ inline int64_t gcd64(int64_t a, int64_t b) {
 }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// The dtype argument: a gn_dtype for x and y in the low bits, or-ed with at
+// most one GN_AFFINE_* value for gamma and beta (none: fp32).
+inline int x_dtype(int dtype) { return dtype & ~GN_AFFINE_MASK; }
 inline bool valid_dtype(int dtype) {
-    return dtype == GN_DTYPE_BF16 || dtype == GN_DTYPE_F16 || dtype == GN_DTYPE_F32;
+    const int xd = x_dtype(dtype), ad = dtype & GN_AFFINE_MASK;
+    return (xd == GN_DTYPE_BF16 || xd == GN_DTYPE_F16 || xd == GN_DTYPE_F32) &&
+           (ad == 0 || ad == GN_AFFINE_F32 || ad == GN_AFFINE_BF16 || ad == GN_AFFINE_F16);
 }
-inline int64_t elem_bytes(int dtype) { return dtype == GN_DTYPE_F32 ? 4 : 2; }
+inline int affine_type(int dtype) {
+    switch (dtype & GN_AFFINE_MASK) {
+        case GN_AFFINE_BF16: return Affine::kBf16;
+        case GN_AFFINE_F16: return Affine::kF16;
+        default: return Affine::kF32;
+    }
+}
+inline int64_t elem_bytes(int dtype) { return x_dtype(dtype) == GN_DTYPE_F32 ? 4 : 2; }
 
 // How a tile is laid over the lanes (see gn_kernels.hpp): R whole rows,
 // T = R*C = A*W*NV elements; the first A lanes each make NV accesses of W
@@ -111,6 +123,7 @@ struct Plan {
     bool fused;       // step 2 runs in the tail of step 1 (G <= kThreads)
     bool apply_ntl;   // step 3 reads x with nontemporal loads
     int dtype;        // gn_dtype of x and y
+    int affine;       // element type of gamma and beta (Affine::kF32, ...)
     Geometry stats;   // chunking of steps 1 and 2
     Geometry apply;   // chunking of step 3
     int64_t N;
@@ -122,7 +135,8 @@ struct Plan {
 Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G, int dtype) {
     Plan p;
     p.N = N;
-    p.dtype = dtype;
+    p.dtype = x_dtype(dtype);
+    p.affine = affine_type(dtype);
     const int64_t E = L * C;
     (void)choose_layout(E, C, dtype, &p.lay);  // check_shape has accepted the shape
     p.fused = G <= kThreads;
@@ -393,7 +407,7 @@ void launch_stats_t(const Plan &p, const void *xv, const StatsOut &o, hipStream_
 
 template <class D, bool SILU>
 void launch_apply_s(const Plan &p, const void *xv, void *yv, const float *mean, const float *rstd,
-                    const float *gamma, const float *beta, hipStream_t s) {
+                    const Affine &af, hipStream_t s) {
     using T = typename D::storage;
     const T *x = static_cast<const T *>(xv);
     T *y = static_cast<T *>(yv);
@@ -406,22 +420,21 @@ void launch_apply_s(const Plan &p, const void *xv, void *yv, const float *mean, 
         constexpr int U = unroll_for(kUnrollApply, NV);
         if (p.apply_ntl)
             gn_apply<D, W, NV, P2, U, SILU, true, true><<<grid, block, 0, s>>>(
-                x, y, p.apply, mean, rstd, gamma, beta);
+                x, y, p.apply, mean, rstd, af);
         else
             gn_apply<D, W, NV, P2, U, SILU, false, true><<<grid, block, 0, s>>>(
-                x, y, p.apply, mean, rstd, gamma, beta);
+                x, y, p.apply, mean, rstd, af);
     });
 }
 
 template <class D>
 void launch_apply_t(const Plan &p, const void *x, void *y, const float *mean, const float *rstd,
-                    const float *gamma, const float *beta, int silu, hipStream_t s,
-                    const Events *ev) {
+                    const Affine &af, int silu, hipStream_t s, const Events *ev) {
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotApply], s);
     if (silu)
-        launch_apply_s<D, true>(p, x, y, mean, rstd, gamma, beta, s);
+        launch_apply_s<D, true>(p, x, y, mean, rstd, af, s);
     else
-        launch_apply_s<D, false>(p, x, y, mean, rstd, gamma, beta, s);
+        launch_apply_s<D, false>(p, x, y, mean, rstd, af, s);
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotApply + 1], s);
 }
 
@@ -435,18 +448,16 @@ void launch_stats(const Plan &p, const void *x, const StatsOut &o, hipStream_t s
 }
 
 void launch_apply(const Plan &p, const void *x, void *y, const float *mean, const float *rstd,
-                  const float *gamma, const float *beta, int silu, hipStream_t s,
+                  const void *gamma, const void *beta, int silu, hipStream_t s,
                   const Events *ev) {
+    Affine af;
+    af.gamma = gamma;
+    af.beta = beta;
+    af.type = p.affine;
     switch (p.dtype) {
-        case GN_DTYPE_F16:
-            launch_apply_t<Fp16>(p, x, y, mean, rstd, gamma, beta, silu, s, ev);
-            break;
-        case GN_DTYPE_F32:
-            launch_apply_t<F32>(p, x, y, mean, rstd, gamma, beta, silu, s, ev);
-            break;
-        default:
-            launch_apply_t<Bf16>(p, x, y, mean, rstd, gamma, beta, silu, s, ev);
-            break;
+        case GN_DTYPE_F16: launch_apply_t<Fp16>(p, x, y, mean, rstd, af, silu, s, ev); break;
+        case GN_DTYPE_F32: launch_apply_t<F32>(p, x, y, mean, rstd, af, silu, s, ev); break;
+        default: launch_apply_t<Bf16>(p, x, y, mean, rstd, af, silu, s, ev); break;
     }
 }
 
@@ -468,6 +479,14 @@ gn_status begin_call(void *stream, const std::vector<const void *> &ptrs, Call *
     return GN_OK;
 }
 
+// gamma and beta aligned to their element type.
+gn_status check_affine(const void *gamma, const void *beta, int dtype) {
+    const uintptr_t m = affine_type(dtype) == Affine::kF32 ? 3u : 1u;
+    for (const void *q : {gamma, beta})
+        if (q != nullptr && (reinterpret_cast<uintptr_t>(q) & m) != 0) return GN_UNSUPPORTED;
+    return GN_OK;
+}
+
 gn_status finish_launch() {
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? GN_OK : GN_DEVICE_ERROR;
@@ -478,6 +497,7 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
                    int64_t L, int64_t C, int64_t G, float eps, int apply_silu, int dtype,
                    void *stream, int iters, float *kernel_ms) {
     gn_status st = check_shape(x, y, N, L, C, G, eps, apply_silu, true, dtype);
+    if (st == GN_OK) st = check_affine(gamma, beta, dtype);
     if (st != GN_OK) return st;
     if (N * L == 0) {
         if (kernel_ms)
@@ -817,6 +837,7 @@ gn_status gn_apply_rows_dtype(const void *x, const float *mean, const float *rst
                               void *stream) {
     if (mean == nullptr || rstd == nullptr) return GN_INVALID_ARGUMENT;
     gn_status st = check_shape(x, y, N, L, C, G, 0.0f, apply_silu, true, dtype);
+    if (st == GN_OK) st = check_affine(gamma, beta, dtype);
     if (st != GN_OK) return st;
     if (N * L == 0) return GN_OK;
     Call c;

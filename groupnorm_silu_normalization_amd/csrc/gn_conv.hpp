@@ -111,7 +111,7 @@ __device__ __forceinline__ float silu(float t) {
 // Workgroup -> (sample, tile, output-channel block).  Dispatch hands
 // consecutive workgroups to the 8 XCDs in turn; with xcd_map, the XCDs are
 // split into nb sets, each set working on one output-channel block (so each
-// XCD's L2 holds one 128-channel slice of the weights) and all sets walking
+// XCD's L2 holds one slice of the weights: 128 or 256 channels) and all sets walking
 // the pixel tiles in the same order (so the nb reads of an input tile fall
 // close together in time and share the Infinity Cache).
 __device__ __forceinline__ bool map_block(const ConvArgs &a, int64_t b, int64_t *tile,

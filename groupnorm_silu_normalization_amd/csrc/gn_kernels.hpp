@@ -536,11 +536,26 @@ __device__ __forceinline__ void finalize_sample(const typename D::storage *xs,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// gamma and beta: C values each, or null (1 and 0), of element type kF32,
+// kBf16 or kF16; widened exactly to fp32 before the fold.
+struct Affine {
+    enum : int { kF32 = 0, kBf16 = 1, kF16 = 2 };
+    const void *gamma;
+    const void *beta;
+    int type;
+};
+
+__device__ __forceinline__ float affine_at(const void *p, int c, int type, float absent) {
+    if (p == nullptr) return absent;
+    if (type == Affine::kBf16) return Bf16::to_f32(static_cast<const uint16_t *>(p)[c]);
+    if (type == Affine::kF16) return Fp16::to_f32(static_cast<const uint16_t *>(p)[c]);
+    return static_cast<const float *>(p)[c];
+}
+
 // scale = gamma*rstd, shift = beta - mean*scale for the lane's slots.
 template <class L, bool POW2>
 __device__ __forceinline__ void fold_affine(const float *mean, const float *rstd,
-                                            const float *gamma, const float *beta,
-                                            const Geometry &geo,
+                                            const Affine &af, const Geometry &geo,
                                             const TileGeo<POW2, L::kSlots> &tg_, int64_t n,
                                             int tid, float (&sc)[L::kSlots],
                                             float (&sh)[L::kSlots]) {
@@ -548,8 +563,8 @@ __device__ __forceinline__ void fold_affine(const float *mean, const float *rstd
     for (int j = 0; j < L::kSlots; ++j) {
         const int c = tg_.channel(L::slot_offset(tg_.lanes(), tid, j));
         const int64_t gi = n * geo.G + tg_.group_of(c);
-        const float ga = gamma ? gamma[c] : 1.0f;
-        const float be = beta ? beta[c] : 0.0f;
+        const float ga = affine_at(af.gamma, c, af.type, 1.0f);
+        const float be = affine_at(af.beta, c, af.type, 0.0f);
         sc[j] = ga * rstd[gi];
         sh[j] = fmaf(-mean[gi], sc[j], be);
     }
@@ -723,8 +738,7 @@ __global__ __launch_bounds__(kThreads) void gn_zero_u32(unsigned *p, int64_t n) 
 template <class D, int W, int NV, bool POW2, int UNROLL, bool SILU, bool NTL, bool NTS>
 __global__ __launch_bounds__(kThreads) void gn_apply(
     const typename D::storage *x, typename D::storage *y, Geometry geo,
-    const float *__restrict__ mean, const float *__restrict__ rstd,
-    const float *__restrict__ gamma, const float *__restrict__ beta) {
+    const float *__restrict__ mean, const float *__restrict__ rstd, Affine af) {
     using L = Lane<D, W, NV>;
     constexpr int S = L::kSlots;
     const TileGeo<POW2, S> tg(geo);
@@ -737,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void gn_apply(
     const int64_t k = wg - n * geo.K;
 
     float sc[S], sh[S];
-    fold_affine<L, POW2>(mean, rstd, gamma, beta, geo, tg, n, tid, sc, sh);
+    fold_affine<L, POW2>(mean, rstd, af, geo, tg, n, tid, sc, sh);
 
     const int64_t base = n * geo.E;
     const ChunkRange cr = chunk_range(geo, k);

@@ -97,6 +97,27 @@ typedef enum gn_dtype {
     GN_DTYPE_F32 = 2
 } gn_dtype;
 
+/* Element type of gamma and beta, or-ed into the dtype argument of the
+ * *_dtype entry points that take them (gn_silu_*_dtype, gn_apply_rows_dtype,
+ * gn_profile_rows_dtype; the others accept and ignore it).  The decoder
+ * fast path folds its weights in fp32 ("FLUX.2 VAE decoder fast path behind
+ * quality=high", the summary after Motivation) and the GroupNorm affine
+ * parameters into fp32 scale/shift (Modifications, the kernel item), while
+ * a model cast to bf16 or fp16 holds gamma and beta in that type: with
+ * GN_AFFINE_BF16 or GN_AFFINE_F16 the gamma and beta
+ * pointers (declared const float *) point at C 16-bit values of that type,
+ * 2-byte aligned, each widened exactly to fp32 before the fold; without a
+ * GN_AFFINE_* value, or with GN_AFFINE_F32, they point at C fp32 values,
+ * 4-byte aligned.  A misaligned gamma or beta is GN_UNSUPPORTED; a dtype
+ * argument with other bits set, or two GN_AFFINE_* values, is
+ * GN_INVALID_ARGUMENT. */
+enum {
+    GN_AFFINE_F32 = 0x10,
+    GN_AFFINE_BF16 = 0x20,
+    GN_AFFINE_F16 = 0x30,
+    GN_AFFINE_MASK = 0x30
+};
+
 /* Largest channel count the library accepts.  The pages' kernel stops at
  * 2048 (Modifications section 1); the tile layout here reaches 8192. */
 #define GN_MAX_CHANNELS 8192

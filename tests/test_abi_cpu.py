@@ -19,6 +19,8 @@ import subprocess
 
 import pytest
 
+torch = pytest.importorskip("torch")
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gnsilu.h")
 
@@ -121,6 +123,52 @@ def test_dtype_entry_points_share_the_checks():
                                      None) == GnStatus.OK
         assert gn.gn_silu_nhwc_dtype(None, None, None, Y, 1, 4, 4, 64, 32, 1e-6, 1, dt,
                                      None) == GnStatus.INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("dtype", [0x40, 0x100, 0x23, 0x13, 0x33, -0x10])
+def test_invalid_affine_flags(dtype):
+    assert gn.gn_silu_rows_dtype(X, None, None, Y, 1, 16, 64, 32, 1e-6, 1, dtype,
+                                 None) == GnStatus.INVALID_ARGUMENT
+    assert gn.gn_stats_rows_dtype(X, 1, 16, 64, 32, 1e-6, dtype, Y, Y,
+                                  None) == GnStatus.INVALID_ARGUMENT
+
+
+def test_affine_flags_checked_before_any_hip_call():
+    odd, even2 = ctypes.c_void_p(0x30001), ctypes.c_void_p(0x30002)
+    for dt in (0, 1, 2):
+        for af in (0, 0x10, 0x20, 0x30):
+            assert gn.gn_silu_rows_dtype(X, None, None, Y, 0, 16, 64, 32, 1e-6, 1, dt | af,
+                                         None) == GnStatus.OK
+            # the launch plan does not depend on the type of gamma and beta
+            assert gn.plan_rows(3, 1000, 320, 32, dt | af) == gn.plan_rows(3, 1000, 320, 32, dt)
+        # gamma / beta misaligned for their element type: declined
+        assert gn.gn_silu_rows_dtype(X, odd, None, Y, 1, 16, 64, 32, 1e-6, 1, dt | 0x20,
+                                     None) == GnStatus.UNSUPPORTED
+        assert gn.gn_silu_rows_dtype(X, None, odd, Y, 1, 16, 64, 32, 1e-6, 1, dt | 0x30,
+                                     None) == GnStatus.UNSUPPORTED
+        assert gn.gn_silu_rows_dtype(X, even2, None, Y, 1, 16, 64, 32, 1e-6, 1, dt,
+                                     None) == GnStatus.UNSUPPORTED
+        assert gn.gn_silu_rows_dtype(X, None, even2, Y, 1, 16, 64, 32, 1e-6, 1, dt | 0x10,
+                                     None) == GnStatus.UNSUPPORTED
+        assert gn.gn_apply_rows_dtype(X, Y, Y, odd, None, Y, 1, 16, 64, 32, 1, dt | 0x20,
+                                      None) == GnStatus.UNSUPPORTED
+
+
+def test_affine_flags_match_the_header():
+    text = open(HEADER).read()
+    vals = {k: int(v, 16) for k, v in re.findall(r"(GN_AFFINE_\w+) = (0x[0-9a-fA-F]+)", text)}
+    assert vals["GN_AFFINE_F32"] == gn.AFFINE_FLAG[torch.float32]
+    assert vals["GN_AFFINE_BF16"] == gn.AFFINE_FLAG[torch.bfloat16]
+    assert vals["GN_AFFINE_F16"] == gn.AFFINE_FLAG[torch.float16]
+    assert vals["GN_AFFINE_MASK"] == 0x30
+    # the binding's choice of flag for weight and bias
+    from groupnorm_silu_normalization_amd.binding import _affine_flag
+    t = torch.zeros(4)
+    assert _affine_flag(None, None) == 0
+    assert _affine_flag(t, None) == 0x10
+    assert _affine_flag(t.bfloat16(), t.bfloat16()) == 0x20
+    assert _affine_flag(None, t.half()) == 0x30
+    assert _affine_flag(t, t.bfloat16()) is None
 
 
 def test_plan_uses_element_size_for_the_cache_threshold():

@@ -350,7 +350,10 @@ def test_unsupported_inputs_return_none(gn, dev):
         assert gn.group_norm_silu_4d(x, 32, g, g) is None                          # not channels_last
         xc = x.to(memory_format=torch.channels_last)
         assert gn.group_norm_silu_4d(xc, 32, g, g) is not None
-        assert gn.group_norm_silu_4d(xc.half(), 32, g.half(), g.half()) is None    # fp16
+        assert gn.group_norm_silu_4d(xc.half(), 32, g.half(), g.half()) is not None  # fp16
+        assert gn.group_norm_silu_4d(xc, 32, g.double(), g.double()) is None       # fp64 affine
+        assert gn.group_norm_silu_4d(xc, 32, g.half(), g) is None                  # mixed affine
+        assert gn.group_norm_silu_4d(xc.double(), 32, g, g) is None                # fp64 x
         x3k = torch.randn(1, 3000, 4, 4, device=dev).to(torch.bfloat16).to(memory_format=torch.channels_last)
         assert gn.group_norm_silu_4d(x3k, 8) is None                               # no tile layout
         x16k = torch.randn(1, 16384, 2, 2, device=dev).to(torch.bfloat16).to(memory_format=torch.channels_last)
