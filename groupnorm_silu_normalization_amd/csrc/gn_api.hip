@@ -292,10 +292,18 @@ gn_status zero_counters(unsigned *p, int64_t n, hipStream_t s) {
     return hipGetLastError() == hipSuccess ? GN_OK : GN_DEVICE_ERROR;
 }
 
+// Buffers a stream has outgrown.  They are never freed: work already
+// enqueued, and HIP graphs captured with calls of this library, keep their
+// addresses and may run (or be replayed) at any later time.  Growth doubles,
+// so the retired buffers of a stream total less than its current one.
+std::vector<void *> &retired_scratch() {
+    static auto *v = new std::vector<void *>;
+    return *v;
+}
+
 // Caller holds scratch_mutex().  Returns the arrival counter words (>= n of
 // them, all zero in stream order) and the payload (>= payload bytes).  Grows the
-// buffer when needed; the old one is released only after the stream has
-// drained the work that used it.
+// buffer when needed; the old one is retired, not freed.
 gn_status scratch_for(int dev, hipStream_t s, int64_t n, size_t payload, unsigned **counters,
                       char **payload_ptr) {
     Scratch &sc = scratch_map()[{dev, reinterpret_cast<uintptr_t>(s)}];
@@ -304,12 +312,6 @@ gn_status scratch_for(int dev, hipStream_t s, int64_t n, size_t payload, unsigne
     const size_t need = head + payload;
     bool clear = want_arrivals > sc.arrivals;  // the counter region grows
     if (sc.bytes < need) {
-        if (sc.ptr != nullptr) {
-            if (hipStreamSynchronize(s) != hipSuccess) return GN_DEVICE_ERROR;
-            (void)hipFree(sc.ptr);
-            sc.ptr = nullptr;
-            sc.bytes = 0;
-        }
         size_t sz = size_t{1} << 16;
         while (sz < need) sz <<= 1;
         void *p = nullptr;
@@ -317,6 +319,7 @@ gn_status scratch_for(int dev, hipStream_t s, int64_t n, size_t payload, unsigne
             (void)hipGetLastError();
             return GN_DEVICE_ERROR;
         }
+        if (sc.ptr != nullptr) retired_scratch().push_back(sc.ptr);
         sc.ptr = static_cast<char *>(p);
         sc.bytes = sz;
         clear = true;  // fresh memory

@@ -42,9 +42,15 @@
  *   they must stay valid until the stream has executed the call.  The
  *   library owns a scratch buffer per (device, stream) for the partial sums
  *   and per-sample arrival counters (tens of KiB for the decoder shapes,
- *   grown on demand, held until the process ends).  Calls enqueued on one
- *   stream from several host threads are serialised by the library; calls on
- *   different streams use different scratch buffers.
+ *   grown on demand by doubling; a buffer that is outgrown is kept, not
+ *   freed, and every buffer is held until the process ends, so work already
+ *   enqueued and HIP graphs captured with these calls stay valid).  Calls
+ *   enqueued on one stream from several host threads are serialised by the
+ *   library; calls on different streams use different scratch buffers.  A
+ *   captured graph uses the scratch of the stream it was captured on:
+ *   replay it on that stream, or ordered with that stream's work.  A call
+ *   under capture must not need a larger buffer than that stream already
+ *   has (make one call of the same shape on the stream before capturing).
  * Synchrony: every compute call is asynchronous on `stream` and returns once
  *   the kernels are enqueued; a fault inside a kernel surfaces at the
  *   caller's next synchronisation (gn_profile_rows excepted, which

@@ -456,3 +456,37 @@ def test_arrival_counters_alternating_modes(gn, dev, oracle):
     x_bits, gamma, beta = data[0][3:]
     compare(from_dev_bits(first[0].view(torch.bfloat16)),
             oracle.gn_silu(x_bits, gamma, beta, N, L, C, G, 1e-6, 1), "two-level arrival")
+
+
+# ------------------------------------------------------------- HIP graphs
+def test_graph_replays_after_the_scratch_grows(gn, dev):
+    """A GroupNorm captured into a HIP graph keeps the stream's scratch buffer
+    of capture time.  A later call on the same stream that needs a larger
+    buffer retires the old one without freeing it, so every replay, before
+    and after, equals the eager result bit for bit."""
+    small, big = (1, 4096, 128, 32), (4, 16384, 512, 32)
+    assert gn.plan_rows(*small)["scratch_bytes"] <= 1 << 16 < gn.plan_rows(*big)["scratch_bytes"]
+    gen = torch.Generator(device="cpu").manual_seed(21)
+    xs = torch.randn(small[:3], generator=gen).bfloat16().to(dev)
+    xb = torch.randn(big[:3], generator=gen).bfloat16().to(dev)
+    stream = torch.cuda.Stream(dev)
+    with torch.no_grad():
+        with torch.cuda.stream(stream):
+            ref = gn.group_norm_silu_rows(xs, 32).clone()  # allocates the stream's scratch
+            gn.group_norm_silu_rows(xs, 32)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            out = gn.group_norm_silu_rows(xs, 32)
+        for rep in range(3):
+            with torch.cuda.stream(stream):
+                g.replay()
+                refb = gn.group_norm_silu_rows(xb, 32)  # grows the scratch on the first pass
+            stream.synchronize()
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "replay %d" % rep
+            with torch.cuda.stream(stream):
+                g.replay()                               # after the growth
+                again = gn.group_norm_silu_rows(xb, 32)
+            stream.synchronize()
+            assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "replay %d" % rep
+            assert torch.equal(again.view(torch.int16), refb.view(torch.int16))
