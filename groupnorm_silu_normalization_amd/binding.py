@@ -352,7 +352,7 @@ def apply_rows(x, mean, rstd, weight=None, bias=None, apply_silu=True, out=None)
 
 
 PLAN_FIELDS = ("slots", "tiles", "full", "tpc1", "K1", "tpc2", "K2", "scratch_bytes",
-               "apply_nontemporal_loads", "W", "A", "T", "stats_plain_tail")
+               "apply_nontemporal_loads", "W", "A", "T", "stats_plain_tail", "late_finalize")
 
 
 def _dtype_arg(x):

@@ -121,6 +121,7 @@ bool choose_layout(int64_t E, int64_t C, int dtype, Layout *out) {
 struct Plan {
     Layout lay;       // tile layout
     bool fused;       // step 2 runs in the tail of step 1 (G <= kThreads)
+    bool late;        // ... or, for a small x, in the prologue of step 3 (LateStats)
     bool apply_ntl;   // step 3 reads x with nontemporal loads
     int dtype;        // gn_dtype of x and y
     int affine;       // element type of gamma and beta (Affine::kF32, ...)
@@ -183,6 +184,13 @@ Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G, int dtype) {
     p.apply.tpc = std::max<int64_t>(1, ceil_div(total, apply_blocks));
     p.apply.K = ceil_div(g.tiles, p.apply.tpc);
     p.inv_m = 1.0 / (static_cast<double>(L) * static_cast<double>(C / G));
+    // The late finalize: for a small x (latency-bound) whose sample's step-1
+    // partials one finalize batch per thread covers, step 1 only writes its
+    // partials and every step-3 workgroup reduces them itself: the arrival
+    // count and the last workgroup's round trips leave the chain.  Bounded to
+    // small x because every step-3 workgroup re-reads the sample's partials.
+    p.late = p.fused && bytes <= kStatsSmallBytes &&
+             p.stats.K <= kFinalizeBatch * (kThreads / G);
     return p;
 }
 
@@ -381,8 +389,10 @@ void with_layout(const Plan &p, F &&f) {
 // many tiles of four.
 constexpr int unroll_for(int base, int nv) { return nv <= 2 ? base : base / 4; }
 
+// late: the plan's late finalize runs in step 3, so step 1 only writes its
+// partials (false for a caller that needs mean/rstd from steps 1-2 alone).
 template <class D>
-void launch_stats_t(const Plan &p, const void *xv, const StatsOut &o, hipStream_t s,
+void launch_stats_t(const Plan &p, const void *xv, const StatsOut &o, bool late, hipStream_t s,
                     const Events *ev) {
     using T = typename D::storage;
     const T *x = static_cast<const T *>(xv);
@@ -394,13 +404,13 @@ void launch_stats_t(const Plan &p, const void *xv, const StatsOut &o, hipStream_
         constexpr int NV = decltype(nvc)::value;
         constexpr bool P2 = decltype(pc)::value != 0;
         constexpr int U = unroll_for(kUnrollStats, NV);
-        if (p.fused)
+        if (p.fused && !late)
             gn_partial_stats<D, W, NV, P2, U, true><<<grid1, block, 0, s>>>(x, p.stats, o);
         else
             gn_partial_stats<D, W, NV, P2, U, false><<<grid1, block, 0, s>>>(x, p.stats, o);
     });
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotStats + 1], s);
-    if (!p.fused) {
+    if (!p.fused) {  // (late implies fused)
         const dim3 grid2(static_cast<unsigned>(p.N * p.stats.G));
         if (ev) (void)hipEventRecord(ev->ev[2 * kSlotFinalize], s);
         gn_finalize_stats<D><<<grid2, block, 0, s>>>(x, p.stats, o);
@@ -408,9 +418,10 @@ void launch_stats_t(const Plan &p, const void *xv, const StatsOut &o, hipStream_
     }
 }
 
+// ls.part_s non-null: the late finalize (the plan's `late`).
 template <class D, bool SILU>
 void launch_apply_s(const Plan &p, const void *xv, void *yv, const float *mean, const float *rstd,
-                    const Affine &af, hipStream_t s) {
+                    const Affine &af, const LateStats &ls, hipStream_t s) {
     using T = typename D::storage;
     const T *x = static_cast<const T *>(xv);
     T *y = static_cast<T *>(yv);
@@ -422,45 +433,59 @@ void launch_apply_s(const Plan &p, const void *xv, void *yv, const float *mean, 
         constexpr bool P2 = decltype(pc)::value != 0;
         constexpr int U = unroll_for(kUnrollApply, NV);
         if (p.apply_ntl)
-            gn_apply<D, W, NV, P2, U, SILU, true, true><<<grid, block, 0, s>>>(
-                x, y, p.apply, mean, rstd, af);
+            gn_apply<D, W, NV, P2, U, SILU, true, true, false><<<grid, block, 0, s>>>(
+                x, y, p.apply, mean, rstd, af, ls);
+        else if (ls.part_s != nullptr)
+            gn_apply<D, W, NV, P2, U, SILU, false, true, true><<<grid, block, 0, s>>>(
+                x, y, p.apply, mean, rstd, af, ls);
         else
-            gn_apply<D, W, NV, P2, U, SILU, false, true><<<grid, block, 0, s>>>(
-                x, y, p.apply, mean, rstd, af);
+            gn_apply<D, W, NV, P2, U, SILU, false, true, false><<<grid, block, 0, s>>>(
+                x, y, p.apply, mean, rstd, af, ls);
     });
 }
 
 template <class D>
 void launch_apply_t(const Plan &p, const void *x, void *y, const float *mean, const float *rstd,
-                    const Affine &af, int silu, hipStream_t s, const Events *ev) {
+                    const Affine &af, const LateStats &ls, int silu, hipStream_t s,
+                    const Events *ev) {
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotApply], s);
     if (silu)
-        launch_apply_s<D, true>(p, x, y, mean, rstd, af, s);
+        launch_apply_s<D, true>(p, x, y, mean, rstd, af, ls, s);
     else
-        launch_apply_s<D, false>(p, x, y, mean, rstd, af, s);
+        launch_apply_s<D, false>(p, x, y, mean, rstd, af, ls, s);
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotApply + 1], s);
 }
 
-void launch_stats(const Plan &p, const void *x, const StatsOut &o, hipStream_t s,
+void launch_stats(const Plan &p, const void *x, const StatsOut &o, bool late, hipStream_t s,
                   const Events *ev) {
     switch (p.dtype) {
-        case GN_DTYPE_F16: launch_stats_t<Fp16>(p, x, o, s, ev); break;
-        case GN_DTYPE_F32: launch_stats_t<F32>(p, x, o, s, ev); break;
-        default: launch_stats_t<Bf16>(p, x, o, s, ev); break;
+        case GN_DTYPE_F16: launch_stats_t<Fp16>(p, x, o, late, s, ev); break;
+        case GN_DTYPE_F32: launch_stats_t<F32>(p, x, o, late, s, ev); break;
+        default: launch_stats_t<Bf16>(p, x, o, late, s, ev); break;
     }
 }
 
+// late (non-null): step 3 runs the late finalize from these partials; else it
+// reads mean/rstd.
 void launch_apply(const Plan &p, const void *x, void *y, const float *mean, const float *rstd,
-                  const void *gamma, const void *beta, int silu, hipStream_t s,
-                  const Events *ev) {
+                  const StatsOut *late, const void *gamma, const void *beta, int silu,
+                  hipStream_t s, const Events *ev) {
     Affine af;
     af.gamma = gamma;
     af.beta = beta;
     af.type = p.affine;
+    LateStats ls{};
+    if (late != nullptr) {
+        ls.part_s = late->part_s;
+        ls.part_q = late->part_q;
+        ls.K1 = p.stats.K;
+        ls.inv_m = late->inv_m;
+        ls.eps = late->eps;
+    }
     switch (p.dtype) {
-        case GN_DTYPE_F16: launch_apply_t<Fp16>(p, x, y, mean, rstd, af, silu, s, ev); break;
-        case GN_DTYPE_F32: launch_apply_t<F32>(p, x, y, mean, rstd, af, silu, s, ev); break;
-        default: launch_apply_t<Bf16>(p, x, y, mean, rstd, af, silu, s, ev); break;
+        case GN_DTYPE_F16: launch_apply_t<Fp16>(p, x, y, mean, rstd, af, ls, silu, s, ev); break;
+        case GN_DTYPE_F32: launch_apply_t<F32>(p, x, y, mean, rstd, af, ls, silu, s, ev); break;
+        default: launch_apply_t<Bf16>(p, x, y, mean, rstd, af, ls, silu, s, ev); break;
     }
 }
 
@@ -533,8 +558,9 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
     void *yb = y;
 
     if (iters <= 0) {
-        launch_stats(p, xb, o, c.stream, nullptr);
-        launch_apply(p, xb, yb, o.mean, o.rstd, gamma, beta, apply_silu, c.stream, nullptr);
+        launch_stats(p, xb, o, p.late, c.stream, nullptr);
+        launch_apply(p, xb, yb, o.mean, o.rstd, p.late ? &o : nullptr, gamma, beta, apply_silu,
+                     c.stream, nullptr);
         return finish_launch();
     }
 
@@ -550,8 +576,9 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
     for (int done = 0; done < iters && st == GN_OK;) {
         const int nb = std::min(kBatch, iters - done);
         for (int i = 0; i < nb; ++i) {
-            launch_stats(p, xb, o, c.stream, &evs[i]);
-            launch_apply(p, xb, yb, o.mean, o.rstd, gamma, beta, apply_silu, c.stream, &evs[i]);
+            launch_stats(p, xb, o, p.late, c.stream, &evs[i]);
+            launch_apply(p, xb, yb, o.mean, o.rstd, p.late ? &o : nullptr, gamma, beta,
+                         apply_silu, c.stream, &evs[i]);
         }
         st = finish_launch();
         if (st == GN_OK && hipStreamSynchronize(c.stream) != hipSuccess) st = GN_DEVICE_ERROR;
@@ -825,7 +852,7 @@ gn_status gn_stats_rows_dtype(const void *x, int64_t N, int64_t L, int64_t C, in
     o.rstd = rstd_out;
     o.inv_m = p.inv_m;
     o.eps = eps;
-    launch_stats(p, x, o, c.stream, nullptr);
+    launch_stats(p, x, o, false, c.stream, nullptr);
     return finish_launch();
 }
 
@@ -847,7 +874,7 @@ gn_status gn_apply_rows_dtype(const void *x, const float *mean, const float *rst
     st = begin_call(stream, {x, y, mean, rstd, gamma, beta}, &c);
     if (st != GN_OK) return st;
     const Plan p = make_plan(N, L, C, G, dtype);
-    launch_apply(p, x, y, mean, rstd, gamma, beta, apply_silu, c.stream, nullptr);
+    launch_apply(p, x, y, mean, rstd, nullptr, gamma, beta, apply_silu, c.stream, nullptr);
     return finish_launch();
 }
 
@@ -877,14 +904,14 @@ gn_status gn_profile_rows(const void *x, const float *gamma, const float *beta, 
 }
 
 gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dtype,
-                             int64_t plan_out[13]) {
+                             int64_t plan_out[14]) {
     if (plan_out == nullptr) return GN_INVALID_ARGUMENT;
     static const uint16_t aligned_probe[8] __attribute__((aligned(16))) = {};
     const gn_status st =
         check_shape(aligned_probe, aligned_probe, N, L, C, G, 0.0f, 0, true, dtype);
     if (st != GN_OK) return st;
     if (N * L == 0) {
-        for (int i = 0; i < 13; ++i) plan_out[i] = 0;
+        for (int i = 0; i < 14; ++i) plan_out[i] = 0;
         return GN_OK;
     }
     const Plan p = make_plan(N, L, C, G, dtype);
@@ -901,12 +928,13 @@ gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dty
     plan_out[10] = p.lay.a;
     plan_out[11] = p.lay.t;
     plan_out[12] = p.stats.plain_tail;
+    plan_out[13] = p.late ? 1 : 0;
     return GN_OK;
 }
 
 gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_out[8]) {
     if (plan_out == nullptr) return GN_INVALID_ARGUMENT;
-    int64_t full[13] = {};
+    int64_t full[14] = {};
     const gn_status st = gn_plan_rows_dtype(N, L, C, G, GN_DTYPE_BF16, full);
     if (st == GN_OK)
         for (int i = 0; i < 8; ++i) plan_out[i] = full[i];

@@ -477,12 +477,64 @@ __device__ __forceinline__ bool arrive_is_last(const StatsOut &out, int64_t n, i
 constexpr int kFinalizeBatch = 16;
 constexpr int64_t kFinalizeOverread = int64_t{kFinalizeBatch - 1} * kThreads;
 
+// One batch of the finalize's partial loads for the thread of (group g, part
+// j): chunks kk + b*tpg, b < kFinalizeBatch, issued together so their round
+// trips overlap.  A slot past K reads up to (kFinalizeBatch-1)*tpg*G floats
+// beyond the sample's partials -- the next sample's, the partial squares
+// after the sums, or the kFinalizeOverread floats of padding after the
+// squares -- and is not added.  COHERENT: agent-scope loads (the partials
+// were written by other workgroups of the same kernel).
+template <bool COHERENT> struct FinalizeBatch {
+    float vs[kFinalizeBatch], vq[kFinalizeBatch];
+    __device__ __forceinline__ void load(const float *ps, const float *pq, int64_t kk, int tpg,
+                                         int G) {
+#pragma unroll
+        for (int b = 0; b < kFinalizeBatch; ++b) {
+            const int64_t o = (kk + b * tpg) * G;
+            if constexpr (COHERENT) {
+                vs[b] = __hip_atomic_load(ps + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                vq[b] = __hip_atomic_load(pq + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                vs[b] = ps[o];
+                vq[b] = pq[o];
+            }
+        }
+    }
+    // Adds the batch's chunks below K, in increasing order.
+    __device__ __forceinline__ void add(int64_t kk, int tpg, int64_t K, float &as,
+                                       float &aq) const {
+#pragma unroll
+        for (int b = 0; b < kFinalizeBatch; ++b) {
+            if (kk + b * tpg < K) {
+                as += vs[b];
+                aq += vq[b];
+            }
+        }
+    }
+};
+
+// The end of step 2 for one sample, every thread of the workgroup taking
+// part: thread tid = g + G*j holds its sum (as, aq) over the chunks
+// k = j, j + tpg, ...; a fixed tree over j follows and the thread j = 0 of
+// each group writes mean/rstd through mean_g/rstd_g (global memory or LDS).
+__device__ __forceinline__ void finalize_groups(float as, float aq, bool has, int j, int g,
+                                                int G, int tpg, float pivot, double inv_m,
+                                                float eps, float *red_s, float *red_q, int tid,
+                                                float *mean_g, float *rstd_g) {
+    red_s[tid] = as;
+    red_q[tid] = aq;
+    __syncthreads();
+    tree_sum(red_s, red_q, g, G, has ? j : -1, tpg);
+    if (has && j == 0) group_moments(red_s[tid], red_q[tid], pivot, inv_m, eps, mean_g, rstd_g);
+}
+
 // Step 2 for sample n, run by the last workgroup to arrive (G <= kThreads):
 // tpg = kThreads / G threads per group; thread tid = g + G*j (j < tpg) sums
 // the chunks k = j, j + tpg, ... in increasing order (coalesced along g;
-// loads issued kBatch at a time so their round trips overlap), a fixed tree
-// over j follows, and mean/rstd are written.  The arrival counter is reset
-// to zero for the next call.
+// loads issued kFinalizeBatch at a time), a fixed tree over j follows, and
+// mean/rstd are written.  The arrival counter is reset to zero for the next
+// call.  Every batch, the last one included, issues all its loads before the
+// first add, so a short tail costs one round trip, not one per chunk.
 template <class D>
 __device__ __forceinline__ void finalize_sample(const typename D::storage *xs,
                                                 const Geometry &geo, int64_t n,
@@ -493,48 +545,37 @@ __device__ __forceinline__ void finalize_sample(const typename D::storage *xs,
     const bool has = tid < tpg * G;
     const int g = tid % G;
     const int j = tid / G;
-    constexpr int kBatch = kFinalizeBatch;
     float as = 0.0f, aq = 0.0f;
     if (has) {
         const float *ps = out.part_s + n * geo.K * G + g;
         const float *pq = out.part_q + n * geo.K * G + g;
-        // Every batch, the last one included, issues all kBatch loads before
-        // the first add, so a short tail costs one round trip, not one per
-        // chunk.  A slot past K reads up to (kBatch-1)*tpg*G floats beyond the
-        // sample's partials -- the next sample's, the partial squares after
-        // the sums, or the kFinalizeOverread floats of padding after the
-        // squares -- and is not added.
-        for (int64_t kk = j; kk < geo.K; kk += kBatch * tpg) {
-            float vs[kBatch], vq[kBatch];
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                const int64_t o = (kk + b * tpg) * G;
-                vs[b] = __hip_atomic_load(ps + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                vq[b] = __hip_atomic_load(pq + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+        for (int64_t kk = j; kk < geo.K; kk += kFinalizeBatch * tpg) {
+            FinalizeBatch<true> fb;
+            fb.load(ps, pq, kk, tpg, G);
             __builtin_amdgcn_sched_barrier(0);  // all loads issued before the adds
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                if (kk + b * tpg < geo.K) {
-                    as += vs[b];
-                    aq += vq[b];
-                }
-            }
+            fb.add(kk, tpg, geo.K, as, aq);
         }
     }
-    red_s[tid] = as;
-    red_q[tid] = aq;
-    __syncthreads();
-    tree_sum(red_s, red_q, g, G, has ? j : -1, tpg);
-    if (has && j == 0) {
-        const float pivot = D::to_f32(xs[static_cast<int64_t>(g) * geo.Cg]);
-        group_moments(red_s[tid], red_q[tid], pivot, out.inv_m, out.eps, out.mean + n * G + g,
-                      out.rstd + n * G + g);
-    }
+    const float pivot = has && j == 0 ? D::to_f32(xs[static_cast<int64_t>(g) * geo.Cg]) : 0.0f;
+    finalize_groups(as, aq, has, j, g, G, tpg, pivot, out.inv_m, out.eps, red_s, red_q, tid,
+                    out.mean + n * G + g, out.rstd + n * G + g);
     if (tid == 0)
         __hip_atomic_store(out.arrivals + n * arrival_stride(geo.K), 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Step 2 folded into step 3 (the "late" finalize, for samples whose chunk
+// partials one batch covers: K1 <= kFinalizeBatch * (kThreads / G)): step 1
+// only writes its partials, and every step-3 workgroup reduces its sample's
+// partials itself, with the loads, the order of the adds and the tree of the
+// fused finalize, so mean/rstd are bitwise the same.
+struct LateStats {
+    const float *part_s;  // [N][K1][G] from step 1
+    const float *part_q;
+    int64_t K1;           // chunks per sample of step 1
+    double inv_m;         // 1 / (L*Cg)
+    float eps;
+};
 
 // gamma and beta: C values each, or null (1 and 0), of element type kF32,
 // kBf16 or kF16; widened exactly to fp32 before the fold.
@@ -545,28 +586,71 @@ struct Affine {
     int type;
 };
 
-__device__ __forceinline__ float affine_at(const void *p, int c, int type, float absent) {
-    if (p == nullptr) return absent;
-    if (type == Affine::kBf16) return Bf16::to_f32(static_cast<const uint16_t *>(p)[c]);
-    if (type == Affine::kF16) return Fp16::to_f32(static_cast<const uint16_t *>(p)[c]);
-    return static_cast<const float *>(p)[c];
+// A lane's channel parameters as loaded: the raw bits of gamma and beta (of
+// the Affine type) and its groups' mean and rstd.  They are widened and
+// combined only later, in fold_affine, so no instruction between the loads
+// waits for them.
+template <int S> struct SlotParams {
+    uint32_t g[S], b[S];
+    float mu[S], rs[S];
+};
+
+// Issues the loads of the lane's parameters; their round trips overlap.  An
+// absent gamma or beta is read from `mean` with stride 0 (any valid address)
+// and replaced by 1 or 0 in fold_affine.
+// STATS: also load mean/rstd of the slots' groups from mean[n*G + g] (else
+// the caller fills pr.mu / pr.rs; `mean` is then only a valid address).
+template <class L, bool POW2, bool STATS>
+__device__ __forceinline__ void load_slot_params(const float *mean, const float *rstd,
+                                                 const Affine &af, const Geometry &geo,
+                                                 const TileGeo<POW2, L::kSlots> &tg_, int64_t n,
+                                                 int tid, SlotParams<L::kSlots> &pr) {
+    constexpr int S = L::kSlots;
+    int c[S];
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+        c[j] = tg_.channel(L::slot_offset(tg_.lanes(), tid, j));
+        if constexpr (STATS) {
+            const int64_t gi = n * geo.G + tg_.group_of(c[j]);
+            pr.mu[j] = mean[gi];
+            pr.rs[j] = rstd[gi];
+        }
+    }
+    const void *gp = af.gamma ? af.gamma : static_cast<const void *>(mean);
+    const void *bp = af.beta ? af.beta : static_cast<const void *>(mean);
+    const int gs = af.gamma ? 1 : 0, bs = af.beta ? 1 : 0;
+    if (af.type == Affine::kF32) {
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+            pr.g[j] = static_cast<const uint32_t *>(gp)[c[j] * gs];
+            pr.b[j] = static_cast<const uint32_t *>(bp)[c[j] * bs];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+            pr.g[j] = static_cast<const uint16_t *>(gp)[c[j] * gs];
+            pr.b[j] = static_cast<const uint16_t *>(bp)[c[j] * bs];
+        }
+    }
+}
+
+// gamma or beta bits of the Affine type, widened exactly to fp32.
+__device__ __forceinline__ float widen_affine(uint32_t bits, int type) {
+    const float f16 = Fp16::to_f32(static_cast<uint16_t>(bits));
+    const float b16 = Bf16::to_f32(static_cast<uint16_t>(bits));
+    return type == Affine::kBf16 ? b16 : (type == Affine::kF16 ? f16 : __uint_as_float(bits));
 }
 
 // scale = gamma*rstd, shift = beta - mean*scale for the lane's slots.
-template <class L, bool POW2>
-__device__ __forceinline__ void fold_affine(const float *mean, const float *rstd,
-                                            const Affine &af, const Geometry &geo,
-                                            const TileGeo<POW2, L::kSlots> &tg_, int64_t n,
-                                            int tid, float (&sc)[L::kSlots],
-                                            float (&sh)[L::kSlots]) {
+template <int S>
+__device__ __forceinline__ void fold_affine(const SlotParams<S> &pr, const Affine &af,
+                                            float (&sc)[S], float (&sh)[S]) {
 #pragma unroll
-    for (int j = 0; j < L::kSlots; ++j) {
-        const int c = tg_.channel(L::slot_offset(tg_.lanes(), tid, j));
-        const int64_t gi = n * geo.G + tg_.group_of(c);
-        const float ga = affine_at(af.gamma, c, af.type, 1.0f);
-        const float be = affine_at(af.beta, c, af.type, 0.0f);
-        sc[j] = ga * rstd[gi];
-        sh[j] = fmaf(-mean[gi], sc[j], be);
+    for (int j = 0; j < S; ++j) {
+        const float ga = af.gamma ? widen_affine(pr.g[j], af.type) : 1.0f;
+        const float be = af.beta ? widen_affine(pr.b[j], af.type) : 0.0f;
+        sc[j] = ga * pr.rs[j];
+        sh[j] = fmaf(-pr.mu[j], sc[j], be);
     }
 }
 
@@ -735,28 +819,81 @@ __global__ __launch_bounds__(kThreads) void gn_zero_u32(unsigned *p, int64_t n) 
 // x and y may be the same buffer (each element is read, then written, by one
 // lane), so they carry no __restrict__.
 // ---------------------------------------------------------------------------
-template <class D, int W, int NV, bool POW2, int UNROLL, bool SILU, bool NTL, bool NTS>
+// FIN: the late finalize -- the workgroup first reduces its sample's step-1
+// partials (ls) to mean/rstd in LDS, every thread taking part, and `mean` /
+// `rstd` are not read.
+template <class D, int W, int NV, bool POW2, int UNROLL, bool SILU, bool NTL, bool NTS, bool FIN>
 __global__ __launch_bounds__(kThreads) void gn_apply(
     const typename D::storage *x, typename D::storage *y, Geometry geo,
-    const float *__restrict__ mean, const float *__restrict__ rstd, Affine af) {
+    const float *__restrict__ mean, const float *__restrict__ rstd, Affine af, LateStats ls) {
     using L = Lane<D, W, NV>;
     constexpr int S = L::kSlots;
     const TileGeo<POW2, S> tg(geo);
     const int64_t T = tg.tile();
     const int A = tg.lanes();
     const int tid = threadIdx.x;
-    if (tid >= A) return;
+    const bool active = tid < A;
+    if constexpr (!FIN) {
+        if (!active) return;
+    }
     const int64_t wg = blockIdx.x;
     const int64_t n = wg / geo.K;
     const int64_t k = wg - n * geo.K;
-
-    float sc[S], sh[S];
-    fold_affine<L, POW2>(mean, rstd, af, geo, tg, n, tid, sc, sh);
-
     const int64_t base = n * geo.E;
+
+    // Late finalize, first its loads: the partials of (group g, part j) --
+    // K1 <= kFinalizeBatch*tpg, so the fused finalize's first (only) batch,
+    // loaded, like there, only by the parts j < K1 -- and the group's pivot
+    // x[n, 0, g*Cg].
+    const int G = geo.G;
+    const int tpg = kThreads / G;
+    const bool fin_has = FIN && tid < tpg * G;
+    const int fg = tid % G;
+    const int fj = tid / G;
+    FinalizeBatch<false> fb;
+    float pivot = 0.0f;
+    if constexpr (FIN) {
+        if (fin_has && fj < ls.K1) {
+            fb.load(ls.part_s + n * ls.K1 * G + fg, ls.part_q + n * ls.K1 * G + fg, fj, tpg, G);
+            if (fj == 0) pivot = D::to_f32(x[base + static_cast<int64_t>(fg) * geo.Cg]);
+        }
+    }
+
+    // The parameter loads are issued next and the chunk's first batch of x
+    // right after them; the fold then waits for the parameters only (loads
+    // return in order), so the round trips overlap.
+    SlotParams<S> pr;
+    if (active) load_slot_params<L, POW2, !FIN>(mean, rstd, af, geo, tg, n, tid, pr);
+
     const ChunkRange cr = chunk_range(geo, k);
     int64_t off = base + cr.t_begin * T;  // current tile
     int64_t tt = cr.t_begin;
+    const int64_t nb = (cr.t_full_end - tt) / UNROLL;  // whole batches
+    L a[UNROLL], b[UNROLL];
+    auto load_batch = [&](L (&v)[UNROLL], int64_t o0) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) v[u] = L::template load<NTL>(x + o0 + u * T, A, tid);
+    };
+    if (active && nb > 0) load_batch(a, off);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (FIN) {
+        __shared__ float red_s[kThreads], red_q[kThreads];
+        __shared__ float s_mean[kThreads], s_rstd[kThreads];
+        float as = 0.0f, aq = 0.0f;
+        if (fin_has && fj < ls.K1) fb.add(fj, tpg, ls.K1, as, aq);
+        finalize_groups(as, aq, fin_has, fj, fg, G, tpg, pivot, ls.inv_m, ls.eps, red_s, red_q,
+                        tid, s_mean + fg, s_rstd + fg);
+        __syncthreads();
+        if (!active) return;
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+            const int g = tg.group_of(tg.channel(L::slot_offset(A, tid, j)));
+            pr.mu[j] = s_mean[g];
+            pr.rs[j] = s_rstd[g];
+        }
+    }
+    float sc[S], sh[S];
+    fold_affine<S>(pr, af, sc, sh);
     auto apply_batch = [&](const L (&v)[UNROLL], int64_t o0) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
@@ -774,15 +911,8 @@ __global__ __launch_bounds__(kThreads) void gn_apply(
     // still loaded before it is stored.  Measured on MI355X against the plain
     // load-then-store loop: 2-5% faster step 3 for 16-bit data from 32 MiB to
     // 1 GiB, 3-15% on wide tiles, 0-3% in fp32, 2% slower at C = 1280.
-    const int64_t nb = (cr.t_full_end - tt) / UNROLL;
-    if (nb > 0) {
+    if (nb > 0) {  // batch 0 is in flight in a
         const int64_t step = UNROLL * T;
-        L a[UNROLL], b[UNROLL];
-        auto load_batch = [&](L (&v)[UNROLL], int64_t o0) {
-#pragma unroll
-            for (int u = 0; u < UNROLL; ++u) v[u] = L::template load<NTL>(x + o0 + u * T, A, tid);
-        };
-        load_batch(a, off);
         int64_t i = 0;
         for (; i + 3 <= nb; i += 2) {  // batches i, i+1 and i+2 exist
             load_batch(b, off + step);

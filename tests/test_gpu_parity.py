@@ -260,19 +260,39 @@ def test_exact_statistics_integer_inputs(gn, dev):
     assert ulp.max() <= 1, ulp.max()
 
 
-def test_stats_then_apply_equals_full_path(gn, dev):
+# (N, L, C, G, dtype): shapes whose full path runs the late finalize (step 2
+# inside every step-3 workgroup; the 16 MiB decoder shape among them) and
+# shapes that run the fused one; gn_stats_rows always runs the fused one.
+SPLIT_CASES = [
+    (2, 20000, 128, 32, "bf16"), (1, 16384, 512, 32, "bf16"), (1, 4096, 128, 32, "bf16"),
+    (3, 777, 320, 32, "bf16"), (2, 1000, 64, 1, "bf16"), (1, 3000, 256, 256, "bf16"),
+    (4, 4096, 512, 32, "bf16"), (1, 16384, 512, 32, "f16"), (1, 8192, 256, 32, "f32"),
+    (2, 9, 8, 8, "bf16"), (1, 300, 256, 256, "bf16"), (1, 65536, 512, 32, "bf16"),
+    (1, 2000, 512, 512, "bf16"),
+]
+
+
+@pytest.mark.parametrize("N,L,C,G,dt", SPLIT_CASES)
+def test_stats_then_apply_equals_full_path(gn, dev, N, L, C, G, dt):
+    """The full path equals steps 1-2 (gn_stats_rows) followed by step 3 given
+    mean/rstd, bit for bit, whichever finalize the full path runs."""
     from gn_inputs import make_custom
-    N, L, C, G = 2, 20000, 128, 32
-    x_bits, gamma, beta = make_custom(N, L, C, seed=31, mean_range=(-2, 2))
-    x = to_dev_bits(x_bits, dev).reshape(N, L, C)
+    x_np, gamma, beta = make_custom(N, L, C, seed=31, mean_range=(-2, 2), dtype=dt)
+    if dt == "bf16":
+        x = to_dev_bits(x_np, dev).reshape(N, L, C)
+    else:
+        x = torch.from_numpy(x_np).to(dev).reshape(N, L, C)
     g = torch.from_numpy(gamma).to(dev)
     b = torch.from_numpy(beta).to(dev)
+    late = gn.plan_rows(N, L, C, G, gn.dtype_code(x.dtype))["late_finalize"]
+    print("case N=%d L=%d C=%d G=%d %s late=%d" % (N, L, C, G, dt, late), flush=True)
     with torch.no_grad():
         full = gn.group_norm_silu_rows(x, G, g, b, 1e-6)
         mean, rstd = gn.group_stats_rows(x, G, 1e-6)
         split = gn.apply_rows(x, mean, rstd, g, b, apply_silu=True)
     torch.cuda.synchronize()
-    assert torch.equal(full.view(torch.int16), split.view(torch.int16))
+    iv = torch.int32 if dt == "f32" else torch.int16
+    assert torch.equal(full.view(iv), split.view(iv))
 
 
 def test_deterministic_repeats(gn, dev):

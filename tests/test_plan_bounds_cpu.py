@@ -178,6 +178,12 @@ def check_plan(N, L, C, G, dtype):
     cache = 256 << 20
     want = p["tpc1"] if nbytes <= cache else max(1, -(-p["tpc1"] * cache // nbytes))
     assert p["stats_plain_tail"] == want
+    # the late finalize (step 2 in every step-3 workgroup): small x, G <= 256,
+    # and one finalize batch per thread covering the sample's chunks, so its
+    # partial reads are exactly the fused finalize's first batch (bounded above)
+    late = (G <= THREADS and nbytes <= 16 << 20
+            and p["K1"] <= FINALIZE_BATCH * (THREADS // G))
+    assert p["late_finalize"] == int(late)
     return p
 
 
