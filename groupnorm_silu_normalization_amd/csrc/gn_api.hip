@@ -478,6 +478,7 @@ void launch_apply(const Plan &p, const void *x, void *y, const float *mean, cons
     if (late != nullptr) {
         ls.part_s = late->part_s;
         ls.part_q = late->part_q;
+        ls.pivot = late->pivot;
         ls.K1 = p.stats.K;
         ls.inv_m = late->inv_m;
         ls.eps = late->eps;
@@ -551,6 +552,8 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
     o.part_q = o.part_s + nparts;
     o.mean = o.part_q + nparts + kFinalizeOverread;
     o.rstd = o.mean + nstats;
+    // The late finalize leaves mean/rstd unused: step 1 saves its pivots there.
+    o.pivot = p.late ? o.mean : nullptr;
     o.arrivals = counters;
     o.inv_m = p.inv_m;
     o.eps = eps;
@@ -850,6 +853,7 @@ gn_status gn_stats_rows_dtype(const void *x, int64_t N, int64_t L, int64_t C, in
     o.arrivals = counters;
     o.mean = mean_out;
     o.rstd = rstd_out;
+    o.pivot = nullptr;
     o.inv_m = p.inv_m;
     o.eps = eps;
     launch_stats(p, x, o, false, c.stream, nullptr);

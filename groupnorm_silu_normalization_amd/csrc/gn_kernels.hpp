@@ -256,6 +256,9 @@ struct StatsOut {
                           // (fused finalize only); zero between calls
     float *mean;          // [N][G]
     float *rstd;          // [N][G]
+    float *pivot;         // [N][G] or null: the group pivots x[n, 0, g*Cg], saved by
+                          // chunk 0 of each sample for the late finalize (which must
+                          // not read x: with y == x step 3 overwrites row 0)
     double inv_m;         // 1 / (L*Cg)
     float eps;
 };
@@ -572,6 +575,7 @@ __device__ __forceinline__ void finalize_sample(const typename D::storage *xs,
 struct LateStats {
     const float *part_s;  // [N][K1][G] from step 1
     const float *part_q;
+    const float *pivot;   // [N][G], the pivots step 1 used (StatsOut::pivot)
     int64_t K1;           // chunks per sample of step 1
     double inv_m;         // 1 / (L*Cg)
     float eps;
@@ -716,6 +720,11 @@ gn_partial_stats(
         q[j] = 0.0f;
     }
 
+    if (!FUSED && out.pivot != nullptr && k == 0) {
+        for (int g = tid; g < geo.G; g += kThreads)
+            out.pivot[n * geo.G + g] = D::to_f32(xs[static_cast<int64_t>(g) * geo.Cg]);
+    }
+
     const ChunkRange cr = chunk_range(geo, k);
     if (active) {
         const typename D::storage *p = xs + cr.t_begin * T;  // current tile
@@ -844,7 +853,7 @@ __global__ __launch_bounds__(kThreads) void gn_apply(
     // Late finalize, first its loads: the partials of (group g, part j) --
     // K1 <= kFinalizeBatch*tpg, so the fused finalize's first (only) batch,
     // loaded, like there, only by the parts j < K1 -- and the group's pivot
-    // x[n, 0, g*Cg].
+    // x[n, 0, g*Cg] as step 1 saved it (x itself may already hold y here).
     const int G = geo.G;
     const int tpg = kThreads / G;
     const bool fin_has = FIN && tid < tpg * G;
@@ -855,7 +864,7 @@ __global__ __launch_bounds__(kThreads) void gn_apply(
     if constexpr (FIN) {
         if (fin_has && fj < ls.K1) {
             fb.load(ls.part_s + n * ls.K1 * G + fg, ls.part_q + n * ls.K1 * G + fg, fj, tpg, G);
-            if (fj == 0) pivot = D::to_f32(x[base + static_cast<int64_t>(fg) * geo.Cg]);
+            if (fj == 0) pivot = ls.pivot[n * G + fg];
         }
     }
 

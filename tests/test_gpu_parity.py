@@ -202,11 +202,18 @@ def test_rows_variant_as_attention(gn, dev, oracle):
     compare(from_dev_bits(y), ref, "rows attention")
 
 
-def test_in_place(gn, dev, oracle):
+# In place (y == x): step 3 overwrites x while other workgroups of the same
+# sample still run, so nothing in step 3 may read x beyond its own elements
+# (the late finalize takes its group pivots from step 1, not from x).  Late
+# finalize shapes (x <= 16 MiB) and a fused one.
+@pytest.mark.parametrize("N,L,C,G", [(2, 3000, 256, 32), (1, 16384, 512, 32), (8, 512, 128, 32),
+                                     (3, 777, 320, 32), (1, 65536, 512, 32)])
+def test_in_place(gn, dev, oracle, N, L, C, G):
     from gn_inputs import make_custom
-    N, L, C, G = 2, 3000, 256, 32
     x_bits, gamma, beta = make_custom(N, L, C, seed=11, mean_range=(-2, 2))
     y = run_rows(gn, dev, x_bits, gamma, beta, N, L, C, G, 1e-6, 1, inplace=True)
+    y_oop = run_rows(gn, dev, x_bits, gamma, beta, N, L, C, G, 1e-6, 1)
+    assert np.array_equal(y, y_oop), "in place differs from out of place"
     compare(y, oracle.gn_silu(x_bits, gamma, beta, N, L, C, G, 1e-6, 1), "in place")
 
 
