@@ -126,6 +126,33 @@ def test_extra_workload_full_size(gn, dev, oracle, idx):
     compare(y_bits, ref, w.name)
 
 
+def test_beyond_2_31_elements_periodic(gn, dev, oracle):
+    """A sample of more than 2^31 elements (4 GiB of bf16): 64-bit offsets in
+    both steps.  x repeats a P-row block R times along the rows, so the exact
+    group statistics over all L = R*P rows are those of one block and every
+    output row l equals the oracle's output row l mod P; rows of the first
+    block, rows around element 2^31 and the last rows are compared."""
+    from gn_inputs import make_custom
+    P, C, G, R = 4096, 512, 32, 1025
+    L = P * R
+    assert L * C > 2 ** 31
+    blk_bits, gamma, beta = make_custom(1, P, C, seed=77, mean_range=(-1, 1), std_range=(0.5, 2))
+    ref = oracle.gn_silu(blk_bits, gamma, beta, 1, P, C, G, 1e-6, 1).reshape(P, C)
+    print("case periodic N=1 L=%d C=%d G=%d (%d elements)" % (L, C, G, L * C), flush=True)
+    blk = to_dev_bits(blk_bits, dev).reshape(P, C)
+    x = blk.repeat(R, 1).reshape(1, L, C)
+    g = torch.from_numpy(gamma).to(dev)
+    b = torch.from_numpy(beta).to(dev)
+    with torch.no_grad():
+        y = gn.group_norm_silu_rows(x, G, g, b, 1e-6)
+    torch.cuda.synchronize()
+    del x
+    mid = 2 ** 31 // C
+    rows = np.concatenate([np.arange(0, P), np.arange(mid - 8, mid + 8), np.arange(L - 300, L)])
+    got = from_dev_bits(y[0, torch.from_numpy(rows).to(dev)])
+    compare(got, ref[rows % P], "periodic beyond 2^31")
+
+
 @pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
 def test_decoder_workload_statistics(gn, dev, oracle, idx):
     """fp32 mean/rstd against the oracle's fp64 ones.
