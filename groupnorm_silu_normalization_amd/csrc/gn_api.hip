@@ -1095,7 +1095,7 @@ const char *gn_status_string(gn_status s) {
     return "unknown gn_status";
 }
 
-int gn_version(void) { return 401; }
+int gn_version(void) { return 500; }
 
 gn_status gn_device_info(int device, int64_t info_out[6]) {
     if (info_out == nullptr || device < 0) return GN_INVALID_ARGUMENT;
