@@ -118,8 +118,30 @@ bool choose_layout(int64_t E, int64_t C, int dtype, Layout *out) {
     return found;
 }
 
+// Step 3 of a channel count whose 256-lane layout leaves lanes idle or needs
+// more than the minimal accesses per lane (C = 1280, 2560: 2560 = 5*512, so
+// no 256-lane tile of whole rows keeps every lane busy) runs in workgroups of
+// kApplyWideThreads = 320 lanes (five waves) when those are all busy with the
+// minimal NV: one row of 2560 or two of 1280 per tile.  Step 3 is elementwise,
+// so its tiles need not be step 1's.
+constexpr int kApplyWideThreads = 320;
+bool choose_apply_layout(int64_t C, int dtype, const Layout &lay, Layout *out) {
+    *out = lay;
+    const int nv_min = (lay.w == 4) ? 2 : 1;
+    if (lay.w == 1) return false;  // 1-element accesses: keep step 1's tiles
+    if (lay.nv == nv_min && 4 * lay.a >= 3 * kThreads) return false;  // >= 75% busy already
+    const int64_t m = C / gcd64(C, static_cast<int64_t>(lay.w) * nv_min);
+    if (kApplyWideThreads % m != 0) return false;
+    *out = Layout{lay.w, nv_min, kApplyWideThreads,
+                  static_cast<int64_t>(kApplyWideThreads) * lay.w * nv_min};
+    (void)dtype;
+    return true;
+}
+
 struct Plan {
     Layout lay;       // tile layout
+    Layout alay;      // tile layout of step 3 (lay, or the 320-lane one)
+    int apply_threads;  // lanes per step-3 workgroup: kThreads or kApplyWideThreads
     bool fused;       // step 2 runs in the tail of step 1 (G <= kThreads)
     bool late;        // ... or, for a small x, in the prologue of step 3 (LateStats)
     bool apply_ntl;   // step 3 reads x with nontemporal loads
@@ -191,6 +213,25 @@ Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G, int dtype) {
     // small x because every step-3 workgroup re-reads the sample's partials.
     p.late = p.fused && bytes <= kStatsSmallBytes &&
              p.stats.K <= kFinalizeBatch * (kThreads / G);
+    // The late finalize needs step 3 in 256-lane workgroups; small x keeps
+    // them, larger x may take the 320-lane layout.
+    p.alay = p.lay;
+    p.apply_threads = kThreads;
+    if (!p.late && choose_apply_layout(C, dtype, p.lay, &p.alay)) {
+        p.apply_threads = kApplyWideThreads;
+        Geometry a = p.apply;
+        a.T = p.alay.t;
+        a.A = p.alay.a;
+        a.tiles = ceil_div(E, a.T);
+        a.full = E / a.T;
+        a.cg_shift = 0;
+        const int64_t atotal = N * a.tiles;
+        const int64_t ablocks = std::min(
+            kApplyMaxBlocks, std::max(kApplyMinBlocks, atotal * a.T / kApplyElemsPerBlock));
+        a.tpc = std::max<int64_t>(1, ceil_div(atotal, ablocks));
+        a.K = ceil_div(a.tiles, a.tpc);
+        p.apply = a;
+    }
     return p;
 }
 
@@ -356,26 +397,26 @@ struct Events {
 
 template <int V> using IC = std::integral_constant<int, V>;
 
-// Calls f(IC<W>, IC<NV>, IC<POW2>) with the plan's layout as compile-time
-// constants; POW2 = all 256 lanes busy, which happens exactly when C is a
-// power of two.
+// Calls f(IC<W>, IC<NV>, IC<POW2>) with a layout as compile-time constants;
+// POW2 = all 256 lanes of a 256-lane workgroup busy, which happens exactly
+// when C is a power of two.
 template <class D, class F>
-void with_layout(const Plan &p, F &&f) {
+void with_layout(const Layout &lay, F &&f) {
     constexpr int W16 = static_cast<int>(16 / sizeof(typename D::storage));
     auto by_pow2 = [&](auto wc, auto nvc) {
-        if (p.lay.a == kThreads)
+        if (lay.a == kThreads)
             f(wc, nvc, IC<1>{});
         else
             f(wc, nvc, IC<0>{});
     };
-    if (p.lay.w == 1) {
-        switch (p.lay.nv) {
+    if (lay.w == 1) {
+        switch (lay.nv) {
             case 1: by_pow2(IC<1>{}, IC<1>{}); break;
             case 2: by_pow2(IC<1>{}, IC<2>{}); break;
             default: by_pow2(IC<1>{}, IC<4>{}); break;
         }
     } else {
-        switch (p.lay.nv) {
+        switch (lay.nv) {
             case 1:
                 if constexpr (W16 != 4) by_pow2(IC<W16>{}, IC<1>{});  // fp32 starts at NV = 2
                 break;
@@ -399,7 +440,7 @@ void launch_stats_t(const Plan &p, const void *xv, const StatsOut &o, bool late,
     const dim3 block(kThreads);
     const dim3 grid1(static_cast<unsigned>(p.N * p.stats.K));
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotStats], s);
-    with_layout<D>(p, [&](auto wc, auto nvc, auto pc) {
+    with_layout<D>(p.lay, [&](auto wc, auto nvc, auto pc) {
         constexpr int W = decltype(wc)::value;
         constexpr int NV = decltype(nvc)::value;
         constexpr bool P2 = decltype(pc)::value != 0;
@@ -418,16 +459,37 @@ void launch_stats_t(const Plan &p, const void *xv, const StatsOut &o, bool late,
     }
 }
 
-// ls.part_s non-null: the late finalize (the plan's `late`).
+// ls.part_s non-null: the late finalize (the plan's `late`).  Workgroups of
+// p.apply_threads lanes: kThreads, or kApplyWideThreads for the wide layout
+// (16-byte accesses, minimal NV, never the power-of-two or late kernels).
 template <class D, bool SILU>
 void launch_apply_s(const Plan &p, const void *xv, void *yv, const float *mean, const float *rstd,
                     const Affine &af, const LateStats &ls, hipStream_t s) {
     using T = typename D::storage;
     const T *x = static_cast<const T *>(xv);
     T *y = static_cast<T *>(yv);
-    const dim3 block(kThreads);
     const dim3 grid(static_cast<unsigned>(p.N * p.apply.K));
-    with_layout<D>(p, [&](auto wc, auto nvc, auto pc) {
+    if (p.apply_threads == kApplyWideThreads) {
+        const dim3 block(kApplyWideThreads);
+        with_layout<D>(p.alay, [&](auto wc, auto nvc, auto pc) {
+            constexpr int W = decltype(wc)::value;
+            constexpr int NV = decltype(nvc)::value;
+            constexpr bool P2 = decltype(pc)::value != 0;
+            if constexpr (W > 1 && NV == (W == 4 ? 2 : 1) && !P2) {
+                constexpr int U = unroll_for(kUnrollApply, NV);
+                constexpr int NT = kApplyWideThreads;
+                if (p.apply_ntl)
+                    gn_apply<D, W, NV, false, U, SILU, true, true, false, NT>
+                        <<<grid, block, 0, s>>>(x, y, p.apply, mean, rstd, af, ls);
+                else
+                    gn_apply<D, W, NV, false, U, SILU, false, true, false, NT>
+                        <<<grid, block, 0, s>>>(x, y, p.apply, mean, rstd, af, ls);
+            }
+        });
+        return;
+    }
+    const dim3 block(kThreads);
+    with_layout<D>(p.lay, [&](auto wc, auto nvc, auto pc) {
         constexpr int W = decltype(wc)::value;
         constexpr int NV = decltype(nvc)::value;
         constexpr bool P2 = decltype(pc)::value != 0;
@@ -908,14 +970,14 @@ gn_status gn_profile_rows(const void *x, const float *gamma, const float *beta, 
 }
 
 gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dtype,
-                             int64_t plan_out[14]) {
+                             int64_t plan_out[17]) {
     if (plan_out == nullptr) return GN_INVALID_ARGUMENT;
     static const uint16_t aligned_probe[8] __attribute__((aligned(16))) = {};
     const gn_status st =
         check_shape(aligned_probe, aligned_probe, N, L, C, G, 0.0f, 0, true, dtype);
     if (st != GN_OK) return st;
     if (N * L == 0) {
-        for (int i = 0; i < 14; ++i) plan_out[i] = 0;
+        for (int i = 0; i < 17; ++i) plan_out[i] = 0;
         return GN_OK;
     }
     const Plan p = make_plan(N, L, C, G, dtype);
@@ -933,12 +995,15 @@ gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dty
     plan_out[11] = p.lay.t;
     plan_out[12] = p.stats.plain_tail;
     plan_out[13] = p.late ? 1 : 0;
+    plan_out[14] = p.alay.a;
+    plan_out[15] = p.alay.t;
+    plan_out[16] = p.apply_threads;
     return GN_OK;
 }
 
 gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_out[8]) {
     if (plan_out == nullptr) return GN_INVALID_ARGUMENT;
-    int64_t full[14] = {};
+    int64_t full[17] = {};
     const gn_status st = gn_plan_rows_dtype(N, L, C, G, GN_DTYPE_BF16, full);
     if (st == GN_OK)
         for (int i = 0; i < 8; ++i) plan_out[i] = full[i];

@@ -830,11 +830,15 @@ __global__ __launch_bounds__(kThreads) void gn_zero_u32(unsigned *p, int64_t n) 
 // ---------------------------------------------------------------------------
 // FIN: the late finalize -- the workgroup first reduces its sample's step-1
 // partials (ls) to mean/rstd in LDS, every thread taking part, and `mean` /
-// `rstd` are not read.
-template <class D, int W, int NV, bool POW2, int UNROLL, bool SILU, bool NTL, bool NTS, bool FIN>
-__global__ __launch_bounds__(kThreads) void gn_apply(
+// `rstd` are not read.  NT: lanes per workgroup (kThreads, or more for the
+// wide-channel layouts whose tiles need more lanes to keep all of them busy).
+template <class D, int W, int NV, bool POW2, int UNROLL, bool SILU, bool NTL, bool NTS, bool FIN,
+          int NT = kThreads>
+__global__ __launch_bounds__(NT) void gn_apply(
     const typename D::storage *x, typename D::storage *y, Geometry geo,
     const float *__restrict__ mean, const float *__restrict__ rstd, Affine af, LateStats ls) {
+    static_assert(NT == kThreads || (!FIN && !POW2), "the late finalize and the power-of-two "
+                                                   "tiles take 256-lane workgroups");
     using L = Lane<D, W, NV>;
     constexpr int S = L::kSlots;
     const TileGeo<POW2, S> tg(geo);

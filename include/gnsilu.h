@@ -207,7 +207,7 @@ gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_
 
 /* The same calls for x and y of element type `dtype` (a gn_dtype value);
  * the bf16 entry points above are these with dtype = GN_DTYPE_BF16.
- * gn_plan_rows_dtype writes 14 values, the 8 above and
+ * gn_plan_rows_dtype writes 17 values, the 8 above and
  *   [8]  1 when step 3 reads x with nontemporal loads (tensors larger than
  *        the 256 MB Infinity Cache), else 0
  *   [9]  W, elements per lane access (16 bytes' worth, or 1)
@@ -221,6 +221,15 @@ gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_
  *        16 * floor(256 / G) chunks, G <= 256): step 1 only writes its
  *        partials and every step-3 workgroup reduces its sample's partials
  *        in the fused finalize's order, so mean/rstd are bitwise the same
+ *   [14] A2, lanes of a step-3 workgroup that hold slots
+ *   [15] T2, elements per step-3 tile (a multiple of C; [5] and [6] count
+ *        these tiles)
+ *   [16] lanes per step-3 workgroup: 256, or 320 for the channel counts
+ *        whose 256-lane layout leaves a quarter or more of the lanes idle or
+ *        needs more accesses per lane, when 320 lanes are all busy with the
+ *        minimal accesses per lane (C = 1280, 2560, ...; not with the late
+ *        finalize); step 3 then uses the 16-byte accesses of [9] in tiles of
+ *        A2 * W * NV2 elements, NV2 = T2 / (A2 * W)
  * gn_silu_ndhwc_strided_dtype is the strided form for 5-D: strides of the
  * logical (N, C, D, H, W) dimensions, dense channels-last only
  * ((D*H*W*C, 1, H*W*C, W*C, C), extent-1 dimensions free). */
@@ -256,7 +265,7 @@ gn_status gn_profile_rows_dtype(const void *x, const float *gamma, const float *
                                 float eps, int apply_silu, int dtype, void *stream,
                                 int iters, float *kernel_ms, int *n_kernels);
 gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dtype,
-                             int64_t plan_out[14]);
+                             int64_t plan_out[17]);
 
 /* The GroupNorm(+SiLU) fused into the neighbouring 3x3 convolution of the
  * decoder's ResnetBlock2D (Modifications section 2: "ResnetBlock2D

@@ -170,6 +170,42 @@ def test_wide_stats_then_apply_and_determinism(gn, dev, C, G):
     assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
 
 
+# ---------------------------------------------- 320-lane step 3 (C = 1280, 2560)
+# Above 16 MiB (no late finalize) these channel counts run step 3 in workgroups
+# of 320 lanes, all busy, with tiles of their own (one row of 2560 or two of
+# 1280); step 1 keeps its 256-lane tiles.  Ragged last tiles, N = 2, all dtypes.
+WIDE_APPLY = [(2, 3333, 2560, 32, "bf16"), (1, 7001, 1280, 32, "bf16"),
+              (1, 7001, 1280, 32, "f16"), (2, 1777, 2560, 32, "f32"),
+              (1, 6501, 1280, 16, "f32"), (1, 9001, 1280, 40, "bf16")]
+
+
+@pytest.mark.parametrize("N,L,C,G,dtype", WIDE_APPLY)
+def test_wide_apply_320_lanes(gn, dev, oracle, N, L, C, G, dtype):
+    from gn_inputs import make_custom
+    p = gn.plan_rows(N, L, C, G, CODE[dtype])
+    print("case N=%d L=%d C=%d G=%d %s A2=%d T2=%d threads=%d" % (
+        N, L, C, G, dtype, p["A2"], p["T2"], p["apply_threads"]), flush=True)
+    assert p["apply_threads"] == 320 and p["A2"] == 320 and not p["late_finalize"]
+    x, gamma, beta = make_custom(N, L, C, seed=9000 + C + L, mean_range=(-1, 1),
+                                 std_range=(0.5, 2.0), dtype=dtype)
+    y = run_rows(gn, dev, x, gamma, beta, N, L, C, G, 1e-6, 1, dtype)
+    compare(y, oracle.gn_silu(x, gamma, beta, N, L, C, G, 1e-6, 1), dtype,
+            "320 lanes C=%d %s" % (C, dtype))
+    # in place equals out of place bit for bit
+    y_in = run_rows(gn, dev, x, gamma, beta, N, L, C, G, 1e-6, 1, dtype, inplace=True)
+    assert np.array_equal(y_in, y)
+    # steps 1-2 then step 3 given mean/rstd equal the full path bit for bit
+    xt = to_dev(x, dev).reshape(N, L, C)
+    g = torch.from_numpy(gamma).to(dev)
+    b = torch.from_numpy(beta).to(dev)
+    with torch.no_grad():
+        full = gn.group_norm_silu_rows(xt, G, g, b, 1e-6)
+        mean, rstd = gn.group_stats_rows(xt, G, 1e-6)
+        split = gn.apply_rows(xt, mean, rstd, g, b)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(full), to_host(split))
+
+
 # ------------------------------------------------------------------ 5-D NDHWC
 @pytest.mark.parametrize("N,C,D,H,W,G,dtype", [
     (1, 128, 4, 32, 32, 32, "bf16"), (2, 320, 3, 17, 19, 32, "bf16"),

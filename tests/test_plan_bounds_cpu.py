@@ -87,6 +87,35 @@ def chunks(tiles, full, tpc, K):
     return out
 
 
+def apply_layout(p, E, C, dtype):
+    """The step-3 layout: step 1's, or 320 lanes when those are all busy with
+    the minimal accesses per lane and step 1's leaves lanes idle (or needs
+    more accesses); returns (layout dict for check_streaming_pass, offsets)."""
+    W, S, A = p["W"], p["slots"], p["A"]
+    nv_min = 2 if W == 4 else 1
+    m = C // gcd(C, W * nv_min)
+    wide = (W > 1 and (S // W > nv_min or 4 * A < 3 * THREADS) and 320 % m == 0
+            and not p["late_finalize"])
+    assert p["apply_threads"] == (320 if wide else THREADS)
+    if not wide:
+        assert p["A2"] == A and p["T2"] == p["T"]
+        return p, lane_offsets(p)
+    A2, T2 = p["A2"], p["T2"]
+    assert A2 == 320 and T2 == 320 * W * nv_min and T2 % C == 0
+    q = dict(p, A=A2, T=T2, slots=W * nv_min, tiles=-(-E // T2), full=E // T2)
+    o = lane_offsets(q)
+    assert np.array_equal(np.sort(o.ravel()), np.arange(T2))
+    for a in range(nv_min):
+        blk = o[:, a * W:(a + 1) * W]
+        assert np.all(blk[:, 0] % W == 0) and np.all(np.diff(blk, axis=1) == 1)
+        for w0 in range(0, A2, 64):
+            starts = blk[w0:w0 + 64, 0]
+            assert np.array_equal(starts, starts[0] + W * np.arange(starts.size))
+    # each slot keeps one channel from tile to tile
+    assert T2 % C == 0
+    return q, o
+
+
 def check_streaming_pass(N, E, p, o, tpc, K):
     T, tiles, full = p["T"], p["tiles"], p["full"]
     assert N * K < 2 ** 24, "grid too large"
@@ -141,7 +170,8 @@ def check_plan(N, L, C, G, dtype):
     E = L * C
     o = check_layout(p, E, C, dtype)
     check_streaming_pass(N, E, p, o, p["tpc1"], p["K1"])
-    check_streaming_pass(N, E, p, o, p["tpc2"], p["K2"])
+    p2, o2 = apply_layout(p, E, C, dtype)
+    check_streaming_pass(N, E, p2, o2, p["tpc2"], p["K2"])
     # each lane slot keeps one channel across tiles: o mod C, and its group
     ch = o % C
     assert np.all((ch // (C // G)) < G)
