@@ -118,30 +118,26 @@ bool choose_layout(int64_t E, int64_t C, int dtype, Layout *out) {
     return found;
 }
 
-// Step 3 of a channel count whose 256-lane layout leaves lanes idle or needs
-// more than the minimal accesses per lane (C = 1280, 2560: 2560 = 5*512, so
-// no 256-lane tile of whole rows keeps every lane busy) runs in workgroups of
-// kApplyWideThreads = 320 lanes (five waves) when those are all busy with the
-// minimal NV: one row of 2560 or two of 1280 per tile.  Step 3 is elementwise,
-// so its tiles need not be step 1's.
-constexpr int kApplyWideThreads = 320;
-bool choose_apply_layout(int64_t C, int dtype, const Layout &lay, Layout *out) {
-    *out = lay;
+// Channel counts whose 256-lane layout leaves a quarter or more of the lanes
+// idle or needs more than the minimal accesses per lane (C = 1280, 2560:
+// 2560 = 5*512, so no 256-lane tile of whole rows keeps every lane busy) run
+// in workgroups of kWideThreads = 320 lanes (five waves) when those are all
+// busy with the minimal accesses: one row of 2560 or two of 1280 per tile.
+constexpr int kWideThreads = 320;
+bool choose_wide_layout(int64_t C, const Layout &lay, Layout *out) {
     const int nv_min = (lay.w == 4) ? 2 : 1;
-    if (lay.w == 1) return false;  // 1-element accesses: keep step 1's tiles
+    if (lay.w == 1) return false;                                     // 1-element accesses
     if (lay.nv == nv_min && 4 * lay.a >= 3 * kThreads) return false;  // >= 75% busy already
     const int64_t m = C / gcd64(C, static_cast<int64_t>(lay.w) * nv_min);
-    if (kApplyWideThreads % m != 0) return false;
-    *out = Layout{lay.w, nv_min, kApplyWideThreads,
-                  static_cast<int64_t>(kApplyWideThreads) * lay.w * nv_min};
-    (void)dtype;
+    if (kWideThreads % m != 0) return false;
+    *out = Layout{lay.w, nv_min, kWideThreads,
+                  static_cast<int64_t>(kWideThreads) * lay.w * nv_min};
     return true;
 }
 
 struct Plan {
-    Layout lay;       // tile layout
-    Layout alay;      // tile layout of step 3 (lay, or the 320-lane one)
-    int apply_threads;  // lanes per step-3 workgroup: kThreads or kApplyWideThreads
+    Layout lay;       // tile layout of all three steps
+    int threads;      // lanes per workgroup of steps 1 and 3: kThreads or kWideThreads
     bool fused;       // step 2 runs in the tail of step 1 (G <= kThreads)
     bool late;        // ... or, for a small x, in the prologue of step 3 (LateStats)
     bool apply_ntl;   // step 3 reads x with nontemporal loads
@@ -162,6 +158,17 @@ Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G, int dtype) {
     p.affine = affine_type(dtype);
     const int64_t E = L * C;
     (void)choose_layout(E, C, dtype, &p.lay);  // check_shape has accepted the shape
+    // Beyond the latency-bound sizes (where the late finalize, laid out for 256
+    // threads, may run), both passes take the 320-lane layout where it keeps
+    // every lane busy and the 256-lane one does not.
+    p.threads = kThreads;
+    if (N * E * elem_bytes(dtype) > kStatsSmallBytes) {
+        Layout wide;
+        if (choose_wide_layout(C, p.lay, &wide)) {
+            p.lay = wide;
+            p.threads = kWideThreads;
+        }
+    }
     p.fused = G <= kThreads;
     p.apply_ntl = N * E * elem_bytes(dtype) > kCacheResidentBytes;
     Geometry g;
@@ -213,25 +220,6 @@ Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G, int dtype) {
     // small x because every step-3 workgroup re-reads the sample's partials.
     p.late = p.fused && bytes <= kStatsSmallBytes &&
              p.stats.K <= kFinalizeBatch * (kThreads / G);
-    // The late finalize needs step 3 in 256-lane workgroups; small x keeps
-    // them, larger x may take the 320-lane layout.
-    p.alay = p.lay;
-    p.apply_threads = kThreads;
-    if (!p.late && choose_apply_layout(C, dtype, p.lay, &p.alay)) {
-        p.apply_threads = kApplyWideThreads;
-        Geometry a = p.apply;
-        a.T = p.alay.t;
-        a.A = p.alay.a;
-        a.tiles = ceil_div(E, a.T);
-        a.full = E / a.T;
-        a.cg_shift = 0;
-        const int64_t atotal = N * a.tiles;
-        const int64_t ablocks = std::min(
-            kApplyMaxBlocks, std::max(kApplyMinBlocks, atotal * a.T / kApplyElemsPerBlock));
-        a.tpc = std::max<int64_t>(1, ceil_div(atotal, ablocks));
-        a.K = ceil_div(a.tiles, a.tpc);
-        p.apply = a;
-    }
     return p;
 }
 
@@ -440,16 +428,36 @@ void launch_stats_t(const Plan &p, const void *xv, const StatsOut &o, bool late,
     const dim3 block(kThreads);
     const dim3 grid1(static_cast<unsigned>(p.N * p.stats.K));
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotStats], s);
-    with_layout<D>(p.lay, [&](auto wc, auto nvc, auto pc) {
-        constexpr int W = decltype(wc)::value;
-        constexpr int NV = decltype(nvc)::value;
-        constexpr bool P2 = decltype(pc)::value != 0;
-        constexpr int U = unroll_for(kUnrollStats, NV);
-        if (p.fused && !late)
-            gn_partial_stats<D, W, NV, P2, U, true><<<grid1, block, 0, s>>>(x, p.stats, o);
-        else
-            gn_partial_stats<D, W, NV, P2, U, false><<<grid1, block, 0, s>>>(x, p.stats, o);
-    });
+    if (p.threads == kWideThreads) {
+        const dim3 wblock(kWideThreads);
+        with_layout<D>(p.lay, [&](auto wc, auto nvc, auto pc) {
+            constexpr int W = decltype(wc)::value;
+            constexpr int NV = decltype(nvc)::value;
+            constexpr bool P2 = decltype(pc)::value != 0;
+            if constexpr (W > 1 && NV == (W == 4 ? 2 : 1) && !P2) {
+                constexpr int U = unroll_for(kUnrollStats, NV);
+                constexpr int NT = kWideThreads;
+                if (p.fused && !late)
+                    gn_partial_stats<D, W, NV, false, U, true, NT><<<grid1, wblock, 0, s>>>(
+                        x, p.stats, o);
+                else
+                    gn_partial_stats<D, W, NV, false, U, false, NT><<<grid1, wblock, 0, s>>>(
+                        x, p.stats, o);
+            }
+        });
+    } else {
+        with_layout<D>(p.lay, [&](auto wc, auto nvc, auto pc) {
+            constexpr int W = decltype(wc)::value;
+            constexpr int NV = decltype(nvc)::value;
+            constexpr bool P2 = decltype(pc)::value != 0;
+            constexpr int U = unroll_for(kUnrollStats, NV);
+            if (p.fused && !late)
+                gn_partial_stats<D, W, NV, P2, U, true><<<grid1, block, 0, s>>>(x, p.stats, o);
+            else
+                gn_partial_stats<D, W, NV, P2, U, false><<<grid1, block, 0, s>>>(x, p.stats,
+                                                                                  o);
+        });
+    }
     if (ev) (void)hipEventRecord(ev->ev[2 * kSlotStats + 1], s);
     if (!p.fused) {  // (late implies fused)
         const dim3 grid2(static_cast<unsigned>(p.N * p.stats.G));
@@ -460,8 +468,8 @@ void launch_stats_t(const Plan &p, const void *xv, const StatsOut &o, bool late,
 }
 
 // ls.part_s non-null: the late finalize (the plan's `late`).  Workgroups of
-// p.apply_threads lanes: kThreads, or kApplyWideThreads for the wide layout
-// (16-byte accesses, minimal NV, never the power-of-two or late kernels).
+// p.threads lanes: kThreads, or kWideThreads for the wide layout (16-byte
+// accesses, minimal NV, never the power-of-two or late kernels).
 template <class D, bool SILU>
 void launch_apply_s(const Plan &p, const void *xv, void *yv, const float *mean, const float *rstd,
                     const Affine &af, const LateStats &ls, hipStream_t s) {
@@ -469,15 +477,15 @@ void launch_apply_s(const Plan &p, const void *xv, void *yv, const float *mean, 
     const T *x = static_cast<const T *>(xv);
     T *y = static_cast<T *>(yv);
     const dim3 grid(static_cast<unsigned>(p.N * p.apply.K));
-    if (p.apply_threads == kApplyWideThreads) {
-        const dim3 block(kApplyWideThreads);
-        with_layout<D>(p.alay, [&](auto wc, auto nvc, auto pc) {
+    if (p.threads == kWideThreads) {
+        const dim3 block(kWideThreads);
+        with_layout<D>(p.lay, [&](auto wc, auto nvc, auto pc) {
             constexpr int W = decltype(wc)::value;
             constexpr int NV = decltype(nvc)::value;
             constexpr bool P2 = decltype(pc)::value != 0;
             if constexpr (W > 1 && NV == (W == 4 ? 2 : 1) && !P2) {
                 constexpr int U = unroll_for(kUnrollApply, NV);
-                constexpr int NT = kApplyWideThreads;
+                constexpr int NT = kWideThreads;
                 if (p.apply_ntl)
                     gn_apply<D, W, NV, false, U, SILU, true, true, false, NT>
                         <<<grid, block, 0, s>>>(x, y, p.apply, mean, rstd, af, ls);
@@ -995,9 +1003,9 @@ gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dty
     plan_out[11] = p.lay.t;
     plan_out[12] = p.stats.plain_tail;
     plan_out[13] = p.late ? 1 : 0;
-    plan_out[14] = p.alay.a;
-    plan_out[15] = p.alay.t;
-    plan_out[16] = p.apply_threads;
+    plan_out[14] = p.lay.a;
+    plan_out[15] = p.lay.t;
+    plan_out[16] = p.threads;
     return GN_OK;
 }
 

@@ -349,7 +349,7 @@ __device__ __forceinline__ ChunkRange chunk_range(const Geometry &geo, int64_t k
 // G <= kThreads: tg = kThreads / G threads per group, thread (g, part) sums
 // the entries e = part, part + tg, ... of its group, then a fixed tree over
 // the parts.  G > kThreads: each thread sums whole groups.
-template <class L, bool POW2, bool COHERENT>
+template <class L, bool POW2, bool COHERENT, int NT = kThreads>
 __device__ __forceinline__ void write_group_partials(const float (&s)[L::kSlots],
                                                      const float (&q)[L::kSlots], float *red_s,
                                                      float *red_q, const Geometry &geo,
@@ -404,7 +404,7 @@ __device__ __forceinline__ void write_group_partials(const float (&s)[L::kSlots]
         }
     } else {
         // Each thread sums whole groups, entries in increasing order.
-        for (int g = tid; g < G; g += kThreads) {
+        for (int g = tid; g < G; g += NT) {
             float as = 0.0f, aq = 0.0f;
             int r = 0, u = 0;
             for (int e = 0; e < P; ++e) {
@@ -692,14 +692,18 @@ __device__ __forceinline__ float transform1(float x, float sc, float sh) {
 // UNROLL tiles in flight and starts accumulating as the first arrives, where
 // a higher target made it interleave waits into the loads (fully serialized
 // for 16-bit wide tiles) to save registers.
-template <class D, int W, int NV, bool POW2, int UNROLL, bool FUSED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 2))) void
+// NT: lanes per workgroup, kThreads or more for the wide-channel layouts
+// (the group reduction and the fused finalize keep their 256-thread mapping;
+// the other threads of a wider workgroup hold no entry there).
+template <class D, int W, int NV, bool POW2, int UNROLL, bool FUSED, int NT = kThreads>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
 gn_partial_stats(
     const typename D::storage *__restrict__ x, Geometry geo, StatsOut out) {
+    static_assert(NT == kThreads || !POW2, "power-of-two tiles take 256-lane workgroups");
     using L = Lane<D, W, NV>;
     constexpr int S = L::kSlots;
-    __shared__ float red_s[kThreads * S];
-    __shared__ float red_q[kThreads * S];
+    __shared__ float red_s[NT * S];
+    __shared__ float red_q[NT * S];
 
     const TileGeo<POW2, S> tg(geo);
     const int64_t T = tg.tile();
@@ -721,7 +725,7 @@ gn_partial_stats(
     }
 
     if (!FUSED && out.pivot != nullptr && k == 0) {
-        for (int g = tid; g < geo.G; g += kThreads)
+        for (int g = tid; g < geo.G; g += NT)
             out.pivot[n * geo.G + g] = D::to_f32(xs[static_cast<int64_t>(g) * geo.Cg]);
     }
 
@@ -770,7 +774,7 @@ gn_partial_stats(
         }
     }
 
-    write_group_partials<L, POW2, FUSED>(s, q, red_s, red_q, geo, tg, n, k, out, tid);
+    write_group_partials<L, POW2, FUSED, NT>(s, q, red_s, red_q, geo, tg, n, k, out, tid);
     if constexpr (FUSED) {
         if (arrive_is_last(out, n, geo.K, k, tid))
             finalize_sample<D>(xs, geo, n, out, red_s, red_q, tid);

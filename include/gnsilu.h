@@ -211,7 +211,7 @@ gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_
  *   [8]  1 when step 3 reads x with nontemporal loads (tensors larger than
  *        the 256 MB Infinity Cache), else 0
  *   [9]  W, elements per lane access (16 bytes' worth, or 1)
- *   [10] A, lanes of the 256-lane workgroup that hold slots
+ *   [10] A, lanes of the workgroup ([16] lanes) that hold slots
  *   [11] T, elements per tile (= A*W*NV, a multiple of C)
  *   [12] the last tiles of each statistics chunk read with plain loads (the
  *        rest nontemporal): all of the chunk when the tensor fits the
@@ -221,15 +221,12 @@ gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_
  *        16 * floor(256 / G) chunks, G <= 256): step 1 only writes its
  *        partials and every step-3 workgroup reduces its sample's partials
  *        in the fused finalize's order, so mean/rstd are bitwise the same
- *   [14] A2, lanes of a step-3 workgroup that hold slots
- *   [15] T2, elements per step-3 tile (a multiple of C; [5] and [6] count
- *        these tiles)
- *   [16] lanes per step-3 workgroup: 256, or 320 for the channel counts
- *        whose 256-lane layout leaves a quarter or more of the lanes idle or
- *        needs more accesses per lane, when 320 lanes are all busy with the
- *        minimal accesses per lane (C = 1280, 2560, ...; not with the late
- *        finalize); step 3 then uses the 16-byte accesses of [9] in tiles of
- *        A2 * W * NV2 elements, NV2 = T2 / (A2 * W)
+ *   [14] A2 = [10] and [15] T2 = [11]: steps 1 and 3 share the tile layout
+ *   [16] lanes per workgroup of steps 1 and 3: 256, or 320 for a tensor above
+ *        16 MiB whose channel count's 256-lane layout leaves a quarter or
+ *        more of the lanes idle or needs more accesses per lane, when 320
+ *        lanes are all busy with the minimal accesses per lane (C = 1280,
+ *        2560, ...: one row of 2560 or two of 1280 per tile)
  * gn_silu_ndhwc_strided_dtype is the strided form for 5-D: strides of the
  * logical (N, C, D, H, W) dimensions, dense channels-last only
  * ((D*H*W*C, 1, H*W*C, W*C, C), extent-1 dimensions free). */

@@ -170,17 +170,17 @@ def test_wide_stats_then_apply_and_determinism(gn, dev, C, G):
     assert torch.equal(y1.view(torch.int16), y3.view(torch.int16))
 
 
-# ---------------------------------------------- 320-lane step 3 (C = 1280, 2560)
-# Above 16 MiB (no late finalize) these channel counts run step 3 in workgroups
-# of 320 lanes, all busy, with tiles of their own (one row of 2560 or two of
-# 1280); step 1 keeps its 256-lane tiles.  Ragged last tiles, N = 2, all dtypes.
+# ------------------------------------------ 320-lane workgroups (C = 1280, 2560)
+# Above 16 MiB these channel counts run steps 1 and 3 in workgroups of 320
+# lanes, all busy, one 16-byte access per lane (one row of 2560 or two of 1280
+# per tile).  Ragged last tiles, N = 2, all dtypes.
 WIDE_APPLY = [(2, 3333, 2560, 32, "bf16"), (1, 7001, 1280, 32, "bf16"),
               (1, 7001, 1280, 32, "f16"), (2, 1777, 2560, 32, "f32"),
               (1, 6501, 1280, 16, "f32"), (1, 9001, 1280, 40, "bf16")]
 
 
 @pytest.mark.parametrize("N,L,C,G,dtype", WIDE_APPLY)
-def test_wide_apply_320_lanes(gn, dev, oracle, N, L, C, G, dtype):
+def test_wide_320_lanes(gn, dev, oracle, N, L, C, G, dtype):
     from gn_inputs import make_custom
     p = gn.plan_rows(N, L, C, G, CODE[dtype])
     print("case N=%d L=%d C=%d G=%d %s A2=%d T2=%d threads=%d" % (

@@ -58,7 +58,8 @@ def check_layout(p, E, C, dtype):
     assert W in (1, WIDE[dtype]) and S % W == 0 and NV in (1, 2, 4)
     assert W == 1 or (dtype == F32 and NV >= 2) or dtype != F32
     assert E % W == 0, "a 16-byte access must not straddle two samples"
-    assert 0 < A <= THREADS and T == A * S
+    assert 0 < A <= p["apply_threads"] and T == A * S
+    assert p["A2"] == A and p["T2"] == T
     assert T % C == 0, "a tile must be whole rows so each slot keeps one channel"
     # the kernels take masks and shifts for channel and group indices when all
     # 256 lanes are busy: that must happen exactly for power-of-two C
@@ -87,33 +88,20 @@ def chunks(tiles, full, tpc, K):
     return out
 
 
-def apply_layout(p, E, C, dtype):
-    """The step-3 layout: step 1's, or 320 lanes when those are all busy with
-    the minimal accesses per lane and step 1's leaves lanes idle (or needs
-    more accesses); returns (layout dict for check_streaming_pass, offsets)."""
-    W, S, A = p["W"], p["slots"], p["A"]
+def wide_layout(E, C, dtype, nbytes):
+    """(W, NV, 320) when both passes take 320-lane workgroups: a tensor above
+    16 MiB whose 256-lane layout leaves a quarter or more of the lanes idle or
+    needs more than the minimal accesses, and 320 lanes are all busy with the
+    minimal ones; else None."""
+    base = expected_layout(E, C, dtype)
+    if base is None or nbytes <= 16 << 20:
+        return None
+    W, nv, A = base
     nv_min = 2 if W == 4 else 1
+    if W == 1 or (nv == nv_min and 4 * A >= 3 * THREADS):
+        return None
     m = C // gcd(C, W * nv_min)
-    wide = (W > 1 and (S // W > nv_min or 4 * A < 3 * THREADS) and 320 % m == 0
-            and not p["late_finalize"])
-    assert p["apply_threads"] == (320 if wide else THREADS)
-    if not wide:
-        assert p["A2"] == A and p["T2"] == p["T"]
-        return p, lane_offsets(p)
-    A2, T2 = p["A2"], p["T2"]
-    assert A2 == 320 and T2 == 320 * W * nv_min and T2 % C == 0
-    q = dict(p, A=A2, T=T2, slots=W * nv_min, tiles=-(-E // T2), full=E // T2)
-    o = lane_offsets(q)
-    assert np.array_equal(np.sort(o.ravel()), np.arange(T2))
-    for a in range(nv_min):
-        blk = o[:, a * W:(a + 1) * W]
-        assert np.all(blk[:, 0] % W == 0) and np.all(np.diff(blk, axis=1) == 1)
-        for w0 in range(0, A2, 64):
-            starts = blk[w0:w0 + 64, 0]
-            assert np.array_equal(starts, starts[0] + W * np.arange(starts.size))
-    # each slot keeps one channel from tile to tile
-    assert T2 % C == 0
-    return q, o
+    return (W, nv_min, 320) if 320 % m == 0 else None
 
 
 def check_streaming_pass(N, E, p, o, tpc, K):
@@ -138,11 +126,12 @@ def check_streaming_pass(N, E, p, o, tpc, K):
 
 def check_lds(p, C, G):
     """The workgroup reduction of step 1: slot (tid, j) goes to LDS entry
-    o(tid, j) < T <= 256*slots; group g's P = T/G entries are read back."""
+    o(tid, j) < T <= lanes*slots (the LDS arrays); group g's P = T/G entries
+    are read back by the first 256 threads (every workgroup width)."""
     T, S = p["T"], p["slots"]
     Cg = C // G
     P = T // G
-    assert T <= THREADS * S
+    assert T <= p["apply_threads"] * S
     seen = np.zeros(T, np.int64)
     if G <= THREADS:
         tg = THREADS // G
@@ -168,10 +157,13 @@ def check_plan(N, L, C, G, dtype):
     p = gn.plan_rows(N, L, C, G, dtype)
     assert p is not None, (N, L, C, G, dtype)
     E = L * C
+    wide = wide_layout(E, C, dtype, N * E * (4 if dtype == F32 else 2))
+    want = wide or expected_layout(E, C, dtype)
+    assert (p["W"], p["slots"] // p["W"], p["A"]) == want, (N, L, C, G, dtype, p)
+    assert p["apply_threads"] == (320 if wide else THREADS)
     o = check_layout(p, E, C, dtype)
     check_streaming_pass(N, E, p, o, p["tpc1"], p["K1"])
-    p2, o2 = apply_layout(p, E, C, dtype)
-    check_streaming_pass(N, E, p2, o2, p["tpc2"], p["K2"])
+    check_streaming_pass(N, E, p, o, p["tpc2"], p["K2"])
     # each lane slot keeps one channel across tiles: o mod C, and its group
     ch = o % C
     assert np.all((ch // (C // G)) < G)
@@ -275,18 +267,25 @@ def test_wide_layouts_follow_the_rule():
     for C in (320, 640, 960, 1280, 1920, 2560, 4096, 8192, 96, 24, 3, 300, 1000, 6144):
         for L in (1, 8, 4096):
             for dtype in DTYPES:
-                want = expected_layout(L * C, C, dtype)
+                nbytes = L * C * (4 if dtype == F32 else 2)
+                want = wide_layout(L * C, C, dtype, nbytes) or expected_layout(L * C, C, dtype)
                 p = gn.plan_rows(1, L, C, 1, dtype)
                 if want is None:
                     assert p is None
                     continue
                 assert (p["W"], p["slots"] // p["W"], p["A"]) == want, (C, L, dtype, p)
-    # UNet channel counts in bf16: one 16-byte access per lane where half the
-    # lanes suffice (1280: 160 lanes), two for 2560 (160 lanes)
-    assert [gn.plan_rows(1, 4096, C, 32)["slots"] for C in (320, 1280, 2560, 8192)] == \
+    # UNet channel counts in bf16 up to 16 MiB: one 16-byte access per lane
+    # where half the lanes suffice (1280: 160 lanes), two for 2560 (160 lanes)
+    assert [gn.plan_rows(1, 1024, C, 32)["slots"] for C in (320, 1280, 2560, 8192)] == \
         [8, 8, 16, 32]
-    assert [gn.plan_rows(1, 4096, C, 32)["A"] for C in (320, 1280, 2560, 8192)] == \
+    assert [gn.plan_rows(1, 1024, C, 32)["A"] for C in (320, 1280, 2560, 8192)] == \
         [240, 160, 160, 256]
+    # above 16 MiB, 1280 and 2560 take 320-lane workgroups, one access per lane
+    for C in (1280, 2560):
+        p = gn.plan_rows(1, 16384, C, 32)
+        assert (p["A"], p["slots"], p["T"], p["apply_threads"]) == (320, 8, 2560, 320)
+    assert gn.plan_rows(1, 16384, 320, 32)["apply_threads"] == 256
+    assert gn.plan_rows(1, 16384, 960, 32)["apply_threads"] == 256
 
 
 def test_supported_set_matches_the_header_rule():
