@@ -176,7 +176,9 @@ def test_wide_stats_then_apply_and_determinism(gn, dev, C, G):
 # per tile).  Ragged last tiles, N = 2, all dtypes.
 WIDE_APPLY = [(2, 3333, 2560, 32, "bf16"), (1, 7001, 1280, 32, "bf16"),
               (1, 7001, 1280, 32, "f16"), (2, 1777, 2560, 32, "f32"),
-              (1, 6501, 1280, 16, "f32"), (1, 9001, 1280, 40, "bf16")]
+              (1, 6501, 1280, 16, "f32"), (1, 9001, 1280, 40, "bf16"),
+              # more groups than 256 threads: whole groups per thread, separate finalize
+              (1, 3333, 2560, 640, "bf16"), (1, 3333, 2560, 2560, "bf16")]
 
 
 @pytest.mark.parametrize("N,L,C,G,dtype", WIDE_APPLY)
