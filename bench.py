@@ -498,8 +498,7 @@ def main():
                 "apply_frac_of_peak": round(wapply / HBM_PEAK_GBS, 4),
                 "kernels_us": {k: round(v * 1e3, 2) for k, v in wk.items()},
                 "tile": {"A": plan["A"], "W": plan["W"], "slots": plan["slots"], "T": plan["T"]},
-                "apply_tile": {"A": plan["A2"], "T": plan["T2"],
-                               "threads": plan["apply_threads"]},
+                "threads": plan["threads"],
             }
             del wx, wy
 

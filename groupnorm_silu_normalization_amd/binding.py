@@ -353,7 +353,7 @@ def apply_rows(x, mean, rstd, weight=None, bias=None, apply_silu=True, out=None)
 
 PLAN_FIELDS = ("slots", "tiles", "full", "tpc1", "K1", "tpc2", "K2", "scratch_bytes",
                "apply_nontemporal_loads", "W", "A", "T", "stats_plain_tail", "late_finalize",
-               "A2", "T2", "apply_threads")
+               "threads")
 
 
 def _dtype_arg(x):

@@ -978,14 +978,14 @@ gn_status gn_profile_rows(const void *x, const float *gamma, const float *beta, 
 }
 
 gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dtype,
-                             int64_t plan_out[17]) {
+                             int64_t plan_out[15]) {
     if (plan_out == nullptr) return GN_INVALID_ARGUMENT;
     static const uint16_t aligned_probe[8] __attribute__((aligned(16))) = {};
     const gn_status st =
         check_shape(aligned_probe, aligned_probe, N, L, C, G, 0.0f, 0, true, dtype);
     if (st != GN_OK) return st;
     if (N * L == 0) {
-        for (int i = 0; i < 17; ++i) plan_out[i] = 0;
+        for (int i = 0; i < 15; ++i) plan_out[i] = 0;
         return GN_OK;
     }
     const Plan p = make_plan(N, L, C, G, dtype);
@@ -1003,15 +1003,13 @@ gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dty
     plan_out[11] = p.lay.t;
     plan_out[12] = p.stats.plain_tail;
     plan_out[13] = p.late ? 1 : 0;
-    plan_out[14] = p.lay.a;
-    plan_out[15] = p.lay.t;
-    plan_out[16] = p.threads;
+    plan_out[14] = p.threads;
     return GN_OK;
 }
 
 gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_out[8]) {
     if (plan_out == nullptr) return GN_INVALID_ARGUMENT;
-    int64_t full[17] = {};
+    int64_t full[15] = {};
     const gn_status st = gn_plan_rows_dtype(N, L, C, G, GN_DTYPE_BF16, full);
     if (st == GN_OK)
         for (int i = 0; i < 8; ++i) plan_out[i] = full[i];

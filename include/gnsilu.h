@@ -207,11 +207,11 @@ gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_
 
 /* The same calls for x and y of element type `dtype` (a gn_dtype value);
  * the bf16 entry points above are these with dtype = GN_DTYPE_BF16.
- * gn_plan_rows_dtype writes 17 values, the 8 above and
+ * gn_plan_rows_dtype writes 15 values, the 8 above and
  *   [8]  1 when step 3 reads x with nontemporal loads (tensors larger than
  *        the 256 MB Infinity Cache), else 0
  *   [9]  W, elements per lane access (16 bytes' worth, or 1)
- *   [10] A, lanes of the workgroup ([16] lanes) that hold slots
+ *   [10] A, lanes of the workgroup ([14] lanes) that hold slots
  *   [11] T, elements per tile (= A*W*NV, a multiple of C)
  *   [12] the last tiles of each statistics chunk read with plain loads (the
  *        rest nontemporal): all of the chunk when the tensor fits the
@@ -221,8 +221,7 @@ gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_
  *        16 * floor(256 / G) chunks, G <= 256): step 1 only writes its
  *        partials and every step-3 workgroup reduces its sample's partials
  *        in the fused finalize's order, so mean/rstd are bitwise the same
- *   [14] A2 = [10] and [15] T2 = [11]: steps 1 and 3 share the tile layout
- *   [16] lanes per workgroup of steps 1 and 3: 256, or 320 for a tensor above
+ *   [14] lanes per workgroup of steps 1 and 3: 256, or 320 for a tensor above
  *        16 MiB whose channel count's 256-lane layout leaves a quarter or
  *        more of the lanes idle or needs more accesses per lane, when 320
  *        lanes are all busy with the minimal accesses per lane (C = 1280,
@@ -262,7 +261,7 @@ gn_status gn_profile_rows_dtype(const void *x, const float *gamma, const float *
                                 float eps, int apply_silu, int dtype, void *stream,
                                 int iters, float *kernel_ms, int *n_kernels);
 gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dtype,
-                             int64_t plan_out[17]);
+                             int64_t plan_out[15]);
 
 /* The GroupNorm(+SiLU) fused into the neighbouring 3x3 convolution of the
  * decoder's ResnetBlock2D (Modifications section 2: "ResnetBlock2D

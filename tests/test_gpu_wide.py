@@ -185,9 +185,9 @@ WIDE_APPLY = [(2, 3333, 2560, 32, "bf16"), (1, 7001, 1280, 32, "bf16"),
 def test_wide_320_lanes(gn, dev, oracle, N, L, C, G, dtype):
     from gn_inputs import make_custom
     p = gn.plan_rows(N, L, C, G, CODE[dtype])
-    print("case N=%d L=%d C=%d G=%d %s A2=%d T2=%d threads=%d" % (
-        N, L, C, G, dtype, p["A2"], p["T2"], p["apply_threads"]), flush=True)
-    assert p["apply_threads"] == 320 and p["A2"] == 320 and not p["late_finalize"]
+    print("case N=%d L=%d C=%d G=%d %s A=%d T=%d threads=%d" % (
+        N, L, C, G, dtype, p["A"], p["T"], p["threads"]), flush=True)
+    assert p["threads"] == 320 and p["A"] == 320 and not p["late_finalize"]
     x, gamma, beta = make_custom(N, L, C, seed=9000 + C + L, mean_range=(-1, 1),
                                  std_range=(0.5, 2.0), dtype=dtype)
     y = run_rows(gn, dev, x, gamma, beta, N, L, C, G, 1e-6, 1, dtype)

@@ -58,8 +58,7 @@ def check_layout(p, E, C, dtype):
     assert W in (1, WIDE[dtype]) and S % W == 0 and NV in (1, 2, 4)
     assert W == 1 or (dtype == F32 and NV >= 2) or dtype != F32
     assert E % W == 0, "a 16-byte access must not straddle two samples"
-    assert 0 < A <= p["apply_threads"] and T == A * S
-    assert p["A2"] == A and p["T2"] == T
+    assert 0 < A <= p["threads"] and T == A * S
     assert T % C == 0, "a tile must be whole rows so each slot keeps one channel"
     # the kernels take masks and shifts for channel and group indices when all
     # 256 lanes are busy: that must happen exactly for power-of-two C
@@ -131,7 +130,7 @@ def check_lds(p, C, G):
     T, S = p["T"], p["slots"]
     Cg = C // G
     P = T // G
-    assert T <= p["apply_threads"] * S
+    assert T <= p["threads"] * S
     seen = np.zeros(T, np.int64)
     if G <= THREADS:
         tg = THREADS // G
@@ -160,7 +159,7 @@ def check_plan(N, L, C, G, dtype):
     wide = wide_layout(E, C, dtype, N * E * (4 if dtype == F32 else 2))
     want = wide or expected_layout(E, C, dtype)
     assert (p["W"], p["slots"] // p["W"], p["A"]) == want, (N, L, C, G, dtype, p)
-    assert p["apply_threads"] == (320 if wide else THREADS)
+    assert p["threads"] == (320 if wide else THREADS)
     o = check_layout(p, E, C, dtype)
     check_streaming_pass(N, E, p, o, p["tpc1"], p["K1"])
     check_streaming_pass(N, E, p, o, p["tpc2"], p["K2"])
@@ -283,9 +282,9 @@ def test_wide_layouts_follow_the_rule():
     # above 16 MiB, 1280 and 2560 take 320-lane workgroups, one access per lane
     for C in (1280, 2560):
         p = gn.plan_rows(1, 16384, C, 32)
-        assert (p["A"], p["slots"], p["T"], p["apply_threads"]) == (320, 8, 2560, 320)
-    assert gn.plan_rows(1, 16384, 320, 32)["apply_threads"] == 256
-    assert gn.plan_rows(1, 16384, 960, 32)["apply_threads"] == 256
+        assert (p["A"], p["slots"], p["T"], p["threads"]) == (320, 8, 2560, 320)
+    assert gn.plan_rows(1, 16384, 320, 32)["threads"] == 256
+    assert gn.plan_rows(1, 16384, 960, 32)["threads"] == 256
 
 
 def test_supported_set_matches_the_header_rule():
