@@ -787,28 +787,38 @@ gn_status check_conv(const void *x, const float *nmean, const float *nrstd, int6
     return GN_OK;
 }
 
-template <int WM, int WN, bool SILU>
+template <int WM, int WN, bool SILU, int WPE = 2>
 void launch_conv_ws(const gnconv::ConvArgs &a, int64_t grid, bool stats, hipStream_t s) {
     const dim3 g(static_cast<unsigned>(grid)), b(64 * WM * WN);
     const bool res = a.res != nullptr;
     if (stats) {
         if (res)
-            gnconv::gn_conv3x3<WM, WN, SILU, true, true><<<g, b, 0, s>>>(a);
+            gnconv::gn_conv3x3<WM, WN, SILU, true, true, WPE><<<g, b, 0, s>>>(a);
         else
-            gnconv::gn_conv3x3<WM, WN, SILU, true, false><<<g, b, 0, s>>>(a);
+            gnconv::gn_conv3x3<WM, WN, SILU, true, false, WPE><<<g, b, 0, s>>>(a);
     } else {
         if (res)
-            gnconv::gn_conv3x3<WM, WN, SILU, false, true><<<g, b, 0, s>>>(a);
+            gnconv::gn_conv3x3<WM, WN, SILU, false, true, WPE><<<g, b, 0, s>>>(a);
         else
-            gnconv::gn_conv3x3<WM, WN, SILU, false, false><<<g, b, 0, s>>>(a);
+            gnconv::gn_conv3x3<WM, WN, SILU, false, false, WPE><<<g, b, 0, s>>>(a);
     }
 }
+
+// Grids of at most this many workgroups (one per CU of an MI355X) run the
+// 128-pixel waves compiled for one wave per SIMD.  Only the speed depends on
+// it: every variant computes each output in the same order.
+constexpr int64_t kConvOneWaveMaxBlocks = 256;
 
 // wn = 2: 2 x 2 waves of 64 pixels x 64 channels; wn = 4: 1 x 4 waves of
 // 128 pixels x 64 channels.  256 lanes either way.
 void launch_conv(const gnconv::ConvArgs &a, int64_t grid, int wn, bool silu, bool stats,
                  hipStream_t s) {
-    if (wn == 4) {
+    if (wn == 4 && grid <= kConvOneWaveMaxBlocks) {
+        if (silu)
+            launch_conv_ws<1, 4, true, 1>(a, grid, stats, s);
+        else
+            launch_conv_ws<1, 4, false, 1>(a, grid, stats, s);
+    } else if (wn == 4) {
         if (silu)
             launch_conv_ws<1, 4, true>(a, grid, stats, s);
         else

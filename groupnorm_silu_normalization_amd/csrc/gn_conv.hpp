@@ -148,9 +148,12 @@ __device__ __forceinline__ bool map_block(const ConvArgs &a, int64_t b, int64_t 
 // Two waves per SIMD (at most 256 registers a lane): one wave stalls on its
 // loads while the other keeps the matrix core busy; left to itself the
 // compiler gives the 128-pixel waves 384 registers and one wave per SIMD,
-// measured 5-18% slower at the decoder shapes.
-template <int WM, int WN, bool SILU, bool STATS, bool RES>
-__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+// measured 5-18% slower at the decoder shapes.  WPE = 1 is for grids of at
+// most one workgroup per CU, where no second wave shares a SIMD anyway and the
+// compiler may use the whole register file (measured at (1,512,128,128):
+// 1-5% faster; with more workgroups 3-11% slower).
+template <int WM, int WN, bool SILU, bool STATS, bool RES, int WPE = 2>
+__global__ __launch_bounds__(64 * WM * WN) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void
 gn_conv3x3(ConvArgs a) {
     static_assert(WM == 1 || WM == 2, "a wave owns 128 or 64 pixels");
     constexpr bool PRO = true;
