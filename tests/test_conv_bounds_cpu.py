@@ -27,7 +27,19 @@ SHAPES = [  # N, H, W, Ci, Co, G2
     (1, 5, 7, 32, 128, 8), (1, 64, 64, 512, 512, 32), (3, 9, 17, 96, 384, 24),
     (1, 128, 128, 512, 512, 32), (2, 1, 1, 32, 1024, 64), (1, 17, 33, 1024, 128, 32),
     (1, 9, 20, 64, 768, 48), (2, 7, 40, 32, 256, 16),
+    (1, 144, 256, 64, 256, 32), (1, 256, 256, 32, 128, 32),
 ]
+
+
+def test_oracle_checked_shapes_reach_the_multi_tile_merge():
+    """The GPU parity shapes with more than 256 tiles per sample: the
+    statistics merge then folds two or more tiles in some threads, and
+    (1, 144, 256) with 256 output channels launches more than 256 workgroups,
+    so it runs the two-waves-per-SIMD build of the 128-pixel waves."""
+    p = gn.conv_plan(1, 144, 256, 64, 256, 32)
+    assert p["tiles_h"] * p["tiles_w"] == 288 and p["wn"] == 4 and p["blocks"] == 288
+    q = gn.conv_plan(1, 256, 256, 32, 128, 32)
+    assert q["tiles_h"] * q["tiles_w"] == 512 and q["wn"] == 2
 
 
 def block_map(p, b):

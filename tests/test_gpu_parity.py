@@ -5,8 +5,10 @@ The GPU output is bf16 (relative rounding <= 2^-9 = 1.95e-3) computed from
 fp32 statistics; the bound leaves room for the rounding of t = x*scale+shift
 and of SiLU but fails any dropped term, wrong group or wrong pivot.
 
-The five decoder shapes run at full size through gn_silu_nhwc, in the launch
-configuration the benchmark times (the plan depends on the shape only).
+The five decoder shapes run at full size twice: through the tensor-level
+group_norm_silu_4d (whose channels-last view goes to gn_silu_nhwc_strided_dtype)
+and through the C entry gn_silu_nhwc itself, the call the benchmark times, in
+the same launch configuration (the plan depends on the shape only).
 """
 import ctypes
 
@@ -110,6 +112,29 @@ def test_decoder_workload_full_size(gn, dev, oracle, idx):
     ref = oracle.gn_silu(x_bits, gamma, beta, w.N, w.L, w.C, w.G, w.eps, w.apply_silu,
                          out_dtype=np.float32)
     compare(y_bits, ref, w.name)
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_decoder_workload_through_gn_silu_nhwc(gn, dev, oracle, idx):
+    """The C entry gn_silu_nhwc, called directly with device pointers and the
+    current stream exactly as the benchmark calls it, at full size."""
+    from gn_inputs import WORKLOADS, make_inputs
+    w = WORKLOADS[idx]
+    print("case gn_silu_nhwc %s %s" % (w.name, w.label()), flush=True)
+    x_bits, gamma, beta = make_inputs(w)
+    x = to_dev_bits(x_bits, dev)
+    y = torch.empty_like(x)
+    g = torch.from_numpy(gamma).to(dev)
+    b = torch.from_numpy(beta).to(dev)
+    code = gn.gn_silu_nhwc(vp(x), vp(g), vp(b), vp(y), w.N, w.H, w.W, w.C, w.G, float(w.eps),
+                           int(w.apply_silu), stream(dev))
+    assert code == gn.GnStatus.OK, gn.status_text(code)
+    torch.cuda.synchronize()
+    y_bits = from_dev_bits(y)
+    del x, y
+    ref = oracle.gn_silu(x_bits, gamma, beta, w.N, w.L, w.C, w.G, w.eps, w.apply_silu,
+                         out_dtype=np.float32)
+    compare(y_bits, ref, "gn_silu_nhwc " + w.name)
 
 
 @pytest.mark.parametrize("idx", [0, 1, 2])
