@@ -25,7 +25,8 @@ call raises RuntimeError.
 The raw C entry points are re-exported under their C names (gn_silu_nhwc,
 gn_silu_rows, gn_silu_nhwc_strided, gn_silu_ndhwc, gn_stats_rows,
 gn_apply_rows, gn_profile_rows, gn_plan_rows, their *_dtype forms,
-gn_kernel_name, gn_status_string, gn_version, gn_device_info).
+gn_silu_rows_noalloc, gn_kernel_name, gn_status_string, gn_version,
+gn_device_info).
 """
 import ctypes
 import enum
@@ -83,6 +84,7 @@ lib.gn_silu_nhwc_dtype.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _
                                    _int, _vp]
 lib.gn_silu_rows_dtype.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _int,
                                    _vp]
+lib.gn_silu_rows_noalloc.argtypes = lib.gn_silu_rows_dtype.argtypes
 lib.gn_silu_nhwc_strided_dtype.argtypes = [_vp, _i64p, _vp, _vp, _vp, _i64p, _i64, _i64, _i64,
                                            _i64, _i64, _f32, _int, _int, _vp]
 lib.gn_silu_ndhwc.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f32, _int,
@@ -108,7 +110,8 @@ for _name in ("gn_silu_nhwc", "gn_silu_rows", "gn_silu_nhwc_strided", "gn_stats_
               "gn_silu_nhwc_strided_dtype", "gn_stats_rows_dtype", "gn_apply_rows_dtype",
               "gn_profile_rows_dtype", "gn_plan_rows_dtype", "gn_silu_ndhwc",
               "gn_silu_ndhwc_dtype", "gn_silu_ndhwc_strided_dtype", "gn_conv3x3_nhwc",
-              "gn_conv3x3_plan", "gn_conv3x3_pack_weights", "gn_conv3x3_nhwc_packed"):
+              "gn_conv3x3_plan", "gn_conv3x3_pack_weights", "gn_conv3x3_nhwc_packed",
+              "gn_silu_rows_noalloc"):
     getattr(lib, _name).restype = _int
 lib.gn_plan_rows.argtypes = [_i64, _i64, _i64, _i64, _i64p]
 lib.gn_plan_rows.restype = _int
@@ -132,6 +135,7 @@ gn_kernel_name = lib.gn_kernel_name
 gn_plan_rows = lib.gn_plan_rows
 gn_silu_nhwc_dtype = lib.gn_silu_nhwc_dtype
 gn_silu_rows_dtype = lib.gn_silu_rows_dtype
+gn_silu_rows_noalloc = lib.gn_silu_rows_noalloc
 gn_silu_nhwc_strided_dtype = lib.gn_silu_nhwc_strided_dtype
 gn_silu_ndhwc = lib.gn_silu_ndhwc
 gn_silu_ndhwc_dtype = lib.gn_silu_ndhwc_dtype
@@ -149,6 +153,7 @@ gn_version = lib.gn_version
 gn_device_info = lib.gn_device_info
 
 MAX_CHANNELS = 8192
+NOALLOC_SCRATCH_BYTES = 1 << 20   # GN_NOALLOC_SCRATCH_BYTES
 
 
 class GnDtype(enum.IntEnum):
@@ -191,6 +196,7 @@ class GnStatus(enum.IntEnum):
     UNSUPPORTED = 1
     INVALID_ARGUMENT = 2
     DEVICE_ERROR = 3
+    SCRATCH_TOO_SMALL = 4
 
 
 def status_text(code: int) -> str:

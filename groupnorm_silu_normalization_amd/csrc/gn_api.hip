@@ -27,6 +27,14 @@
 #include "gn_kernels.hpp"
 #include "gnsilu.h"
 
+// The scratch of gn_silu_rows_noalloc: one fixed buffer per device, part of
+// the library's code object (allocated by the runtime when the code is loaded
+// on a device, held until the process ends).  In host code this name is only
+// a stand-in for the symbol; the device address of each device's copy comes
+// from hipGetSymbolAddress (fixed_scratch below) and is the only form of it
+// that host code passes on.
+static __device__ __align__(256) char scratch[GN_NOALLOC_SCRATCH_BYTES];
+
 namespace gnsilu {
 namespace {
 
@@ -591,32 +599,47 @@ gn_status finish_launch() {
     return e == hipSuccess ? GN_OK : GN_DEVICE_ERROR;
 }
 
-// The full path, optionally with events around each kernel (iters > 0).
-gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y, int64_t N,
-                   int64_t L, int64_t C, int64_t G, float eps, int apply_silu, int dtype,
-                   void *stream, int iters, float *kernel_ms) {
-    gn_status st = check_shape(x, y, N, L, C, G, eps, apply_silu, true, dtype);
-    if (st == GN_OK) st = check_affine(gamma, beta, dtype);
-    if (st != GN_OK) return st;
-    if (N * L == 0) {
-        if (kernel_ms)
-            for (int i = 0; i < kSlots; ++i) kernel_ms[i] = -1.0f;
+// Scratch bytes of the full path for a plan: the arrival counter words, then
+// the payload (partials, padding, mean/rstd).  gn_plan_rows_dtype reports it.
+size_t full_path_scratch_bytes(const Plan &p) {
+    return arrivals_bytes(arrival_words(p)) + payload_bytes(p, true);
+}
+
+// ---- the fixed scratch of gn_silu_rows_noalloc -------------------------------
+// Device address of this device's copy of `scratch`, looked up once per
+// device (with that device current) and kept.
+std::mutex &fixed_scratch_mutex() {
+    static std::mutex *m = new std::mutex;
+    return *m;
+}
+std::map<int, char *> &fixed_scratch_map() {
+    static auto *m = new std::map<int, char *>;
+    return *m;
+}
+gn_status fixed_scratch(int dev, char **out) {
+    std::lock_guard<std::mutex> lock(fixed_scratch_mutex());
+    auto it = fixed_scratch_map().find(dev);
+    if (it != fixed_scratch_map().end()) {
+        *out = it->second;
         return GN_OK;
     }
-    Call c;
-    st = begin_call(stream, {x, y, gamma, beta}, &c);
-    if (st != GN_OK) return st;
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+        (void)hipGetLastError();
+        return GN_DEVICE_ERROR;
+    }
+    fixed_scratch_map()[dev] = static_cast<char *>(ptr);
+    *out = static_cast<char *>(ptr);
+    return GN_OK;
+}
 
-    const Plan p = make_plan(N, L, C, G, dtype);
+// Enqueues the full path with the given scratch: `counters` (arrival words,
+// zero in stream order) and `payload`.  Events around each kernel when ev.
+void enqueue_rows(const Plan &p, const void *x, const void *gamma, const void *beta, void *y,
+                  int apply_silu, float eps, unsigned *counters, char *payload, hipStream_t s,
+                  const Events *ev) {
     const size_t nparts = partial_floats(p);
-    const size_t nstats = static_cast<size_t>(N) * G;
-
-    std::lock_guard<std::mutex> lock(scratch_mutex());
-    unsigned *counters = nullptr;
-    char *payload = nullptr;
-    st = scratch_for(c.dev, c.stream, arrival_words(p), payload_bytes(p, true), &counters,
-                     &payload);
-    if (st != GN_OK) return st;
+    const size_t nstats = static_cast<size_t>(p.N) * p.stats.G;
     StatsOut o;
     o.part_s = reinterpret_cast<float *>(payload);
     o.part_q = o.part_s + nparts;
@@ -627,13 +650,59 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
     o.arrivals = counters;
     o.inv_m = p.inv_m;
     o.eps = eps;
-    const void *xb = x;
-    void *yb = y;
+    launch_stats(p, x, o, p.late, s, ev);
+    launch_apply(p, x, y, o.mean, o.rstd, p.late ? &o : nullptr, gamma, beta, apply_silu, s, ev);
+}
+
+// The full path, optionally with events around each kernel (iters > 0).
+// fixed: the scratch is the fixed buffer (gn_silu_rows_noalloc), not the
+// stream's allocated one.
+gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y, int64_t N,
+                   int64_t L, int64_t C, int64_t G, float eps, int apply_silu, int dtype,
+                   void *stream, int iters, float *kernel_ms, bool fixed = false) {
+    gn_status st = check_shape(x, y, N, L, C, G, eps, apply_silu, true, dtype);
+    if (st == GN_OK) st = check_affine(gamma, beta, dtype);
+    if (st != GN_OK) return st;
+    if (N * L == 0) {
+        if (kernel_ms)
+            for (int i = 0; i < kSlots; ++i) kernel_ms[i] = -1.0f;
+        return GN_OK;
+    }
+    const Plan p = make_plan(N, L, C, G, dtype);
+    if (fixed && full_path_scratch_bytes(p) > static_cast<size_t>(GN_NOALLOC_SCRATCH_BYTES))
+        return GN_SCRATCH_TOO_SMALL;
+    Call c;
+    st = begin_call(stream, {x, y, gamma, beta}, &c);
+    if (st != GN_OK) return st;
+
+    if (fixed) {
+        // Same layout as the stream scratch: counters at the front, then the
+        // payload.  The counters this call uses are cleared first (a fill
+        // kernel), so whatever an earlier call left in the buffer -- possibly
+        // payload of another layout where these counters sit -- is irrelevant.
+        char *base = nullptr;
+        st = fixed_scratch(c.dev, &base);
+        if (st != GN_OK) return st;
+        unsigned *counters = reinterpret_cast<unsigned *>(base);
+        const int64_t words = arrival_words(p);
+        if (p.fused && !p.late) {
+            st = zero_counters(counters, words, c.stream);
+            if (st != GN_OK) return st;
+        }
+        enqueue_rows(p, x, gamma, beta, y, apply_silu, eps, counters,
+                     base + arrivals_bytes(words), c.stream, nullptr);
+        return finish_launch();
+    }
+
+    std::lock_guard<std::mutex> lock(scratch_mutex());
+    unsigned *counters = nullptr;
+    char *payload = nullptr;
+    st = scratch_for(c.dev, c.stream, arrival_words(p), payload_bytes(p, true), &counters,
+                     &payload);
+    if (st != GN_OK) return st;
 
     if (iters <= 0) {
-        launch_stats(p, xb, o, p.late, c.stream, nullptr);
-        launch_apply(p, xb, yb, o.mean, o.rstd, p.late ? &o : nullptr, gamma, beta, apply_silu,
-                     c.stream, nullptr);
+        enqueue_rows(p, x, gamma, beta, y, apply_silu, eps, counters, payload, c.stream, nullptr);
         return finish_launch();
     }
 
@@ -648,11 +717,9 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
     st = GN_OK;
     for (int done = 0; done < iters && st == GN_OK;) {
         const int nb = std::min(kBatch, iters - done);
-        for (int i = 0; i < nb; ++i) {
-            launch_stats(p, xb, o, p.late, c.stream, &evs[i]);
-            launch_apply(p, xb, yb, o.mean, o.rstd, p.late ? &o : nullptr, gamma, beta,
-                         apply_silu, c.stream, &evs[i]);
-        }
+        for (int i = 0; i < nb; ++i)
+            enqueue_rows(p, x, gamma, beta, y, apply_silu, eps, counters, payload, c.stream,
+                         &evs[i]);
         st = finish_launch();
         if (st == GN_OK && hipStreamSynchronize(c.stream) != hipSuccess) st = GN_DEVICE_ERROR;
         for (int i = 0; i < nb && st == GN_OK; ++i)
@@ -843,6 +910,13 @@ gn_status gn_silu_rows_dtype(const void *x, const float *gamma, const float *bet
     return run_rows(x, gamma, beta, y, N, L, C, G, eps, apply_silu, dtype, stream, 0, nullptr);
 }
 
+gn_status gn_silu_rows_noalloc(const void *x, const float *gamma, const float *beta, void *y,
+                               int64_t N, int64_t L, int64_t C, int64_t G, float eps,
+                               int apply_silu, int dtype, void *stream) {
+    return run_rows(x, gamma, beta, y, N, L, C, G, eps, apply_silu, dtype, stream, 0, nullptr,
+                    true);
+}
+
 gn_status gn_silu_rows(const void *x, const float *gamma, const float *beta, void *y, int64_t N,
                        int64_t L, int64_t C, int64_t G, float eps, int apply_silu,
                        void *stream) {
@@ -1006,7 +1080,7 @@ gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dty
     plan_out[4] = p.stats.K;
     plan_out[5] = p.apply.tpc;
     plan_out[6] = p.apply.K;
-    plan_out[7] = static_cast<int64_t>(arrivals_bytes(arrival_words(p)) + payload_bytes(p, true));
+    plan_out[7] = static_cast<int64_t>(full_path_scratch_bytes(p));
     plan_out[8] = p.apply_ntl ? 1 : 0;
     plan_out[9] = p.lay.w;
     plan_out[10] = p.lay.a;
@@ -1172,6 +1246,9 @@ const char *gn_status_string(gn_status s) {
         case GN_UNSUPPORTED: return "GN_UNSUPPORTED: input outside the supported set; fall back";
         case GN_INVALID_ARGUMENT: return "GN_INVALID_ARGUMENT: not a valid GroupNorm call";
         case GN_DEVICE_ERROR: return "GN_DEVICE_ERROR: a HIP call failed";
+        case GN_SCRATCH_TOO_SMALL:
+            return "GN_SCRATCH_TOO_SMALL: the call needs more scratch than the fixed "
+                   "no-allocation buffer holds";
     }
     return "unknown gn_status";
 }

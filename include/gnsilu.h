@@ -92,7 +92,8 @@ typedef enum gn_status {
     GN_OK = 0,
     GN_UNSUPPORTED = 1,
     GN_INVALID_ARGUMENT = 2,
-    GN_DEVICE_ERROR = 3
+    GN_DEVICE_ERROR = 3,
+    GN_SCRATCH_TOO_SMALL = 4  /* gn_silu_rows_noalloc only: see there */
 } gn_status;
 
 /* Element type of x and y for the *_dtype entry points.  The page's kernel
@@ -134,6 +135,33 @@ enum {
 gn_status gn_silu_nhwc(const void *x, const float *gamma, const float *beta, void *y,
                        int64_t N, int64_t H, int64_t W, int64_t C, int64_t G,
                        float eps, int apply_silu, void *stream);
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the full
+ * path of gn_silu_rows_dtype (same arguments, same checks, same kernels and
+ * launch plan, so bitwise the same output), with the library's scratch (the
+ * arrival counters, partial sums and statistics) taken from a fixed buffer of
+ * GN_NOALLOC_SCRATCH_BYTES compiled into the library instead of the
+ * per-(device, stream) buffer the other entry points allocate.  Each device
+ * the library runs on holds one such buffer, reserved when the library's
+ * code is loaded on it and kept until the process ends.  The call allocates
+ * and frees nothing (no hipMalloc / hipFree); its first call on a device
+ * looks up that device's buffer address once.
+ * Sharing: every call of this entry point on one device uses the same
+ * buffer, which keeps the last call's contents; each call first clears the
+ * arrival counters it uses (a fill kernel on `stream`, no memset), so nothing
+ * an earlier call left behind is read.  Calls ordered on one stream are safe;
+ * calls that may overlap on one device (enqueued on different streams without
+ * ordering between them, or from several host threads at once) race on the
+ * buffer and give undefined results.
+ * Errors: as gn_silu_rows_dtype; then, still before any HIP call,
+ * GN_SCRATCH_TOO_SMALL when the shape needs more scratch than the buffer
+ * holds (gn_plan_rows_dtype's plan_out[7] gives a shape's need: about 80 KiB
+ * at the decoder shapes). */
+#define GN_NOALLOC_SCRATCH_BYTES (1 << 20)
+gn_status gn_silu_rows_noalloc(const void *x, const float *gamma, const float *beta, void *y,
+                               int64_t N, int64_t L, int64_t C, int64_t G,
+                               float eps, int apply_silu, int dtype, void *stream);
 
 /* group_norm_silu_rows: (N, L, C) rows with C innermost, the form the pages'
  * tests exercise "as used by attention" (Accuracy section, unit tests). */

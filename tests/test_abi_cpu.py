@@ -269,3 +269,35 @@ def test_one_hip_runtime_whatever_the_import_order():
     out = subprocess.run(["python", "-c", code], cwd=ROOT, capture_output=True, text=True,
                          check=True).stdout.strip().splitlines()[-1]
     assert out == "1"
+
+
+def noalloc(x=X, y=Y, N=1, L=16, C=64, G=32, eps=1e-6, silu=1, dtype=0):
+    return gn.gn_silu_rows_noalloc(x, None, None, y, N, L, C, G, eps, silu, dtype, None)
+
+
+def test_noalloc_checks_before_any_hip_call():
+    """gn_silu_rows_noalloc: the argument checks of gn_silu_rows_dtype, then the
+    fixed buffer's size, all before any HIP call (the fake pointers here are
+    never dereferenced)."""
+    assert noalloc(x=None) == GnStatus.INVALID_ARGUMENT
+    assert noalloc(C=64, G=3) == GnStatus.INVALID_ARGUMENT
+    assert noalloc(dtype=3) == GnStatus.INVALID_ARGUMENT
+    assert noalloc(C=257, G=1) == GnStatus.UNSUPPORTED
+    assert noalloc(x=ctypes.c_void_p(0x10002)) == GnStatus.UNSUPPORTED
+    assert noalloc(N=0) == GnStatus.OK and noalloc(L=0) == GnStatus.OK
+    # 4096 groups: the partials of 256 chunks need 8 MiB, more than the buffer
+    need = gn.plan_rows(1, 65536, 4096, 4096)["scratch_bytes"]
+    assert need > gn.NOALLOC_SCRATCH_BYTES
+    assert noalloc(N=1, L=65536, C=4096, G=4096) == GnStatus.SCRATCH_TOO_SMALL
+    # an invalid argument still wins over the size
+    assert noalloc(N=1, L=65536, C=4096, G=4096, eps=-1.0) == GnStatus.INVALID_ARGUMENT
+
+
+def test_noalloc_buffer_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define GN_NOALLOC_SCRATCH_BYTES \(1 << (\d+)\)", text)
+    assert m and (1 << int(m.group(1))) == gn.NOALLOC_SCRATCH_BYTES
+    # the decoder shapes fit
+    for N, L, C, G in ((1, 4096, 128, 32), (1, 16384, 512, 32), (1, 262144, 512, 32),
+                       (1, 1048576, 256, 32), (1, 1048576, 128, 32)):
+        assert gn.plan_rows(N, L, C, G)["scratch_bytes"] <= gn.NOALLOC_SCRATCH_BYTES
