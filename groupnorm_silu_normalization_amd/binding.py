@@ -105,13 +105,14 @@ lib.gn_profile_rows_dtype.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64
                                       _int, _vp, _int, ctypes.POINTER(_f32),
                                       ctypes.POINTER(_int)]
 lib.gn_plan_rows_dtype.argtypes = [_i64, _i64, _i64, _i64, _int, _i64p]
+lib.gn_plan_single_launch.argtypes = [_i64, _i64, _i64, _i64, _int, _i64p]
 for _name in ("gn_silu_nhwc", "gn_silu_rows", "gn_silu_nhwc_strided", "gn_stats_rows",
               "gn_apply_rows", "gn_profile_rows", "gn_silu_nhwc_dtype", "gn_silu_rows_dtype",
               "gn_silu_nhwc_strided_dtype", "gn_stats_rows_dtype", "gn_apply_rows_dtype",
               "gn_profile_rows_dtype", "gn_plan_rows_dtype", "gn_silu_ndhwc",
               "gn_silu_ndhwc_dtype", "gn_silu_ndhwc_strided_dtype", "gn_conv3x3_nhwc",
               "gn_conv3x3_plan", "gn_conv3x3_pack_weights", "gn_conv3x3_nhwc_packed",
-              "gn_silu_rows_noalloc"):
+              "gn_silu_rows_noalloc", "gn_plan_single_launch"):
     getattr(lib, _name).restype = _int
 lib.gn_plan_rows.argtypes = [_i64, _i64, _i64, _i64, _i64p]
 lib.gn_plan_rows.restype = _int
@@ -148,6 +149,7 @@ gn_stats_rows_dtype = lib.gn_stats_rows_dtype
 gn_apply_rows_dtype = lib.gn_apply_rows_dtype
 gn_profile_rows_dtype = lib.gn_profile_rows_dtype
 gn_plan_rows_dtype = lib.gn_plan_rows_dtype
+gn_plan_single_launch = lib.gn_plan_single_launch
 gn_status_string = lib.gn_status_string
 gn_version = lib.gn_version
 gn_device_info = lib.gn_device_info
@@ -377,6 +379,20 @@ def plan_rows(N, L, C, G, dtype=GnDtype.BF16):
     if r is None:
         return None
     return dict(zip(PLAN_FIELDS, list(buf)))
+
+
+SINGLE_LAUNCH_FIELDS = ("single_launch", "groups_per_workgroup", "pieces_per_row", "workgroups",
+                        "threads", "pieces_per_lane")
+
+
+def plan_single_launch(N, L, C, G, dtype=GnDtype.BF16):
+    """Whether (and how) a rows shape runs as one launch (dict), or None if declined."""
+    buf = (_i64 * 6)()
+    code = lib.gn_plan_single_launch(N, L, C, G, int(dtype), buf)
+    r = _result(code, True)
+    if r is None:
+        return None
+    return dict(zip(SINGLE_LAUNCH_FIELDS, list(buf)))
 
 
 def profile_rows(x, num_groups, weight, bias, eps, apply_silu, out, iters):

@@ -56,6 +56,14 @@ constexpr int64_t kApplyMaxBlocks = 2048;
 // does not evict it.  A tensor larger than the cache cannot be served from it
 // whole, and step 3 then streams x with nontemporal loads.
 constexpr int64_t kCacheResidentBytes = int64_t{256} << 20;
+// The single launch (gn_strip), measured on MI355X against the three-step
+// path over N in {1..16}, L in {256..4096}, C in {128, 256, 512}: 10-30%
+// faster with at most one workgroup per CU, at most kStripPieces pieces per
+// lane and up to 4 MiB; slower beyond (a second round of workgroups: up to
+// 4x; four pieces per lane: 2-20%; the (1,128,64,64) decoder shape is one of
+// those, 2% slower).
+constexpr int64_t kStripMaxBytes = int64_t{4} << 20;
+constexpr int64_t kStripMaxBlocks = 256;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t gcd64(int64_t a, int64_t b) {
@@ -155,7 +163,51 @@ struct Plan {
     Geometry apply;   // chunking of step 3
     int64_t N;
     double inv_m;     // 1 / (L*Cg)
+    bool strip;       // steps 1-3 in one launch (gn_strip), no scratch
+    int strip_sub;    // SUB of gn_strip: min(Cg, W)
+    StripGeo sg;
 };
+
+// The single launch: one workgroup per strip of gpw whole, consecutive groups
+// of a sample.  Needs 16-byte rows (C*esize % 16 == 0) and groups that split
+// into 16-byte pieces or fill them exactly: Cg a multiple of W (gpw = 1,
+// P = Cg/W pieces per row, a power of two <= 64) or a divisor of W (gpw =
+// W/Cg groups per piece, P = 1).
+bool choose_strip(int64_t N, int64_t L, int64_t C, int64_t G, int dtype, StripGeo *sg, int *sub) {
+    const int64_t es = elem_bytes(dtype);
+    const int64_t W = 16 / es;
+    if ((C * es) % 16 != 0) return false;
+    const int64_t Cg = C / G;
+    int64_t gpw;
+    if (Cg >= W) {
+        if (Cg % W != 0) return false;
+        gpw = 1;
+        *sub = static_cast<int>(W);
+    } else {
+        if (W % Cg != 0) return false;
+        gpw = W / Cg;
+        if (G % gpw != 0) return false;
+        *sub = static_cast<int>(Cg);
+    }
+    const int64_t P = gpw * Cg / W;
+    if (P > 64 || (P & (P - 1)) != 0) return false;
+    if (N * L * C * es > kStripMaxBytes) return false;
+    if (N * (G / gpw) > kStripMaxBlocks) return false;
+    if (ceil_div(L, kStripThreads / P) > kStripPieces) return false;
+    sg->L = L;
+    sg->E = L * C;
+    sg->C = static_cast<int>(C);
+    sg->G = static_cast<int>(G);
+    sg->Cg = static_cast<int>(Cg);
+    sg->gpw = static_cast<int>(gpw);
+    sg->P = static_cast<int>(P);
+    sg->S = static_cast<int>(G / gpw);
+    sg->blocks = N * sg->S;
+    sg->xcd = (sg->blocks % 8 == 0) ? 1 : 0;
+    sg->inv_m = 1.0 / (static_cast<double>(L) * static_cast<double>(Cg));
+    sg->eps = 0.0f;
+    return true;
+}
 
 // The plan depends on the shape only, never on the device, so the order of
 // every floating-point reduction is fixed by (N, L, C, G).
@@ -228,6 +280,7 @@ Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G, int dtype) {
     // small x because every step-3 workgroup re-reads the sample's partials.
     p.late = p.fused && bytes <= kStatsSmallBytes &&
              p.stats.K <= kFinalizeBatch * (kThreads / G);
+    p.strip = choose_strip(N, L, C, G, dtype, &p.sg, &p.strip_sub);
     return p;
 }
 
@@ -384,14 +437,18 @@ gn_status scratch_for(int dev, hipStream_t s, int64_t n, size_t payload, unsigne
 
 // ---- launches ---------------------------------------------------------------
 // Kernel slots, as reported by gn_profile_rows / gn_kernel_name.
-enum { kSlotStats = 0, kSlotFinalize = 1, kSlotApply = 2, kSlots = 3 };
-const char *kKernelNames[kSlots] = {"gn_partial_stats", "gn_finalize_stats", "gn_apply"};
+enum { kSlotStats = 0, kSlotFinalize = 1, kSlotApply = 2, kSlotStrip = 3, kSlots = 4 };
+const char *kKernelNames[kSlots] = {"gn_partial_stats", "gn_finalize_stats", "gn_apply",
+                                    "gn_strip"};
 
 struct Events {
     hipEvent_t ev[2 * kSlots];  // start/stop per slot
 };
 
 template <int V> using IC = std::integral_constant<int, V>;
+template <class T> struct TypeTag {
+    using type = T;
+};
 
 // Calls f(IC<W>, IC<NV>, IC<POW2>) with a layout as compile-time constants;
 // POW2 = all 256 lanes of a 256-lane workgroup busy, which happens exactly
@@ -568,6 +625,53 @@ void launch_apply(const Plan &p, const void *x, void *y, const float *mean, cons
     }
 }
 
+// The single launch.  stats_only: steps 1-2 alone, mean/rstd to mo/ro.
+template <class D, bool SILU>
+void launch_strip_s(const Plan &p, const void *x, void *y, const Affine &af, float eps,
+                    int stats_only, float *mo, float *ro, hipStream_t s) {
+    using T = typename D::storage;
+    constexpr int W = static_cast<int>(16 / sizeof(T));
+    StripGeo sg = p.sg;
+    sg.eps = eps;
+    const dim3 grid(static_cast<unsigned>(sg.blocks)), block(kStripThreads);
+    const T *xt = static_cast<const T *>(x);
+    T *yt = static_cast<T *>(y);
+    auto go = [&](auto subc) {
+        constexpr int SUB = decltype(subc)::value;
+        if constexpr (W % SUB == 0)
+            gn_strip<D, SUB, SILU><<<grid, block, 0, s>>>(xt, yt, sg, af, stats_only, mo, ro);
+    };
+    switch (p.strip_sub) {
+        case 1: go(IC<1>{}); break;
+        case 2: go(IC<2>{}); break;
+        case 4: go(IC<4>{}); break;
+        default: go(IC<8>{}); break;
+    }
+}
+
+void launch_strip(const Plan &p, const void *x, void *y, const void *gamma, const void *beta,
+                  int silu, float eps, int stats_only, float *mo, float *ro, hipStream_t s,
+                  const Events *ev) {
+    Affine af;
+    af.gamma = gamma;
+    af.beta = beta;
+    af.type = p.affine;
+    if (ev) (void)hipEventRecord(ev->ev[2 * kSlotStrip], s);
+    auto by_type = [&](auto dc) {
+        using D = typename decltype(dc)::type;
+        if (silu && !stats_only)
+            launch_strip_s<D, true>(p, x, y, af, eps, stats_only, mo, ro, s);
+        else
+            launch_strip_s<D, false>(p, x, y, af, eps, stats_only, mo, ro, s);
+    };
+    switch (p.dtype) {
+        case GN_DTYPE_F16: by_type(TypeTag<Fp16>{}); break;
+        case GN_DTYPE_F32: by_type(TypeTag<F32>{}); break;
+        default: by_type(TypeTag<Bf16>{}); break;
+    }
+    if (ev) (void)hipEventRecord(ev->ev[2 * kSlotStrip + 1], s);
+}
+
 // Everything a compute entry point needs after its argument checks.
 struct Call {
     hipStream_t stream;
@@ -602,6 +706,7 @@ gn_status finish_launch() {
 // Scratch bytes of the full path for a plan: the arrival counter words, then
 // the payload (partials, padding, mean/rstd).  gn_plan_rows_dtype reports it.
 size_t full_path_scratch_bytes(const Plan &p) {
+    if (p.strip) return 0;  // the single launch keeps everything on chip
     return arrivals_bytes(arrival_words(p)) + payload_bytes(p, true);
 }
 
@@ -638,6 +743,10 @@ gn_status fixed_scratch(int dev, char **out) {
 void enqueue_rows(const Plan &p, const void *x, const void *gamma, const void *beta, void *y,
                   int apply_silu, float eps, unsigned *counters, char *payload, hipStream_t s,
                   const Events *ev) {
+    if (p.strip) {
+        launch_strip(p, x, y, gamma, beta, apply_silu, eps, 0, nullptr, nullptr, s, ev);
+        return;
+    }
     const size_t nparts = partial_floats(p);
     const size_t nstats = static_cast<size_t>(p.N) * p.stats.G;
     StatsOut o;
@@ -675,7 +784,13 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
     st = begin_call(stream, {x, y, gamma, beta}, &c);
     if (st != GN_OK) return st;
 
-    if (fixed) {
+    if (p.strip) {  // one launch, no scratch
+        if (iters <= 0) {
+            enqueue_rows(p, x, gamma, beta, y, apply_silu, eps, nullptr, nullptr, c.stream,
+                         nullptr);
+            return finish_launch();
+        }
+    } else if (fixed) {
         // Same layout as the stream scratch: counters at the front, then the
         // payload.  The counters this call uses are cleared first (a fill
         // kernel), so whatever an earlier call left in the buffer -- possibly
@@ -694,12 +809,15 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
         return finish_launch();
     }
 
-    std::lock_guard<std::mutex> lock(scratch_mutex());
+    std::unique_lock<std::mutex> lock(scratch_mutex(), std::defer_lock);
     unsigned *counters = nullptr;
     char *payload = nullptr;
-    st = scratch_for(c.dev, c.stream, arrival_words(p), payload_bytes(p, true), &counters,
-                     &payload);
-    if (st != GN_OK) return st;
+    if (!p.strip) {
+        lock.lock();
+        st = scratch_for(c.dev, c.stream, arrival_words(p), payload_bytes(p, true), &counters,
+                         &payload);
+        if (st != GN_OK) return st;
+    }
 
     if (iters <= 0) {
         enqueue_rows(p, x, gamma, beta, y, apply_silu, eps, counters, payload, c.stream, nullptr);
@@ -712,8 +830,11 @@ gn_status run_rows(const void *x, const float *gamma, const float *beta, void *y
     for (auto &e : evs)
         for (auto &h : e.ev)
             if (hipEventCreate(&h) != hipSuccess) return GN_DEVICE_ERROR;
-    double sum_ms[kSlots] = {0.0, 0.0, 0.0};
-    auto launched = [&](int k) { return !(k == kSlotFinalize && p.fused); };
+    double sum_ms[kSlots] = {0.0, 0.0, 0.0, 0.0};
+    auto launched = [&](int k) {
+        if (p.strip) return k == kSlotStrip;
+        return k != kSlotStrip && !(k == kSlotFinalize && p.fused);
+    };
     st = GN_OK;
     for (int done = 0; done < iters && st == GN_OK;) {
         const int nb = std::min(kBatch, iters - done);
@@ -994,6 +1115,12 @@ gn_status gn_stats_rows_dtype(const void *x, int64_t N, int64_t L, int64_t C, in
     st = begin_call(stream, {x, mean_out, rstd_out}, &c);
     if (st != GN_OK) return st;
     const Plan p = make_plan(N, L, C, G, dtype);
+    if (p.strip) {  // the single launch's own statistics, so that steps 1-2 then 3
+                    // give the full path's y bit for bit
+        launch_strip(p, x, const_cast<void *>(x), nullptr, nullptr, 0, eps, 1, mean_out, rstd_out,
+                     c.stream, nullptr);
+        return finish_launch();
+    }
     const size_t nparts = partial_floats(p);
     std::lock_guard<std::mutex> lock(scratch_mutex());
     unsigned *counters = nullptr;
@@ -1088,6 +1215,26 @@ gn_status gn_plan_rows_dtype(int64_t N, int64_t L, int64_t C, int64_t G, int dty
     plan_out[12] = p.stats.plain_tail;
     plan_out[13] = p.late ? 1 : 0;
     plan_out[14] = p.threads;
+    return GN_OK;
+}
+
+gn_status gn_plan_single_launch(int64_t N, int64_t L, int64_t C, int64_t G, int dtype,
+                                int64_t plan_out[6]) {
+    if (plan_out == nullptr) return GN_INVALID_ARGUMENT;
+    static const uint16_t aligned_probe[8] __attribute__((aligned(16))) = {};
+    const gn_status st =
+        check_shape(aligned_probe, aligned_probe, N, L, C, G, 0.0f, 0, true, dtype);
+    if (st != GN_OK) return st;
+    for (int i = 0; i < 6; ++i) plan_out[i] = 0;
+    if (N * L == 0) return GN_OK;
+    const Plan p = make_plan(N, L, C, G, dtype);
+    if (!p.strip) return GN_OK;
+    plan_out[0] = 1;
+    plan_out[1] = p.sg.gpw;
+    plan_out[2] = p.sg.P;
+    plan_out[3] = p.sg.blocks;
+    plan_out[4] = kStripThreads;
+    plan_out[5] = ceil_div(L, kStripThreads / p.sg.P);
     return GN_OK;
 }
 

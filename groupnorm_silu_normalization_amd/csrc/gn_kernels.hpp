@@ -983,4 +983,223 @@ __global__ __launch_bounds__(NT) void gn_apply(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Single launch for small tensors: steps 1-3 in one kernel with no
+// communication between workgroups.  A workgroup owns a strip of gpw whole,
+// consecutive groups of one sample -- every row of those gpw*Cg channels --
+// so it finishes their statistics alone: it loads the strip once into
+// registers (at most kStripPieces 16-byte pieces per lane), reduces each
+// group in a fixed order, folds gamma/beta and applies from the registers.
+// Nothing waits on another workgroup, so no co-residency is needed and no
+// partials go through memory.
+//
+// Where it pays: a strip row is narrower than a cache line, so every row a
+// workgroup reads costs a whole line fill of its CU's L1 -- the strip's rows,
+// not its bytes, set the time, and one workgroup per group cannot spread a
+// long group over more CUs.  The host takes this path only for short strips
+// (at most kStripPieces pieces per lane) and at most one workgroup per CU;
+// larger tensors take the three-step path.
+//
+// Layout: the strip's rows are P 16-byte pieces wide (P = gpw*Cg / W, a power
+// of two <= 64); lane tid always takes piece p = tid % P of rows
+// tid / P + k*(NT/P), k < kStripPieces, so its W slots keep the channels
+// cs + p*W + j (cs: the strip's first channel) and its scale/shift stay in
+// registers.  SUB = min(Cg, W): a piece holds W/SUB whole groups (Cg <= W) or
+// a W-channel part of one group (Cg > W).
+// Reduction, fixed order: each lane sums its pieces per slot (pivot-shifted,
+// as in step 1), its slots per group part, then a butterfly over the lanes
+// of its wave with the same p; per (wave, piece, part) one LDS entry; per
+// group a tree over its entries (waves x pieces of the group).
+// ---------------------------------------------------------------------------
+constexpr int kStripThreads = 1024;  // 16 waves: one workgroup per CU
+constexpr int kStripPieces = 2;      // 16-byte pieces per lane, at most
+
+struct StripGeo {
+    int64_t L;        // rows per sample
+    int64_t E;        // elements per sample, L*C
+    int C, G, Cg;
+    int gpw;          // groups per strip
+    int P;            // 16-byte pieces per strip row (power of two, <= 64)
+    int S;            // strips per sample, G / gpw
+    int xcd;          // 1: workgroup b takes strip (b % 8) * (blocks / 8) + b / 8
+    int64_t blocks;   // N * S
+    double inv_m;     // 1 / (L*Cg)
+    float eps;
+};
+
+// v summed over the lanes of the wave whose lane index agrees with this
+// lane's in the bits below `low` (a power of two): xor butterfly, fixed
+// order, every such lane ends with the same total.
+__device__ __forceinline__ float wave_sum_same_low(float v, int low) {
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    for (int m = 32; m >= low; m >>= 1) {
+        const int o = __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, __float_as_int(v));
+        v += __int_as_float(o);
+    }
+    return v;
+}
+
+// stats_only (uniform, at run time): write the strip's groups' mean/rstd to
+// mean_out/rstd_out [N][G] and stop (steps 1-2 alone; the apply kernel then
+// gives the same y as the full single launch, bit for bit: the same fold and
+// transform of the same fp32 statistics).
+template <class D, int SUB, bool SILU>
+__global__ __launch_bounds__(kStripThreads) void gn_strip(
+    const typename D::storage *x, typename D::storage *y, StripGeo geo, Affine af,
+    int stats_only, float *__restrict__ mean_out, float *__restrict__ rstd_out) {
+    using T = typename D::storage;
+    constexpr int W = static_cast<int>(16 / sizeof(T));
+    constexpr int NT = kStripThreads;
+    constexpr int NW = NT / 64;
+    constexpr int NS = W / SUB;  // group parts per piece
+    using V = Vec<D, W>;
+    static_assert(W % SUB == 0, "SUB divides the piece");
+    __shared__ float ent_s[NW * 64 * NS], ent_q[NW * 64 * NS];  // per (wave, piece, part)
+    __shared__ float red_s[NT], red_q[NT];
+    __shared__ float s_mean[64 * NS], s_rstd[64 * NS];
+
+    const int tid = threadIdx.x;
+    int64_t b = blockIdx.x;
+    if (geo.xcd) b = (b % 8) * (geo.blocks / 8) + b / 8;
+    const int64_t n = b / geo.S;
+    const int strip = static_cast<int>(b - n * geo.S);
+    const int cs = strip * geo.gpw * geo.Cg;
+    const T *xs = x + n * geo.E + cs;
+    T *ys = y + n * geo.E + cs;
+    const int P = geo.P;
+    const int p = tid & (P - 1);
+    const int64_t r0 = tid / P;
+    const int64_t rstep = NT / P;
+    const int cw = p * W;  // the piece's first channel within the strip
+    const int64_t C = geo.C;
+
+    // the strip's pieces, issued first
+    V v[kStripPieces];
+#pragma unroll
+    for (int k = 0; k < kStripPieces; ++k) {
+        const int64_t r = r0 + k * rstep;
+        if (r < geo.L) v[k].template load<false>(xs + r * C + cw);
+    }
+    // pivots: the group's first element in row 0 (as step 1 takes them)
+    float piv[W], s[W], q[W];
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+        const int lg = (cw + j) / geo.Cg;
+        piv[j] = D::to_f32(xs[lg * geo.Cg]);
+        s[j] = 0.0f;
+        q[j] = 0.0f;
+    }
+    // gamma / beta of the lane's channels: issued now, used after the reduction
+    SlotParams<W> pr;
+    {
+        const void *gp = af.gamma ? af.gamma : static_cast<const void *>(x);
+        const void *bp = af.beta ? af.beta : static_cast<const void *>(x);
+        const int gs = af.gamma ? 1 : 0, bs = af.beta ? 1 : 0;
+        const int c0 = cs + cw;
+        if (af.type == Affine::kF32) {
+#pragma unroll
+            for (int j = 0; j < W; ++j) {
+                pr.g[j] = static_cast<const uint32_t *>(gp)[(c0 + j) * gs];
+                pr.b[j] = static_cast<const uint32_t *>(bp)[(c0 + j) * bs];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < W; ++j) {
+                pr.g[j] = static_cast<const uint16_t *>(gp)[(c0 + j) * gs];
+                pr.b[j] = static_cast<const uint16_t *>(bp)[(c0 + j) * bs];
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kStripPieces; ++k) {
+        if (r0 + k * rstep < geo.L) {
+#pragma unroll
+            for (int j = 0; j < W; ++j) accumulate1(v[k].get(j), piv[j], s[j], q[j]);
+        }
+    }
+
+    // slots -> group parts (SUB consecutive slots each), then the wave's
+    // lanes with the same piece
+    const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        float ps = 0.0f, pq = 0.0f;
+#pragma unroll
+        for (int j = u * SUB; j < (u + 1) * SUB; ++j) {
+            ps += s[j];
+            pq += q[j];
+        }
+        ps = wave_sum_same_low(ps, P);
+        pq = wave_sum_same_low(pq, P);
+        if (lane < P) {
+            ent_s[(wave * P + lane) * NS + u] = ps;
+            ent_q[(wave * P + lane) * NS + u] = pq;
+        }
+    }
+    __syncthreads();
+
+    // Entries of local group lg: Cg <= W: one per wave, piece lg*Cg / W,
+    // part (lg*Cg % W) / SUB; Cg > W: Cg/W per wave, the group's pieces.
+    // Entry e = wave*EPW + k, EPW = max(1, Cg/W): EPW*NW entries per group, a
+    // power of two; thread lg*EN + e holds entry e of group lg, a fixed tree
+    // over e follows.
+    const int EPW = geo.Cg > W ? geo.Cg / W : 1;
+    const int EN = EPW * NW;
+    {
+        const int lg = tid / EN, e = tid - lg * EN;
+        const bool has = lg < geo.gpw;
+        float as = 0.0f, aq = 0.0f;
+        if (has) {
+            const int w = e / EPW, k = e - w * EPW;
+            int pc, part;
+            if (geo.Cg > W) {
+                pc = lg * EPW + k;
+                part = 0;
+            } else {
+                pc = (lg * geo.Cg) / W;
+                part = ((lg * geo.Cg) % W) / SUB;
+            }
+            as = ent_s[(w * P + pc) * NS + part];
+            aq = ent_q[(w * P + pc) * NS + part];
+        }
+        red_s[tid] = as;
+        red_q[tid] = aq;
+        __syncthreads();
+        tree_sum(red_s, red_q, lg * EN, 1, has ? e : -1, EN);
+        if (has && e == 0) {
+            float mu, rs;
+            group_moments(red_s[tid], red_q[tid], D::to_f32(xs[lg * geo.Cg]), geo.inv_m,
+                          geo.eps, &mu, &rs);
+            s_mean[lg] = mu;
+            s_rstd[lg] = rs;
+            if (stats_only) {
+                const int64_t gi = n * geo.G + static_cast<int64_t>(strip) * geo.gpw + lg;
+                mean_out[gi] = mu;
+                rstd_out[gi] = rs;
+            }
+        }
+    }
+    if (stats_only) return;
+    __syncthreads();
+
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+        const int lg = (cw + j) / geo.Cg;
+        pr.mu[j] = s_mean[lg];
+        pr.rs[j] = s_rstd[lg];
+    }
+    float sc[W], sh[W];
+    fold_affine<W>(pr, af, sc, sh);
+#pragma unroll
+    for (int k = 0; k < kStripPieces; ++k) {
+        const int64_t r = r0 + k * rstep;
+        if (r < geo.L) {
+            float o[W];
+#pragma unroll
+            for (int j = 0; j < W; ++j) o[j] = transform1<SILU>(v[k].get(j), sc[j], sh[j]);
+            V::template store<true>(ys + r * C + cw, o);
+        }
+    }
+}
+
 }  // namespace gnsilu

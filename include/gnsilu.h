@@ -209,7 +209,7 @@ gn_status gn_apply_rows(const void *x, const float *mean, const float *rstd,
  * pair of HIP events around every kernel launch, synchronises, and writes
  * the mean duration in milliseconds of each kernel slot of the path to
  * kernel_ms[0 .. *n_kernels-1] (capacity 4); gn_kernel_name(i) names the
- * slots: 0 statistics, 1 separate finalize, 2 apply.  A slot whose kernel is
+ * slots: 0 statistics, 1 separate finalize, 2 apply, 3 the single launch.  A slot whose kernel is
  * not launched for this shape (the separate finalize, when the statistics
  * kernel finishes the groups itself) reads -1.
  * iters must be in [1, 100000]. */
@@ -232,6 +232,29 @@ gn_status gn_profile_rows(const void *x, const float *gamma, const float *beta, 
  * Returns the status gn_silu_rows would return from its argument checks
  * for 16-byte-aligned pointers. */
 gn_status gn_plan_rows(int64_t N, int64_t L, int64_t C, int64_t G, int64_t plan_out[8]);
+
+/* Whether the full path of a shape runs as a single launch, and its shape;
+ * no HIP call.  Steps 1-3 run in one kernel -- one workgroup of 1024 lanes
+ * per strip of whole, consecutive groups of a sample, which reduces its
+ * groups itself, holds the strip in registers and needs no scratch -- when
+ * the tensor is at most 4 MiB, its rows are 16-byte multiples (C times the
+ * element size a multiple of 16), Cg is a multiple of W (8 for 16-bit types,
+ * 4 for fp32) with Cg/W a power of two up to 64 or a divisor of W, at most
+ * 256 workgroups result (one per CU) and each lane holds at most two 16-byte
+ * pieces (L * pieces per row <= 2048): the short strips where one launch
+ * beats three steps.  Writes 6 values:
+ *   [0] 1 when the single launch runs, else 0 (and [1]-[5] are 0)
+ *   [1] groups per workgroup (a strip of consecutive groups)
+ *   [2] 16-byte pieces per row of a strip (a power of two)
+ *   [3] workgroups, N * G / [1]
+ *   [4] lanes per workgroup
+ *   [5] pieces each lane holds in registers
+ * Returns the status gn_silu_rows_dtype would return from its argument
+ * checks for aligned pointers.  gn_stats_rows takes the single launch's
+ * statistics for such shapes, so steps 1-2 then step 3 still give the full
+ * path's output bit for bit. */
+gn_status gn_plan_single_launch(int64_t N, int64_t L, int64_t C, int64_t G, int dtype,
+                                int64_t plan_out[6]);
 
 /* The same calls for x and y of element type `dtype` (a gn_dtype value);
  * the bf16 entry points above are these with dtype = GN_DTYPE_BF16.

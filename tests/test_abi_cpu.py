@@ -47,7 +47,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for must in ("gn_silu_nhwc", "gn_silu_rows", "gn_silu_nhwc_strided", "gn_stats_rows",
                  "gn_apply_rows", "gn_profile_rows", "gn_status_string", "gn_silu_ndhwc",
-                 "gn_silu_ndhwc_strided_dtype"):
+                 "gn_silu_ndhwc_strided_dtype", "gn_plan_single_launch", "gn_silu_rows_noalloc"):
         assert must in names
 
 
@@ -72,9 +72,9 @@ def test_status_strings_and_version():
     for s in GnStatus:
         assert gn.status_text(s).startswith("GN_" + s.name)
     assert gn.gn_version() >= 100
-    assert [gn.gn_kernel_name(i).decode() for i in range(3)] == [
-        "gn_partial_stats", "gn_finalize_stats", "gn_apply"]
-    assert gn.gn_kernel_name(3) is None and gn.gn_kernel_name(-1) is None
+    assert [gn.gn_kernel_name(i).decode() for i in range(4)] == [
+        "gn_partial_stats", "gn_finalize_stats", "gn_apply", "gn_strip"]
+    assert gn.gn_kernel_name(4) is None and gn.gn_kernel_name(-1) is None
 
 
 def rows(x=X, y=Y, N=1, L=16, C=64, G=32, eps=1e-6, silu=1):

@@ -415,10 +415,16 @@ def test_profile_helper(gn, dev):
     # G = 32, large: the statistics kernel finishes the groups itself (no finalize launch)
     assert set(ms) == {"gn_partial_stats", "gn_apply"}
     assert all(v > 0 for v in ms.values())
-    x2 = to_dev_bits(make_inputs(w)[0][: 4 * 16384 * 512], dev).reshape(4, 16384, 512)
+    x2 = to_dev_bits(make_inputs(w)[0][: 8 * 16384 * 512], dev).reshape(8, 16384, 512)
+    assert not gn.plan_single_launch(8, 16384, 512, 512)["single_launch"]
     ms2 = gn.profile_rows(x2, 512, None, None, w.eps, True, torch.empty_like(x2), 2)
     # G = 512 > 256 threads: a separate finalize kernel
     assert set(ms2) == {"gn_partial_stats", "gn_finalize_stats", "gn_apply"}
+    # a small tensor: the single launch, nothing else
+    x3 = x2[:2, :1024, :256].contiguous()
+    assert gn.plan_single_launch(2, 1024, 256, 32)["single_launch"]
+    ms3 = gn.profile_rows(x3, 32, None, None, w.eps, True, torch.empty_like(x3), 2)
+    assert set(ms3) == {"gn_strip"} and ms3["gn_strip"] > 0
 
 
 # ------------------------------------------------------ unsupported contract

@@ -190,7 +190,11 @@ def check_plan(N, L, C, G, dtype):
     # plus a total, each on its own 128-byte line, when a sample has >= 64 chunks
     words = N * ((8 + 1) * 32 if p["K1"] >= 64 else 1)
     counters = -(-4 * words // 256) * 256
-    assert p["scratch_bytes"] == counters + 4 * (2 * nparts + pad + 2 * N * G)
+    single = gn.plan_single_launch(N, L, C, G, dtype)["single_launch"]
+    # the single launch keeps everything on chip (the three-step plan above
+    # still serves steps 1-2 and 3 called alone)
+    assert p["scratch_bytes"] == (0 if single else
+                                  counters + 4 * (2 * nparts + pad + 2 * N * G))
     assert N * G < 2 ** 24
     check_lds(p, C, G)
     # step 1's plain-load tail: the whole chunk when the tensor fits the
@@ -336,3 +340,108 @@ def test_plan_declines_like_the_entry_points():
     with pytest.raises(ValueError):
         gn.plan_rows(1, 16, 64, 3)                    # C % G != 0
     assert gn.plan_rows(0, 16, 64, 32)["K1"] == 0     # empty: nothing launched
+
+
+# ---------------------------------------------------------------- single launch
+STRIP_THREADS, STRIP_PIECES = 1024, 2
+STRIP_SHAPES = [
+    (2, 32 * 32, 256, 32), (1, 256, 128, 32), (4, 2048, 256, 32), (16, 256, 64, 32),
+    (3, 999, 64, 32), (2, 77, 8, 8), (1, 5, 16, 1), (4, 1000, 128, 128), (2, 513, 256, 256),
+    (1, 1, 8, 1), (5, 123, 16, 16), (1, 1024, 32, 32), (8, 1024, 128, 32), (2, 256, 1024, 32),
+    (1, 32, 4096, 8), (1, 16, 2048, 4), (2, 1000, 512, 32), (16, 1024, 128, 32),
+    # not taken: too many rows per lane, too many workgroups, too large, odd groups
+    (1, 64 * 64, 128, 32), (32, 256, 128, 32), (1, 128 * 128, 512, 32), (2, 1024, 96, 32),
+]
+
+
+def strip_replay(N, L, C, G, dtype):
+    """Replays gn_strip's index arithmetic for the plan the library reports:
+    every access in bounds, every element of x read (and y written) exactly
+    once, each lane's slots on fixed channels of its own strip, and the LDS
+    entries of each group covering exactly its channels.  False when the
+    shape does not take the single launch."""
+    q = gn.plan_single_launch(N, L, C, G, dtype)
+    if not q["single_launch"]:
+        assert all(v == 0 for v in q.values())
+        return False
+    es = 4 if dtype == F32 else 2
+    W = 16 // es
+    Cg = C // G
+    gpw, P, blocks, NT = q["groups_per_workgroup"], q["pieces_per_row"], q["workgroups"], q["threads"]
+    assert NT == STRIP_THREADS and (C * es) % 16 == 0 and N * L * C * es <= 4 << 20
+    assert P & (P - 1) == 0 and 1 <= P <= 64 and gpw * Cg == P * W
+    S = G // gpw
+    assert blocks == N * S and blocks <= 256
+    SUB = min(Cg, W)
+    NS = W // SUB
+    NW = NT // 64
+    rstep = NT // P
+    assert q["pieces_per_lane"] == -(-L // rstep) <= STRIP_PIECES
+    xcd = blocks % 8 == 0
+    seen = np.zeros(N * L * C, dtype=np.int32)
+    strips = set()
+    tid = np.arange(NT)
+    for b0 in range(blocks):
+        b = (b0 % 8) * (blocks // 8) + b0 // 8 if xcd else b0
+        n, strip = divmod(b, S)
+        strips.add((n, strip))
+        cs = strip * gpw * Cg
+        p = tid & (P - 1)
+        r0 = tid // P
+        cw = p * W
+        for j in range(W):                    # pivots: group starts inside the strip
+            assert np.all((cw + j) // Cg < gpw)
+        for k in range(STRIP_PIECES):         # pieces: rows r0 + k*rstep < L
+            r = r0 + k * rstep
+            ok = r < L
+            base = n * L * C + cs + r[ok] * C + cw[ok]
+            assert np.all(base >= 0) and np.all(base + W <= N * L * C)
+            assert np.all((base * es) % 16 == 0)
+            for j in range(W):
+                seen[base + j] += 1
+        ent = (np.arange(NW)[:, None] * P + np.arange(P)[None, :]) * NS
+        assert ent.max() + NS - 1 < NW * 64 * NS
+        EPW = Cg // W if Cg > W else 1
+        EN = EPW * NW
+        assert gpw * EN <= NT and EN & (EN - 1) == 0 and gpw <= 64 * NS
+        for lg in range(gpw):
+            chans = set()
+            for e in range(EN):
+                w, k = divmod(e, EPW)
+                if Cg > W:
+                    pc, part = lg * EPW + k, 0
+                else:
+                    pc, part = (lg * Cg) // W, ((lg * Cg) % W) // SUB
+                assert 0 <= pc < P and 0 <= part < NS
+                chans |= set(range(pc * W + part * SUB, pc * W + part * SUB + SUB))
+            assert chans == set(range(lg * Cg, (lg + 1) * Cg)), "entries of a group"
+    assert len(strips) == blocks
+    assert np.all(seen == 1), "each element once"
+    return True
+
+
+@pytest.mark.parametrize("N,L,C,G", STRIP_SHAPES)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_single_launch_indices_in_bounds(N, L, C, G, dtype):
+    if gn.plan_rows(N, L, C, G, dtype) is None:
+        pytest.skip("declined")
+    strip_replay(N, L, C, G, dtype)
+
+
+def test_single_launch_selection():
+    """The single launch's domain: at most 4 MiB, 16-byte rows, groups that
+    fill or split into a power of two of 16-byte pieces, at most 256
+    workgroups and two pieces per lane."""
+    on = lambda *a: gn.plan_single_launch(*a)["single_launch"] == 1  # noqa: E731
+    assert on(2, 1024, 256, 32, BF16) and on(8, 1024, 128, 32, BF16) and on(2, 1024, 256, 32, F32)
+    assert on(1, 2048, 128, 32, BF16) and on(16, 1024, 128, 32, BF16)
+    assert not on(1, 4096, 128, 32, BF16)          # four pieces per lane
+    assert not on(1, 16384, 512, 32, BF16)         # 16 MiB
+    assert not on(32, 256, 128, 32, BF16)          # 512 workgroups
+    assert not on(16, 256, 256, 32, BF16)          # 512 workgroups
+    assert not on(1, 256, 4, 1, BF16)              # 8-byte rows
+    assert not on(1, 256, 96, 32, BF16)            # Cg = 3
+    assert not on(1, 256, 384, 16, BF16)           # Cg = 24: three pieces
+    assert on(1, 256, 384, 48, BF16)               # Cg = 8
+    n_on = sum(strip_replay(*s, BF16) for s in STRIP_SHAPES)
+    assert n_on == len(STRIP_SHAPES) - 4
