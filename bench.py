@@ -12,7 +12,9 @@ bf16 tensor (3 * 2 * numel), per call.
 Prints ONE JSON line.  Besides the contract fields it carries
   roofline     -- the dominant kernel (gn_apply): algorithmic bytes per
                   launch / its mean duration from HIP events recorded around
-                  each launch on the stream it runs on;
+                  each launch on the stream it runs on (an effective rate: the
+                  Infinity Cache serves part of its re-read of x), beside the
+                  whole call's fraction, warm and cold;
   cpu_baseline -- the fp64 oracle (test infrastructure) timed on the host's
                   cores on the same tensor, and once on one core;
   kernels_ms   -- mean duration of each kernel from the same events;
@@ -25,6 +27,8 @@ Prints ONE JSON line.  Besides the contract fields it carries
   per_call     -- the headline call timed call by call: warm (back to back)
                   and cold (a 1 GiB buffer written, or read, before each call,
                   so the Infinity Cache holds none of x): mean / median / min;
+  single_launch_shapes -- small rows shapes that take the single launch
+                  (steps 1-3 in one kernel), us/call;
   resnet_block -- the decoder's ResnetBlock2D (GroupNorm -> SiLU -> conv3x3 ->
                   GroupNorm -> SiLU -> conv3x3 + shortcut) with the GroupNorms
                   fused into the convolutions, against the same block run as
@@ -47,6 +51,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E, published peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak, published
 RESNET_SHAPES = ((1, 512, 128, 128), (1, 512, 256, 256), (1, 256, 512, 512))
+# small rows shapes (N, L, C), G = 32, that take the single launch
+SINGLE_LAUNCH_SHAPES = ((2, 1024, 256), (8, 1024, 128), (4, 2048, 256))
 H200_US = {                        # the pages' new-kernel column (H200), context only
     "gn_silu_1x512x128x128": 76.0,
     "gn_silu_1x512x256x256": 121.0,
@@ -338,6 +344,7 @@ def main():
     ap.add_argument("--no-wide-shapes", action="store_true")
     ap.add_argument("--no-extra-shapes", action="store_true")
     ap.add_argument("--no-resnet-block", action="store_true")
+    ap.add_argument("--no-single-launch", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -534,6 +541,38 @@ def main():
             }
             del ex, ey
 
+    single = {}
+    if not args.no_single_launch:
+        for (sN, sL, sC) in SINGLE_LAUNCH_SHAPES:
+            sG = 32
+            plan = gn.plan_single_launch(sN, sL, sC, sG)
+            log("single-launch shape (%d,%d,%d) %s" % (sN, sL, sC, plan))
+            gen = torch.Generator(device="cpu").manual_seed(sN * 1000 + sC)
+            sx = (torch.randn(sN, sL, sC, generator=gen) * 1.5 + 0.2).bfloat16().to(dev)
+            sy = torch.empty_like(sx)
+            sgt = (1 + 0.1 * torch.randn(sC, generator=gen)).to(dev)
+            sbt = (0.1 * torch.randn(sC, generator=gen)).to(dev)
+            sxp, syp = ctypes.c_void_p(sx.data_ptr()), ctypes.c_void_p(sy.data_ptr())
+            sgp, sbp = ctypes.c_void_p(sgt.data_ptr()), ctypes.c_void_p(sbt.data_ptr())
+
+            def sstep(sN=sN, sL=sL, sC=sC, sG=sG, sxp=sxp, syp=syp, sgp=sgp, sbp=sbp):
+                code = gn.gn_silu_rows(sxp, sgp, sbp, syp, sN, sL, sC, sG, 1e-6, 1, sh)
+                if code != 0:
+                    raise RuntimeError(gn.status_text(code))
+
+            sms, _ = time_calls(torch, sstep, max(args.steps, 100), args.warmup, stream)
+            sk = gn.profile_rows(sx, sG, sgt, sbt, 1e-6, True, sy, args.steps)
+            sbytes = 6 * sN * sL * sC
+            single["rows_%dx%dx%d" % (sN, sL, sC)] = {
+                "shape_rows": [sN, sL, sC], "groups": sG,
+                "plan": plan,
+                "us_per_call": round(sms * 1e3, 2),
+                "GB_s": round(sbytes / (sms * 1e-3) / 1e9, 1),
+                "frac_of_peak": round(sbytes / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "kernels_us": {k: round(v * 1e3, 2) for k, v in sk.items()},
+            }
+            del sx, sy
+
     resnet = {}
     if not args.no_resnet_block:
         for shp in RESNET_SHAPES:
@@ -593,6 +632,22 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": apply_bytes,
             "mean_launch_ms": round(apply_ms, 5),
+            "achieved_is": "algorithmic bytes (one read + one write of the tensor) / the "
+                           "kernel's mean duration: an effective rate, not measured HBM "
+                           "bandwidth -- part of step 3's read of x is served by the 256 MB "
+                           "Infinity Cache, which step 1 fills with the last cache's worth of x",
+            "traffic_is": "FETCH_SIZE + WRITE_SIZE per launch, scaled by a plain copy: requests "
+                          "the L2 sends toward memory, whether the Infinity Cache or HBM serves "
+                          "them (this part exposes no memory-side counter), so it shows no "
+                          "wasted re-reads but cannot split HBM from Infinity-Cache bytes",
+            "whole_call": {
+                "what": "the whole call (both kernels), algorithmic bytes (two reads + one "
+                        "write) / event-timed ms_per_step",
+                "achieved": round(value, 1),
+                "frac": round(value / HBM_PEAK_GBS, 4),
+                "cold_after_write_frac": per_call["cold_after_write"]["frac_of_peak_median"],
+                "cold_after_read_frac": per_call["cold_after_read"]["frac_of_peak_median"],
+            },
         },
         "kernels_ms": {k: round(v, 5) for k, v in kms.items()},
         "per_call": per_call,
@@ -604,6 +659,7 @@ def main():
         "other_dtypes": dtypes,
         "wide_shapes": wide,
         "extra_shapes": extra,
+        "single_launch_shapes": single,
         "resnet_block": resnet,
         "wall_s_timed_region": round(wall, 4),
         "device": dict({"name": props.name, "cus": props.multi_processor_count,

@@ -602,9 +602,11 @@ void launch_stats(const Plan &p, const void *x, const StatsOut &o, bool late, hi
 
 // late (non-null): step 3 runs the late finalize from these partials; else it
 // reads mean/rstd.
+// arrivals (non-null): step 1's arrival counters of this call, cleared by
+// step 3 (LateStats::arrivals).
 void launch_apply(const Plan &p, const void *x, void *y, const float *mean, const float *rstd,
                   const StatsOut *late, const void *gamma, const void *beta, int silu,
-                  hipStream_t s, const Events *ev) {
+                  hipStream_t s, const Events *ev, unsigned *arrivals = nullptr) {
     Affine af;
     af.gamma = gamma;
     af.beta = beta;
@@ -617,6 +619,10 @@ void launch_apply(const Plan &p, const void *x, void *y, const float *mean, cons
         ls.K1 = p.stats.K;
         ls.inv_m = late->inv_m;
         ls.eps = late->eps;
+    }
+    if (arrivals != nullptr) {
+        ls.arrivals = arrivals;
+        ls.arrival_words = arrival_stride(p.stats.K);
     }
     switch (p.dtype) {
         case GN_DTYPE_F16: launch_apply_t<Fp16>(p, x, y, mean, rstd, af, ls, silu, s, ev); break;
@@ -760,7 +766,8 @@ void enqueue_rows(const Plan &p, const void *x, const void *gamma, const void *b
     o.inv_m = p.inv_m;
     o.eps = eps;
     launch_stats(p, x, o, p.late, s, ev);
-    launch_apply(p, x, y, o.mean, o.rstd, p.late ? &o : nullptr, gamma, beta, apply_silu, s, ev);
+    launch_apply(p, x, y, o.mean, o.rstd, p.late ? &o : nullptr, gamma, beta, apply_silu, s, ev,
+                 p.fused && !p.late ? counters : nullptr);
 }
 
 // The full path, optionally with events around each kernel (iters > 0).

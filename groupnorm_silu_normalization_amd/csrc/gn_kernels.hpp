@@ -471,6 +471,11 @@ __device__ __forceinline__ bool arrive_is_last(const StatsOut &out, int64_t n, i
         }
     }
     __syncthreads();
+    // The last workgroup reads the other workgroups' partials next: an
+    // agent-scope acquire (invalidating what this CU's caches hold that is not
+    // coherent at agent scope) so those reads see every partial whose arrival
+    // was counted.  Paid once per sample.
+    if (last != 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     return last != 0;
 }
 
@@ -579,6 +584,12 @@ struct LateStats {
     int64_t K1;           // chunks per sample of step 1
     double inv_m;         // 1 / (L*Cg)
     float eps;
+    // Not the late finalize: the arrival counters step 1 of the same call
+    // used (or null), arrival_words per sample.  Workgroup 0 of each sample
+    // sets them to zero, so a counter left non-zero by calls that overlapped
+    // on the same scratch cannot disturb the calls after this one.
+    unsigned *arrivals;
+    int64_t arrival_words;
 };
 
 // gamma and beta: C values each, or null (1 and 0), of element type kF32,
@@ -850,13 +861,18 @@ __global__ __launch_bounds__(NT) void gn_apply(
     const int A = tg.lanes();
     const int tid = threadIdx.x;
     const bool active = tid < A;
-    if constexpr (!FIN) {
-        if (!active) return;
-    }
     const int64_t wg = blockIdx.x;
     const int64_t n = wg / geo.K;
     const int64_t k = wg - n * geo.K;
     const int64_t base = n * geo.E;
+    if (ls.arrivals != nullptr && k == 0) {
+        for (int64_t w = tid; w < ls.arrival_words; w += NT)
+            __hip_atomic_store(ls.arrivals + n * ls.arrival_words + w, 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if constexpr (!FIN) {
+        if (!active) return;
+    }
 
     // Late finalize, first its loads: the partials of (group g, part j) --
     // K1 <= kFinalizeBatch*tpg, so the fused finalize's first (only) batch,

@@ -51,6 +51,13 @@
  *   replay it on that stream, or ordered with that stream's work.  A call
  *   under capture must not need a larger buffer than that stream already
  *   has (make one call of the same shape on the stream before capturing).
+ *   Calls that overlap on one stream's buffer (such a graph replayed on
+ *   another stream while a call on the first is running) give undefined
+ *   results for those calls; the calls after them are unaffected, because
+ *   step 3 clears the arrival counters step 1 used.  The buffer is found by
+ *   the stream handle's value: synchronise a stream before destroying it, or
+ *   a new stream that receives the same handle shares the buffer with work
+ *   still pending on the old one.
  * Synchrony: every compute call is asynchronous on `stream` and returns once
  *   the kernels are enqueued; a fault inside a kernel surfaces at the
  *   caller's next synchronisation (gn_profile_rows excepted, which

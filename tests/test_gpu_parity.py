@@ -575,3 +575,38 @@ def test_graph_replays_after_the_scratch_grows(gn, dev):
             stream.synchronize()
             assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "replay %d" % rep
             assert torch.equal(again.view(torch.int16), refb.view(torch.int16))
+
+
+def test_counters_recover_after_overlapping_calls(gn, dev):
+    """A graph captured on stream A and replayed on stream B while eager calls
+    run on A: the overlapping calls share A's scratch (the header calls their
+    results undefined; no kernel waits on another, so they all finish).
+    Afterwards every call on A is bitwise the reference again: step 3 clears
+    the arrival counters step 1 used, so nothing the overlap left behind
+    reaches the later calls."""
+    N, L, C, G = 1, 65536, 512, 32        # 256 chunks: the two-level arrival count
+    p = gn.plan_rows(N, L, C, G)
+    assert p["K1"] >= 64 and not p["late_finalize"]
+    assert not gn.plan_single_launch(N, L, C, G)["single_launch"]
+    gen = torch.Generator(device="cpu").manual_seed(77)
+    x = torch.randn(N, L, C, generator=gen).bfloat16().to(dev)
+    a, b = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    with torch.no_grad():
+        with torch.cuda.stream(a):
+            ref = gn.group_norm_silu_rows(x, G).clone()
+            gn.group_norm_silu_rows(x, G)
+        a.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=a):
+            gn.group_norm_silu_rows(x, G)
+        for _ in range(20):                   # overlap: B replays while A computes
+            with torch.cuda.stream(b):
+                g.replay()
+            with torch.cuda.stream(a):
+                gn.group_norm_silu_rows(x, G)
+        torch.cuda.synchronize()
+        for rep in range(5):
+            with torch.cuda.stream(a):
+                y = gn.group_norm_silu_rows(x, G)
+            a.synchronize()
+            assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), "call %d after" % rep
