@@ -45,6 +45,8 @@ constexpr int kUnrollApply = 4;             // 16-byte loads in flight per lane,
 constexpr int64_t kStatsBlocks = 256;       // step-1 workgroups in total: one per CU ...
 constexpr int64_t kStatsBlocksSmall = 128;  // ... or half that for x up to kStatsSmallBytes,
 constexpr int64_t kStatsSmallBytes = int64_t{16} << 20;  // where latency, not bandwidth, rules
+constexpr int64_t kSepFinalizeMaxBytes = int64_t{64} << 20;  // step 2 as its own kernel above
+                                                             // kStatsSmallBytes up to this
 constexpr int64_t kStatsMinTiles = 8;       // tiles per workgroup, at least
 constexpr int64_t kStatsMaxTiles = 1024;    // caps each lane's sequential fp32 run
 constexpr int64_t kApplyElemsPerBlock = 16 * 2048;  // step-3 workgroups: elements / 32768 ...
@@ -229,7 +231,14 @@ Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G, int dtype) {
             p.threads = kWideThreads;
         }
     }
-    p.fused = G <= kThreads;
+    // Step 2 runs in the tail of step 1 (the last workgroup of each sample)
+    // when one workgroup's threads cover the groups, except from 16 to 64 MiB,
+    // where the separate finalize kernel is faster: measured on MI355X, the
+    // last workgroup's chain (write-through partials, arrival, coherent reads)
+    // costs more there than a third launch (64 MiB: 40.2 -> 39.5 us, 32 MiB:
+    // 25.8 -> 25.2 us); from 128 MiB up the two are within noise.
+    const int64_t xbytes = N * E * elem_bytes(dtype);
+    p.fused = G <= kThreads && !(xbytes > kStatsSmallBytes && xbytes <= kSepFinalizeMaxBytes);
     p.apply_ntl = N * E * elem_bytes(dtype) > kCacheResidentBytes;
     Geometry g;
     g.E = E;
