@@ -45,8 +45,8 @@ constexpr int kUnrollApply = 4;             // 16-byte loads in flight per lane,
 constexpr int64_t kStatsBlocks = 256;       // step-1 workgroups in total: one per CU ...
 constexpr int64_t kStatsBlocksSmall = 128;  // ... or half that for x up to kStatsSmallBytes,
 constexpr int64_t kStatsSmallBytes = int64_t{16} << 20;  // where latency, not bandwidth, rules
-constexpr int64_t kSepFinalizeMaxBytes = int64_t{64} << 20;  // step 2 as its own kernel above
-                                                             // kStatsSmallBytes up to this
+constexpr int64_t kSepFinalizeMaxBytes = int64_t{160} << 20;  // step 2 as its own kernel above
+                                                              // kStatsSmallBytes up to this
 constexpr int64_t kStatsMinTiles = 8;       // tiles per workgroup, at least
 constexpr int64_t kStatsMaxTiles = 1024;    // caps each lane's sequential fp32 run
 constexpr int64_t kApplyElemsPerBlock = 16 * 2048;  // step-3 workgroups: elements / 32768 ...
@@ -232,11 +232,12 @@ Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G, int dtype) {
         }
     }
     // Step 2 runs in the tail of step 1 (the last workgroup of each sample)
-    // when one workgroup's threads cover the groups, except from 16 to 64 MiB,
+    // when one workgroup's threads cover the groups, except from 16 to 160 MiB,
     // where the separate finalize kernel is faster: measured on MI355X, the
     // last workgroup's chain (write-through partials, arrival, coherent reads)
     // costs more there than a third launch (64 MiB: 40.2 -> 39.5 us, 32 MiB:
-    // 25.8 -> 25.2 us); from 128 MiB up the two are within noise.
+    // 25.8 -> 25.2 us, 80-160 MiB: 0.4-0.7 us less); from 256 MiB up the two
+    // are within noise.
     const int64_t xbytes = N * E * elem_bytes(dtype);
     p.fused = G <= kThreads && !(xbytes > kStatsSmallBytes && xbytes <= kSepFinalizeMaxBytes);
     p.apply_ntl = N * E * elem_bytes(dtype) > kCacheResidentBytes;
@@ -253,6 +254,7 @@ Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G, int dtype) {
     while ((int64_t{1} << g.cg_shift) < C / G) ++g.cg_shift;
     if (p.lay.a != kThreads) g.cg_shift = 0;  // only the power-of-two kernels use it
     g.plain_tail = 0;
+    g.rem = 0;
     const int64_t total = N * g.tiles;
     const int64_t bytes = N * E * elem_bytes(dtype);
     p.stats = g;
@@ -277,10 +279,19 @@ Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G, int dtype) {
             ? p.stats.tpc
             : std::max<int64_t>(1, ceil_div(p.stats.tpc * kCacheResidentBytes, bytes));
     p.apply = g;
-    const int64_t apply_blocks = std::min(
+    // Step 3: about one workgroup per 32768 elements, between 256 and 2048,
+    // rounded to whole rounds of 256 (one workgroup on every CU of an MI355X
+    // per round) and the tiles split evenly (the first tiles % K chunks take
+    // one more), so every CU ends its last round with the same work.
+    // Measured on MI355X against the previous rule (whole-tile chunks of
+    // ceil(total / blocks) tiles, e.g. 1821 workgroups at (1,960,256,256)):
+    // y bitwise the same (the chunking of step 3 changes no arithmetic).
+    int64_t apply_blocks = std::min(
         kApplyMaxBlocks, std::max(kApplyMinBlocks, total * g.T / kApplyElemsPerBlock));
-    p.apply.tpc = std::max<int64_t>(1, ceil_div(total, apply_blocks));
-    p.apply.K = ceil_div(g.tiles, p.apply.tpc);
+    apply_blocks = (apply_blocks + kApplyMinBlocks / 2) / kApplyMinBlocks * kApplyMinBlocks;
+    p.apply.K = std::max<int64_t>(1, std::min(g.tiles, ceil_div(apply_blocks, N)));
+    p.apply.tpc = g.tiles / p.apply.K;
+    p.apply.rem = g.tiles - p.apply.tpc * p.apply.K;
     p.inv_m = 1.0 / (static_cast<double>(L) * static_cast<double>(C / G));
     // The late finalize: for a small x (latency-bound) whose sample's step-1
     // partials one finalize batch per thread covers, step 1 only writes its

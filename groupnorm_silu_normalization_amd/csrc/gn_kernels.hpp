@@ -200,7 +200,9 @@ struct Geometry {
     int64_t T;      // elements per tile: R whole rows, a multiple of C (T = A*S)
     int64_t tiles;  // tiles per sample, ceil(E / T)
     int64_t full;   // tiles per sample lying entirely inside the sample
-    int64_t tpc;    // tiles per chunk (one workgroup's share)
+    int64_t tpc;    // tiles per chunk (one workgroup's share) ...
+    int64_t rem;    // ... plus one for the first `rem` chunks of a sample (step 3;
+                    // step 1's chunks are tpc tiles, the last one cut at the end)
     int64_t K;      // chunks per sample
     int C;          // channels
     int G;          // groups
@@ -337,6 +339,17 @@ __device__ __forceinline__ ChunkRange chunk_range(const Geometry &geo, int64_t k
     ChunkRange r;
     r.t_begin = k * geo.tpc;
     r.t_end = r.t_begin + geo.tpc < geo.tiles ? r.t_begin + geo.tpc : geo.tiles;
+    r.t_full_end = r.t_end < geo.full ? r.t_end : geo.full;
+    if (r.t_full_end < r.t_begin) r.t_full_end = r.t_begin;
+    return r;
+}
+// Step 3's chunks: the sample's tiles split evenly, the first geo.rem chunks
+// one tile longer.
+__device__ __forceinline__ ChunkRange chunk_range_even(const Geometry &geo, int64_t k) {
+    ChunkRange r;
+    r.t_begin = k * geo.tpc + (k < geo.rem ? k : geo.rem);
+    const int64_t end = r.t_begin + geo.tpc + (k < geo.rem ? 1 : 0);
+    r.t_end = end < geo.tiles ? end : geo.tiles;
     r.t_full_end = r.t_end < geo.full ? r.t_end : geo.full;
     if (r.t_full_end < r.t_begin) r.t_full_end = r.t_begin;
     return r;
@@ -898,7 +911,7 @@ __global__ __launch_bounds__(NT) void gn_apply(
     SlotParams<S> pr;
     if (active) load_slot_params<L, POW2, !FIN>(mean, rstd, af, geo, tg, n, tid, pr);
 
-    const ChunkRange cr = chunk_range(geo, k);
+    const ChunkRange cr = chunk_range_even(geo, k);
     int64_t off = base + cr.t_begin * T;  // current tile
     int64_t tt = cr.t_begin;
     const int64_t nb = (cr.t_full_end - tt) / UNROLL;  // whole batches

@@ -233,7 +233,8 @@ gn_status gn_profile_rows(const void *x, const float *gamma, const float *beta, 
  *   [2] full    tiles per sample lying wholly inside the sample
  *   [3] tpc1    tiles per workgroup, statistics pass
  *   [4] K1      workgroups per sample, statistics pass (N*K1 launched)
- *   [5] tpc2    tiles per workgroup, apply pass
+ *   [5] tpc2    tiles per workgroup, apply pass (the first tiles % K2
+ *               workgroups of each sample take one tile more)
  *   [6] K2      workgroups per sample, apply pass (N*K2 launched)
  *   [7] scratch bytes of library-owned scratch the call needs
  * Returns the status gn_silu_rows would return from its argument checks

@@ -518,9 +518,9 @@ def test_arrival_counters_alternating_modes(gn, dev, oracle):
     counter left non-zero would misplace the finalize), and the two-level one
     matches the oracle."""
     from gn_inputs import make_custom
-    # (above 64 MiB the statistics kernel finishes the groups itself: the
-    # two-level count runs there)
-    cases = [(3, 200001, 128, 32), (1, 4096, 128, 32), (2, 140000, 256, 32), (16, 16384, 512, 32)]
+    # (above 160 MiB the statistics kernel finishes the groups itself: the
+    # arrival counts run there)
+    cases = [(3, 250001, 128, 32), (1, 4096, 128, 32), (2, 200000, 256, 32), (16, 16384, 512, 32)]
     ks = [gn.plan_rows(*c)["K1"] for c in cases]
     assert ks[0] >= 64 and ks[2] >= 64 and ks[1] < 64 and ks[3] < 64
     data = []
@@ -586,7 +586,7 @@ def test_counters_recover_after_overlapping_calls(gn, dev):
     Afterwards every call on A is bitwise the reference again: step 3 clears
     the arrival counters step 1 used, so nothing the overlap left behind
     reaches the later calls."""
-    N, L, C, G = 1, 131072, 512, 32       # 128 MiB, 256 chunks: the two-level arrival count
+    N, L, C, G = 1, 196608, 512, 32       # 192 MiB, 256 chunks: the two-level arrival count
     p = gn.plan_rows(N, L, C, G)
     assert p["K1"] >= 64 and not p["late_finalize"]
     assert not gn.plan_single_launch(N, L, C, G)["single_launch"]

@@ -78,11 +78,13 @@ def check_layout(p, E, C, dtype):
     return o
 
 
-def chunks(tiles, full, tpc, K):
+def chunks(tiles, full, tpc, K, rem=0):
+    """Chunk k: tiles [k*tpc + min(k, rem), + tpc + (k < rem)), clipped to the
+    sample (step 1: rem = 0; step 3: an even split, rem = tiles % K)."""
     out = []
     for k in range(K):
-        t_begin = k * tpc
-        t_end = min(t_begin + tpc, tiles)
+        t_begin = k * tpc + min(k, rem)
+        t_end = min(t_begin + tpc + (1 if k < rem else 0), tiles)
         out.append((t_begin, t_end, max(min(t_end, full), t_begin)))
     return out
 
@@ -103,11 +105,11 @@ def wide_layout(E, C, dtype, nbytes):
     return (W, nv_min, 320) if 320 % m == 0 else None
 
 
-def check_streaming_pass(N, E, p, o, tpc, K):
+def check_streaming_pass(N, E, p, o, tpc, K, rem=0):
     T, tiles, full = p["T"], p["tiles"], p["full"]
     assert N * K < 2 ** 24, "grid too large"
     assert tiles == -(-E // T) and full == E // T
-    cs = chunks(tiles, full, tpc, K)
+    cs = chunks(tiles, full, tpc, K, rem)
     # the chunks cover tiles [0, tiles) once, in order
     assert cs[0][0] == 0 and cs[-1][1] == tiles
     for a, b in zip(cs, cs[1:]):
@@ -162,7 +164,9 @@ def check_plan(N, L, C, G, dtype):
     assert p["threads"] == (320 if wide else THREADS)
     o = check_layout(p, E, C, dtype)
     check_streaming_pass(N, E, p, o, p["tpc1"], p["K1"])
-    check_streaming_pass(N, E, p, o, p["tpc2"], p["K2"])
+    # step 3: K2 chunks splitting the tiles evenly, K2 from whole rounds of 256
+    assert p["tpc2"] == p["tiles"] // p["K2"] >= 1
+    check_streaming_pass(N, E, p, o, p["tpc2"], p["K2"], p["tiles"] % p["K2"])
     # each lane slot keeps one channel across tiles: o mod C, and its group
     ch = o % C
     assert np.all((ch // (C // G)) < G)
