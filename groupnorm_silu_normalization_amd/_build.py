@@ -37,6 +37,48 @@ def compile_command(out: str):
     ]
 
 
+def sanitizer_command(out: str):
+    """The host-sanitizer build: host code with AddressSanitizer and
+    UndefinedBehaviorSanitizer (every -fsanitize after -Xarch_host, so no
+    device code is instrumented), device code unoptimised (it is never
+    launched: the build serves the CPU tests of the argument checks and the
+    plan)."""
+    return [
+        hipcc(), "--offload-arch=" + ARCH, "-O1", "-g", "-std=c++17", "-fPIC", "-shared",
+        "-fno-omit-frame-pointer", "-Xarch_device", "-O0", "-Xarch_device", "-g0",
+        "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+        "-Xarch_host", "-fno-sanitize-recover=undefined",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-unused-command-line-argument",
+        "-I", INCLUDE, "-I", CSRC, "-o", out, *SOURCES,
+    ]
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's AddressSanitizer runtime (to preload into a
+    Python that is not itself instrumented), or '' if there is none."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "bin", "clang")
+    for cand in (clang, "/opt/rocm/llvm/bin/clang", shutil.which("clang")):
+        if cand and os.path.exists(cand):
+            res = subprocess.run([cand, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                                 capture_output=True, text=True)
+            path = res.stdout.strip()
+            if res.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+                return path
+    return ""
+
+
+def build_host_sanitized(out: str, verbose: bool = False) -> str:
+    cmd = sanitizer_command(out)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building the host-sanitizer library")
+    return out
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = compile_command(tmp)
@@ -56,5 +98,9 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
-    print(LIB)
+    if len(sys.argv) > 2 and sys.argv[1] == "--host-sanitizers":
+        print(build_host_sanitized(sys.argv[2], verbose=True))
+        print("preload:", asan_runtime())
+    else:
+        build(verbose=True)
+        print(LIB)

@@ -41,7 +41,9 @@ import os
 import torch  # noqa: F401
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libgnsilu.so")
+# GNSILU_LIBRARY names another build of the same library (the host-sanitizer
+# build of _build.py, for the CPU tests); by default the in-tree build.
+LIB_PATH = os.environ.get("GNSILU_LIBRARY") or os.path.join(_PKG, "libgnsilu.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
