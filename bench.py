@@ -307,8 +307,16 @@ def resnet_block(torch, gn, dev, shp, args):
         t_cp = best(conv_plain, stream, 2)
         t_cu = best(conv_unpacked, stream, 2)
         t_tc = best(lambda: torch.nn.functional.conv2d(x, ws[0], bb[0], padding=1), stream, 2)
+        # the same contraction as a plain library GEMM (hipBLASLt through
+        # torch.matmul, contiguous bf16 operands): M = pixels, K = 9*C, N = C
+        ga_ = torch.randn(N * H * W, 9 * C, device=dev, dtype=torch.bfloat16)
+        gb_ = torch.randn(9 * C, C, device=dev, dtype=torch.bfloat16)
+        t_gemm = best(lambda: torch.matmul(ga_, gb_), stream, 2)
+        del ga_, gb_
     flops = 2.0 * N * H * W * C * 9 * C
     tf = flops / (t_c1 * 1e-3) / 1e12
+    tf_plain = flops / (t_cp * 1e-3) / 1e12
+    tf_gemm = flops / (t_gemm * 1e-3) / 1e12
     return {
         "shape_nchw": [N, C, H, W],
         "fused_us": round(t_f * 1e3, 1),
@@ -328,7 +336,17 @@ def resnet_block(torch, gn, dev, shp, args):
                           "bound": "mfma", "achieved": round(tf, 1),
                           "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                           "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
-                          "flops_per_launch": flops},
+                          "flops_per_launch": flops,
+                          "plain_conv_frac": round(tf_plain / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "library_gemm_reference": {
+            "what": "torch.matmul (hipBLASLt) on the same contraction as one plain GEMM: "
+                    "[N*H*W, 9*C] x [9*C, C], contiguous bf16, no halo, no fusion",
+            "us": round(t_gemm * 1e3, 1),
+            "TFLOP_s": round(tf_gemm, 1),
+            "frac": round(tf_gemm / MFMA_BF16_PEAK_TFLOPS, 4),
+            "fused_conv_over_gemm_time": round(t_c1 / t_gemm, 3),
+            "plain_conv_over_gemm_time": round(t_cp / t_gemm, 3),
+        },
     }
 
 
