@@ -87,6 +87,7 @@ lib.gn_silu_nhwc_dtype.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _
 lib.gn_silu_rows_dtype.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _int,
                                    _vp]
 lib.gn_silu_rows_noalloc.argtypes = lib.gn_silu_rows_dtype.argtypes
+lib.gn_noalloc_scratch.argtypes = [_int, ctypes.POINTER(_vp), ctypes.POINTER(ctypes.c_int64)]
 lib.gn_silu_nhwc_strided_dtype.argtypes = [_vp, _i64p, _vp, _vp, _vp, _i64p, _i64, _i64, _i64,
                                            _i64, _i64, _f32, _int, _int, _vp]
 lib.gn_silu_ndhwc.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f32, _int,
@@ -114,7 +115,7 @@ for _name in ("gn_silu_nhwc", "gn_silu_rows", "gn_silu_nhwc_strided", "gn_stats_
               "gn_profile_rows_dtype", "gn_plan_rows_dtype", "gn_silu_ndhwc",
               "gn_silu_ndhwc_dtype", "gn_silu_ndhwc_strided_dtype", "gn_conv3x3_nhwc",
               "gn_conv3x3_plan", "gn_conv3x3_pack_weights", "gn_conv3x3_nhwc_packed",
-              "gn_silu_rows_noalloc", "gn_plan_single_launch"):
+              "gn_silu_rows_noalloc", "gn_plan_single_launch", "gn_noalloc_scratch"):
     getattr(lib, _name).restype = _int
 lib.gn_plan_rows.argtypes = [_i64, _i64, _i64, _i64, _i64p]
 lib.gn_plan_rows.restype = _int
@@ -139,6 +140,7 @@ gn_plan_rows = lib.gn_plan_rows
 gn_silu_nhwc_dtype = lib.gn_silu_nhwc_dtype
 gn_silu_rows_dtype = lib.gn_silu_rows_dtype
 gn_silu_rows_noalloc = lib.gn_silu_rows_noalloc
+gn_noalloc_scratch = lib.gn_noalloc_scratch
 gn_silu_nhwc_strided_dtype = lib.gn_silu_nhwc_strided_dtype
 gn_silu_ndhwc = lib.gn_silu_ndhwc
 gn_silu_ndhwc_dtype = lib.gn_silu_ndhwc_dtype

@@ -1065,6 +1065,18 @@ gn_status gn_silu_rows_noalloc(const void *x, const float *gamma, const float *b
                     true);
 }
 
+gn_status gn_noalloc_scratch(int device, void **ptr_out, int64_t *bytes_out) {
+    if (ptr_out == nullptr || bytes_out == nullptr || device < 0) return GN_INVALID_ARGUMENT;
+    DeviceGuard guard;
+    if (guard.enter(device) != GN_OK) return GN_DEVICE_ERROR;
+    char *base = nullptr;
+    const gn_status st = fixed_scratch(device, &base);
+    if (st != GN_OK) return st;
+    *ptr_out = base;
+    *bytes_out = GN_NOALLOC_SCRATCH_BYTES;
+    return GN_OK;
+}
+
 gn_status gn_silu_rows(const void *x, const float *gamma, const float *beta, void *y, int64_t N,
                        int64_t L, int64_t C, int64_t G, float eps, int apply_silu,
                        void *stream) {

@@ -170,6 +170,16 @@ gn_status gn_silu_rows_noalloc(const void *x, const float *gamma, const float *b
                                int64_t N, int64_t L, int64_t C, int64_t G,
                                float eps, int apply_silu, int dtype, void *stream);
 
+/* Diagnostics (tests): the device address of device `device`'s fixed
+ * no-allocation buffer and its size in bytes.  Its layout for a call is the
+ * one gn_plan_rows_dtype's scratch_bytes counts: arrival counters from the
+ * start, then the partial sums, the partial squares, read-only padding and
+ * mean/rstd; a call writes nothing past its scratch_bytes.  Writing into the
+ * buffer while a call runs is undefined.  GN_INVALID_ARGUMENT for a null
+ * output or a negative device, GN_DEVICE_ERROR when the device cannot be
+ * selected. */
+gn_status gn_noalloc_scratch(int device, void **ptr_out, int64_t *bytes_out);
+
 /* group_norm_silu_rows: (N, L, C) rows with C innermost, the form the pages'
  * tests exercise "as used by attention" (Accuracy section, unit tests). */
 gn_status gn_silu_rows(const void *x, const float *gamma, const float *beta, void *y,
