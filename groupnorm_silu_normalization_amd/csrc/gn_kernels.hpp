@@ -806,38 +806,50 @@ gn_partial_stats(
 }
 
 // ---------------------------------------------------------------------------
-// Step 2 as its own kernel, used when G > kThreads (too many groups for one
-// workgroup to finish quickly): one workgroup per (n, g), a fixed-order tree
-// over the K chunk partials.
+// Step 2 as its own kernel (G > kThreads: too many groups for one workgroup
+// to finish quickly; and from 16 to 160 MiB, where it measured faster than
+// the fused tail): one workgroup per (n, g).  Thread t sums chunks t,
+// t + kThreads, ... in increasing order; each wave reduces its 64 sums with
+// an xor butterfly (every lane ends with the same bits), and thread 0 adds
+// the four wave sums in wave order -- a fixed order, so the statistics are
+// reproducible.  The group's pivot is loaded with the partials, not after
+// the reduction, so the kernel waits for one memory round trip, not two.
 // ---------------------------------------------------------------------------
 template <class D>
 __global__ __launch_bounds__(kThreads) void gn_finalize_stats(
     const typename D::storage *__restrict__ x, Geometry geo, StatsOut out) {
-    __shared__ float rs[kThreads];
-    __shared__ float rq[kThreads];
+    constexpr int kWaves = kThreads / 64;
+    __shared__ float ws[kWaves], wq[kWaves];
     const int tid = threadIdx.x;
     const int64_t ng = blockIdx.x;
     const int64_t n = ng / geo.G;
     const int g = static_cast<int>(ng - n * geo.G);
+    const float pivot =
+        tid == 0 ? D::to_f32(x[n * geo.E + static_cast<int64_t>(g) * geo.Cg]) : 0.0f;
     float s = 0.0f, q = 0.0f;
     for (int64_t k = tid; k < geo.K; k += kThreads) {
         const int64_t o = (n * geo.K + k) * geo.G + g;
         s += out.part_s[o];
         q += out.part_q[o];
     }
-    rs[tid] = s;
-    rq[tid] = q;
-    __syncthreads();
-    for (int stride = kThreads / 2; stride > 0; stride >>= 1) {
-        if (tid < stride) {
-            rs[tid] += rs[tid + stride];
-            rq[tid] += rq[tid + stride];
-        }
-        __syncthreads();
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) {
+        s += __shfl_xor(s, m, 64);
+        q += __shfl_xor(q, m, 64);
     }
+    if ((tid & 63) == 0) {
+        ws[tid >> 6] = s;
+        wq[tid >> 6] = q;
+    }
+    __syncthreads();
     if (tid == 0) {
-        const float pivot = D::to_f32(x[n * geo.E + static_cast<int64_t>(g) * geo.Cg]);
-        group_moments(rs[0], rq[0], pivot, out.inv_m, out.eps, out.mean + ng, out.rstd + ng);
+        float ts = ws[0], tq = wq[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) {
+            ts += ws[w];
+            tq += wq[w];
+        }
+        group_moments(ts, tq, pivot, out.inv_m, out.eps, out.mean + ng, out.rstd + ng);
     }
 }
 
