@@ -322,7 +322,7 @@ def test_exact_statistics_integer_inputs(gn, dev):
 # (N, L, C, G, dtype): shapes whose full path runs the late finalize (step 2
 # inside every step-3 workgroup; the 16 MiB decoder shape among them), the
 # separate finalize kernel ((1, 65536, 512): 64 MiB; G = 512) or the fused
-# tail of step 1.  gn_stats_rows runs the fused tail where the full path runs
+# tail of step 1 ((1, 163848, 512): 160 MiB + 8 KiB).  gn_stats_rows runs the fused tail where the full path runs
 # the late finalize (the same order of additions), else the full path's own
 # step 2.
 SPLIT_CASES = [
@@ -330,7 +330,7 @@ SPLIT_CASES = [
     (3, 777, 320, 32, "bf16"), (2, 1000, 64, 1, "bf16"), (1, 3000, 256, 256, "bf16"),
     (4, 4096, 512, 32, "bf16"), (1, 16384, 512, 32, "f16"), (1, 8192, 256, 32, "f32"),
     (2, 9, 8, 8, "bf16"), (1, 300, 256, 256, "bf16"), (1, 65536, 512, 32, "bf16"),
-    (1, 2000, 512, 512, "bf16"),
+    (1, 2000, 512, 512, "bf16"), (1, 163848, 512, 32, "bf16"),
 ]
 
 
