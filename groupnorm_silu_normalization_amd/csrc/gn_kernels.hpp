@@ -174,6 +174,8 @@ template <class D> struct Vec<D, 1> {  // one value
 // ---- a lane's S = W*NV slots of one tile -------------------------------------
 template <class D, int W, int NV> struct Lane {
     static constexpr int kSlots = W * NV;
+    static constexpr int kW = W;
+    static constexpr int kNV = NV;
     using T = typename D::storage;
     Vec<D, W> v[NV];
     __device__ __forceinline__ static int slot_offset(int A, int tid, int j) {
@@ -362,6 +364,72 @@ __device__ __forceinline__ ChunkRange chunk_range_even(const Geometry &geo, int6
 // G <= kThreads: tg = kThreads / G threads per group, thread (g, part) sums
 // the entries e = part, part + tg, ... of its group, then a fixed tree over
 // the parts.  G > kThreads: each thread sums whole groups.
+// The same reduction for the power-of-two 16-byte layouts of 16-bit types
+// (256 lanes, lane tid holding the 8 consecutive channels
+// c0 = 8 * (tid mod C/8) ... c0 + 7 of row tid / (C/8) of the tile) whose
+// groups are at least 8 channels wide (Cg >= 8, so a lane's slots lie in one
+// group), G <= kThreads, without the LDS passes: each lane adds its 8 slots
+// (j in increasing order); an xor butterfly over the lane bits that keep the
+// group (the bits below Cg/8: the lanes of one row sharing the group; the
+// bits from C/8 up: the rows of the wave) leaves every lane of a group with
+// the same sum; one lane per (wave, group) writes it to LDS, and thread g
+// adds the entries of the waves that hold channels of group g in wave order.
+// A fixed order, so the partials are reproducible; every mode of the path
+// (fused tail, late finalize, separate finalize, steps 1-2 alone) reads the
+// same partials.  Measured on MI355X against the LDS reduction below, in one
+// process: 4% less at (1,512,128,128), 1.5% at 64 MiB, 5.5% at
+// (2,4096,256); for groups narrower than 8 channels a variant with one sum
+// per group slice was 3% slower at (1,128,64,64), so those shapes keep the
+// LDS reduction.
+template <bool COHERENT>
+__device__ __forceinline__ void write_group_partials_wave(const float (&s)[8], const float (&q)[8],
+                                                          float *red_s, float *red_q,
+                                                          const Geometry &geo, int64_t n,
+                                                          int64_t k, const StatsOut &out,
+                                                          int tid) {
+    const int G = geo.G, Cg = geo.Cg;
+    const int cb = geo.C >> 3;       // lanes per row of the tile (channel blocks)
+    const int gb = Cg >> 3;          // blocks per group
+    const int lane = tid & 63, wave = tid >> 6;
+    const int blk = tid & (cb - 1);  // the lane's channel block
+    float vs = 0.0f, vq = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        vs += s[j];
+        vq += q[j];
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        if (m < gb || m >= cb) {  // uniform: the same for every lane
+            vs += __shfl_xor(vs, m, 64);
+            vq += __shfl_xor(vq, m, 64);
+        }
+    }
+    if ((lane & (gb - 1)) == 0 && (cb >= 64 || lane < cb)) {
+        red_s[wave * G + blk / gb] = vs;
+        red_q[wave * G + blk / gb] = vq;
+    }
+    __syncthreads();
+    if (tid < G) {
+        // channel blocks [b0, b1) of group tid; wave w holds blocks [lo, lo + 64)
+        // (all of them when a row is at most 64 blocks)
+        const int b0 = tid * gb, b1 = b0 + gb;
+        float ts = 0.0f, tq = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) {
+            const int lo = cb <= 64 ? 0 : (w * 64) & (cb - 1);
+            const int hi = cb <= 64 ? cb : lo + 64;
+            if (b0 < hi && b1 > lo) {
+                ts += red_s[w * G + tid];
+                tq += red_q[w * G + tid];
+            }
+        }
+        const int64_t o = (n * geo.K + k) * G + tid;
+        store_partial<COHERENT>(out.part_s + o, ts);
+        store_partial<COHERENT>(out.part_q + o, tq);
+    }
+}
+
 template <class L, bool POW2, bool COHERENT, int NT = kThreads>
 __device__ __forceinline__ void write_group_partials(const float (&s)[L::kSlots],
                                                      const float (&q)[L::kSlots], float *red_s,
@@ -369,6 +437,12 @@ __device__ __forceinline__ void write_group_partials(const float (&s)[L::kSlots]
                                                      const TileGeo<POW2, L::kSlots> &tg_,
                                                      int64_t n, int64_t k, const StatsOut &out,
                                                      int tid) {
+    if constexpr (POW2 && L::kW == 8 && L::kNV == 1 && NT == kThreads) {
+        if (geo.Cg >= 8 && geo.G <= kThreads) {
+            write_group_partials_wave<COHERENT>(s, q, red_s, red_q, geo, n, k, out, tid);
+            return;
+        }
+    }
     const int A = tg_.lanes();
     if (tid < A) {
 #pragma unroll

@@ -449,3 +449,54 @@ def test_single_launch_selection():
     assert on(1, 256, 384, 48, BF16)               # Cg = 8
     n_on = sum(strip_replay(*s, BF16) for s in STRIP_SHAPES)
     assert n_on == len(STRIP_SHAPES) - 4
+
+
+def wave_reduction_replay(C, G):
+    """The wave-level partial reduction of step 1 (power-of-two 16-byte
+    layouts of 16-bit types: 256 lanes, lane tid holding channels
+    8*(tid mod C/8) .. +7 of row tid // (C/8); groups of 8 channels or
+    more, so a lane's slots lie in one group), replayed with the kernel's
+    own index arithmetic on sets of (lane, slot) ids: the butterfly over the
+    lane bits that keep the group, one LDS entry per (wave, group) written by
+    its leader lane, and thread g adding the entries of the waves whose
+    channel blocks meet group g.  Each group's partial must be exactly the
+    slots of its channels, each once, and every LDS index in bounds and
+    written once."""
+    Cg = C // G
+    assert Cg >= 8
+    cb = C >> 3
+    gb = Cg >> 3
+    NT, W = 256, 8
+    red = {}
+    for wave in range(NT // 64):
+        masks = [m for m in (1, 2, 4, 8, 16, 32) if m < gb or m >= cb]
+        for lane in range(64):
+            tid = wave * 64 + lane
+            if not ((lane & (gb - 1)) == 0 and (cb >= 64 or lane < cb)):
+                continue
+            # the leader's sum after the butterfly: every slot of the lanes
+            # reachable from it by the masks
+            orbit = {lane}
+            for m in masks:
+                orbit |= {o ^ m for o in orbit}
+            idx = wave * G + (tid & (cb - 1)) // gb
+            assert 0 <= idx < 4 * G <= NT * W and idx not in red
+            red[idx] = [(wave * 64 + o, j) for o in sorted(orbit) for j in range(W)]
+    for g in range(G):
+        b0, b1 = g * gb, g * gb + gb
+        total = []
+        for w in range(NT // 64):
+            lo = 0 if cb <= 64 else (w * 64) & (cb - 1)
+            hi = cb if cb <= 64 else lo + 64
+            if b0 < hi and b1 > lo:
+                assert w * G + g in red, (C, G, g, w)
+                total.extend(red[w * G + g])
+        want = [(tid, j) for tid in range(NT) for j in range(W)
+                if ((8 * (tid & (cb - 1)) + j) // Cg) == g]
+        assert sorted(total) == sorted(want), (C, G, g)
+
+
+@pytest.mark.parametrize("C", [8, 16, 32, 64, 128, 256, 512, 1024, 2048])
+def test_wave_reduction_counts_each_slot_once(C):
+    for G in [g for g in (1, 2, 4, 8, 16, 32, 64, 128, 256) if C % g == 0 and C // g >= 8]:
+        wave_reduction_replay(C, G)
