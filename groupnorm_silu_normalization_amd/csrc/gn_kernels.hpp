@@ -378,9 +378,7 @@ __device__ __forceinline__ ChunkRange chunk_range_even(const Geometry &geo, int6
 // (fused tail, late finalize, separate finalize, steps 1-2 alone) reads the
 // same partials.  Measured on MI355X against the LDS reduction below, in one
 // process: 4% less at (1,512,128,128), 1.5% at 64 MiB, 5.5% at
-// (2,4096,256); for groups narrower than 8 channels a variant with one sum
-// per group slice was 3% slower at (1,128,64,64), so those shapes keep the
-// LDS reduction.
+// (2,4096,256).
 template <bool COHERENT>
 __device__ __forceinline__ void write_group_partials_wave(const float (&s)[8], const float (&q)[8],
                                                           float *red_s, float *red_q,
@@ -430,6 +428,70 @@ __device__ __forceinline__ void write_group_partials_wave(const float (&s)[8], c
     }
 }
 
+// The same for groups narrower than a lane's 8 channels (Cg = 8 / PER, PER
+// groups per lane, Cg consecutive slots each): the lane adds the slots of
+// each of its groups, the butterfly runs over the row bits of the wave only,
+// and the lanes of the first row of each wave write their PER sums.  PER is
+// a template parameter: with Cg known only at run time the per-group sums
+// were indexed dynamically, and that version was 3% slower than the LDS
+// reduction at (1,128,64,64); this one is 6% faster there (3.5% at Cg = 4
+// and 2% at Cg = 2 for 8 MiB shapes).
+template <bool COHERENT, int PER>
+__device__ __forceinline__ void write_group_partials_wave_narrow(
+    const float (&s)[8], const float (&q)[8], float *red_s, float *red_q, const Geometry &geo,
+    int64_t n, int64_t k, const StatsOut &out, int tid) {
+    constexpr int CG = 8 / PER;
+    const int G = geo.G;
+    const int cb = geo.C >> 3;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int blk = tid & (cb - 1);
+    float vs[PER], vq[PER];
+#pragma unroll
+    for (int h = 0; h < PER; ++h) {
+        vs[h] = 0.0f;
+        vq[h] = 0.0f;
+#pragma unroll
+        for (int u = 0; u < CG; ++u) {
+            vs[h] += s[h * CG + u];
+            vq[h] += q[h * CG + u];
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        if (m >= cb) {
+#pragma unroll
+            for (int h = 0; h < PER; ++h) {
+                vs[h] += __shfl_xor(vs[h], m, 64);
+                vq[h] += __shfl_xor(vq[h], m, 64);
+            }
+        }
+    }
+    if (cb >= 64 || lane < cb) {
+#pragma unroll
+        for (int h = 0; h < PER; ++h) {
+            red_s[wave * G + blk * PER + h] = vs[h];
+            red_q[wave * G + blk * PER + h] = vq[h];
+        }
+    }
+    __syncthreads();
+    if (tid < G) {
+        const int b = tid / PER;  // the group's channel block
+        float ts = 0.0f, tq = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) {
+            const int lo = cb <= 64 ? 0 : (w * 64) & (cb - 1);
+            const int hi = cb <= 64 ? cb : lo + 64;
+            if (b >= lo && b < hi) {
+                ts += red_s[w * G + tid];
+                tq += red_q[w * G + tid];
+            }
+        }
+        const int64_t o = (n * geo.K + k) * G + tid;
+        store_partial<COHERENT>(out.part_s + o, ts);
+        store_partial<COHERENT>(out.part_q + o, tq);
+    }
+}
+
 template <class L, bool POW2, bool COHERENT, int NT = kThreads>
 __device__ __forceinline__ void write_group_partials(const float (&s)[L::kSlots],
                                                      const float (&q)[L::kSlots], float *red_s,
@@ -441,6 +503,20 @@ __device__ __forceinline__ void write_group_partials(const float (&s)[L::kSlots]
         if (geo.Cg >= 8 && geo.G <= kThreads) {
             write_group_partials_wave<COHERENT>(s, q, red_s, red_q, geo, n, k, out, tid);
             return;
+        }
+        if (geo.G <= kThreads && geo.C >= 8) {
+            if (geo.Cg == 4) {
+                write_group_partials_wave_narrow<COHERENT, 2>(s, q, red_s, red_q, geo, n, k, out, tid);
+                return;
+            }
+            if (geo.Cg == 2) {
+                write_group_partials_wave_narrow<COHERENT, 4>(s, q, red_s, red_q, geo, n, k, out, tid);
+                return;
+            }
+            if (geo.Cg == 1) {
+                write_group_partials_wave_narrow<COHERENT, 8>(s, q, red_s, red_q, geo, n, k, out, tid);
+                return;
+            }
         }
     }
     const int A = tg_.lanes();

@@ -500,3 +500,49 @@ def wave_reduction_replay(C, G):
 def test_wave_reduction_counts_each_slot_once(C):
     for G in [g for g in (1, 2, 4, 8, 16, 32, 64, 128, 256) if C % g == 0 and C // g >= 8]:
         wave_reduction_replay(C, G)
+
+
+def narrow_wave_reduction_replay(C, G):
+    """The wave-level reduction for groups narrower than a lane's 8 channels
+    (Cg = 8 / PER): each lane sums its Cg slots per group, the butterfly runs
+    over the row bits of the wave, the first row's lanes write PER entries,
+    and thread g adds the entries of the waves holding its channel block."""
+    Cg = C // G
+    assert Cg < 8 and 8 % Cg == 0
+    PER = 8 // Cg
+    cb = C >> 3
+    NT, W = 256, 8
+    red = {}
+    for wave in range(NT // 64):
+        masks = [m for m in (1, 2, 4, 8, 16, 32) if m >= cb]
+        for lane in range(64):
+            tid = wave * 64 + lane
+            if not (cb >= 64 or lane < cb):
+                continue
+            orbit = {lane}
+            for m in masks:
+                orbit |= {o ^ m for o in orbit}
+            blk = tid & (cb - 1)
+            for h in range(PER):
+                idx = wave * G + blk * PER + h
+                assert 0 <= idx < 4 * G <= NT * W and idx not in red
+                red[idx] = [(wave * 64 + o, h * Cg + u) for o in sorted(orbit) for u in range(Cg)]
+    for g in range(G):
+        b = g // PER
+        total = []
+        for w in range(NT // 64):
+            lo = 0 if cb <= 64 else (w * 64) & (cb - 1)
+            hi = cb if cb <= 64 else lo + 64
+            if lo <= b < hi:
+                assert w * G + g in red, (C, G, g, w)
+                total.extend(red[w * G + g])
+        want = [(tid, j) for tid in range(NT) for j in range(W)
+                if ((8 * (tid & (cb - 1)) + j) // Cg) == g]
+        assert sorted(total) == sorted(want), (C, G, g)
+
+
+@pytest.mark.parametrize("C", [8, 16, 32, 64, 128, 256])
+def test_narrow_wave_reduction_counts_each_slot_once(C):
+    for Cg in (1, 2, 4):
+        if C % Cg == 0 and C // Cg <= 256:
+            narrow_wave_reduction_replay(C, C // Cg)
