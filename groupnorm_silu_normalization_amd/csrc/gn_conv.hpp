@@ -43,8 +43,8 @@
 // z with 16-byte accesses; the bf16-rounded values (what the next GroupNorm
 // reads) give, per tile and per output group, the count, mean and sum of
 // squared deviations (M2), in a fixed order.  gn_conv_stats_finalize merges
-// the tiles of each (n, group) with the parallel-variance formula in fp64, in
-// a fixed order, so the statistics are reproducible bit for bit.
+// the tiles of each (n, group) in fp64 (pivot-shifted sums, one pass), in a
+// fixed order, so the statistics are reproducible bit for bit.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -556,44 +556,61 @@ __global__ __launch_bounds__(kThreads) void gn_conv_pack_weights(const uint16_t 
 }
 
 // Merge of the per-tile (count, mean, M2) of each (n, group) into fp32 mean
-// and rstd: thread j folds tiles j, j + 256, ... in increasing order with the
-// parallel-variance update in fp64, then a fixed tree over the 256 threads.
+// and rstd, in fp64.  Merged, the group's sum of squared deviations is
+// sum_t [M2_t + c_t (m_t - mean)^2]; written about a pivot p (tile 0's mean)
+// with d_t = m_t - p, S0 = sum c_t, S1 = sum c_t d_t and
+// S2 = sum (M2_t + c_t d_t^2), it is S2 - S1^2 / S0 and mean = p + S1 / S0.
+// The pivot keeps that subtraction small when the group's mean is large
+// against its spread (the tiles' means then lie close to p).  One pass over
+// the records: thread j adds tiles j, j + 256, ... in increasing order, an xor
+// butterfly sums each wave (every lane ends with the same bits) and thread 0
+// adds the four wave sums in order -- a fixed order, so the statistics are
+// reproducible bit for bit.
 __global__ __launch_bounds__(kThreads) void gn_conv_stats_finalize(const float *part, int tiles,
                                                                    int G2, float eps, float *mean,
                                                                    float *rstd) {
-    __shared__ double sn[kThreads], sm[kThreads], sq[kThreads];
+    __shared__ double w0[kThreads / 64], w1[kThreads / 64], w2[kThreads / 64];
     const int ng = blockIdx.x;
     const int n = ng / G2, g = ng % G2;
     const int tid = threadIdx.x;
-    double cn = 0.0, cm = 0.0, cq = 0.0;
+    const float *base = part + (static_cast<int64_t>(n) * tiles * G2 + g) * 4;
+    const double p = base[1];
+    double s0 = 0.0, s1 = 0.0, s2 = 0.0;
+#pragma unroll 4
     for (int t = tid; t < tiles; t += kThreads) {
-        const float *p = part + ((static_cast<int64_t>(n) * tiles + t) * G2 + g) * 4;
-        const double bn = p[0], bm = p[1], bq = p[2];
-        const double tn = cn + bn;
-        const double d = bm - cm;
-        cm += d * (bn / tn);
-        cq += bq + d * d * (cn * bn / tn);
-        cn = tn;
+        const float4 r = *reinterpret_cast<const float4 *>(base + static_cast<int64_t>(t) * G2 * 4);
+        const double c = r.x;
+        const double d = static_cast<double>(r.y) - p;
+        const double cd = c * d;
+        s0 += c;
+        s1 += cd;
+        s2 += static_cast<double>(r.z) + cd * d;
     }
-    sn[tid] = cn;
-    sm[tid] = cm;
-    sq[tid] = cq;
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) {
+        s0 += __shfl_xor(s0, m, 64);
+        s1 += __shfl_xor(s1, m, 64);
+        s2 += __shfl_xor(s2, m, 64);
+    }
+    if ((tid & 63) == 0) {
+        w0[tid >> 6] = s0;
+        w1[tid >> 6] = s1;
+        w2[tid >> 6] = s2;
+    }
     __syncthreads();
-    for (int s = kThreads / 2; s > 0; s >>= 1) {
-        if (tid < s && sn[tid + s] > 0.0) {
-            const double an = sn[tid], bn = sn[tid + s];
-            const double tn = an + bn;
-            const double d = sm[tid + s] - sm[tid];
-            sm[tid] += d * (bn / tn);
-            sq[tid] += sq[tid + s] + d * d * (an * bn / tn);
-            sn[tid] = tn;
-        }
-        __syncthreads();
-    }
     if (tid == 0) {
-        const double var = sn[0] > 0.0 ? sq[0] / sn[0] : 0.0;
-        mean[ng] = static_cast<float>(sm[0]);
-        rstd[ng] = static_cast<float>(1.0 / sqrt((var > 0.0 ? var : 0.0) + static_cast<double>(eps)));
+        double t0 = 0.0, t1 = 0.0, t2 = 0.0;
+#pragma unroll
+        for (int w = 0; w < kThreads / 64; ++w) {
+            t0 += w0[w];
+            t1 += w1[w];
+            t2 += w2[w];
+        }
+        const double dm = t1 / t0;  // t0 >= 1: every tile holds a pixel
+        const double m2 = t2 - t1 * dm;
+        const double var = m2 > 0.0 ? m2 / t0 : 0.0;
+        mean[ng] = static_cast<float>(p + dm);
+        rstd[ng] = static_cast<float>(1.0 / sqrt(var + static_cast<double>(eps)));
     }
 }
 
