@@ -165,6 +165,7 @@ gn_conv3x3(ConvArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kLdsBytes];
     __shared__ float s_scale[kMaxCi];
     __shared__ float s_shift[kMaxCi];
+    __shared__ __attribute__((aligned(16))) float s_stat[STATS ? 512 : 4];  // [2][4 waves][64]
     uint16_t *sA = reinterpret_cast<uint16_t *>(smem);  // two halo buffers of A_ELEMS
     float *sO = reinterpret_cast<float *>(smem);
 
@@ -460,71 +461,99 @@ gn_conv3x3(ConvArgs a) {
             emit(std::false_type{});
         else
             emit(std::true_type{});
-        __syncthreads();  // sO fully read: free for the next half or the statistics
-
-        if constexpr (STATS) {
-            // Per channel: sum over this lane's pixels, then over the ROWS
-            // lanes of the same piece in order; per group: over its channels.
-            float *red = sO;                   // [ROWS][64]
-            float *gmean = sO + ROWS * 64;     // [64]: mean of the group of each channel
-            float s8[8];
+        if constexpr (!STATS) {
+            __syncthreads();  // sO fully read: free for the next half
+        } else {
+            // Per output group of the pass (Cg2 channels: a run of the lane's
+            // 8 when Cg2 < 8, else Cg2/8 consecutive pieces), sums in a fixed
+            // order: per lane over its valid pixels; within the lane over the
+            // group's channels (pairs, then pairs of pairs); an xor butterfly
+            // over the lanes of the wave holding the same piece (lane bits
+            // 3-5) and, for Cg2 > 8, over the group's pieces (lane bits 0-2);
+            // then the four waves' sums in wave order.  Every step adds two
+            // equal-ranked operands in either order, so all lanes and
+            // channels of a group hold the same bits, and every lane forms the
+            // group's mean itself.
+            static_assert(NT == 256, "four waves in the statistics");
+            const int wave = tid >> 6;
+            const float count = static_cast<float>(cnt * Cg2);
+            auto reduce = [&](float (&t)[8]) {
+                if (Cg2 >= 8) {
+                    float v = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+#pragma unroll
+                    for (int m = 8; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+#pragma unroll
+                    for (int m = 1; m < 8; m <<= 1)
+                        if (8 * m < Cg2) v += __shfl_xor(v, m, 64);  // uniform
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) t[e] = v;
+                } else {
+                    if (Cg2 >= 2) {
+#pragma unroll
+                        for (int e = 0; e < 8; e += 2) t[e] = t[e + 1] = t[e] + t[e + 1];
+                    }
+                    if (Cg2 >= 4) {
+#pragma unroll
+                        for (int h = 0; h < 8; h += 4)
+#pragma unroll
+                            for (int e = h; e < h + 2; ++e) t[e] = t[e + 2] = t[e] + t[e + 2];
+                    }
+#pragma unroll
+                    for (int m = 8; m < 64; m <<= 1)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) t[e] += __shfl_xor(t[e], m, 64);
+                }
+            };
+            auto publish = [&](float *dst, const float (&t)[8]) {
+                if (lane < 8) {  // the wave's first row: q == lane
+                    *reinterpret_cast<float4 *>(dst + wave * 64 + 8 * q) =
+                        make_float4(t[0], t[1], t[2], t[3]);
+                    *reinterpret_cast<float4 *>(dst + wave * 64 + 8 * q + 4) =
+                        make_float4(t[4], t[5], t[6], t[7]);
+                }
+            };
+            auto wave_sum = [](const float *src, int c) {
+                return ((src[c] + src[64 + c]) + src[128 + c]) + src[192 + c];
+            };
+            float t8[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                float s = 0.0f;
+                float v = 0.0f;
 #pragma unroll
-                for (int i = 0; i < PIX; ++i) s += valid[i] ? vals[i][e] : 0.0f;
-                s8[e] = s;
+                for (int i = 0; i < PIX; ++i) v += valid[i] ? vals[i][e] : 0.0f;
+                t8[e] = v;
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) red[prow * 64 + 8 * q + e] = s8[e];
+            reduce(t8);
+            publish(s_stat, t8);
             __syncthreads();
-            if (tid < 64) {
-                float s = 0.0f;
-                for (int r = 0; r < ROWS; ++r) s += red[r * 64 + tid];
-                red[tid] = s;  // row 0 is read only by this lane below it
+            float mg[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mg[e] = wave_sum(s_stat, 8 * q + e) / count;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float v = 0.0f;
+#pragma unroll
+                for (int i = 0; i < PIX; ++i) {
+                    const float d = vals[i][e] - mg[e];
+                    v = valid[i] ? fmaf(d, d, v) : v;
+                }
+                t8[e] = v;
             }
+            reduce(t8);
+            publish(s_stat + 256, t8);
             __syncthreads();
             const int ngroups = 64 / Cg2;
             if (tid < ngroups) {
-                float s = 0.0f;
-                for (int c = 0; c < Cg2; ++c) s += red[tid * Cg2 + c];
-                const float mg = s / static_cast<float>(cnt * Cg2);
-                for (int c = 0; c < Cg2; ++c) gmean[tid * Cg2 + c] = mg;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float mg = gmean[8 * q + e];
-                float s = 0.0f;
-#pragma unroll
-                for (int i = 0; i < PIX; ++i) {
-                    const float d = vals[i][e] - mg;
-                    s = valid[i] ? fmaf(d, d, s) : s;
-                }
-                s8[e] = s;
-            }
-            __syncthreads();  // gmean read by every lane before red is reused
-#pragma unroll
-            for (int e = 0; e < 8; ++e) red[prow * 64 + 8 * q + e] = s8[e];
-            __syncthreads();
-            if (tid < 64) {
-                float s = 0.0f;
-                for (int r = 0; r < ROWS; ++r) s += red[r * 64 + tid];
-                red[tid] = s;
-            }
-            __syncthreads();
-            if (tid < ngroups) {
-                float m2 = 0.0f;
-                for (int c = 0; c < Cg2; ++c) m2 += red[tid * Cg2 + c];
+                const int c0 = tid * Cg2;
                 const int g2 = (co0 + half * 64) / Cg2 + tid;
                 float *dst = a.part + ((static_cast<int64_t>(n) * tiles_per_sample + tin) *
                                            a.G2 + g2) * 4;
-                dst[0] = static_cast<float>(cnt * Cg2);
-                dst[1] = gmean[tid * Cg2];
-                dst[2] = m2;
+                dst[0] = count;
+                dst[1] = wave_sum(s_stat, c0) / count;
+                dst[2] = wave_sum(s_stat + 256, c0);
                 dst[3] = 0.0f;
             }
-            __syncthreads();  // red and gmean free for the next half
+            __syncthreads();  // sO and s_stat free for the next half
         }
     }
 }

@@ -8,7 +8,10 @@ halo buffers with rows of 40 bf16, epilogue rows of 72 fp32): the workgroup
 -> (tile, channel block) map
 covers every pair once, the halo, weight-fragment, residual and output
 addresses stay inside their tensors, every LDS index stays inside its array,
-and the statistics partials stay inside their buffer.
+and the statistics partials stay inside their buffer.  The epilogue's
+statistics reduction (lane sums, butterflies over the lanes of a wave, the
+four waves' sums) is replayed too: every (pixel, channel) of a group is
+counted once in that group's sum.
 """
 import numpy as np
 import pytest
@@ -127,8 +130,12 @@ def test_conv_plan_and_indices_in_bounds(N, H, W, Ci, Co, G2):
     pixl = 32 * MI * (WM - 1) + 32 * (MI - 1) + m
     assert (pixl * OS + 63).max() < LDS_EPI_FLOATS and m.max() < 32
     ROWS = NT // 8
-    assert ROWS * 64 + 64 <= LDS_EPI_FLOATS and (TH * TW) % ROWS == 0
-    assert max(LDS_MAIN * 2, LDS_EPI_FLOATS * 4) <= 64 * 1024
+    assert (TH * TW) % ROWS == 0
+    # statistics LDS: [sums, squares][4 waves][64 channels], 16-byte writes
+    tid = np.arange(NT)
+    st = (tid >> 6) * 64 + 8 * (tid & 7)
+    assert (st + 256 + 8).max() <= 512
+    assert max(LDS_MAIN * 2, LDS_EPI_FLOATS * 4) + 512 * 4 + 2 * 1024 * 4 <= 64 * 1024
     # output / residual pieces of valid pixels, statistics partials
     for tile in (0, N * tps - 1):
         n, tin = tile // tps, tile % tps
@@ -155,3 +162,72 @@ def test_conv_plan_declines():
     assert gn.conv_plan(0, 8, 8, 64, 128)["grid"] == 0       # empty: nothing launched
     assert gn.conv_plan(1, 2048, 2048, 512, 128) is None      # sample of 2^31 elements
     assert gn.conv_plan(1, 2048, 1024, 512, 128) is not None  # 2^30: 32-bit offsets hold
+
+
+def conv_stats_replay(Cg2):
+    """The statistics reduction of one 64-channel pass, as bit sets of the
+    (pixel, channel) values each sum holds: lane tid (piece q = tid % 8, row
+    prow = tid / 8, wave tid / 64) starts with pixels prow + 32 i of channels
+    8q + e; the in-lane pairs (Cg2 < 8) or the lane's whole piece (Cg2 >= 8);
+    the xor butterfly over lane bits 3-5 and, for Cg2 > 8, over bits 0-2; the
+    wave's first row publishes [wave][8q + e]; the sum of a channel is the four
+    waves' entries.  No value may be added twice, and each channel's sum must
+    hold exactly its group's 128 pixels x Cg2 channels."""
+    NT, PIX, ROWS = 256, 4, 32
+
+    def bit(pix, ch):
+        return 1 << (pix * 64 + ch)
+
+    def add(a, b):
+        assert a & b == 0, "a value counted twice"
+        return a | b
+
+    t = [[0] * 8 for _ in range(NT)]
+    for tid in range(NT):
+        q, prow = tid & 7, tid >> 3
+        for e in range(8):
+            for i in range(PIX):
+                t[tid][e] |= bit(prow + ROWS * i, 8 * q + e)
+    if Cg2 >= 8:
+        v = []
+        for tid in range(NT):
+            x = t[tid]
+            v.append(add(add(add(x[0], x[1]), add(x[2], x[3])), add(add(x[4], x[5]), add(x[6], x[7]))))
+        masks = [8, 16, 32] + [m for m in (1, 2, 4) if 8 * m < Cg2]
+        for m in masks:
+            v = [add(v[tid], v[tid ^ m]) for tid in range(NT)]
+        t = [[v[tid]] * 8 for tid in range(NT)]
+    else:
+        for tid in range(NT):
+            x = t[tid]
+            if Cg2 >= 2:
+                for e in range(0, 8, 2):
+                    x[e] = x[e + 1] = add(x[e], x[e + 1])
+            if Cg2 >= 4:
+                for h in (0, 4):
+                    for e in (h, h + 1):
+                        x[e] = x[e + 2] = add(x[e], x[e + 2])
+        for m in (8, 16, 32):
+            t = [[add(t[tid][e], t[tid ^ m][e]) for e in range(8)] for tid in range(NT)]
+    st = {}
+    for tid in range(NT):
+        if tid & 63 < 8:
+            for e in range(8):
+                idx = (tid >> 6) * 64 + 8 * (tid & 7) + e
+                assert idx < 256 and idx not in st
+                st[idx] = t[tid][e]
+    for c in range(64):
+        total = 0
+        for w in range(4):
+            total = add(total, st[w * 64 + c])
+        g0 = c // Cg2 * Cg2
+        want = 0
+        for pix in range(128):
+            for ch in range(g0, g0 + Cg2):
+                want |= bit(pix, ch)
+        assert total == want, (Cg2, c)
+
+
+@pytest.mark.parametrize("Cg2", [1, 2, 4, 8, 16, 32, 64])
+def test_conv_stats_reduction_counts_each_value_once(Cg2):
+    conv_stats_replay(Cg2)
