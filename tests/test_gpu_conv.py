@@ -156,6 +156,10 @@ SHAPES = [  # N, H, W, Ci, Co, G, G2
     # tiles per thread): 288 tiles over 288 workgroups of 256 output channels,
     # and 512 tiles of 128 output channels
     (1, 144, 256, 64, 256, 32, 32), (1, 256, 256, 32, 128, 8, 32),
+    # output groups of 2 and of 64 channels (the cases above take 4, 8 and
+    # 16, the seeded random problems 1 and 32: every group width the
+    # statistics epilogue handles)
+    (1, 12, 20, 64, 128, 16, 64), (2, 10, 18, 32, 256, 8, 4),
 ]
 
 
