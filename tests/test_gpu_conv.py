@@ -4,8 +4,8 @@ The fused operation is the decoder ResnetBlock2D's GroupNorm -> SiLU ->
 Conv2d(3x3, p1) chain ("FLUX.2 VAE decoder fast path behind quality=high",
 Modifications section 2), with the next GroupNorm's statistics of the conv
 output.  Reference: the fp64 oracle (``oracle.gn_silu`` then
-``oracle.conv3x3``, or ``conv3x3_at`` at sampled pixels of decoder-size
-tensors), which also returns, per output, the sum of the absolute values of
+``oracle.conv3x3``, or ``oracle.gn_silu_conv3x3``, also at the decoder's full
+sizes), which also returns, per output, the sum of the absolute values of
 its terms, mag = |bias| + |res| + sum |w * y|.
 
 Tolerance per output element, from the arithmetic (NaN never passes):
