@@ -41,7 +41,8 @@ namespace {
 // Launch plan constants, measured on MI355X (256 CUs, 256 MB Infinity Cache)
 // over the full three-step sequence at the decoder shapes.
 constexpr int kUnrollStats = 8;             // 16-byte loads in flight per lane, step 1
-constexpr int kUnrollApply = 4;             // 16-byte loads in flight per lane, step 3
+constexpr int kUnrollApply = 4;             // 16-byte loads in flight per lane, step 3 ...
+constexpr int kUnrollApplyDeep = 8;         // ... or twice that (Plan::apply_deep)
 constexpr int64_t kStatsBlocks = 256;       // step-1 workgroups in total: one per CU ...
 constexpr int64_t kStatsBlocksSmall = 128;  // ... or half that for x up to kStatsSmallBytes,
 constexpr int64_t kStatsSmallBytes = int64_t{16} << 20;  // where latency, not bandwidth, rules
@@ -159,6 +160,7 @@ struct Plan {
     bool fused;       // step 2 runs in the tail of step 1 (G <= kThreads)
     bool late;        // ... or, for a small x, in the prologue of step 3 (LateStats)
     bool apply_ntl;   // step 3 reads x with nontemporal loads
+    bool apply_deep;  // step 3 keeps kUnrollApplyDeep loads in flight, not kUnrollApply
     int dtype;        // gn_dtype of x and y
     int affine;       // element type of gamma and beta (Affine::kF32, ...)
     Geometry stats;   // chunking of steps 1 and 2
@@ -292,6 +294,20 @@ Plan make_plan(int64_t N, int64_t L, int64_t C, int64_t G, int dtype) {
     p.apply.K = std::max<int64_t>(1, std::min(g.tiles, ceil_div(apply_blocks, N)));
     p.apply.tpc = g.tiles / p.apply.K;
     p.apply.rem = g.tiles - p.apply.tpc * p.apply.K;
+    // Step 3 keeps twice the loads in flight where every workgroup's tiles
+    // make whole batches of the deeper unroll (at least two, no uneven
+    // split) and x is at most kSepFinalizeMaxBytes.  Measured on MI355X
+    // against four in flight (one process, best of four alternating rounds,
+    // y bitwise the same): 16 MiB -4%, 32 MiB -2.2%, 64 MiB -1.3%,
+    // (1,65536,1280) -3.4%, 128 MiB -0.6%; with a part-filled last batch it
+    // loses (1-2% at 1-4 MiB, 9% at (1,16384,2560), 12-13 tiles per
+    // workgroup), and from 256 MiB up it is within +-1% (the 512 MiB
+    // headline +0.9%), so those keep four.
+    static_assert(kSepFinalizeMaxBytes <= kCacheResidentBytes,
+                  "the deeper step 3 never takes nontemporal loads");
+    const int64_t deep = kUnrollApplyDeep;
+    p.apply_deep = bytes <= kSepFinalizeMaxBytes && p.apply.rem == 0 &&
+                   p.apply.tpc >= 2 * deep && p.apply.tpc % deep == 0;
     p.inv_m = 1.0 / (static_cast<double>(L) * static_cast<double>(C / G));
     // The late finalize: for a small x (latency-bound) whose sample's step-1
     // partials one finalize batch per thread covers, step 1 only writes its
@@ -502,6 +518,12 @@ void with_layout(const Layout &lay, F &&f) {
 // Loads in flight per lane: kUnroll* tiles of up to two accesses, half as
 // many tiles of four.
 constexpr int unroll_for(int base, int nv) { return nv <= 2 ? base : base / 4; }
+// Step 3's loads in flight for Plan::apply_deep: deeper only with one 16-byte
+// access per lane and tile (two or more would spill or were not measured);
+// otherwise the same kernel as without.
+constexpr int deep_unroll_for(int nv) {
+    return nv == 1 ? kUnrollApplyDeep : unroll_for(kUnrollApply, nv);
+}
 
 // late: the plan's late finalize runs in step 3, so step 1 only writes its
 // partials (false for a caller that needs mean/rstd from steps 1-2 alone).
@@ -570,8 +592,12 @@ void launch_apply_s(const Plan &p, const void *xv, void *yv, const float *mean, 
             constexpr bool P2 = decltype(pc)::value != 0;
             if constexpr (W > 1 && NV == (W == 4 ? 2 : 1) && !P2) {
                 constexpr int U = unroll_for(kUnrollApply, NV);
+                constexpr int UD = deep_unroll_for(NV);
                 constexpr int NT = kWideThreads;
-                if (p.apply_ntl)
+                if (p.apply_deep)  // never with nontemporal loads (x <= 160 MiB)
+                    gn_apply<D, W, NV, false, UD, SILU, false, true, false, NT>
+                        <<<grid, block, 0, s>>>(x, y, p.apply, mean, rstd, af, ls);
+                else if (p.apply_ntl)
                     gn_apply<D, W, NV, false, U, SILU, true, true, false, NT>
                         <<<grid, block, 0, s>>>(x, y, p.apply, mean, rstd, af, ls);
                 else
@@ -587,7 +613,15 @@ void launch_apply_s(const Plan &p, const void *xv, void *yv, const float *mean, 
         constexpr int NV = decltype(nvc)::value;
         constexpr bool P2 = decltype(pc)::value != 0;
         constexpr int U = unroll_for(kUnrollApply, NV);
-        if (p.apply_ntl)
+        constexpr int UD = deep_unroll_for(NV);
+        if (p.apply_deep) {  // never with nontemporal loads (x <= 160 MiB)
+            if (ls.part_s != nullptr)
+                gn_apply<D, W, NV, P2, UD, SILU, false, true, true><<<grid, block, 0, s>>>(
+                    x, y, p.apply, mean, rstd, af, ls);
+            else
+                gn_apply<D, W, NV, P2, UD, SILU, false, true, false><<<grid, block, 0, s>>>(
+                    x, y, p.apply, mean, rstd, af, ls);
+        } else if (p.apply_ntl)
             gn_apply<D, W, NV, P2, U, SILU, true, true, false><<<grid, block, 0, s>>>(
                 x, y, p.apply, mean, rstd, af, ls);
         else if (ls.part_s != nullptr)
