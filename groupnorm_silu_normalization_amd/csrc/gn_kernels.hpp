@@ -909,10 +909,19 @@ gn_partial_stats(
         int64_t tt = cr.t_begin;
         int64_t t_plain = cr.t_end - geo.plain_tail;  // first tile read with plain loads
         if (t_plain > cr.t_full_end) t_plain = cr.t_full_end;
+        // Each batch issues all its loads before the first add.  Where the
+        // compiler did not do so by itself, a scheduling barrier keeps it
+        // from moving adds, and the waits they need, in between: in the
+        // 320-lane fp16 build it had waited for every load before issuing the
+        // next, and some builds with two or four accesses per lane and tile
+        // waited part-way.  (One access per lane in 256-lane workgroups
+        // already issued whole batches, and is left as it was.)
+        constexpr bool kPin = NT != kThreads || NV > 1;
         for (; tt + UNROLL <= t_plain; tt += UNROLL) {
             L v[UNROLL];
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) v[u] = L::template load<true>(p + u * T, A, tid);
+            if constexpr (kPin) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) accumulate<L>(v[u], piv, s, q);
             p += UNROLL * T;
@@ -921,6 +930,7 @@ gn_partial_stats(
             L v[UNROLL];
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) v[u] = L::template load<false>(p + u * T, A, tid);
+            if constexpr (kPin) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) accumulate<L>(v[u], piv, s, q);
             p += UNROLL * T;
@@ -933,6 +943,7 @@ gn_partial_stats(
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u)
                 v[u] = L::template load<false>(p + (u < rem ? u : rem - 1) * T, A, tid);
+            if constexpr (kPin) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u)
                 if (u < rem) accumulate<L>(v[u], piv, s, q);
