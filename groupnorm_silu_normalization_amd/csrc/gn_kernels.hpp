@@ -973,8 +973,8 @@ gn_partial_stats(
 // t + kThreads, ... in increasing order; each wave reduces its 64 sums with
 // an xor butterfly (every lane ends with the same bits), and thread 0 adds
 // the four wave sums in wave order -- a fixed order, so the statistics are
-// reproducible.  The group's pivot is loaded with the partials, not after
-// the reduction, so the kernel waits for one memory round trip, not two.
+// reproducible.  The group's pivot is loaded with the partials (by every
+// thread, see below), so the kernel waits for one memory round trip, not two.
 // ---------------------------------------------------------------------------
 template <class D>
 __global__ __launch_bounds__(kThreads) void gn_finalize_stats(
@@ -985,8 +985,11 @@ __global__ __launch_bounds__(kThreads) void gn_finalize_stats(
     const int64_t ng = blockIdx.x;
     const int64_t n = ng / geo.G;
     const int g = static_cast<int>(ng - n * geo.G);
-    const float pivot =
-        tid == 0 ? D::to_f32(x[n * geo.E + static_cast<int64_t>(g) * geo.Cg]) : 0.0f;
+    // Every thread loads the pivot's raw bits (one address for the
+    // workgroup), converted only at the end: loaded under a branch on tid,
+    // the compiler waited for it at the branch's end, before issuing the
+    // partial loads, so the kernel waited for two round trips.
+    const typename D::storage praw = x[n * geo.E + static_cast<int64_t>(g) * geo.Cg];
     float s = 0.0f, q = 0.0f;
     for (int64_t k = tid; k < geo.K; k += kThreads) {
         const int64_t o = (n * geo.K + k) * geo.G + g;
@@ -1010,7 +1013,8 @@ __global__ __launch_bounds__(kThreads) void gn_finalize_stats(
             ts += ws[w];
             tq += wq[w];
         }
-        group_moments(ts, tq, pivot, out.inv_m, out.eps, out.mean + ng, out.rstd + ng);
+        group_moments(ts, tq, D::to_f32(praw), out.inv_m, out.eps, out.mean + ng,
+                      out.rstd + ng);
     }
 }
 
