@@ -46,9 +46,9 @@ def make(dev, N, C, H, W, G, xdt, adt, seed):
     return x, g, b
 
 
-SHAPES = [  # N, C, H, W, G
+SHAPES = [  # N, C, H, W, G; the last three take the single launch (gn_strip)
     (1, 128, 64, 64, 32), (2, 320, 24, 40, 32), (1, 2560, 16, 16, 32), (1, 512, 128, 128, 32),
-    (3, 96, 7, 9, 24),
+    (3, 96, 7, 9, 24), (2, 256, 32, 32, 32), (4, 128, 32, 32, 32),
 ]
 
 
@@ -73,6 +73,37 @@ def test_16bit_affine_equals_fp32_affine(gn, dev, shape, xdt, adt):
     assert torch.equal(bits(y16), bits(y32))
     assert torch.equal(bits(yg16), bits(yg32))
     assert torch.equal(bits(yb16), bits(yb32))
+
+
+def test_single_launch_shapes_listed(gn):
+    """The shapes above reach both the single launch and the three steps."""
+    single = [gn.plan_single_launch(N, H * W, C, G, 0)["single_launch"]
+              for N, C, H, W, G in SHAPES]
+    assert any(single) and not all(single)
+
+
+@pytest.mark.parametrize("adt", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("shape", [(3, 96, 7, 9, 24), (2, 256, 32, 32, 32),
+                                   (1, 512, 128, 128, 32), (2, 320, 24, 40, 32)])
+def test_16bit_affine_at_an_odd_element_offset(gn, dev, shape, adt):
+    """16-bit gamma/beta need only 2-byte alignment: views one element into
+    a buffer (addresses 2 mod 4) give, bit for bit, the output of fp32 copies
+    of the same values, in the single launch and in the three steps."""
+    N, C, H, W, G = shape
+    print("case odd offset N=%d C=%d H=%d W=%d G=%d affine=%s" % (N, C, H, W, G, adt),
+          flush=True)
+    x, g, b = make(dev, N, C, H, W, G, torch.bfloat16, adt, seed=C + W)
+    gbuf = torch.empty(C + 1, dtype=adt, device=dev)
+    bbuf = torch.empty(C + 1, dtype=adt, device=dev)
+    gbuf[1:] = g
+    bbuf[1:] = b
+    go, bo = gbuf[1:], bbuf[1:]
+    assert go.data_ptr() % 4 == 2 and bo.data_ptr() % 4 == 2
+    with torch.no_grad():
+        y16 = gn.group_norm_silu_4d(x, G, go, bo, 1e-6)
+        y32 = gn.group_norm_silu_4d(x, G, g.float(), b.float(), 1e-6)
+    assert y16 is not None and y32 is not None
+    assert torch.equal(bits(y16), bits(y32))
 
 
 @pytest.mark.parametrize("adt", [torch.bfloat16, torch.float16])
