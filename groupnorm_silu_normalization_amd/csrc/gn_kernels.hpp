@@ -655,12 +655,15 @@ constexpr int64_t kFinalizeOverread = int64_t{kFinalizeBatch - 1} * kThreads;
 // after the sums, or the kFinalizeOverread floats of padding after the
 // squares -- and is not added.  COHERENT: agent-scope loads (the partials
 // were written by other workgroups of the same kernel).
-template <bool COHERENT> struct FinalizeBatch {
-    float vs[kFinalizeBatch], vq[kFinalizeBatch];
+// B: slots per batch (kFinalizeBatch, or fewer for the late finalize of a
+// sample with few chunks: every load instruction counts in its latency).
+template <bool COHERENT, int B = kFinalizeBatch> struct FinalizeBatch {
+    static_assert(B >= 1 && B <= kFinalizeBatch, "the over-read bound assumes B <= 16");
+    float vs[B], vq[B];
     __device__ __forceinline__ void load(const float *ps, const float *pq, int64_t kk, int tpg,
                                          int G) {
 #pragma unroll
-        for (int b = 0; b < kFinalizeBatch; ++b) {
+        for (int b = 0; b < B; ++b) {
             const int64_t o = (kk + b * tpg) * G;
             if constexpr (COHERENT) {
                 vs[b] = __hip_atomic_load(ps + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -675,7 +678,7 @@ template <bool COHERENT> struct FinalizeBatch {
     __device__ __forceinline__ void add(int64_t kk, int tpg, int64_t K, float &as,
                                        float &aq) const {
 #pragma unroll
-        for (int b = 0; b < kFinalizeBatch; ++b) {
+        for (int b = 0; b < B; ++b) {
             if (kk + b * tpg < K) {
                 as += vs[b];
                 aq += vq[b];
@@ -1037,7 +1040,10 @@ __global__ __launch_bounds__(kThreads) void gn_zero_u32(unsigned *p, int64_t n) 
 // partials (ls) to mean/rstd in LDS, every thread taking part, and `mean` /
 // `rstd` are not read.  NT: lanes per workgroup (kThreads, or more for the
 // wide-channel layouts whose tiles need more lanes to keep all of them busy).
-template <class D, int W, int NV, bool POW2, int UNROLL, bool SILU, bool NTL, bool NTS, bool FIN,
+// FIN: 0, or the late finalize with batches of FIN slots (4, 8 or 16: the
+// fewest that cover the sample's chunks, K1 <= FIN * kThreads / G; the same
+// chunks, added in the same order, whatever FIN is).
+template <class D, int W, int NV, bool POW2, int UNROLL, bool SILU, bool NTL, bool NTS, int FIN,
           int NT = kThreads>
 __global__ __launch_bounds__(NT) void gn_apply(
     const typename D::storage *x, typename D::storage *y, Geometry geo,
@@ -1073,7 +1079,7 @@ __global__ __launch_bounds__(NT) void gn_apply(
     const bool fin_has = FIN && tid < tpg * G;
     const int fg = tid % G;
     const int fj = tid / G;
-    FinalizeBatch<false> fb;
+    FinalizeBatch<false, (FIN > 0 ? FIN : 1)> fb;
     float pivot = 0.0f;
     if constexpr (FIN) {
         if (fin_has && fj < ls.K1) {
