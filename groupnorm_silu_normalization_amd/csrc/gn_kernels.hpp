@@ -767,18 +767,53 @@ struct Affine {
     int type;
 };
 
-// A lane's channel parameters as loaded: the raw bits of gamma and beta (of
-// the Affine type) and its groups' mean and rstd.  They are widened and
-// combined only later, in fold_affine, so no instruction between the loads
-// waits for them.
+// A lane's channel parameters as loaded: the 32-bit words holding gamma and
+// beta (of the Affine type; a 16-bit value starts at bit hg[j] / hb[j] of its
+// word) and its groups' mean and rstd.  They are widened and combined only
+// later, in fold_affine, so no instruction between the loads waits for them.
 template <int S> struct SlotParams {
     uint32_t g[S], b[S];
+    uint32_t hg[S], hb[S];
     float mu[S], rs[S];
 };
 
+// Reads gamma and beta of one channel.  An absent one is read from
+// `fallback` (any valid 4-byte-aligned address, offset 0) and replaced by 1 or
+// 0 in fold_affine.  Every element type is read with the same 32-bit load of
+// the aligned word that holds the value, so no branch on the type separates
+// the loads (at the end of such a branch the compiler waits for the loads
+// issued in it).  A 16-bit value shares its word with a neighbour that may lie
+// just outside the array; an aligned 32-bit word never crosses a page.
+struct AffineReader {
+    const char *gw, *bw;  // each array's start rounded down to 4 bytes
+    uint32_t g2, b2;      // start mod 4 (0 or 2)
+    uint32_t gm, bm;      // channel mask: all ones, or 0 for an absent parameter
+    int es;               // log2 of the element size
+    __device__ __forceinline__ AffineReader(const Affine &af, const void *fallback) {
+        const char *g = static_cast<const char *>(af.gamma ? af.gamma : fallback);
+        const char *b = static_cast<const char *>(af.beta ? af.beta : fallback);
+        g2 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(g)) & 2u;
+        b2 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(b)) & 2u;
+        gw = g - g2;
+        bw = b - b2;
+        gm = af.gamma ? ~0u : 0u;
+        bm = af.beta ? ~0u : 0u;
+        es = af.type == Affine::kF32 ? 2 : 1;
+    }
+    // t: the value's byte offset from the rounded-down start.
+    __device__ __forceinline__ static uint32_t word(const char *w, uint32_t t, uint32_t &h) {
+        h = (t & 2u) * 8;  // 0 or 16; 0 for fp32
+        return *reinterpret_cast<const uint32_t *>(w + (t & ~3u));
+    }
+    template <int S>
+    __device__ __forceinline__ void load(int c, int j, SlotParams<S> &pr) const {
+        pr.g[j] = word(gw, ((static_cast<uint32_t>(c) & gm) << es) + g2, pr.hg[j]);
+        pr.b[j] = word(bw, ((static_cast<uint32_t>(c) & bm) << es) + b2, pr.hb[j]);
+    }
+};
+
 // Issues the loads of the lane's parameters; their round trips overlap.  An
-// absent gamma or beta is read from `mean` with stride 0 (any valid address)
-// and replaced by 1 or 0 in fold_affine.
+// absent gamma or beta is read from `mean` (AffineReader).
 // STATS: also load mean/rstd of the slots' groups from mean[n*G + g] (else
 // the caller fills pr.mu / pr.rs; `mean` is then only a valid address).
 template <class L, bool POW2, bool STATS>
@@ -797,41 +832,46 @@ __device__ __forceinline__ void load_slot_params(const float *mean, const float 
             pr.rs[j] = rstd[gi];
         }
     }
-    const void *gp = af.gamma ? af.gamma : static_cast<const void *>(mean);
-    const void *bp = af.beta ? af.beta : static_cast<const void *>(mean);
-    const int gs = af.gamma ? 1 : 0, bs = af.beta ? 1 : 0;
-    if (af.type == Affine::kF32) {
+    const AffineReader rd(af, mean);
 #pragma unroll
-        for (int j = 0; j < S; ++j) {
-            pr.g[j] = static_cast<const uint32_t *>(gp)[c[j] * gs];
-            pr.b[j] = static_cast<const uint32_t *>(bp)[c[j] * bs];
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < S; ++j) {
-            pr.g[j] = static_cast<const uint16_t *>(gp)[c[j] * gs];
-            pr.b[j] = static_cast<const uint16_t *>(bp)[c[j] * bs];
-        }
-    }
+    for (int j = 0; j < S; ++j) rd.load(c[j], j, pr);
 }
 
-// gamma or beta bits of the Affine type, widened exactly to fp32.
-__device__ __forceinline__ float widen_affine(uint32_t bits, int type) {
-    const float f16 = Fp16::to_f32(static_cast<uint16_t>(bits));
-    const float b16 = Bf16::to_f32(static_cast<uint16_t>(bits));
-    return type == Affine::kBf16 ? b16 : (type == Affine::kF16 ? f16 : __uint_as_float(bits));
+// gamma or beta bits of the Affine type for the lane's slots, widened exactly
+// to fp32 (`absent` where the parameter is null).  Presence and type are the
+// same for the whole launch, so they are decided once, outside the slots: a
+// choice per slot and value compiles to a chain of scalar branches for each
+// of them, which the fold runs after the statistics are known.
+template <int S>
+__device__ __forceinline__ void widen_affine(const uint32_t (&bits)[S], const uint32_t (&h)[S],
+                                             const void *p, int type, float absent,
+                                             float (&out)[S]) {
+    if (p == nullptr) {
+#pragma unroll
+        for (int j = 0; j < S; ++j) out[j] = absent;
+    } else if (type == Affine::kBf16) {
+#pragma unroll
+        for (int j = 0; j < S; ++j) out[j] = Bf16::to_f32(static_cast<uint16_t>(bits[j] >> h[j]));
+    } else if (type == Affine::kF16) {
+#pragma unroll
+        for (int j = 0; j < S; ++j) out[j] = Fp16::to_f32(static_cast<uint16_t>(bits[j] >> h[j]));
+    } else {
+#pragma unroll
+        for (int j = 0; j < S; ++j) out[j] = __uint_as_float(bits[j]);
+    }
 }
 
 // scale = gamma*rstd, shift = beta - mean*scale for the lane's slots.
 template <int S>
 __device__ __forceinline__ void fold_affine(const SlotParams<S> &pr, const Affine &af,
                                             float (&sc)[S], float (&sh)[S]) {
+    float ga[S], be[S];
+    widen_affine<S>(pr.g, pr.hg, af.gamma, af.type, 1.0f, ga);
+    widen_affine<S>(pr.b, pr.hb, af.beta, af.type, 0.0f, be);
 #pragma unroll
     for (int j = 0; j < S; ++j) {
-        const float ga = af.gamma ? widen_affine(pr.g[j], af.type) : 1.0f;
-        const float be = af.beta ? widen_affine(pr.b[j], af.type) : 0.0f;
-        sc[j] = ga * pr.rs[j];
-        sh[j] = fmaf(-pr.mu[j], sc[j], be);
+        sc[j] = ga[j] * pr.rs[j];
+        sh[j] = fmaf(-pr.mu[j], sc[j], be[j]);
     }
 }
 
@@ -890,7 +930,7 @@ gn_partial_stats(
     const int64_t n = wg / geo.K;
     const int64_t k = wg - n * geo.K;
     const typename D::storage *xs = x + n * geo.E;
-    const bool active = tid < A;
+    const bool active = POW2 || tid < A;  // power-of-two tiles: every lane
 
     float piv[S], s[S], q[S];
 #pragma unroll
@@ -1056,7 +1096,7 @@ __global__ __launch_bounds__(NT) void gn_apply(
     const int64_t T = tg.tile();
     const int A = tg.lanes();
     const int tid = threadIdx.x;
-    const bool active = tid < A;
+    const bool active = POW2 || tid < A;  // power-of-two tiles: every lane
     const int64_t wg = blockIdx.x;
     const int64_t n = wg / geo.K;
     const int64_t k = wg - n * geo.K;
@@ -1071,21 +1111,28 @@ __global__ __launch_bounds__(NT) void gn_apply(
     }
 
     // Late finalize, first its loads: the partials of (group g, part j) --
-    // K1 <= kFinalizeBatch*tpg, so the fused finalize's first (only) batch,
-    // loaded, like there, only by the parts j < K1 -- and the group's pivot
-    // x[n, 0, g*Cg] as step 1 saved it (x itself may already hold y here).
+    // K1 <= kFinalizeBatch*tpg, so the fused finalize's first (only) batch;
+    // a thread with no part (j >= K1) loads part 0's, which stays within the
+    // same bound, and adds none -- and the group's pivot x[n, 0, g*Cg] as
+    // step 1 saved it (x itself may already hold y here).
     const int G = geo.G;
     const int tpg = kThreads / G;
     const bool fin_has = FIN && tid < tpg * G;
     const int fg = tid % G;
     const int fj = tid / G;
     FinalizeBatch<false, (FIN > 0 ? FIN : 1)> fb;
+    // No load of the prologue sits under a branch on the thread index: at the
+    // end of such a branch the compiler waits for the loads issued in it (or
+    // for an add it moved in there), before the loads after it are issued.
+    // So every thread loads its group's pivot (only the part j = 0 uses it)
+    // and a batch of partials.
+    const bool fin_part = fin_has && fj < ls.K1;
     float pivot = 0.0f;
     if constexpr (FIN) {
-        if (fin_has && fj < ls.K1) {
-            fb.load(ls.part_s + n * ls.K1 * G + fg, ls.part_q + n * ls.K1 * G + fg, fj, tpg, G);
-            if (fj == 0) pivot = ls.pivot[n * G + fg];
-        }
+        pivot = ls.pivot[n * G + fg];
+        fb.load(ls.part_s + n * ls.K1 * G + fg, ls.part_q + n * ls.K1 * G + fg,
+                fin_part ? fj : 0, tpg, G);
+        __builtin_amdgcn_sched_barrier(0);  // these first: the finalize waits for them only
     }
 
     // The parameter loads are issued next and the chunk's first batch of x
@@ -1103,13 +1150,22 @@ __global__ __launch_bounds__(NT) void gn_apply(
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) v[u] = L::template load<NTL>(x + o0 + u * T, A, tid);
     };
-    if (active && nb > 0) load_batch(a, off);
+    // A chunk with fewer than UNROLL whole tiles has one batch, the tail batch
+    // (its surplus slots re-reading the last whole tile): it is issued here
+    // too, so that its round trip also overlaps the parameters'.
+    auto load_tail = [&](L (&v)[UNROLL], int64_t o0, int rem) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            v[u] = L::template load<NTL>(x + o0 + (u < rem ? u : rem - 1) * T, A, tid);
+    };
+    const int first = nb > 0 ? UNROLL : static_cast<int>(cr.t_full_end - tt);
+    if (active && first > 0) load_tail(a, off, first);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (FIN) {
         __shared__ float red_s[kThreads], red_q[kThreads];
         __shared__ float s_mean[kThreads], s_rstd[kThreads];
         float as = 0.0f, aq = 0.0f;
-        if (fin_has && fj < ls.K1) fb.add(fj, tpg, ls.K1, as, aq);
+        fb.add(fin_part ? fj : 0, tpg, fin_part ? ls.K1 : 0, as, aq);
         finalize_groups(as, aq, fin_has, fj, fg, G, tpg, pivot, ls.inv_m, ls.eps, red_s, red_q,
                         tid, s_mean + fg, s_rstd + fg);
         __syncthreads();
@@ -1166,19 +1222,17 @@ __global__ __launch_bounds__(NT) void gn_apply(
     }
     if (tt < cr.t_full_end) {
         // Fewer than UNROLL whole tiles left: one batch of loads (the surplus
-        // re-reading the last whole tile, before any store of the batch), and
-        // stores for the real tiles only.
+        // re-reading the last whole tile, before any store of the batch; in
+        // a chunk with no whole batch, loaded ahead of the fold), and stores
+        // for the real tiles only.
         const int rem = static_cast<int>(cr.t_full_end - tt);
-        L v[UNROLL];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-            v[u] = L::template load<NTL>(x + off + (u < rem ? u : rem - 1) * T, A, tid);
+        if (nb > 0) load_tail(a, off, rem);
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             if (u < rem) {
                 float o[S];
 #pragma unroll
-                for (int j = 0; j < S; ++j) o[j] = transform1<SILU>(v[u].get(j), sc[j], sh[j]);
+                for (int j = 0; j < S; ++j) o[j] = transform1<SILU>(a[u].get(j), sc[j], sh[j]);
                 L::template store<NTS>(y + off + u * T, A, tid, o);
             }
         }
@@ -1301,7 +1355,10 @@ __global__ __launch_bounds__(kStripThreads) void gn_strip(
         s[j] = 0.0f;
         q[j] = 0.0f;
     }
-    // gamma / beta of the lane's channels: issued now, used after the reduction
+    // gamma / beta of the lane's channels: issued now, used after the reduction.
+    // The loads of x are already in flight and the sums wait for them anyway,
+    // so here a branch on the element type costs little, and the typed loads
+    // take fewer address instructions than AffineReader's (measured faster).
     SlotParams<W> pr;
     {
         const void *gp = af.gamma ? af.gamma : static_cast<const void *>(x);
@@ -1321,6 +1378,8 @@ __global__ __launch_bounds__(kStripThreads) void gn_strip(
                 pr.b[j] = static_cast<const uint16_t *>(bp)[(c0 + j) * bs];
             }
         }
+#pragma unroll
+        for (int j = 0; j < W; ++j) pr.hg[j] = pr.hb[j] = 0;  // each value at bit 0
     }
 #pragma unroll
     for (int k = 0; k < kStripPieces; ++k) {

@@ -190,6 +190,10 @@ def check_plan(N, L, C, G, dtype):
         kk_last = max(kk for j in range(tpg) for kk in range(j, K, FINALIZE_BATCH * tpg))
         top = ((N - 1) * K + kk_last + (FINALIZE_BATCH - 1) * tpg) * G + G - 1
         assert top < nparts + pad
+        # the late finalize: a thread with no part (j >= K1, or a thread past
+        # tpg*G) loads part 0's batch and adds none of it -- no higher
+        top0 = ((N - 1) * K + (FINALIZE_BATCH - 1) * tpg) * G + G - 1
+        assert top0 <= top
     # arrival counters: one word per sample, or a two-level count of 8 groups
     # plus a total, each on its own 128-byte line, when a sample has >= 64 chunks
     words = N * ((8 + 1) * 32 if p["K1"] >= 64 else 1)
