@@ -124,7 +124,10 @@ typedef enum gn_dtype {
  * GN_AFFINE_* value, or with GN_AFFINE_F32, they point at C fp32 values,
  * 4-byte aligned.  A misaligned gamma or beta is GN_UNSUPPORTED; a dtype
  * argument with other bits set, or two GN_AFFINE_* values, is
- * GN_INVALID_ARGUMENT. */
+ * GN_INVALID_ARGUMENT.  The kernels read each 16-bit value through the
+ * aligned 4-byte word that holds it, so the 2 bytes just before the first
+ * or after the last value of a 16-bit array may be read (never written, and
+ * never across a page). */
 enum {
     GN_AFFINE_F32 = 0x10,
     GN_AFFINE_BF16 = 0x20,
